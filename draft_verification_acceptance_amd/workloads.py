@@ -1,0 +1,333 @@
+"""Seeded synthetic verify workloads (inputs only; no verify / accept / commit arithmetic lives here).
+
+Both the HIP library's tests / bench and the CPU oracle consume these arrays; neither side's code is used
+to make them. Shapes follow the workloads the pages describe: Qwen-family vocab 151,936 and Llama-3 vocab
+128,256; DFlash blocks of 16 (anchor + 15); DSpark / EAGLE chains of 7-8; EAGLE trees of 64 nodes;
+high-concurrency ragged batches with per-request draft length 0..15.
+
+Recipe (all numpy PCG64; seed = 1000*k for workload k; np.random.SeedSequence(seed).spawn(B + 1): child 0
+drives the batch structure, child b+1 drives request b and is split again into logits / noise / tokens /
+uniforms streams, so requests can be generated independently and in parallel):
+  * target logits  3*N(0,1) per entry, plus 8 added to one uniformly chosen token per row
+                   (tiny workload: N(0, 2^2), float32, no planted token);
+  * draft logits   target (float32, before rounding) + N(0, sigma^2);
+  * bf16           round-to-nearest-even of the float32 values (stored as uint16 bit patterns);
+  * draft tokens   sampling workloads: d_{j+1} ~ q_j = softmax(stored draft row j / T), drawn in float64
+                   with np.searchsorted over the cumulative sum (the drafter's own sampling, so d ~ q exactly
+                   as the verifier sees q); greedy block workload: a planted accepted prefix (see
+                   block_greedy); trees: EAGLE-style top-c expansion (see tree);
+  * uniforms       Generator.random(dtype=float32), in [0, 1).
+"""
+from __future__ import annotations
+
+import os
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass, field
+
+import numpy as np
+
+QWEN_VOCAB = 151936
+LLAMA3_VOCAB = 128256
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bit patterns (uint16), round to nearest, ties to even (finite inputs)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    rounded = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
+    return rounded.astype(np.uint16)
+
+
+def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
+    return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def _pool_map(fn, items, parallel: bool):
+    items = list(items)
+    if not parallel or len(items) < 4:
+        return [fn(i) for i in items]
+    workers = max(1, min(16, os.cpu_count() or 1))
+    with ThreadPoolExecutor(workers) as ex:
+        return list(ex.map(fn, items))
+
+
+def _target_rows(rng: np.random.Generator, n: int, V: int, planted: bool, scale: float) -> np.ndarray:
+    x = rng.standard_normal((n, V), dtype=np.float32)
+    x *= np.float32(scale)
+    if planted and n:
+        cols = rng.integers(0, V, size=n)
+        x[np.arange(n), cols] += np.float32(8.0)
+    return x
+
+
+def _draw_from_rows(rows_bits_or_f32: np.ndarray, temperature: float, u: np.ndarray) -> np.ndarray:
+    """The drafter's sampling: token ~ softmax(row / T) per row (float64, inverse CDF via searchsorted)."""
+    out = np.empty(len(rows_bits_or_f32), np.int32)
+    for i, row in enumerate(rows_bits_or_f32):
+        x = (bf16_to_f32(row) if row.dtype == np.uint16 else row).astype(np.float64) / temperature
+        e = np.exp(x - x.max())
+        cdf = np.cumsum(e)
+        k = int(np.searchsorted(cdf, float(u[i]) * cdf[-1], side="right"))
+        out[i] = min(k, len(cdf) - 1)
+    return out
+
+
+@dataclass
+class ChainWorkload:
+    name: str
+    vocab: int
+    batch: int
+    offsets: np.ndarray          # int32 [B+1]
+    target: np.ndarray           # [T_rows, V] uint16 (bf16 bits) or float32
+    draft: np.ndarray | None     # [T_rows - B, V] or None (greedy-only workloads)
+    draft_tokens: np.ndarray     # int32 [T_rows - B]
+    u_accept: np.ndarray         # float32 [T_rows - B]
+    u_final: np.ndarray          # float32 [B]
+    temperature: float
+    modes: tuple
+    max_verify_len: int
+    planted_r: np.ndarray | None = None     # block_greedy only: accept length fixed by construction
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def total_rows(self) -> int:
+        return int(self.offsets[-1])
+
+    @property
+    def dtype(self) -> str:
+        return "bf16" if self.target.dtype == np.uint16 else "f32"
+
+    def algorithmic_bytes(self, mode: str) -> int:
+        """Every target row (and draft row in rejection mode) read once."""
+        rows = self.total_rows + (self.total_rows - self.batch if mode == "rejection" else 0)
+        return rows * self.vocab * self.target.itemsize
+
+
+@dataclass
+class TreeWorkload:
+    name: str
+    vocab: int
+    batch: int
+    n_nodes: int
+    target: np.ndarray           # [B*N, V]
+    parents: np.ndarray          # int32 [B*N]
+    tokens: np.ndarray           # int32 [B*N]
+    u_accept: np.ndarray         # float32 [B*N]
+    u_final: np.ndarray          # float32 [B]
+    temperature: float
+    modes: tuple = ("greedy", "target_only")
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def total_rows(self) -> int:
+        return self.batch * self.n_nodes
+
+    @property
+    def dtype(self) -> str:
+        return "bf16" if self.target.dtype == np.uint16 else "f32"
+
+    def algorithmic_bytes(self, mode: str) -> int:
+        return self.total_rows * self.vocab * self.target.itemsize
+
+
+def _chain_from_lengths(name, seed, kids, lens, V, *, bf16, planted, scale, draft_sigma, temperature,
+                        modes, max_len, parallel):
+    B = len(lens)
+    offsets = np.zeros(B + 1, np.int32)
+    offsets[1:] = np.cumsum(lens)
+    T = int(offsets[-1])
+    D = T - B
+    tdtype = np.uint16 if bf16 else np.float32
+    target = np.empty((T, V), tdtype)
+    draft = np.empty((D, V), tdtype) if draft_sigma is not None else None
+    tokens = np.empty(D, np.int32)
+    u_accept = np.empty(D, np.float32)
+    u_final = np.empty(B, np.float32)
+
+    def one(b):
+        s_logit, s_noise, s_tok, s_unif = [np.random.Generator(np.random.PCG64(s)) for s in kids[b + 1].spawn(4)]
+        n = int(lens[b])
+        m = n - 1
+        t = _target_rows(s_logit, n, V, planted, scale)
+        lo, dlo = int(offsets[b]), int(offsets[b]) - b
+        target[lo:lo + n] = bf16_bits(t) if bf16 else t
+        if draft is not None and m > 0:
+            d = t[:m] + s_noise.standard_normal((m, V), dtype=np.float32) * np.float32(draft_sigma)
+            draft[dlo:dlo + m] = bf16_bits(d) if bf16 else d
+            tokens[dlo:dlo + m] = _draw_from_rows(draft[dlo:dlo + m], temperature,
+                                                  s_tok.random(m, dtype=np.float32))
+        u_accept[dlo:dlo + m] = s_unif.random(m, dtype=np.float32)
+        u_final[b] = s_unif.random(dtype=np.float32)
+
+    _pool_map(one, range(B), parallel)
+    return ChainWorkload(name, V, B, offsets, target, draft, tokens, u_accept, u_final, temperature, modes,
+                         max_len, meta={"seed": seed})
+
+
+def tiny_chain(seed: int = 1000, batch: int = 4, m: int = 4, vocab: int = 32) -> ChainWorkload:
+    """Tiny chain: B 4, m 4 (verify length 5), V 32, float32 logits; target ~ N(0, 2^2), draft = target +
+    N(0, 0.5^2), T 1.0; drafts drawn from q; both greedy and rejection run on the same inputs."""
+    kids = np.random.SeedSequence(seed).spawn(batch + 1)
+    lens = np.full(batch, m + 1, np.int64)
+    return _chain_from_lengths("tiny_chain", seed, kids, lens, vocab, bf16=False, planted=False, scale=2.0,
+                               draft_sigma=0.5, temperature=1.0, modes=("greedy", "rejection"),
+                               max_len=m + 1, parallel=False)
+
+
+def chain_rejection(seed: int = 2000, batch: int = 64, m: int = 7, vocab: int = QWEN_VOCAB,
+                    parallel: bool = True) -> ChainWorkload:
+    """Chain rejection sampling: B 64, m 7 (verify length 8), V 151,936, bf16; draft = target + N(0, 1),
+    T 1.0, topk 1."""
+    kids = np.random.SeedSequence(seed).spawn(batch + 1)
+    lens = np.full(batch, m + 1, np.int64)
+    return _chain_from_lengths("chain_rejection", seed, kids, lens, vocab, bf16=True, planted=True, scale=3.0,
+                               draft_sigma=1.0, temperature=1.0, modes=("rejection",), max_len=m + 1,
+                               parallel=parallel)
+
+
+def ragged(seed: int = 5000, batch: int = 512, m_max: int = 15, vocab: int = QWEN_VOCAB,
+           temperature: float = 0.7, parallel: bool = True) -> ChainWorkload:
+    """High-concurrency ragged verify: B 512, m_i ~ U{0..15}, V 151,936, bf16 target and draft;
+    draft = target + N(0, 0.8^2), T 0.7, rejection; rows packed by offsets."""
+    kids = np.random.SeedSequence(seed).spawn(batch + 1)
+    s_struct = np.random.Generator(np.random.PCG64(kids[0]))
+    lens = s_struct.integers(0, m_max + 1, size=batch) + 1
+    return _chain_from_lengths("ragged", seed, kids, lens, vocab, bf16=True, planted=True, scale=3.0,
+                               draft_sigma=0.8, temperature=temperature, modes=("rejection",),
+                               max_len=m_max + 1, parallel=parallel)
+
+
+def block_greedy(seed: int = 3000, batch: int = 32, block: int = 16, vocab: int = QWEN_VOCAB,
+                 tie_rate: float = 0.01, parallel: bool = True) -> ChainWorkload:
+    """DFlash-shaped greedy verify: B 32, block 16 (anchor + 15 drafts), V 151,936, bf16 target only.
+
+    Planted accept length r0 ~ Geometric(0.25) on {0, 1, ..} (P(r0 = k) = 0.75^k * 0.25) clipped to
+    block-1. d_1..d_r0 equal the target argmax (lowest id among the row's maxima, np.argmax); d_{r0+1} is
+    uniform over the ids outside the row's maximal set; later drafts are uniform. In `tie_rate` of the rows
+    the max value is copied to another random id (an exact tie); inside the prefix, half of the tied rows
+    make the draft use the HIGHER tied id, which ends the accepted prefix there. planted_r holds the accept
+    length these choices fix."""
+    kids = np.random.SeedSequence(seed).spawn(batch + 1)
+    s_struct = np.random.Generator(np.random.PCG64(kids[0]))
+    r0 = np.minimum(s_struct.geometric(0.25, size=batch) - 1, block - 1)
+    m = block - 1
+    offsets = (np.arange(batch + 1) * block).astype(np.int32)
+    T = batch * block
+    target = np.empty((T, vocab), np.uint16)
+    tokens = np.empty(batch * m, np.int32)
+    planted = np.empty(batch, np.int64)
+    n_ties = np.zeros(batch, np.int64)
+
+    def one(b):
+        s_logit, s_noise, s_tok, s_unif = [np.random.Generator(np.random.PCG64(s)) for s in kids[b + 1].spawn(4)]
+        rows = bf16_bits(_target_rows(s_logit, block, vocab, True, 3.0))
+        tie = s_noise.random(block) < tie_rate
+        use_high = s_noise.random(block) < 0.5
+        r_exp = int(r0[b])
+        for j in range(block):
+            f = bf16_to_f32(rows[j])
+            top = int(np.argmax(f))
+            if tie[j]:
+                other = int(s_noise.integers(0, vocab - 1))
+                other += other >= top
+                rows[j, other] = rows[j, top]
+                n_ties[b] += 1
+        for j in range(1, m + 1):           # d_j is judged by row j-1
+            f = bf16_to_f32(rows[j - 1])
+            maxset = np.flatnonzero(f == f.max())
+            if j <= r0[b]:
+                d = int(maxset[0])
+                if tie[j - 1] and len(maxset) > 1 and use_high[j - 1]:
+                    d = int(maxset[-1])
+                    r_exp = min(r_exp, j - 1)
+            elif j == r0[b] + 1:
+                d = int(s_tok.integers(0, vocab - len(maxset)))
+                for t in maxset:            # skip the maximal ids
+                    d += d >= t
+            else:
+                d = int(s_tok.integers(0, vocab))
+            tokens[b * m + j - 1] = d
+        target[b * block:(b + 1) * block] = rows
+        planted[b] = r_exp
+
+    _pool_map(one, range(batch), parallel)
+    wl = ChainWorkload("block_greedy", vocab, batch, offsets, target, None, tokens,
+                       np.zeros(batch * m, np.float32), np.zeros(batch, np.float32), 1.0, ("greedy",), block,
+                       planted_r=planted, meta={"seed": seed, "tie_rows": int(n_ties.sum())})
+    return wl
+
+
+def tree(seed: int = 4000, batch: int = 32, n_nodes: int = 64, vocab: int = LLAMA3_VOCAB, max_depth: int = 8,
+         max_branch: int = 8, temperature: float = 1.0, bf16: bool = True, parallel: bool = True) -> TreeWorkload:
+    """EAGLE-style tree verify: B 32, 64 nodes per request including the root, V 128,256, bf16 target.
+
+    parent[i] is uniform over the earlier nodes j with depth(j) < max_depth and fewer than max_branch
+    children. A node with c children gives them, in child-index order, the top-c ids (distinct, by value
+    descending, lowest id first among equal values) of its own target row plus N(0, 1) noise (a stand-in
+    for a draft's top-k expansion). The root's token is random and unused."""
+    kids = np.random.SeedSequence(seed).spawn(batch + 1)
+    N = n_nodes
+    tdtype = np.uint16 if bf16 else np.float32
+    target = np.empty((batch * N, vocab), tdtype)
+    parents = np.empty(batch * N, np.int32)
+    tokens = np.empty(batch * N, np.int32)
+    u_accept = np.empty(batch * N, np.float32)
+    u_final = np.empty(batch, np.float32)
+
+    def one(b):
+        s_logit, s_noise, s_tok, s_unif = [np.random.Generator(np.random.PCG64(s)) for s in kids[b + 1].spawn(4)]
+        x = _target_rows(s_logit, N, vocab, True, 3.0)
+        rows = bf16_bits(x) if bf16 else x
+        par = np.full(N, -1, np.int64)
+        depth = np.zeros(N, np.int64)
+        nchild = np.zeros(N, np.int64)
+        for i in range(1, N):
+            cand = [j for j in range(i) if depth[j] < max_depth and nchild[j] < max_branch]
+            p = int(cand[int(s_tok.integers(0, len(cand)))])
+            par[i] = p
+            depth[i] = depth[p] + 1
+            nchild[p] += 1
+        tok = np.zeros(N, np.int64)
+        tok[0] = s_tok.integers(0, vocab)
+        for j in range(N):
+            kids_j = [i for i in range(j + 1, N) if par[i] == j]
+            if not kids_j:
+                continue
+            base = bf16_to_f32(rows[j]) if bf16 else rows[j]
+            noisy = base + s_noise.standard_normal(vocab, dtype=np.float32)
+            c = len(kids_j)
+            kth = np.partition(noisy, vocab - c)[vocab - c]
+            cand = np.flatnonzero(noisy >= kth)
+            order = np.lexsort((cand, -noisy[cand]))
+            for i, t in zip(kids_j, cand[order][:c]):
+                tok[i] = int(t)
+        sl = slice(b * N, (b + 1) * N)
+        target[sl] = rows
+        parents[sl] = par
+        tokens[sl] = tok
+        u_accept[sl] = s_unif.random(N, dtype=np.float32)
+        u_final[b] = s_unif.random(dtype=np.float32)
+
+    _pool_map(one, range(batch), parallel)
+    return TreeWorkload("tree", vocab, batch, N, target, parents, tokens, u_accept, u_final, temperature,
+                        meta={"seed": seed})
+
+
+def verify_slots_for(total_rows: int, seed: int = 7) -> np.ndarray:
+    """Synthetic KV slot ids of the verify rows (a shuffled range, int64)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return rng.permutation(np.arange(10_000, 10_000 + 4 * total_rows, 4, dtype=np.int64))[:total_rows]
+
+
+def seq_lens_for(batch: int, seed: int = 8) -> np.ndarray:
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return rng.integers(16, 4096, size=batch).astype(np.int32)
+
+
+# Full-size workloads (name -> builder); each builder's defaults are the full shapes.
+FULL = {
+    "tiny_chain": tiny_chain,
+    "chain_rejection": chain_rejection,
+    "block_greedy": block_greedy,
+    "tree": tree,
+    "ragged": ragged,
+}

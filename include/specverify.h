@@ -1,0 +1,242 @@
+/*
+ * specverify.h — C ABI of the speculative-decoding verify / accept / commit path (gfx950, HIP).
+ *
+ * Sources (web pages; cited by page and section):
+ *   [EAGLE→DFlash2]  tom-jerr.github.io, "从 EAGLE 到 DFlash 2：SGLang 与 SpecForge 的投机解码训练和推理"
+ *   [DSpark]         ggaaooppeenngg.github.io, "DSpark：半自回归 + 置信度调度的 Speculative Decoding 深度分析"
+ *   [DFlash]         astro-wiki.dev.mem.ac, "DFlash"
+ *   [SpecDec]        zdszero.github.io, "speculative_decoding"
+ *
+ * One verify round (the draft → verify → commit loop of [SpecDec] "抽象：draft → verify → commit" and
+ * [EAGLE→DFlash2] §1.1): the target has scored the verify rows [anchor, d1 .. dm] in one forward, so row j
+ * holds the logits that judge d_{j+1} and the last row yields the bonus token. This library decides the
+ * accepted prefix, draws the correction / bonus token and produces the KV-slot lists to commit.
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer in an argument struct is a DEVICE pointer owned by the caller, except where noted.
+ *     The library never allocates device memory and never synchronises: all work is enqueued on `stream`
+ *     (NULL = the null stream) and outputs are valid once the stream reaches that point.
+ *   - Logits are row-major [rows, vocab] with row stride == vocab elements, dtype SPEC_DTYPE_F32 (IEEE
+ *     float) or SPEC_DTYPE_BF16 (bfloat16 bit patterns, 2 bytes). Token ids are int32 in [0, vocab).
+ *   - The return code reports only what the host can see (argument shapes, null pointers, enums,
+ *     workspace size, launch failures). Problems in the DATA never abort: they set bits in the per-request
+ *     `status` output (SPEC_ST_*), and the call still runs to completion.
+ *   - Random decisions use caller-supplied uniforms in [0,1) (fp32). Given the uniforms the result is a
+ *     deterministic function of the inputs: one uniform per row under test (`u_accept`) and one per
+ *     request for the single final draw (`u_final`).
+ *   - A workspace serves one call at a time. Its first use must see it zero-filled (spec_workspace_init
+ *     does that); every call leaves it ready for the next call on the same stream.
+ */
+#ifndef SPECVERIFY_H
+#define SPECVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same opaque types as the HIP runtime headers declare. */
+typedef struct ihipStream_t* hipStream_t;
+typedef struct ihipEvent_t* hipEvent_t;
+
+#define SPEC_ABI_VERSION 1
+
+/* Host-visible return codes. */
+typedef enum spec_status {
+  SPEC_OK = 0,
+  SPEC_EINVAL = 1,        /* null pointer where one is required, or a size / count out of range          */
+  SPEC_EDTYPE = 2,        /* dtype is neither SPEC_DTYPE_F32 nor SPEC_DTYPE_BF16                          */
+  SPEC_EUNSUPPORTED = 3,  /* valid request this library does not implement (mode/kind pair, thresholds) */
+  SPEC_EWORKSPACE = 4,    /* workspace NULL or smaller than spec_workspace_bytes()                        */
+  SPEC_ELAUNCH = 5,       /* a kernel launch or event record returned an error                           */
+} spec_status;
+
+typedef enum spec_dtype { SPEC_DTYPE_F32 = 0, SPEC_DTYPE_BF16 = 1 } spec_dtype;
+
+/*
+ * Verify modes.
+ *   GREEDY       accept d_j while d_j == argmax(row j-1); the first mismatch is replaced by that argmax and
+ *                a fully accepted draft gets argmax(row m) as bonus. Ties go to the LOWEST token id.
+ *                Chain or tree. [SpecDec] "为什么结果不受 draft 影响" (verify_tree_greedy; a chain is a
+ *                tree with one child per node); [EAGLE→DFlash2] §1.2 (same numerics and tie-breaking).
+ *   REJECTION    chain only: accept d_j iff u_j < alpha_j = min(1, p_{j-1}(d_j)/q_{j-1}(d_j)); on the first
+ *                rejection draw from [p-q]_+ / sum[p-q]_+, after full acceptance draw the bonus from p_m.
+ *                p, q = softmax(logits / temperature). [EAGLE→DFlash2] §1.2 (alpha, residual p'),
+ *                §1.1 (m+1 tokens on full acceptance); [SpecDec] (chain_speculative_sampling, topk = 1).
+ *   TARGET_ONLY  tree only: judge children with the target probabilities alone (draft probabilities taken
+ *                as zero), thresholds single/acc = 1.0 only. [SpecDec] "为什么结果不受 draft 影响"
+ *                (tree_speculative_sampling_target_only). Rule used: walking down from the root, at node
+ *                `cur` add p_cur(token) of each child in ascending node order (a token already seen among
+ *                earlier siblings adds nothing) into acc and accept the first child with u_cur < acc; if
+ *                none is accepted draw from p_cur with the tried tokens zeroed; at a leaf draw from p_cur.
+ */
+typedef enum spec_mode { SPEC_MODE_GREEDY = 0, SPEC_MODE_REJECTION = 1, SPEC_MODE_TARGET_ONLY = 2 } spec_mode;
+
+typedef enum spec_kind { SPEC_KIND_CHAIN = 0, SPEC_KIND_TREE = 1, SPEC_KIND_COMMIT = 2 } spec_kind;
+
+/* Per-request status bits (output `status[b]`). */
+#define SPEC_ST_NONFINITE     (1u << 0) /* a NaN logit in one of the request's rows; in sampling modes also
+                                           +inf, or a row whose logits are all -inf                         */
+#define SPEC_ST_BAD_TOKEN     (1u << 1) /* a draft / node token outside [0, vocab); it is never accepted    */
+#define SPEC_ST_BAD_OFFSETS   (1u << 2) /* off[b] / off[b+1] inconsistent: then the whole batch's outputs
+                                           are unspecified (no memory outside the given buffers is touched) */
+#define SPEC_ST_BAD_PARENT    (1u << 3) /* tree: parent[0] != -1 or parent[i] not in [0, i); such a node is
+                                           nobody's child                                                   */
+#define SPEC_ST_BAD_UNIFORM   (1u << 4) /* a uniform that is NaN or outside [0,1); it is used as 0 if NaN,
+                                           else clamped to [0, 1 - 2^-24]                                    */
+#define SPEC_ST_ZERO_Q        (1u << 5) /* rejection: q(d) == 0 at an examined position (alpha = 1 if
+                                           p(d) > 0, else 0)                                                 */
+#define SPEC_ST_ZERO_RESIDUAL (1u << 6) /* the final draw's weights summed to 0; drawn from p instead        */
+#define SPEC_ST_NEAR_ALPHA    (1u << 7) /* diagnostic: |u - alpha| < 1e-5 at an examined accept test        */
+#define SPEC_ST_NEAR_CDF      (1u << 8) /* diagnostic: the final draw's u lies within 1e-5 of a CDF step    */
+#define SPEC_ST_BAD_ACCEPT    (1u << 9) /* commit: accept_len / accept_index outside the request's rows     */
+
+/*
+ * Chain verify (GREEDY or REJECTION).
+ *
+ * Request b owns target rows [off[b], off[b+1]) (the ragged packing of [EAGLE→DFlash2] §5.6.5: verify
+ * lens [4,2,6] -> offsets [0,4,6,12]); m_b = off[b+1] - off[b] - 1 >= 0 drafts. Draft-side arrays are
+ * packed with m_b entries per request starting at off[b] - b; entry j of request b belongs to d_{j+1}:
+ * draft_tokens[off[b]-b+j] = d_{j+1}, draft_logits row off[b]-b+j = the draft logits q_j that proposed
+ * d_{j+1}, u_accept[off[b]-b+j] = the uniform of the test of d_{j+1}.
+ *
+ * Outputs (indexed like the verify rows unless noted; entries past the accepted part are -1):
+ *   accept_len[b]             r = number of accepted drafts, 0 <= r <= m_b
+ *   bonus[b]                  the token emitted after the accepted drafts (correction or bonus)
+ *   out_tokens[off[b]+k]      k < r: d_{k+1}; k == r: bonus; k > r: -1
+ *   accept_index[off[b]+k]    k <= r: off[b]+k (global verify row whose KV is committed); else -1
+ *   status[b]                 SPEC_ST_* bits
+ *   accept_prob[off[b]-b+j]   opt.: alpha_{j+1} where tested (REJECTION), else -1
+ *   residual_mass[b]          opt.: sum of the final draw's weights (REJECTION), -1 in GREEDY
+ */
+typedef struct spec_chain_args {
+  const void* target_logits;     /* [total_rows, vocab]                                   */
+  const int32_t* target_offsets; /* [batch+1], off[0] = 0, off[batch] = total_rows           */
+  const void* draft_logits;      /* [total_rows - batch, vocab]; REJECTION only (else NULL) */
+  const int32_t* draft_tokens;   /* [total_rows - batch]                                   */
+  const float* u_accept;         /* [total_rows - batch]; REJECTION only                   */
+  const float* u_final;          /* [batch]; REJECTION only                                */
+  int32_t* accept_len;           /* [batch]                                                */
+  int32_t* bonus;                /* [batch]                                                */
+  int32_t* out_tokens;           /* [total_rows]                                           */
+  int32_t* accept_index;         /* [total_rows]                                           */
+  uint32_t* status;              /* [batch]                                                */
+  float* accept_prob;            /* optional [total_rows - batch]                          */
+  float* residual_mass;          /* optional [batch]                                       */
+  void* workspace;               /* >= spec_workspace_bytes(SPEC_KIND_CHAIN, ...) bytes    */
+  size_t workspace_bytes;
+  hipEvent_t* profile_events;    /* HOST array, optional: n_profile_events events recorded on
+                                    `stream` before the first kernel, between kernels and after
+                                    the last one (n = kernels + 1; see spec_kernel_count)      */
+  int64_t total_rows;            /* T_rows = sum_b (m_b + 1)                                */
+  int64_t vocab;                 /* V, 1 <= V <= 2^22                                       */
+  int32_t batch;                 /* B >= 0 (B == 0: nothing is launched)                    */
+  int32_t max_verify_len;        /* upper bound on m_b + 1, 1..1024; a longer request is
+                                    reported as SPEC_ST_BAD_OFFSETS                        */
+  int32_t dtype;                 /* spec_dtype                                             */
+  int32_t mode;                  /* SPEC_MODE_GREEDY or SPEC_MODE_REJECTION                */
+  float temperature;             /* REJECTION: finite, > 0; logits are divided by it        */
+  int32_t n_profile_events;
+} spec_chain_args;
+
+/*
+ * Tree verify (GREEDY or TARGET_ONLY). Request b owns n_nodes verify rows b*N .. b*N+N-1 (node-major),
+ * node 0 is the anchor (root), node i > 0 has parent[b*N+i] in [0, i) and token tokens[b*N+i]; row i
+ * holds the target logits that judge node i's children ([EAGLE→DFlash2] §2.4 and §3.4: tree attention
+ * gives every node its own distribution in one forward). Among equal candidates the lowest node index
+ * wins. accept_index lists the path [0, n_1, .., n_r] as global rows b*N + n_k (compaction source for
+ * the topk > 1 accepted path, [EAGLE→DFlash2] §8.2).
+ *
+ * Outputs as for the chain, sized batch*N (accept_prob[b*N+c] = acc when child c was tested in
+ * TARGET_ONLY, else -1; residual_mass is -1 in GREEDY).
+ */
+typedef struct spec_tree_args {
+  const void* target_logits; /* [batch*n_nodes, vocab]                          */
+  const int32_t* parents;    /* [batch*n_nodes]                                 */
+  const int32_t* tokens;     /* [batch*n_nodes] (node 0's entry is ignored)     */
+  const float* u_accept;     /* [batch*n_nodes]: uniform used at node cur; TARGET_ONLY */
+  const float* u_final;      /* [batch]; TARGET_ONLY                            */
+  int32_t* accept_len;       /* [batch]                                         */
+  int32_t* bonus;            /* [batch]                                         */
+  int32_t* out_tokens;       /* [batch*n_nodes]                                 */
+  int32_t* accept_index;     /* [batch*n_nodes]                                 */
+  uint32_t* status;          /* [batch]                                         */
+  float* accept_prob;        /* optional [batch*n_nodes]                        */
+  float* residual_mass;      /* optional [batch]                                */
+  void* workspace;
+  size_t workspace_bytes;
+  hipEvent_t* profile_events; /* HOST array, optional (see spec_chain_args)      */
+  int64_t vocab;
+  int32_t batch;
+  int32_t n_nodes;           /* N, 1..1024                                      */
+  int32_t dtype;
+  int32_t mode;              /* SPEC_MODE_GREEDY or SPEC_MODE_TARGET_ONLY        */
+  float temperature;         /* TARGET_ONLY: finite, > 0                         */
+  float threshold_single;    /* TARGET_ONLY: must be 1.0 (else SPEC_EUNSUPPORTED) */
+  float threshold_acc;       /* TARGET_ONLY: must be 1.0 (else SPEC_EUNSUPPORTED) */
+  int32_t n_profile_events;
+} spec_tree_args;
+
+/*
+ * KV commit compaction ([EAGLE→DFlash2] §5.6.6 and §8.1: commit_lens = correct_len + 1, the KV of the
+ * old anchor plus the r accepted drafts; [SpecDec] "实现：共享的骨架": accepted KV moves to contiguous
+ * positions after seq_lens, rejected slots are reused later).
+ *   commit_offsets[b]            exclusive scan of (accept_len[b] + 1); commit_offsets[batch] = total
+ *   src_slots[commit_offsets[b]+k] = verify_slots[accept_index[row_offsets[b]+k]],  k = 0..accept_len[b]
+ *   dst_pos[commit_offsets[b]+k]   = seq_lens[b] + k
+ *   new_seq_lens[b]              = seq_lens[b] + accept_len[b] + 1
+ *   evict_offsets[b], evict_slots  optional: the request's verify rows NOT listed in its accept_index, in
+ *                                  ascending row order (their KV must stop being visible, §8.2)
+ * row_offsets has the chain meaning (trees: [0, N, 2N, ...]). capacity (length of src_slots / dst_pos /
+ * evict_slots) must be >= total_rows. Invalid accept_len / accept_index set SPEC_ST_BAD_ACCEPT.
+ */
+typedef struct spec_commit_args {
+  const int32_t* row_offsets;  /* [batch+1]                    */
+  const int32_t* accept_len;   /* [batch]                      */
+  const int32_t* accept_index; /* [total_rows]                 */
+  const int64_t* verify_slots; /* [total_rows] KV slot per verify row */
+  const int32_t* seq_lens;     /* [batch] committed length before this round */
+  int32_t* commit_offsets;     /* [batch+1]                    */
+  int64_t* src_slots;          /* [capacity]                   */
+  int32_t* dst_pos;            /* [capacity]                   */
+  int32_t* new_seq_lens;       /* [batch]                      */
+  uint32_t* status;            /* [batch]                      */
+  int64_t* evict_slots;        /* optional [capacity]          */
+  int32_t* evict_offsets;      /* optional [batch+1]           */
+  hipEvent_t* profile_events;  /* HOST array, optional          */
+  int64_t total_rows;
+  int64_t capacity;
+  int32_t batch;
+  int32_t max_verify_len;      /* upper bound on rows per request, 1..1024 */
+  int32_t n_profile_events;
+  int32_t reserved;
+} spec_commit_args;
+
+spec_status spec_verify_chain(const spec_chain_args* args, hipStream_t stream);
+spec_status spec_verify_tree(const spec_tree_args* args, hipStream_t stream);
+spec_status spec_commit_indices(const spec_commit_args* args, hipStream_t stream);
+
+/* Workspace size in bytes for a call of this kind/mode and size (0 for SPEC_KIND_COMMIT). For trees pass
+   total_rows = batch * n_nodes. Returns 0 for invalid arguments. Pure host function. */
+size_t spec_workspace_bytes(int32_t kind, int32_t mode, int64_t total_rows, int64_t vocab, int32_t batch,
+                            int32_t max_verify_len);
+
+/* Zero-fills `bytes` of device memory at `workspace` with a kernel on `stream` (no memset node). */
+spec_status spec_workspace_init(void* workspace, size_t bytes, hipStream_t stream);
+
+/* Number of kernels a call of this kind/mode launches (events: kernels + 1). Pure host function. */
+int32_t spec_kernel_count(int32_t kind, int32_t mode);
+
+/* Static string naming a return code. Pure host function. */
+const char* spec_status_string(spec_status s);
+
+/* SPEC_ABI_VERSION the library was built with, and sizeof of the argument structs (ABI checks). */
+int32_t spec_abi_version(void);
+size_t spec_args_size(int32_t kind);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SPECVERIFY_H */
