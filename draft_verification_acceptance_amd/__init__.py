@@ -1,0 +1,383 @@
+"""Speculative-decoding verify / accept / commit on MI355X (gfx950).
+
+Thin ctypes binding of libspecverify.so (the C ABI declared in include/specverify.h). Every step of the
+verify path runs in the library's HIP kernels; this module only checks and marshals torch tensors (device
+memory) and passes the current torch stream. There is no CPU fallback: without the built library every
+entry point raises.
+
+    verify_chain(...)    greedy or rejection-sampling verify of ragged chains (spec_verify_chain)
+    verify_tree(...)     greedy or target-only verify of draft trees (spec_verify_tree)
+    commit_indices(...)  KV commit compaction of a verify round (spec_commit_indices)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "SpecError", "verify_chain", "verify_tree", "commit_indices", "workspace", "workspace_bytes",
+    "workspace_init", "kernel_count", "status_string", "abi_version", "library_path", "HipEvents",
+    "MODES", "ST",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_PKG, "libspecverify.so")
+
+ABI_VERSION = 1
+MODES = {"greedy": 0, "rejection": 1, "target_only": 2}
+KIND_CHAIN, KIND_TREE, KIND_COMMIT = 0, 1, 2
+DTYPES = {torch.float32: 0, torch.bfloat16: 1}
+
+
+class ST:
+    """Per-request status bits (SPEC_ST_*)."""
+    NONFINITE = 1 << 0
+    BAD_TOKEN = 1 << 1
+    BAD_OFFSETS = 1 << 2
+    BAD_PARENT = 1 << 3
+    BAD_UNIFORM = 1 << 4
+    ZERO_Q = 1 << 5
+    ZERO_RESIDUAL = 1 << 6
+    NEAR_ALPHA = 1 << 7
+    NEAR_CDF = 1 << 8
+    BAD_ACCEPT = 1 << 9
+
+
+class SpecError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"{message} (code {code})")
+        self.code = code
+
+
+_vp, _i32, _i64, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+
+
+class ChainArgs(ctypes.Structure):
+    _fields_ = [("target_logits", _vp), ("target_offsets", _vp), ("draft_logits", _vp), ("draft_tokens", _vp),
+                ("u_accept", _vp), ("u_final", _vp), ("accept_len", _vp), ("bonus", _vp), ("out_tokens", _vp),
+                ("accept_index", _vp), ("status", _vp), ("accept_prob", _vp), ("residual_mass", _vp),
+                ("workspace", _vp), ("workspace_bytes", _sz), ("profile_events", _vp), ("total_rows", _i64),
+                ("vocab", _i64), ("batch", _i32), ("max_verify_len", _i32), ("dtype", _i32), ("mode", _i32),
+                ("temperature", _f32), ("n_profile_events", _i32)]
+
+
+class TreeArgs(ctypes.Structure):
+    _fields_ = [("target_logits", _vp), ("parents", _vp), ("tokens", _vp), ("u_accept", _vp), ("u_final", _vp),
+                ("accept_len", _vp), ("bonus", _vp), ("out_tokens", _vp), ("accept_index", _vp), ("status", _vp),
+                ("accept_prob", _vp), ("residual_mass", _vp), ("workspace", _vp), ("workspace_bytes", _sz),
+                ("profile_events", _vp), ("vocab", _i64), ("batch", _i32), ("n_nodes", _i32), ("dtype", _i32),
+                ("mode", _i32), ("temperature", _f32), ("threshold_single", _f32), ("threshold_acc", _f32),
+                ("n_profile_events", _i32)]
+
+
+class CommitArgs(ctypes.Structure):
+    _fields_ = [("row_offsets", _vp), ("accept_len", _vp), ("accept_index", _vp), ("verify_slots", _vp),
+                ("seq_lens", _vp), ("commit_offsets", _vp), ("src_slots", _vp), ("dst_pos", _vp),
+                ("new_seq_lens", _vp), ("status", _vp), ("evict_slots", _vp), ("evict_offsets", _vp),
+                ("profile_events", _vp), ("total_rows", _i64), ("capacity", _i64), ("batch", _i32),
+                ("max_verify_len", _i32), ("n_profile_events", _i32), ("reserved", _i32)]
+
+
+_LIB = None
+
+
+def _lib():
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(library_path):
+        raise RuntimeError(f"{library_path} is not built; run `python -m draft_verification_acceptance_amd.build`")
+    lib = ctypes.CDLL(library_path)
+    lib.spec_verify_chain.argtypes = [ctypes.POINTER(ChainArgs), _vp]
+    lib.spec_verify_tree.argtypes = [ctypes.POINTER(TreeArgs), _vp]
+    lib.spec_commit_indices.argtypes = [ctypes.POINTER(CommitArgs), _vp]
+    for f in (lib.spec_verify_chain, lib.spec_verify_tree, lib.spec_commit_indices):
+        f.restype = ctypes.c_int
+    lib.spec_workspace_bytes.argtypes = [_i32, _i32, _i64, _i64, _i32, _i32]
+    lib.spec_workspace_bytes.restype = _sz
+    lib.spec_workspace_init.argtypes = [_vp, _sz, _vp]
+    lib.spec_workspace_init.restype = ctypes.c_int
+    lib.spec_kernel_count.argtypes = [_i32, _i32]
+    lib.spec_kernel_count.restype = _i32
+    lib.spec_status_string.argtypes = [ctypes.c_int]
+    lib.spec_status_string.restype = ctypes.c_char_p
+    lib.spec_abi_version.argtypes = []
+    lib.spec_abi_version.restype = _i32
+    lib.spec_args_size.argtypes = [_i32]
+    lib.spec_args_size.restype = _sz
+    if lib.spec_abi_version() != ABI_VERSION:
+        raise RuntimeError(f"libspecverify ABI {lib.spec_abi_version()} != binding ABI {ABI_VERSION}")
+    for kind, st in ((KIND_CHAIN, ChainArgs), (KIND_TREE, TreeArgs), (KIND_COMMIT, CommitArgs)):
+        if lib.spec_args_size(kind) != ctypes.sizeof(st):
+            raise RuntimeError(f"argument struct {st.__name__} size mismatch with the library")
+    _LIB = lib
+    return lib
+
+
+def abi_version() -> int:
+    return int(_lib().spec_abi_version())
+
+
+def status_string(code: int) -> str:
+    return _lib().spec_status_string(int(code)).decode()
+
+
+def kernel_count(kind: str, mode: str) -> int:
+    k = {"chain": KIND_CHAIN, "tree": KIND_TREE, "commit": KIND_COMMIT}[kind]
+    return int(_lib().spec_kernel_count(k, MODES.get(mode, 0)))
+
+
+def _check(code: int):
+    if code != 0:
+        raise SpecError(code, status_string(code))
+
+
+def workspace_bytes(kind: str, mode: str, total_rows: int, vocab: int, batch: int, max_verify_len: int) -> int:
+    k = {"chain": KIND_CHAIN, "tree": KIND_TREE}[kind]
+    return int(_lib().spec_workspace_bytes(k, MODES[mode], int(total_rows), int(vocab), int(batch),
+                                           int(max_verify_len)))
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def workspace_init(ws: torch.Tensor):
+    _check(_lib().spec_workspace_init(ws.data_ptr(), ws.numel() * ws.element_size(), _stream(ws.device)))
+
+
+def workspace(kind: str, mode: str, total_rows: int, vocab: int, batch: int, max_verify_len: int,
+              device="cuda") -> torch.Tensor:
+    """A zero-filled workspace for calls up to this size (reusable by later calls on the same stream)."""
+    n = workspace_bytes(kind, mode, total_rows, vocab, batch, max_verify_len)
+    if n == 0:
+        raise SpecError(1, "invalid workspace request")
+    ws = torch.empty(n, dtype=torch.uint8, device=device)
+    workspace_init(ws)
+    return ws
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _req(t: torch.Tensor, name: str, dtype, n=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if n is not None and t.numel() != n:
+        raise ValueError(f"{name} must have {n} elements, got {t.numel()}")
+    return t
+
+
+class HipEvents:
+    """Timing events created through the HIP runtime, recorded by the library between its kernels."""
+
+    def __init__(self, n: int):
+        self._hip = ctypes.CDLL("libamdhip64.so")
+        self._hip.hipEventCreate.argtypes = [ctypes.POINTER(_vp)]
+        self._hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), _vp, _vp]
+        self._hip.hipEventSynchronize.argtypes = [_vp]
+        self._hip.hipEventDestroy.argtypes = [_vp]
+        self.arr = (_vp * n)()
+        for i in range(n):
+            h = _vp()
+            if self._hip.hipEventCreate(ctypes.byref(h)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.arr[i] = h
+        self.n = n
+
+    def pointer(self):
+        return ctypes.cast(self.arr, _vp)
+
+    def elapsed_ms(self, i: int, j: int) -> float:
+        self._hip.hipEventSynchronize(self.arr[j])
+        ms = ctypes.c_float()
+        if self._hip.hipEventElapsedTime(ctypes.byref(ms), self.arr[i], self.arr[j]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(ms.value)
+
+    def __del__(self):
+        try:
+            for i in range(self.n):
+                self._hip.hipEventDestroy(self.arr[i])
+        except Exception:
+            pass
+
+
+def _outputs(out, device, batch, rows, draft_rows, want_prob, want_resid):
+    if out is None:
+        out = {}
+    def get(name, n, dtype, fill=None):
+        t = out.get(name)
+        if t is None:
+            t = torch.empty(n, dtype=dtype, device=device)
+            out[name] = t
+        return _req(t, name, dtype, n, device)
+    get("accept_len", batch, torch.int32)
+    get("bonus", batch, torch.int32)
+    get("out_tokens", rows, torch.int32)
+    get("accept_index", rows, torch.int32)
+    get("status", batch, torch.int32)
+    if want_prob:
+        get("accept_prob", draft_rows, torch.float32)
+    if want_resid:
+        get("residual_mass", batch, torch.float32)
+    return out
+
+
+def verify_chain(target_logits: torch.Tensor, target_offsets: torch.Tensor, draft_tokens: torch.Tensor,
+                 mode: str = "greedy", *, draft_logits: torch.Tensor | None = None,
+                 u_accept: torch.Tensor | None = None, u_final: torch.Tensor | None = None,
+                 temperature: float = 1.0, max_verify_len: int | None = None, workspace_tensor=None,
+                 out: dict | None = None, accept_prob: bool = True, residual_mass: bool = True,
+                 events: HipEvents | None = None) -> dict:
+    """spec_verify_chain on torch tensors (launched on the current stream; asynchronous).
+
+    target_logits [T_rows, V] bf16/fp32; target_offsets int32 [B+1]; draft-side int32 tokens, float32
+    uniforms and logits packed with m_b entries per request from off[b]-b. Returns the output tensors."""
+    lib = _lib()
+    dev = target_logits.device
+    if target_logits.dim() != 2:
+        raise ValueError("target_logits must be [rows, vocab]")
+    if target_logits.dtype not in DTYPES:
+        raise TypeError("target_logits must be bfloat16 or float32")
+    _req(target_logits, "target_logits", target_logits.dtype, device=dev)
+    T, V = target_logits.shape
+    _req(target_offsets, "target_offsets", torch.int32, device=dev)
+    B = target_offsets.numel() - 1
+    D = T - B
+    if max_verify_len is None:
+        raise ValueError("max_verify_len (upper bound on m_b + 1) is required")
+    _req(draft_tokens, "draft_tokens", torch.int32, D, dev)
+    m = MODES[mode]
+    if mode == "rejection":
+        _req(draft_logits, "draft_logits", target_logits.dtype, D * V, dev)
+        _req(u_accept, "u_accept", torch.float32, D, dev)
+        _req(u_final, "u_final", torch.float32, B, dev)
+    if workspace_tensor is None:
+        workspace_tensor = workspace("chain", mode, T, V, B, max_verify_len, dev)
+    o = _outputs(out, dev, B, T, D, accept_prob, residual_mass)
+    a = ChainArgs()
+    a.target_logits = _ptr(target_logits)
+    a.target_offsets = _ptr(target_offsets)
+    a.draft_logits = _ptr(draft_logits)
+    a.draft_tokens = _ptr(draft_tokens)
+    a.u_accept = _ptr(u_accept)
+    a.u_final = _ptr(u_final)
+    a.accept_len, a.bonus = o["accept_len"].data_ptr(), o["bonus"].data_ptr()
+    a.out_tokens, a.accept_index = o["out_tokens"].data_ptr(), o["accept_index"].data_ptr()
+    a.status = o["status"].data_ptr()
+    a.accept_prob = _ptr(o.get("accept_prob")) if accept_prob else None
+    a.residual_mass = _ptr(o.get("residual_mass")) if residual_mass else None
+    a.workspace = workspace_tensor.data_ptr()
+    a.workspace_bytes = workspace_tensor.numel()
+    a.profile_events = events.pointer() if events is not None else None
+    a.n_profile_events = events.n if events is not None else 0
+    a.total_rows, a.vocab, a.batch = T, V, B
+    a.max_verify_len = int(max_verify_len)
+    a.dtype = DTYPES[target_logits.dtype]
+    a.mode = m
+    a.temperature = float(temperature)
+    _check(lib.spec_verify_chain(ctypes.byref(a), _stream(dev)))
+    return o
+
+
+def verify_tree(target_logits: torch.Tensor, parents: torch.Tensor, tokens: torch.Tensor, n_nodes: int,
+                mode: str = "greedy", *, u_accept=None, u_final=None, temperature: float = 1.0,
+                threshold_single: float = 1.0, threshold_acc: float = 1.0, workspace_tensor=None,
+                out: dict | None = None, accept_prob: bool = True, residual_mass: bool = True,
+                events: HipEvents | None = None) -> dict:
+    """spec_verify_tree on torch tensors: target_logits [B*N, V]; parents, tokens int32 [B*N]."""
+    lib = _lib()
+    dev = target_logits.device
+    if target_logits.dim() != 2 or target_logits.dtype not in DTYPES:
+        raise ValueError("target_logits must be a 2-D bfloat16 / float32 tensor")
+    _req(target_logits, "target_logits", target_logits.dtype, device=dev)
+    rows, V = target_logits.shape
+    N = int(n_nodes)
+    if N < 1 or rows % N:
+        raise ValueError("rows must be a multiple of n_nodes")
+    B = rows // N
+    _req(parents, "parents", torch.int32, rows, dev)
+    _req(tokens, "tokens", torch.int32, rows, dev)
+    if mode == "target_only":
+        _req(u_accept, "u_accept", torch.float32, rows, dev)
+        _req(u_final, "u_final", torch.float32, B, dev)
+    if workspace_tensor is None:
+        workspace_tensor = workspace("tree", mode, rows, V, B, N, dev)
+    o = _outputs(out, dev, B, rows, rows, accept_prob, residual_mass)
+    a = TreeArgs()
+    a.target_logits, a.parents, a.tokens = _ptr(target_logits), _ptr(parents), _ptr(tokens)
+    a.u_accept, a.u_final = _ptr(u_accept), _ptr(u_final)
+    a.accept_len, a.bonus = o["accept_len"].data_ptr(), o["bonus"].data_ptr()
+    a.out_tokens, a.accept_index = o["out_tokens"].data_ptr(), o["accept_index"].data_ptr()
+    a.status = o["status"].data_ptr()
+    a.accept_prob = _ptr(o.get("accept_prob")) if accept_prob else None
+    a.residual_mass = _ptr(o.get("residual_mass")) if residual_mass else None
+    a.workspace = workspace_tensor.data_ptr()
+    a.workspace_bytes = workspace_tensor.numel()
+    a.profile_events = events.pointer() if events is not None else None
+    a.n_profile_events = events.n if events is not None else 0
+    a.vocab, a.batch, a.n_nodes = V, B, N
+    a.dtype = DTYPES[target_logits.dtype]
+    a.mode = MODES[mode]
+    a.temperature = float(temperature)
+    a.threshold_single, a.threshold_acc = float(threshold_single), float(threshold_acc)
+    _check(lib.spec_verify_tree(ctypes.byref(a), _stream(dev)))
+    return o
+
+
+def commit_indices(row_offsets: torch.Tensor, accept_len: torch.Tensor, accept_index: torch.Tensor,
+                   verify_slots: torch.Tensor, seq_lens: torch.Tensor, *, max_verify_len: int,
+                   evict: bool = True, out: dict | None = None, events: HipEvents | None = None) -> dict:
+    """spec_commit_indices on torch tensors. Returns commit_offsets, src_slots, dst_pos, new_seq_lens,
+    status (and evict_offsets, evict_slots). src_slots / dst_pos are sized total_rows; the valid part is
+    commit_offsets[-1] entries long."""
+    lib = _lib()
+    dev = row_offsets.device
+    _req(row_offsets, "row_offsets", torch.int32, device=dev)
+    B = row_offsets.numel() - 1
+    _req(accept_len, "accept_len", torch.int32, B, dev)
+    T = accept_index.numel()
+    _req(accept_index, "accept_index", torch.int32, T, dev)
+    _req(verify_slots, "verify_slots", torch.int64, T, dev)
+    _req(seq_lens, "seq_lens", torch.int32, B, dev)
+    o = {} if out is None else out
+
+    def get(name, n, dtype):
+        t = o.get(name)
+        if t is None:
+            t = torch.empty(n, dtype=dtype, device=dev)
+            o[name] = t
+        return _req(t, name, dtype, n, dev)
+    get("commit_offsets", B + 1, torch.int32)
+    get("src_slots", T, torch.int64)
+    get("dst_pos", T, torch.int32)
+    get("new_seq_lens", B, torch.int32)
+    get("status", B, torch.int32)
+    if evict:
+        get("evict_offsets", B + 1, torch.int32)
+        get("evict_slots", T, torch.int64)
+    a = CommitArgs()
+    a.row_offsets, a.accept_len, a.accept_index = _ptr(row_offsets), _ptr(accept_len), _ptr(accept_index)
+    a.verify_slots, a.seq_lens = _ptr(verify_slots), _ptr(seq_lens)
+    a.commit_offsets, a.src_slots, a.dst_pos = _ptr(o["commit_offsets"]), _ptr(o["src_slots"]), _ptr(o["dst_pos"])
+    a.new_seq_lens, a.status = _ptr(o["new_seq_lens"]), _ptr(o["status"])
+    a.evict_slots = _ptr(o.get("evict_slots")) if evict else None
+    a.evict_offsets = _ptr(o.get("evict_offsets")) if evict else None
+    a.profile_events = events.pointer() if events is not None else None
+    a.n_profile_events = events.n if events is not None else 0
+    a.total_rows, a.capacity, a.batch = T, T, B
+    a.max_verify_len = int(max_verify_len)
+    _check(lib.spec_commit_indices(ctypes.byref(a), _stream(dev)))
+    return o

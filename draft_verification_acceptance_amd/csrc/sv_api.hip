@@ -1,0 +1,258 @@
+// C ABI entry points of libspecverify: host-side argument checks, workspace carve-up, kernel launches.
+// Nothing here allocates, synchronises or reads device memory.
+#include <math.h>
+
+#include <atomic>
+#include <chrono>
+
+#include "sv_internal.h"
+
+using namespace sv;
+
+namespace {
+
+constexpr double kLog2e = 1.4426950408889634;
+
+// Per-call epoch (never 0, the value of a zero-filled workspace); seeded from the clock so that a
+// workspace left by another process is not mistaken for this process's calls.
+uint32_t next_epoch() {
+  static std::atomic<uint32_t> ctr{uint32_t(std::chrono::steady_clock::now().time_since_epoch().count() * 2654435761u)};
+  uint32_t e;
+  do {
+    e = ctr.fetch_add(1u, std::memory_order_relaxed) + 1u;
+  } while (e == 0u);
+  return e;
+}
+
+bool bad_events(hipEvent_t* ev, int32_t n, int32_t kernels) {
+  if (n == 0) return false;
+  return ev == nullptr || n != kernels + 1;
+}
+
+spec_status record(hipEvent_t* ev, int32_t n, int32_t i, hipStream_t stream) {
+  if (n == 0) return SPEC_OK;
+  return hipEventRecord(ev[i], stream) == hipSuccess ? SPEC_OK : SPEC_ELAUNCH;
+}
+
+template <typename A>
+void fill_outputs(StatsParams& p, const A* a) {
+  p.accept_len = a->accept_len;
+  p.bonus = a->bonus;
+  p.out_tokens = a->out_tokens;
+  p.accept_index = a->accept_index;
+  p.status = a->status;
+  p.accept_prob = a->accept_prob;
+  p.residual_mass = a->residual_mass;
+}
+
+void carve(StatsParams& p, DrawParams& d, const Layout& lo, void* ws) {
+  char* w = static_cast<char*>(ws);
+  p.cnt = reinterpret_cast<unsigned long long*>(w + lo.off_cnt);
+  p.part = reinterpret_cast<Part*>(w + lo.off_part);
+  p.desc = reinterpret_cast<DrawDesc*>(w + lo.off_desc);
+  p.seen = reinterpret_cast<int32_t*>(w + lo.off_seen);
+  d.cnt2 = reinterpret_cast<unsigned long long*>(w + lo.off_cnt2);
+  d.desc = p.desc;
+  d.seg = reinterpret_cast<float2*>(w + lo.off_seg);
+  d.seen = p.seen;
+}
+
+spec_status launch_pair(int dtype, int mode, bool tree, StatsParams& p, DrawParams& d, const Layout& lo,
+                        hipEvent_t* ev, int32_t nev, hipStream_t stream) {
+  p.epoch = next_epoch();
+  d.epoch = p.epoch;
+  spec_status s = record(ev, nev, 0, stream);
+  if (s != SPEC_OK) return s;
+  if (launch_stats(dtype, mode, tree, p, lo, stream) != hipSuccess) return SPEC_ELAUNCH;
+  s = record(ev, nev, 1, stream);
+  if (s != SPEC_OK) return s;
+  if (mode == SPEC_MODE_GREEDY) return SPEC_OK;
+  d.target = p.target;
+  d.draft = p.draft;
+  d.bonus = p.bonus;
+  d.out_tokens = p.out_tokens;
+  d.status = p.status;
+  d.residual_mass = p.residual_mass;
+  d.V = p.V;
+  d.B = p.B;
+  d.S2 = lo.S2;
+  d.spc = lo.spc;
+  d.n_seg = lo.n_seg;
+  d.seen_stride = lo.L;
+  if (launch_draw(dtype, d, lo, stream) != hipSuccess) return SPEC_ELAUNCH;
+  return record(ev, nev, 2, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t spec_abi_version(void) { return SPEC_ABI_VERSION; }
+
+size_t spec_args_size(int32_t kind) {
+  switch (kind) {
+    case SPEC_KIND_CHAIN: return sizeof(spec_chain_args);
+    case SPEC_KIND_TREE: return sizeof(spec_tree_args);
+    case SPEC_KIND_COMMIT: return sizeof(spec_commit_args);
+    default: return 0;
+  }
+}
+
+const char* spec_status_string(spec_status s) {
+  switch (s) {
+    case SPEC_OK: return "SPEC_OK";
+    case SPEC_EINVAL: return "SPEC_EINVAL: invalid argument (null pointer or size out of range)";
+    case SPEC_EDTYPE: return "SPEC_EDTYPE: unsupported logits dtype";
+    case SPEC_EUNSUPPORTED: return "SPEC_EUNSUPPORTED: mode / kind / threshold combination not implemented";
+    case SPEC_EWORKSPACE: return "SPEC_EWORKSPACE: workspace missing or too small";
+    case SPEC_ELAUNCH: return "SPEC_ELAUNCH: kernel launch or event record failed";
+    default: return "unknown spec_status";
+  }
+}
+
+int32_t spec_kernel_count(int32_t kind, int32_t mode) {
+  if (kind == SPEC_KIND_COMMIT) return 1;
+  if (kind != SPEC_KIND_CHAIN && kind != SPEC_KIND_TREE) return 0;
+  return mode == SPEC_MODE_GREEDY ? 1 : 2;
+}
+
+size_t spec_workspace_bytes(int32_t kind, int32_t mode, int64_t total_rows, int64_t vocab, int32_t batch,
+                            int32_t max_verify_len) {
+  if (kind == SPEC_KIND_COMMIT) return 0;
+  if (batch < 0 || vocab < 1 || vocab > kMaxVocab || total_rows < batch) return 0;
+  if (mode != SPEC_MODE_GREEDY && mode != SPEC_MODE_REJECTION && mode != SPEC_MODE_TARGET_ONLY) return 0;
+  int32_t L;
+  if (kind == SPEC_KIND_CHAIN) {
+    L = max_verify_len;
+  } else if (kind == SPEC_KIND_TREE) {
+    if (batch == 0) return 256;
+    if (total_rows % batch) return 0;
+    L = int32_t(total_rows / batch);
+  } else {
+    return 0;
+  }
+  if (L < 1 || L > kMaxLen) return 0;
+  return make_layout(kind, mode, total_rows, vocab, batch, L).bytes;
+}
+
+spec_status spec_workspace_init(void* workspace, size_t bytes, hipStream_t stream) {
+  if (!workspace && bytes) return SPEC_EINVAL;
+  return launch_fill_zero(workspace, bytes, stream) == hipSuccess ? SPEC_OK : SPEC_ELAUNCH;
+}
+
+spec_status spec_verify_chain(const spec_chain_args* a, hipStream_t stream) {
+  if (!a) return SPEC_EINVAL;
+  if (a->dtype != SPEC_DTYPE_F32 && a->dtype != SPEC_DTYPE_BF16) return SPEC_EDTYPE;
+  if (a->mode == SPEC_MODE_TARGET_ONLY) return SPEC_EUNSUPPORTED;
+  if (a->mode != SPEC_MODE_GREEDY && a->mode != SPEC_MODE_REJECTION) return SPEC_EINVAL;
+  if (a->batch < 0 || a->vocab < 1 || a->vocab > kMaxVocab || a->total_rows < a->batch ||
+      a->total_rows > INT32_MAX || a->max_verify_len < 1 || a->max_verify_len > kMaxLen)
+    return SPEC_EINVAL;
+  const bool rej = a->mode == SPEC_MODE_REJECTION;
+  if (bad_events(a->profile_events, a->n_profile_events, spec_kernel_count(SPEC_KIND_CHAIN, a->mode)))
+    return SPEC_EINVAL;
+  if (a->batch == 0) {
+    for (int i = 0; i < a->n_profile_events; ++i)
+      if (record(a->profile_events, a->n_profile_events, i, stream) != SPEC_OK) return SPEC_ELAUNCH;
+    return SPEC_OK;
+  }
+  const int64_t D = a->total_rows - a->batch;
+  if (!a->target_logits || !a->target_offsets || !a->accept_len || !a->bonus || !a->out_tokens ||
+      !a->accept_index || !a->status)
+    return SPEC_EINVAL;
+  if (D > 0 && !a->draft_tokens) return SPEC_EINVAL;
+  if (rej) {
+    if (!a->u_final || (D > 0 && (!a->draft_logits || !a->u_accept))) return SPEC_EINVAL;
+    if (!(a->temperature > 0.f) || !isfinite(a->temperature)) return SPEC_EINVAL;
+  }
+  const Layout lo = make_layout(SPEC_KIND_CHAIN, a->mode, a->total_rows, a->vocab, a->batch, a->max_verify_len);
+  if (!a->workspace || a->workspace_bytes < lo.bytes) return SPEC_EWORKSPACE;
+
+  StatsParams p{};
+  DrawParams d{};
+  p.target = a->target_logits;
+  p.draft = a->draft_logits;
+  p.offsets = a->target_offsets;
+  p.draft_tokens = a->draft_tokens;
+  p.u_accept = a->u_accept;
+  p.u_final = a->u_final;
+  fill_outputs(p, a);
+  carve(p, d, lo, a->workspace);
+  p.V = a->vocab;
+  p.total_rows = a->total_rows;
+  p.chunk = lo.chunk;
+  p.B = a->batch;
+  p.L = lo.L;
+  p.P = lo.P;
+  p.S = lo.S;
+  p.coef = rej ? float(kLog2e / double(a->temperature)) : 0.f;
+  return launch_pair(a->dtype, a->mode, false, p, d, lo, a->profile_events, a->n_profile_events, stream);
+}
+
+spec_status spec_verify_tree(const spec_tree_args* a, hipStream_t stream) {
+  if (!a) return SPEC_EINVAL;
+  if (a->dtype != SPEC_DTYPE_F32 && a->dtype != SPEC_DTYPE_BF16) return SPEC_EDTYPE;
+  if (a->mode == SPEC_MODE_REJECTION) return SPEC_EUNSUPPORTED;   // classic p/q rejection needs topk = 1
+  if (a->mode != SPEC_MODE_GREEDY && a->mode != SPEC_MODE_TARGET_ONLY) return SPEC_EINVAL;
+  const bool tgt = a->mode == SPEC_MODE_TARGET_ONLY;
+  if (tgt && (a->threshold_single != 1.f || a->threshold_acc != 1.f)) return SPEC_EUNSUPPORTED;
+  if (a->batch < 0 || a->vocab < 1 || a->vocab > kMaxVocab || a->n_nodes < 1 || a->n_nodes > kMaxLen ||
+      int64_t(a->batch) * a->n_nodes > INT32_MAX)
+    return SPEC_EINVAL;
+  if (bad_events(a->profile_events, a->n_profile_events, spec_kernel_count(SPEC_KIND_TREE, a->mode)))
+    return SPEC_EINVAL;
+  if (a->batch == 0) {
+    for (int i = 0; i < a->n_profile_events; ++i)
+      if (record(a->profile_events, a->n_profile_events, i, stream) != SPEC_OK) return SPEC_ELAUNCH;
+    return SPEC_OK;
+  }
+  if (!a->target_logits || !a->parents || !a->tokens || !a->accept_len || !a->bonus || !a->out_tokens ||
+      !a->accept_index || !a->status)
+    return SPEC_EINVAL;
+  if (tgt) {
+    if (!a->u_accept || !a->u_final) return SPEC_EINVAL;
+    if (!(a->temperature > 0.f) || !isfinite(a->temperature)) return SPEC_EINVAL;
+  }
+  const int64_t rows = int64_t(a->batch) * a->n_nodes;
+  const Layout lo = make_layout(SPEC_KIND_TREE, a->mode, rows, a->vocab, a->batch, a->n_nodes);
+  if (!a->workspace || a->workspace_bytes < lo.bytes) return SPEC_EWORKSPACE;
+
+  StatsParams p{};
+  DrawParams d{};
+  p.target = a->target_logits;
+  p.draft = nullptr;
+  p.parents = a->parents;
+  p.tokens = a->tokens;
+  p.u_accept = a->u_accept;
+  p.u_final = a->u_final;
+  fill_outputs(p, a);
+  carve(p, d, lo, a->workspace);
+  p.V = a->vocab;
+  p.total_rows = rows;
+  p.chunk = lo.chunk;
+  p.B = a->batch;
+  p.L = lo.L;
+  p.P = 1;
+  p.S = lo.S;
+  p.coef = tgt ? float(kLog2e / double(a->temperature)) : 0.f;
+  return launch_pair(a->dtype, a->mode, true, p, d, lo, a->profile_events, a->n_profile_events, stream);
+}
+
+spec_status spec_commit_indices(const spec_commit_args* a, hipStream_t stream) {
+  if (!a) return SPEC_EINVAL;
+  if (a->batch < 0 || a->total_rows < a->batch || a->total_rows > INT32_MAX || a->capacity < a->total_rows ||
+      a->max_verify_len < 1 || a->max_verify_len > kMaxLen)
+    return SPEC_EINVAL;
+  if (bad_events(a->profile_events, a->n_profile_events, 1)) return SPEC_EINVAL;
+  if (!a->row_offsets || !a->commit_offsets) return SPEC_EINVAL;
+  if (a->batch > 0 && (!a->accept_len || !a->accept_index || !a->verify_slots || !a->seq_lens || !a->src_slots ||
+                       !a->dst_pos || !a->new_seq_lens || !a->status))
+    return SPEC_EINVAL;
+  if ((a->evict_slots == nullptr) != (a->evict_offsets == nullptr)) return SPEC_EINVAL;
+  spec_status s = record(a->profile_events, a->n_profile_events, 0, stream);
+  if (s != SPEC_OK) return s;
+  if (launch_commit(*a, stream) != hipSuccess) return SPEC_ELAUNCH;
+  return record(a->profile_events, a->n_profile_events, 1, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,167 @@
+// Device helpers of libspecverify (gfx950, wave64).
+#pragma once
+
+#include "sv_internal.h"
+
+namespace sv {
+
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Element access for the two logit dtypes. A 16-byte vector holds 8 bf16 or 4 fp32 logits.
+template <typename DT>
+struct Elem;
+
+template <>
+struct Elem<uint16_t> {
+  static constexpr int kPerVec = 8;
+  __device__ static __forceinline__ float load(const uint16_t* p, int64_t i) {
+    return __uint_as_float(uint32_t(p[i]) << 16);
+  }
+  __device__ static __forceinline__ void unpack(const uint4& q, float* x) {
+    x[0] = bf_lo(q.x); x[1] = bf_hi(q.x); x[2] = bf_lo(q.y); x[3] = bf_hi(q.y);
+    x[4] = bf_lo(q.z); x[5] = bf_hi(q.z); x[6] = bf_lo(q.w); x[7] = bf_hi(q.w);
+  }
+};
+
+template <>
+struct Elem<float> {
+  static constexpr int kPerVec = 4;
+  __device__ static __forceinline__ float load(const float* p, int64_t i) { return p[i]; }
+  __device__ static __forceinline__ void unpack(const uint4& q, float* x) {
+    x[0] = __uint_as_float(q.x); x[1] = __uint_as_float(q.y);
+    x[2] = __uint_as_float(q.z); x[3] = __uint_as_float(q.w);
+  }
+};
+
+// v_exp_f32: 2^x (inputs below -126 give 0 or a denormal; such masses never matter at fp32 resolution).
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Greedy candidate order: larger value first, then lower index.
+__device__ __forceinline__ bool better(float va, int32_t ia, float vb, int32_t ib) {
+  return va > vb || (va == vb && ia < ib);
+}
+
+// Merge two (max, sum of exp2(x - max)) pairs. An empty side has m = -inf and z = 0.
+__device__ __forceinline__ void merge_mz(float& m, float& z, float m2, float z2) {
+  const float M = fmaxf(m, m2);
+  if (M == -INFINITY) {
+    z = z + z2;
+    return;
+  }
+  // An empty side (m = -inf) has z = 0, or NaN when a NaN logit poisoned it: add it unscaled.
+  const float a = (m == -INFINITY) ? z : z * exp2_fast(m - M);
+  const float c = (m2 == -INFINITY) ? z2 : z2 * exp2_fast(m2 - M);
+  m = M;
+  z = a + c;
+}
+
+// Caller uniform -> value used: NaN -> 0, outside [0,1) -> clamped to [0, 1 - 2^-24]; `bad` reports both.
+__device__ __forceinline__ float sanitize_u(float u, bool& bad) {
+  if (!(u == u)) {
+    bad = true;
+    return 0.f;
+  }
+  if (u >= 0.f && u < 1.f) return u;
+  bad = true;
+  return fminf(fmaxf(u, 0.f), 0x1.fffffep-1f);
+}
+
+// Advance a per-request completion counter of this call (epoch in the high word, count in the low word;
+// a word left by another call restarts at 1). Returns the count after this increment.
+__device__ __forceinline__ uint32_t count_done(unsigned long long* c, uint32_t epoch) {
+  unsigned long long old = __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  while (true) {
+    const unsigned long long want =
+        uint32_t(old >> 32) == epoch ? old + 1ull : ((unsigned long long)epoch << 32) | 1ull;
+    const unsigned long long prev = atomicCAS(c, old, want);
+    if (prev == old) return uint32_t(want);
+    old = prev;
+  }
+}
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+__device__ __forceinline__ uint64_t lanes_below(int lane) {
+  return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+__device__ __forceinline__ int wave_min_i(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o));
+  return v;
+}
+
+__device__ __forceinline__ int wave_max_i(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o));
+  return v;
+}
+
+// Block-wide min over kThreads threads; every thread gets the result. `red` holds >= 4 ints of LDS.
+__device__ __forceinline__ int block_min_i(int v, int* red) {
+  v = wave_min_i(v);
+  __syncthreads();
+  if (lane_id() == 0) red[threadIdx.x / kWave] = v;
+  __syncthreads();
+  int r = red[0];
+#pragma unroll
+  for (int w = 1; w < kThreads / kWave; ++w) r = min(r, red[w]);
+  __syncthreads();
+  return r;
+}
+
+__device__ __forceinline__ int block_max_i(int v, int* red) {
+  v = wave_max_i(v);
+  __syncthreads();
+  if (lane_id() == 0) red[threadIdx.x / kWave] = v;
+  __syncthreads();
+  int r = red[0];
+#pragma unroll
+  for (int w = 1; w < kThreads / kWave; ++w) r = max(r, red[w]);
+  __syncthreads();
+  return r;
+}
+
+// Inclusive wave prefix sum (lane order).
+template <typename T>
+__device__ __forceinline__ T wave_inclusive_sum(T v) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    T n = __shfl_up(v, o);
+    if (lane >= o) v += n;
+  }
+  return v;
+}
+
+// Block prefix sums of doubles over kThreads threads. The bounds are consistent: thread t's `incl` is
+// bit-identical to thread t+1's `excl`, so [excl, incl) ranges partition [0, total).
+__device__ __forceinline__ void block_scan_d(double v, double* red, double& excl, double& incl, double& total) {
+  const int lane = lane_id();
+  const int w = threadIdx.x / kWave;
+  const double inc = wave_inclusive_sum(v);
+  const double prev = __shfl_up(inc, 1);
+  __syncthreads();
+  if (lane == kWave - 1) red[w] = inc;
+  __syncthreads();
+  double base = 0.0, tot = 0.0;
+#pragma unroll
+  for (int i = 0; i < kThreads / kWave; ++i) {
+    if (i < w) base = base + red[i];
+    tot = tot + red[i];
+  }
+  __syncthreads();
+  total = tot;
+  excl = lane == 0 ? base : base + prev;
+  incl = base + inc;
+}
+
+}  // namespace sv

@@ -1,0 +1,240 @@
+// k_draw: the final token of a sampling verify, drawn by inverse CDF from the one row (or row pair) that
+// the request's scan named.
+//   rejection at position j   w = [p_{j-1} - q_{j-1}]_+        ([EAGLE→DFlash2] §1.2, residual p')
+//   every draft accepted      w = p_m                           ([EAGLE→DFlash2] §1.1, bonus)
+//   tree target-only          w = p_cur with the tried child tokens set to 0 ([SpecDec]
+//                             "为什么结果不受 draft 影响", target-only sampling; leaf: w = p_cur)
+// The token is the number of cumulative probabilities u has reached, i.e. the smallest v with
+// sum_{t<=v} w_t > u * sum w ([EAGLE→DFlash2] §6.2, inverse-CDF rule); if rounding leaves u past the last
+// step the last positive-weight token is taken. Weights summing to 0 fall back to p (flagged).
+//
+// Layout of the work: k_draw workgroup (b, c) covers a contiguous range of 512-token segments of request
+// b's row; each wave reduces whole segments (8 tokens per lane, coalesced 128-byte rows of loads) and
+// stores (sum w, sum p) per segment. The request's last workgroup takes a float64 prefix over the
+// segments, then rescans the single segment holding u * Z in float64, token by token.
+#include "sv_device.h"
+
+namespace sv {
+
+namespace {
+
+struct RowCtx {
+  const void* xt;
+  const void* xq;
+  float coef, m_t, inv_zt, m_q, inv_zq;
+};
+
+// Weight of token e: w (residual / masked p) and p itself. Identical arithmetic in both passes.
+template <typename DT>
+__device__ __forceinline__ void weight(const RowCtx& r, int64_t e, const int32_t* seen, int n_seen, float& w,
+                                       float& pv) {
+  const float x = Elem<DT>::load(static_cast<const DT*>(r.xt), e);
+  pv = exp2_fast(fmaf(x, r.coef, -r.m_t)) * r.inv_zt;
+  if (r.xq) {
+    const float y = Elem<DT>::load(static_cast<const DT*>(r.xq), e);
+    const float qv = exp2_fast(fmaf(y, r.coef, -r.m_q)) * r.inv_zq;
+    w = fmaxf(pv - qv, 0.f);
+  } else {
+    w = pv;
+    for (int i = 0; i < n_seen; ++i)
+      if (seen[i] == e) w = 0.f;
+  }
+}
+
+template <typename DT>
+__global__ __launch_bounds__(kThreads) void k_draw(DrawParams p) {
+  __shared__ int32_t s_seen[kMaxLen];
+  __shared__ int s_nseen;
+  __shared__ double red_d[kThreads / kWave];
+  __shared__ int red_i[kThreads / kWave];
+  __shared__ int s_last;
+  __shared__ int s_sel;
+  __shared__ double s_sel_excl;
+
+  const int b = blockIdx.x / p.S2;
+  const int c = blockIdx.x % p.S2;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wv = tid / kWave;
+  const DrawDesc d = p.desc[b];
+  if (d.state != p.epoch) return;   // no draw pending for b in this call (bad offsets): all of b's workgroups agree
+
+  RowCtx r;
+  r.xt = static_cast<const DT*>(p.target) + int64_t(d.row_t) * p.V;
+  r.xq = d.row_q >= 0 ? static_cast<const DT*>(p.draft) + int64_t(d.row_q) * p.V : nullptr;
+  r.coef = d.coef;
+  r.m_t = d.m_t;
+  r.inv_zt = 1.f / d.l_t;
+  r.m_q = d.m_q;
+  r.inv_zq = 1.f / d.l_q;
+
+  const int s_begin = c * p.spc;
+  const int s_end = min(p.n_seg, s_begin + p.spc);
+  const int64_t e_lo = int64_t(s_begin) * kSeg;
+  const int64_t e_hi = int64_t(s_end) * kSeg;
+  // Tried tokens inside this workgroup's range (tree target-only; usually none).
+  if (tid == 0) s_nseen = 0;
+  __syncthreads();
+  for (int i = tid; i < d.n_seen; i += kThreads) {
+    const int32_t t = p.seen[int64_t(b) * p.seen_stride + i];
+    if (t >= e_lo && t < e_hi) s_seen[atomicAdd(&s_nseen, 1)] = t;
+  }
+  __syncthreads();
+  const int n_seen = s_nseen;
+
+  for (int s = s_begin + wv; s < s_end; s += kThreads / kWave) {
+    float sw = 0.f, sp = 0.f;
+#pragma unroll
+    for (int k = 0; k < kSeg / kWave; ++k) {
+      const int64_t e = int64_t(s) * kSeg + k * kWave + lane;
+      if (e < p.V) {
+        float w, pv;
+        weight<DT>(r, e, s_seen, n_seen, w, pv);
+        sw += w;
+        sp += pv;
+      }
+    }
+    sw = wave_sum(sw);
+    sp = wave_sum(sp);
+    if (lane == 0) p.seg[int64_t(b) * p.n_seg + s] = make_float2(sw, sp);
+  }
+
+  __syncthreads();
+  if (tid == 0) {
+    __threadfence();   // release this workgroup's segment sums
+    s_last = count_done(p.cnt2 + b, p.epoch) == uint32_t(p.S2);
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();   // acquire the other workgroups' segment sums
+
+  // ---- selection: float64 prefix over segments, then one segment token by token ----
+  const float2* seg = p.seg + int64_t(b) * p.n_seg;
+  const int R = (p.n_seg + kThreads - 1) / kThreads;
+  const int r_lo = min(p.n_seg, tid * R);
+  const int r_hi = min(p.n_seg, r_lo + R);
+  uint32_t flags = 0;
+  bool use_p = false;
+  double excl, incl, Z;
+  {
+    double loc = 0.0;
+    for (int s = r_lo; s < r_hi; ++s) loc += double(seg[s].x);
+    block_scan_d(loc, red_d, excl, incl, Z);
+  }
+  if (!(Z > 0.0)) {   // weights summed to zero: draw from p instead
+    use_p = true;
+    flags |= SPEC_ST_ZERO_RESIDUAL;
+    double loc = 0.0;
+    for (int s = r_lo; s < r_hi; ++s) loc += double(seg[s].y);
+    block_scan_d(loc, red_d, excl, incl, Z);
+  }
+  const double target = double(d.u) * Z;
+  if (tid == 0) s_sel = -1;
+  __syncthreads();
+  if (excl <= target && target < incl) {
+    double acc = excl;
+    int sel = -1, last_pos = -1;
+    double sel_excl = 0.0, last_excl = 0.0;
+    for (int s = r_lo; s < r_hi; ++s) {
+      const double ws = double(use_p ? seg[s].y : seg[s].x);
+      if (ws > 0.0) { last_pos = s; last_excl = acc; }
+      if (target < acc + ws && ws > 0.0) { sel = s; sel_excl = acc; break; }
+      acc += ws;
+    }
+    if (sel < 0) { sel = last_pos; sel_excl = last_excl; }
+    if (sel >= 0) { s_sel = sel; s_sel_excl = sel_excl; }
+  }
+  __syncthreads();
+  int sel = s_sel;
+  double sel_excl = s_sel_excl;
+  if (sel < 0) {
+    // u * Z beyond every range (rounding or a non-finite row): the last segment with positive weight.
+    int lastpos = -1;
+    for (int s = r_lo; s < r_hi; ++s)
+      if ((use_p ? seg[s].y : seg[s].x) > 0.f) lastpos = s;
+    lastpos = block_max_i(lastpos, red_i);
+    sel = lastpos < 0 ? 0 : lastpos;
+    // its start: recompute the prefix below it
+    double loc = 0.0;
+    for (int s = r_lo; s < min(r_hi, sel); ++s) loc += double(use_p ? seg[s].y : seg[s].x);
+    double e2, i2, t2;
+    block_scan_d(loc, red_d, e2, i2, t2);
+    sel_excl = t2;
+  }
+  // Tried tokens inside the selected segment.
+  __syncthreads();
+  if (tid == 0) s_nseen = 0;
+  __syncthreads();
+  const int64_t g_lo = int64_t(sel) * kSeg;
+  for (int i = tid; i < d.n_seen; i += kThreads) {
+    const int32_t t = p.seen[int64_t(b) * p.seen_stride + i];
+    if (t >= g_lo && t < g_lo + kSeg) s_seen[atomicAdd(&s_nseen, 1)] = t;
+  }
+  __syncthreads();
+  if (tid < kWave) {
+    const int ns = use_p ? 0 : s_nseen;
+    double carry = sel_excl;
+    int64_t x = -1;
+    double c_lo = 0.0, c_hi = 0.0;
+    int64_t last_e = -1;
+    double last_lo = 0.0, last_hi = 0.0;
+    for (int k = 0; k < kSeg / kWave; ++k) {
+      const int64_t e = g_lo + k * kWave + lane;
+      float w = 0.f, pv = 0.f;
+      if (e < p.V) weight<DT>(r, e, s_seen, ns, w, pv);
+      const double wd = double(use_p ? pv : w);
+      const double inc = carry + wave_inclusive_sum(wd);
+      const uint64_t hit = __ballot(wd > 0.0 && target < inc);
+      if (hit) {
+        const int f = __ffsll((unsigned long long)hit) - 1;
+        x = g_lo + k * kWave + f;
+        c_hi = __shfl(inc, f);
+        c_lo = __shfl(inc - wd, f);
+        break;
+      }
+      const uint64_t pos = __ballot(wd > 0.0);
+      if (pos) {
+        const int l = 63 - __clzll((long long)pos);
+        last_e = g_lo + k * kWave + l;
+        last_hi = __shfl(inc, l);
+        last_lo = __shfl(inc - wd, l);
+      }
+      carry = __shfl(inc, kWave - 1);
+    }
+    if (x < 0) {
+      x = last_e >= 0 ? last_e : g_lo;
+      c_hi = last_hi;
+      c_lo = last_lo;
+    }
+    if (lane == 0) {
+      const double u = double(d.u);
+      // Too close to call: within 1e-5 of a step of the normalised CDF, or within 1e-6 in probability
+      // mass (the resolution of fp32 probabilities; matters when the weights' total Z is small).
+      const double gap = fmin(u - c_lo / Z, c_hi / Z - u);
+      if (!(gap >= double(kNear)) || !(gap * Z >= double(kNearMass))) flags |= SPEC_ST_NEAR_CDF;
+      const uint32_t st = d.status | flags;
+      p.bonus[b] = int32_t(x);
+      p.out_tokens[d.out_pos] = int32_t(x);
+      p.status[b] = st;
+      if (p.residual_mass) p.residual_mass[b] = float(Z);
+    }
+  }
+}
+
+template <typename DT>
+hipError_t launch_draw_t(const DrawParams& p, hipStream_t stream) {
+  const int64_t blocks = int64_t(p.B) * p.S2;
+  if (blocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL((k_draw<DT>), dim3(unsigned(blocks)), dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_draw(int dtype, const DrawParams& p, const Layout& lo, hipStream_t stream) {
+  (void)lo;
+  if (dtype == SPEC_DTYPE_BF16) return launch_draw_t<uint16_t>(p, stream);
+  return launch_draw_t<float>(p, stream);
+}
+
+}  // namespace sv

@@ -24,8 +24,10 @@
  *   - Random decisions use caller-supplied uniforms in [0,1) (fp32). Given the uniforms the result is a
  *     deterministic function of the inputs: one uniform per row under test (`u_accept`) and one per
  *     request for the single final draw (`u_final`).
- *   - A workspace serves one call at a time. Its first use must see it zero-filled (spec_workspace_init
- *     does that); every call leaves it ready for the next call on the same stream.
+ *   - A workspace (scratch device memory sized by spec_workspace_bytes) serves one call at a time; calls
+ *     that overlap on one workspace race. Its contents between calls do not matter: every call tags its
+ *     progress counters with a fresh per-call number, so one workspace can be reused by later calls of any
+ *     shape it is large enough for. spec_workspace_init zero-fills one (optional).
  */
 #ifndef SPECVERIFY_H
 #define SPECVERIFY_H
@@ -90,7 +92,8 @@ typedef enum spec_kind { SPEC_KIND_CHAIN = 0, SPEC_KIND_TREE = 1, SPEC_KIND_COMM
                                            p(d) > 0, else 0)                                                 */
 #define SPEC_ST_ZERO_RESIDUAL (1u << 6) /* the final draw's weights summed to 0; drawn from p instead        */
 #define SPEC_ST_NEAR_ALPHA    (1u << 7) /* diagnostic: |u - alpha| < 1e-5 at an examined accept test        */
-#define SPEC_ST_NEAR_CDF      (1u << 8) /* diagnostic: the final draw's u lies within 1e-5 of a CDF step    */
+#define SPEC_ST_NEAR_CDF      (1u << 8) /* diagnostic: the final draw's u lies within 1e-5 of a CDF step, or
+                                           that margin times the weights' total mass Z is below 1e-6        */
 #define SPEC_ST_BAD_ACCEPT    (1u << 9) /* commit: accept_len / accept_index outside the request's rows     */
 
 /*
@@ -223,7 +226,8 @@ spec_status spec_commit_indices(const spec_commit_args* args, hipStream_t stream
 size_t spec_workspace_bytes(int32_t kind, int32_t mode, int64_t total_rows, int64_t vocab, int32_t batch,
                             int32_t max_verify_len);
 
-/* Zero-fills `bytes` of device memory at `workspace` with a kernel on `stream` (no memset node). */
+/* Zero-fills `bytes` of device memory at `workspace` with a kernel on `stream` (no memset node).
+   Returns SPEC_EINVAL for a NULL workspace with bytes > 0, SPEC_ELAUNCH if the launch fails. */
 spec_status spec_workspace_init(void* workspace, size_t bytes, hipStream_t stream);
 
 /* Number of kernels a call of this kind/mode launches (events: kernels + 1). Pure host function. */

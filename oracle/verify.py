@@ -35,6 +35,7 @@ ST_NEAR_CDF = 1 << 8
 ST_BAD_ACCEPT = 1 << 9
 
 NEAR = 1e-5          # width of the "too close to call" band for accept tests and CDF steps
+NEAR_MASS = 1e-6     # the same band measured in probability mass for a draw (gap * Z), see near_cdf()
 U_MAX = 1.0 - 2.0 ** -24   # largest float32 below 1
 
 
@@ -118,6 +119,14 @@ def draw(w: np.ndarray, u: float) -> tuple[int, float, float]:
     lo = float(C[k - 1]) if k > 0 else 0.0
     gap = min(u - lo, float(C[k]) - u)
     return k, gap, Z
+
+
+def near_cdf(gap: float, Z: float) -> bool:
+    """A draw is too close to call when u lies within 1e-5 of a step of the normalised CDF, or when that
+    margin in probability mass, gap * Z, is below 1e-6: probabilities computed in fp32 carry errors of that
+    size, so for a residual of small total mass Z the normalised steps are only known to about 1e-6 / Z.
+    READING: the pages fix no precision; this widens the 1e-5 band only where Z < 0.1."""
+    return gap < NEAR or gap * Z < NEAR_MASS
 
 
 def _sentinel_outputs(n_rows: int, n_draft: int, batch: int) -> dict:
@@ -246,7 +255,7 @@ def _chain_request(out, b, target, offsets, draft_tokens, mode, draft, u_accept,
             st |= ST_ZERO_RESIDUAL  # READING: undefined residual (only from rounding) -> draw from p
             w = ps[r]
         x, gap, resid = draw(w, uf)
-        if gap < NEAR:
+        if near_cdf(gap, resid):
             st |= ST_NEAR_CDF
             flag_pos = r if flag_pos is None else flag_pos
 
@@ -362,7 +371,7 @@ def _tree_request(out, b, target, parents, tokens, N, mode, u_accept, u_final, t
             st |= ST_ZERO_RESIDUAL
             w = p
         x, gap, resid = draw(w, uf)
-        if gap < NEAR:
+        if near_cdf(gap, resid):
             st |= ST_NEAR_CDF
             flag_pos = len(path) - 1 if flag_pos is None else flag_pos
 

@@ -1,0 +1,116 @@
+"""CPU checks of the C ABI library: it loads, exports every symbol include/specverify.h declares, its
+argument structs match the binding, and host-side argument checks return the documented codes before any
+device work (no GPU is touched by these calls)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import draft_verification_acceptance_amd as dva
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "specverify.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(dva.library_path), reason="libspecverify.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(spec_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert {"spec_verify_chain", "spec_verify_tree", "spec_commit_indices", "spec_workspace_bytes",
+            "spec_status_string", "spec_abi_version"} <= set(names)
+    lib = ctypes.CDLL(dva.library_path)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_abi_version_and_struct_sizes():
+    lib = dva._lib()        # raises on ABI or struct-size mismatch
+    assert dva.abi_version() == 1
+    assert lib.spec_args_size(0) == ctypes.sizeof(dva.ChainArgs) == 168
+    assert lib.spec_args_size(1) == ctypes.sizeof(dva.TreeArgs)
+    assert lib.spec_args_size(2) == ctypes.sizeof(dva.CommitArgs)
+
+
+def test_status_strings_and_kernel_counts():
+    for code, word in [(0, "SPEC_OK"), (1, "EINVAL"), (2, "EDTYPE"), (3, "EUNSUPPORTED"), (4, "EWORKSPACE"),
+                       (5, "ELAUNCH")]:
+        assert word in dva.status_string(code)
+    assert "unknown" in dva.status_string(99)
+    assert dva.kernel_count("chain", "greedy") == 1
+    assert dva.kernel_count("chain", "rejection") == 2
+    assert dva.kernel_count("tree", "target_only") == 2
+    assert dva.kernel_count("commit", "greedy") == 1
+
+
+def test_workspace_bytes():
+    b = dva.workspace_bytes("chain", "rejection", 512, 151936, 64, 8)
+    assert b > 0 and b % 256 == 0
+    assert dva.workspace_bytes("chain", "greedy", 512, 151936, 32, 16) > 0
+    assert dva.workspace_bytes("tree", "target_only", 2048, 128256, 32, 64) > 0
+    assert dva.workspace_bytes("chain", "greedy", 10, 0, 2, 5) == 0           # vocab < 1
+    assert dva.workspace_bytes("chain", "greedy", 10, 1 << 23, 2, 5) == 0     # vocab too large
+    assert dva.workspace_bytes("chain", "greedy", 10, 100, 2, 2000) == 0      # rows per request too large
+    assert dva.workspace_bytes("tree", "greedy", 10, 100, 3, 0) == 0          # rows not a multiple of batch
+
+
+def _chain(**kw):
+    a = dva.ChainArgs()
+    a.total_rows, a.vocab, a.batch, a.max_verify_len = 10, 100, 2, 8
+    a.dtype, a.mode, a.temperature = 1, 0, 1.0
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def _call_chain(a):
+    return dva._lib().spec_verify_chain(ctypes.byref(a), None)
+
+
+def test_chain_host_checks():
+    lib = dva._lib()
+    assert lib.spec_verify_chain(None, None) == 1
+    assert _call_chain(_chain(dtype=7)) == 2                                  # EDTYPE
+    assert _call_chain(_chain(mode=2)) == 3                                   # target-only on a chain
+    assert _call_chain(_chain(mode=9)) == 1
+    assert _call_chain(_chain(vocab=0)) == 1
+    assert _call_chain(_chain(max_verify_len=0)) == 1
+    assert _call_chain(_chain(total_rows=1)) == 1                             # fewer rows than requests
+    assert _call_chain(_chain()) == 1                                         # null pointers
+    assert _call_chain(_chain(batch=0, total_rows=0)) == 0                    # empty batch: nothing to do
+    fake = 1 << 40                                                            # never dereferenced
+    full = dict(target_logits=fake, target_offsets=fake, draft_tokens=fake, accept_len=fake, bonus=fake,
+                out_tokens=fake, accept_index=fake, status=fake)
+    assert _call_chain(_chain(**full)) == 4                                   # no workspace
+    assert _call_chain(_chain(**full, workspace=fake, workspace_bytes=16)) == 4
+    rej = dict(full, mode=1, draft_logits=fake, u_accept=fake, u_final=fake)
+    assert _call_chain(_chain(**rej, temperature=0.0)) == 1                   # T must be > 0
+    assert _call_chain(_chain(**rej, temperature=float("inf"))) == 1
+    assert _call_chain(_chain(**dict(rej, u_final=None))) == 1
+    assert _call_chain(_chain(**full, n_profile_events=3)) == 1               # events array missing
+
+
+def test_tree_and_commit_host_checks():
+    lib = dva._lib()
+    a = dva.TreeArgs()
+    a.vocab, a.batch, a.n_nodes, a.dtype, a.mode, a.temperature = 100, 2, 4, 1, 1, 1.0
+    assert lib.spec_verify_tree(ctypes.byref(a), None) == 3                   # rejection on a tree
+    a.mode = 2
+    a.threshold_single, a.threshold_acc = 0.9, 1.0
+    assert lib.spec_verify_tree(ctypes.byref(a), None) == 3                   # thresholds other than 1.0
+    a.threshold_single = 1.0
+    a.n_nodes = 0
+    assert lib.spec_verify_tree(ctypes.byref(a), None) == 1
+    a.n_nodes = 4
+    assert lib.spec_verify_tree(ctypes.byref(a), None) == 1                   # null pointers
+    c = dva.CommitArgs()
+    c.batch, c.total_rows, c.capacity, c.max_verify_len = 2, 10, 5, 8
+    assert lib.spec_commit_indices(ctypes.byref(c), None) == 1                # capacity < total_rows
+    c.capacity = 10
+    assert lib.spec_commit_indices(ctypes.byref(c), None) == 1                # null pointers

@@ -1,0 +1,366 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 CPU oracle on the same seeded inputs.
+
+Sizes: every workload at a reduced vocabulary that still spans several chunks per row and an unaligned
+ragged tail (all requests compared), then at full size in the launch configuration the benchmark times
+(requests sampled for the oracle). Edge cases and statistics follow.
+"""
+import numpy as np
+import pytest
+import torch
+from scipy import stats
+
+import draft_verification_acceptance_amd as dva
+import oracle
+from draft_verification_acceptance_amd import workloads as W
+from gpu_util import (compare_chain, compare_tree, dev, dev_logits, np_out, oracle_chain, oracle_tree, run_chain,
+                      run_tree)
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+# ----------------------------------------------------------------------------------------------------
+# the five workloads
+# ----------------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("mode", ["greedy", "rejection"])
+def test_tiny_chain(mode):
+    w = W.tiny_chain()
+    _say("tiny_chain", mode)
+    g = run_chain(w, mode)
+    o = oracle_chain(w, mode)
+    assert compare_chain(w, mode, o, g) == 0
+
+
+def test_chain_rejection_small_vocab():
+    w = W.chain_rejection(seed=2001, vocab=20011)
+    _say("chain_rejection V=20011")
+    g = run_chain(w, "rejection")
+    o = oracle_chain(w, "rejection")
+    compare_chain(w, "rejection", o, g)
+    assert o["accept_len"].max() >= 2
+
+
+def test_block_greedy_small_vocab():
+    w = W.block_greedy(seed=3001, vocab=20011, tie_rate=0.2)
+    _say("block_greedy V=20011")
+    g = run_chain(w, "greedy")
+    o = oracle_chain(w, "greedy")
+    assert compare_chain(w, "greedy", o, g) == 0
+    assert np.array_equal(g["accept_len"], w.planted_r)
+
+
+@pytest.mark.parametrize("mode", ["greedy", "target_only"])
+def test_tree_small_vocab(mode):
+    w = W.tree(seed=4001, vocab=12007)
+    _say("tree V=12007", mode)
+    g = run_tree(w, mode)
+    o = oracle_tree(w, mode)
+    compare_tree(w, mode, o, g)
+
+
+def test_ragged_small_vocab():
+    w = W.ragged(seed=5001, vocab=4099)
+    _say("ragged V=4099")
+    g = run_chain(w, "rejection")
+    o = oracle_chain(w, "rejection")
+    compare_chain(w, "rejection", o, g)
+
+
+# Full sizes, the benchmark's launch configuration; the oracle checks a sample of requests.
+def test_full_chain_rejection():
+    w = W.chain_rejection()
+    _say("chain_rejection full")
+    g = run_chain(w, "rejection")
+    reqs = [0, 1, 17, 33, 50, 63]
+    o = oracle_chain(w, "rejection", reqs)
+    compare_chain(w, "rejection", o, g, reqs)
+    # properties that hold for every request at any size
+    assert np.all((g["accept_len"] >= 0) & (g["accept_len"] <= 7))
+    assert np.all((g["bonus"] >= 0) & (g["bonus"] < w.vocab))
+    assert not np.any(g["status"] & ~np.uint32(oracle.ST_NEAR_ALPHA | oracle.ST_NEAR_CDF))
+    assert np.all((g["residual_mass"] > 0) & (g["residual_mass"] <= 1.0 + 1e-6))
+
+
+def test_full_block_greedy():
+    w = W.block_greedy()
+    _say("block_greedy full")
+    g = run_chain(w, "greedy")
+    o = oracle_chain(w, "greedy")
+    assert compare_chain(w, "greedy", o, g) == 0
+    assert np.array_equal(g["accept_len"], w.planted_r)
+
+
+@pytest.mark.parametrize("mode", ["greedy", "target_only"])
+def test_full_tree(mode):
+    w = W.tree()
+    _say("tree full", mode)
+    g = run_tree(w, mode)
+    reqs = list(range(0, 32, 3)) if mode == "target_only" else None
+    o = oracle_tree(w, mode, reqs)
+    compare_tree(w, mode, o, g, reqs)
+
+
+def test_full_ragged():
+    w = W.ragged()
+    _say("ragged full", w.total_rows)
+    g = run_chain(w, "rejection")
+    reqs = [0, 1, 2, 100, 255, 256, 400, 510, 511] + [int(b) for b in np.flatnonzero(np.diff(w.offsets) == 1)[:3]]
+    o = oracle_chain(w, "rejection", reqs)
+    compare_chain(w, "rejection", o, g, reqs)
+    m = np.diff(w.offsets) - 1
+    assert np.all((g["accept_len"] >= 0) & (g["accept_len"] <= m))
+
+
+# ----------------------------------------------------------------------------------------------------
+# edge cases
+# ----------------------------------------------------------------------------------------------------
+def _chain_from(target, draft, offsets, tokens, ua, uf, T, max_len):
+    return W.ChainWorkload("edge", target.shape[1], len(offsets) - 1, np.asarray(offsets, np.int32), target, draft,
+                           np.asarray(tokens, np.int32), np.asarray(ua, np.float32), np.asarray(uf, np.float32),
+                           T, ("greedy", "rejection"), max_len)
+
+
+@pytest.mark.parametrize("V", [1, 7, 32, 1000, 8195, 151937])
+def test_vocab_sizes(V):
+    w = W.tiny_chain(seed=77 + V, batch=6, m=3, vocab=V)
+    for mode in ("greedy", "rejection"):
+        _say("vocab", V, mode)
+        for bf16 in (False, True):
+            ww = w
+            if bf16:
+                ww = _chain_from(W.bf16_bits(w.target), W.bf16_bits(w.draft), w.offsets, w.draft_tokens, w.u_accept,
+                                 w.u_final, 1.0, w.max_verify_len)
+            g = run_chain(ww, mode)
+            o = oracle_chain(ww, mode)
+            compare_chain(ww, mode, o, g)
+
+
+@pytest.mark.parametrize("T", [0.05, 0.7, 5.0])
+def test_temperatures(T):
+    w = W.chain_rejection(seed=2100, batch=16, m=5, vocab=3001, parallel=False)
+    w.temperature = T
+    _say("temperature", T)
+    g = run_chain(w, "rejection")
+    o = oracle_chain(w, "rejection")
+    compare_chain(w, "rejection", o, g)
+
+
+def test_ragged_lengths_including_zero_drafts():
+    rng = np.random.default_rng(5)
+    V = 513
+    lens = np.array([1, 1, 5, 1, 9, 2, 1, 16, 3], np.int64)
+    offs = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T, B = int(offs[-1]), len(lens)
+    tl = rng.normal(0, 2, (T, V)).astype(np.float32)
+    dl = (tl[:T - B] + rng.normal(0, 1, (T - B, V))).astype(np.float32)
+    toks = np.array([np.argmax(tl[offs[b] + j]) if rng.random() < 0.7 else rng.integers(V)
+                     for b in range(B) for j in range(lens[b] - 1)], np.int32)
+    w = _chain_from(tl, dl, offs, toks, rng.random(T - B), rng.random(B), 0.9, 16)
+    for mode in ("greedy", "rejection"):
+        g = run_chain(w, mode)
+        o = oracle_chain(w, mode)
+        compare_chain(w, mode, o, g)
+        assert np.all(g["accept_len"][lens == 1] == 0)
+
+
+def test_masked_logits_ties_and_special_rows():
+    rng = np.random.default_rng(11)
+    V, B, m = 700, 12, 4
+    T = B * (m + 1)
+    offs = np.arange(B + 1, dtype=np.int32) * (m + 1)
+    tl = rng.integers(-3, 4, (T, V)).astype(np.float32)        # many exact ties
+    tl[:, rng.random(V) < 0.5] = -np.inf                       # masked vocabulary entries
+    tl[0:5, 5] = 100.0                                          # one-hot-like p (alpha = p(d)/q(d) huge)
+    dl = tl[:T - B].copy() + rng.normal(0, 0.5, (T - B, V)).astype(np.float32)
+    dl[10:14] = tl[12:16]                                       # identical p and q rows for request 2
+    dl[20:24] *= 10.0                                           # very peaked q for request 5
+    toks = np.empty(T - B, np.int32)
+    for b in range(B):
+        for j in range(m):
+            row = tl[offs[b] + j]
+            toks[b * m + j] = np.flatnonzero(row == row.max())[0] if rng.random() < 0.8 else rng.integers(V)
+    w = _chain_from(tl, dl, offs, toks, rng.random(T - B), rng.random(B), 1.0, m + 1)
+    for mode in ("greedy", "rejection"):
+        for bf16 in (False, True):
+            ww = w if not bf16 else _chain_from(W.bf16_bits(tl), W.bf16_bits(dl), offs, toks, w.u_accept, w.u_final,
+                                                1.0, m + 1)
+            g = run_chain(ww, mode)
+            o = oracle_chain(ww, mode)
+            compare_chain(ww, mode, o, g)
+
+
+def test_status_bits_nan_bad_token_bad_uniform_bad_offsets():
+    rng = np.random.default_rng(12)
+    V, B, m = 300, 6, 3
+    T = B * (m + 1)
+    offs = np.arange(B + 1, dtype=np.int32) * (m + 1)
+    tl = rng.normal(0, 1, (T, V)).astype(np.float32)
+    dl = rng.normal(0, 1, (T - B, V)).astype(np.float32)
+    toks = rng.integers(0, V, T - B).astype(np.int32)
+    ua = rng.random(T - B).astype(np.float32)
+    uf = rng.random(B).astype(np.float32)
+    tl[1, 17] = np.nan          # request 0: NaN in a target row
+    dl[5, 3] = np.nan           # request 1: NaN in a draft row
+    toks[8] = V + 5             # request 2: out-of-range token
+    ua[13] = 1.5                # request 4: bad uniform
+    uf[5] = np.nan              # request 5: bad final uniform
+    w = _chain_from(tl, dl, offs, toks, ua, uf, 1.0, m + 1)
+    for mode in ("greedy", "rejection"):
+        g = run_chain(w, mode)
+        o = oracle_chain(w, mode)
+        compare_chain(w, mode, o, g)
+        assert g["status"][0] & oracle.ST_NONFINITE
+        assert g["status"][2] & oracle.ST_BAD_TOKEN
+        if mode == "rejection":
+            assert g["status"][1] & oracle.ST_NONFINITE
+            assert g["status"][4] & oracle.ST_BAD_UNIFORM
+            assert g["status"][5] & oracle.ST_BAD_UNIFORM
+    # offsets that do not describe the rows: reported, nothing else checked
+    bad = offs.copy()
+    bad[3] = bad[2]
+    wb = _chain_from(tl, dl, bad, toks, ua, uf, 1.0, m + 1)
+    g = run_chain(wb, "greedy")
+    assert g["status"][2] & oracle.ST_BAD_OFFSETS
+
+
+def test_tree_edge_cases():
+    rng = np.random.default_rng(13)
+    V = 50
+    # N = 1 (root only), chain-shaped, duplicate sibling tokens, bad parents, one-hot rows
+    for N in (1, 2, 9, 64, 130):
+        B = 5
+        target = rng.integers(-2, 3, (B * N, V)).astype(np.float32)
+        parents = np.zeros(B * N, np.int32)
+        tokens = np.zeros(B * N, np.int32)
+        for b in range(B):
+            parents[b * N] = -1
+            for i in range(1, N):
+                parents[b * N + i] = i - 1 if b == 1 else rng.integers(0, i)
+                p = parents[b * N + i]
+                row = target[b * N + p]
+                tokens[b * N + i] = np.flatnonzero(row == row.max())[0] if rng.random() < 0.6 else rng.integers(V)
+            if b == 2 and N > 3:        # duplicate sibling tokens
+                parents[b * N + 1: b * N + 4] = 0
+                tokens[b * N + 1: b * N + 4] = tokens[b * N + 1]
+            if b == 3 and N > 3:
+                parents[b * N + 3] = 7 if N > 7 else N - 1    # parent not before the node
+        tw = W.TreeWorkload("edge", V, B, N, target, parents, tokens, rng.random(B * N).astype(np.float32),
+                            rng.random(B).astype(np.float32), 1.0)
+        for mode in ("greedy", "target_only"):
+            _say("tree edge N", N, mode)
+            g = run_tree(tw, mode)
+            o = oracle_tree(tw, mode)
+            compare_tree(tw, mode, o, g)
+            if N > 7:
+                assert g["status"][3] & oracle.ST_BAD_PARENT
+
+
+def test_chain_shaped_tree_matches_chain_on_gpu():
+    w = W.block_greedy(seed=3003, batch=16, vocab=5003, parallel=False)
+    N = 16
+    parents = np.tile(np.arange(-1, N - 1, dtype=np.int32), w.batch)
+    tokens = np.concatenate([[0] + list(w.draft_tokens[b * 15:(b + 1) * 15]) for b in range(w.batch)]).astype(np.int32)
+    tw = W.TreeWorkload("chain_tree", w.vocab, w.batch, N, w.target, parents, tokens,
+                        np.zeros(w.batch * N, np.float32), np.zeros(w.batch, np.float32), 1.0)
+    gc = run_chain(w, "greedy")
+    gt = run_tree(tw, "greedy")
+    for k in ("accept_len", "bonus", "out_tokens", "accept_index"):
+        assert np.array_equal(gc[k], gt[k]), k
+
+
+# ----------------------------------------------------------------------------------------------------
+# determinism, unwritten outputs, workspace reuse across calls
+# ----------------------------------------------------------------------------------------------------
+def test_determinism_poisoned_outputs_and_workspace_reuse():
+    wa = W.ragged(seed=5002, batch=64, vocab=30011)
+    wb = W.chain_rejection(seed=2002, batch=8, vocab=30011, parallel=False)
+    ws = dva.workspace("chain", "rejection", wa.total_rows, wa.vocab, wa.batch, 16)
+    outs = []
+    for rep in range(2):
+        for w in (wa, wb):
+            out = {k: torch.full((n,), 0x7EEEEEEE, dtype=torch.int32, device="cuda") for k, n in
+                   (("accept_len", w.batch), ("bonus", w.batch), ("out_tokens", w.total_rows),
+                    ("accept_index", w.total_rows), ("status", w.batch))}
+            g = run_chain(w, "rejection", ws=ws, out=out)
+            for k in ("accept_len", "bonus", "out_tokens", "accept_index", "status"):
+                assert not np.any(g[k].view(np.int32) == 0x7EEEEEEE), k
+            outs.append(g)
+    for a, b in ((outs[0], outs[2]), (outs[1], outs[3])):
+        for k in a:
+            assert np.array_equal(a[k], b[k]), k
+    o = oracle_chain(wb, "rejection")
+    compare_chain(wb, "rejection", o, outs[3])
+
+
+# ----------------------------------------------------------------------------------------------------
+# statistics on the GPU: emitted tokens follow p
+# ----------------------------------------------------------------------------------------------------
+def test_gpu_chi_square_emitted_tokens_follow_p():
+    rng = np.random.default_rng(41)
+    N, m, V, T = 200_000, 3, 16, 0.8
+    tl = rng.normal(0, 1.5, (m + 1, V)).astype(np.float32)
+    sl = (tl[:m] + rng.normal(0, 1.0, (m, V))).astype(np.float32)
+    p = [np.exp(x / T - (x / T).max()) / np.exp(x / T - (x / T).max()).sum() for x in tl.astype(np.float64)]
+    q = [np.exp(x / T - (x / T).max()) / np.exp(x / T - (x / T).max()).sum() for x in sl.astype(np.float64)]
+    target = torch.from_numpy(tl).cuda().repeat(N, 1)
+    draft = torch.from_numpy(sl).cuda().repeat(N, 1)
+    toks = np.stack([rng.choice(V, size=N, p=q[j]) for j in range(m)], 1).reshape(-1).astype(np.int32)
+    offs = (np.arange(N + 1) * (m + 1)).astype(np.int32)
+    o = dva.verify_chain(target, dev(offs), dev(toks), "rejection", draft_logits=draft,
+                         u_accept=dev(rng.random(N * m).astype(np.float32)), u_final=dev(rng.random(N).astype(np.float32)),
+                         temperature=T, max_verify_len=m + 1)
+    g = np_out(o)
+    r = g["accept_len"]
+    pv = []
+    for k in range(m + 1):
+        sel = np.flatnonzero(r >= k)
+        t = g["out_tokens"][offs[sel] + k]
+        pv.append(stats.chisquare(np.bincount(t, minlength=V), p[k] * len(sel)).pvalue)
+    assert min(pv) > 1e-3 / (m + 1), pv
+    beta = [np.minimum(p[j], q[j]).sum() for j in range(m)]
+    er = sum(np.prod(beta[:k]) for k in range(1, m + 1))
+    assert abs(r.mean() - er) < 4 * r.std() / np.sqrt(N)
+
+
+# ----------------------------------------------------------------------------------------------------
+# commit
+# ----------------------------------------------------------------------------------------------------
+def _commit_check(offsets, accept_len, accept_index, slots, seq, max_len):
+    g = np_out(dva.commit_indices(dev(offsets, torch.int32), dev(accept_len, torch.int32),
+                                  dev(accept_index, torch.int32), dev(slots, torch.int64), dev(seq, torch.int32),
+                                  max_verify_len=max_len))
+    o = oracle.commit_indices(offsets, accept_len, accept_index, slots, seq, max_len)
+    n = int(o["commit_offsets"][-1])
+    ne = int(o["evict_offsets"][-1])
+    assert np.array_equal(g["commit_offsets"], o["commit_offsets"])
+    assert np.array_equal(g["src_slots"][:n], o["src_slots"])
+    assert np.array_equal(g["dst_pos"][:n], o["dst_pos"])
+    assert np.array_equal(g["new_seq_lens"], o["new_seq_lens"])
+    assert np.array_equal(g["status"], o["status"])
+    assert np.array_equal(g["evict_offsets"], o["evict_offsets"])
+    assert np.array_equal(g["evict_slots"][:ne], o["evict_slots"])
+    return g
+
+
+def test_commit_parity_chain_and_tree():
+    w = W.ragged(seed=5003, batch=1500, vocab=64, parallel=False)     # > one tile of 1024 requests
+    g = run_chain(w, "rejection")
+    slots = W.verify_slots_for(w.total_rows)
+    seq = W.seq_lens_for(w.batch)
+    _commit_check(w.offsets, g["accept_len"], g["accept_index"], slots, seq, 16)
+    tw = W.tree(seed=4003, batch=8, vocab=2000, parallel=False)
+    gt = run_tree(tw, "greedy")
+    offs = (np.arange(tw.batch + 1) * tw.n_nodes).astype(np.int32)
+    _commit_check(offs, gt["accept_len"], gt["accept_index"], W.verify_slots_for(tw.total_rows), W.seq_lens_for(8),
+                  tw.n_nodes)
+    # worked example: verify D E F G H, E F accepted -> commit D E F after 3 committed tokens
+    _commit_check(np.array([0, 5], np.int32), np.array([2], np.int32), np.array([0, 1, 2, -1, -1], np.int32),
+                  np.arange(100, 105), np.array([3], np.int32), 5)
+    # invalid accept lengths / indices are reported
+    g2 = np_out(dva.commit_indices(dev(np.array([0, 3, 6], np.int32)), dev(np.array([5, 1], np.int32)),
+                                   dev(np.array([0, 1, 2, 3, 3, -1], np.int32)), dev(np.arange(6, dtype=np.int64)),
+                                   dev(np.array([0, 0], np.int32)), max_verify_len=4))
+    assert g2["status"][0] & oracle.ST_BAD_ACCEPT and g2["status"][1] & oracle.ST_BAD_ACCEPT
