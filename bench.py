@@ -1,0 +1,324 @@
+#!/usr/bin/env python3
+"""Throughput of the speculative-decoding verify -> accept -> commit hot path on one MI355X.
+
+One step = one verify round of the timed workload: spec_verify_chain (every target and draft logit row
+streamed once, accept scan, residual / bonus draw, outputs) followed by spec_commit_indices (KV commit
+compaction), both through the C ABI. Inputs are synthetic, seeded and resident in HBM before timing; a
+rotation of input sets keeps the live footprint above twice the 256 MB Infinity Cache so HBM, not the
+cache, serves the stream.
+
+Prints ONE JSON line. value = verified positions per second (target rows judged, sum_b (m_b + 1)).
+roofline: the dominant kernel (k_stats, the logits stream) timed with HIP events the library records around
+it, against its algorithmic bytes (every target and draft row read once). cpu_baseline: the fp64 CPU
+oracle timed on this host on the same inputs.
+
+    python bench.py [--steps K] [--warmup W] [--workload chain_rejection|block_greedy|tree|ragged]
+                    [--no-extra] [--no-cpu-baseline] [--copy-calibration]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor peak
+MALL_BYTES = 256 << 20         # Infinity Cache
+METRIC = "verified draft positions/sec (bf16 logits, V=151936) and % of HBM peak"
+DEFAULT_WORKLOAD = "chain_rejection"
+
+
+def _log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "draft_verification_acceptance_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+# ----------------------------------------------------------------------------------------------------
+# workloads on the device
+# ----------------------------------------------------------------------------------------------------
+def _dev_logits(a):
+    import numpy as np
+    import torch
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(a).cuda()
+
+
+def _dev(a):
+    import numpy as np
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def build_sets(name: str):
+    """Seeded input sets (seed 1000*k + i) until the live footprint exceeds 2x the Infinity Cache."""
+    from draft_verification_acceptance_amd import workloads as W
+    base = {"tiny_chain": 1000, "chain_rejection": 2000, "block_greedy": 3000, "tree": 4000, "ragged": 5000}[name]
+    sets = []
+    total = 0
+    i = 0
+    while total <= 2 * MALL_BYTES or len(sets) < 2:
+        w = W.FULL[name](seed=base + i)
+        mode = w.modes[-1]
+        sets.append(w)
+        total += w.algorithmic_bytes(mode)
+        i += 1
+    return sets
+
+
+class ChainStep:
+    def __init__(self, w, mode):
+        import torch
+
+        import draft_verification_acceptance_amd as dva
+        from draft_verification_acceptance_amd import workloads as W
+        self.w = w
+        t = _dev_logits(w.target)
+        offs = _dev(w.offsets)
+        kw = dict(max_verify_len=w.max_verify_len)
+        if mode == "rejection":
+            kw.update(draft_logits=_dev_logits(w.draft), u_accept=_dev(w.u_accept), u_final=_dev(w.u_final),
+                      temperature=w.temperature)
+        self.verify = dva.prepare_verify_chain(t, offs, _dev(w.draft_tokens), mode, **kw)
+        o = self.verify.outputs
+        self.commit = dva.prepare_commit_indices(offs, o["accept_len"], o["accept_index"],
+                                                 _dev(W.verify_slots_for(w.total_rows)), _dev(W.seq_lens_for(w.batch)),
+                                                 max_verify_len=w.max_verify_len)
+        self.positions = w.total_rows
+        self.draft_positions = w.total_rows - w.batch
+        self.bytes = w.algorithmic_bytes(mode)
+        torch.cuda.synchronize()
+
+
+class TreeStep:
+    def __init__(self, w, mode):
+        import numpy as np
+        import torch
+
+        import draft_verification_acceptance_amd as dva
+        from draft_verification_acceptance_amd import workloads as W
+        self.w = w
+        kw = {}
+        if mode == "target_only":
+            kw = dict(u_accept=_dev(w.u_accept), u_final=_dev(w.u_final), temperature=w.temperature)
+        self.verify = dva.prepare_verify_tree(_dev_logits(w.target), _dev(w.parents), _dev(w.tokens), w.n_nodes, mode,
+                                              **kw)
+        o = self.verify.outputs
+        offs = _dev((np.arange(w.batch + 1) * w.n_nodes).astype(np.int32))
+        self.commit = dva.prepare_commit_indices(offs, o["accept_len"], o["accept_index"],
+                                                 _dev(W.verify_slots_for(w.total_rows)), _dev(W.seq_lens_for(w.batch)),
+                                                 max_verify_len=w.n_nodes)
+        self.positions = w.total_rows
+        self.draft_positions = w.total_rows - w.batch
+        self.bytes = w.algorithmic_bytes(mode)
+        torch.cuda.synchronize()
+
+
+def run_workload(name: str, mode: str | None, steps: int, warmup: int) -> dict:
+    import numpy as np
+    import torch
+
+    import draft_verification_acceptance_amd as dva
+    t0 = time.time()
+    sets = build_sets(name)
+    mode = mode or sets[0].modes[-1]
+    kind = "tree" if name == "tree" else "chain"
+    st = [(TreeStep if kind == "tree" else ChainStep)(w, mode) for w in sets]
+    _log(f"[bench] {name}/{mode}: {len(sets)} input sets, {sum(s.bytes for s in st) / 1e6:.0f} MB live, "
+         f"setup {time.time() - t0:.1f}s")
+    nk = dva.kernel_count(kind, mode)
+    ev_v = [dva.HipEvents(nk + 1) for _ in range(steps)]
+    ev_c = [dva.HipEvents(2) for _ in range(steps)]
+    for i in range(warmup):
+        s = st[i % len(st)]
+        s.verify.run()
+        s.commit.run()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for i in range(steps):
+        s = st[i % len(st)]
+        s.verify.run(ev_v[i])
+        s.commit.run(ev_c[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t1
+    k_stats = np.array([e.elapsed_ms(0, 1) for e in ev_v])
+    k_draw = np.array([e.elapsed_ms(1, 2) for e in ev_v]) if nk > 1 else np.zeros(steps)
+    k_commit = np.array([e.elapsed_ms(0, 1) for e in ev_c])
+    verify_ms = k_stats + k_draw
+    positions = np.mean([st[i % len(st)].positions for i in range(steps)])
+    draft_positions = np.mean([st[i % len(st)].draft_positions for i in range(steps)])
+    nbytes = np.mean([st[i % len(st)].bytes for i in range(steps)])
+    # Sanity of the last results (no data faults in these synthetic inputs).
+    stat = st[(steps - 1) % len(st)].verify.outputs["status"].cpu().numpy().view(np.uint32)
+    bad = int(np.count_nonzero(stat & ~np.uint32(dva.ST.NEAR_ALPHA | dva.ST.NEAR_CDF)))
+    acc = st[(steps - 1) % len(st)].verify.outputs["accept_len"].float().mean().item()
+    ms_step = wall * 1e3 / steps
+    stats_ms = float(np.mean(k_stats))
+    return {
+        "workload": name, "mode": mode, "batch": sets[0].batch, "vocab": sets[0].vocab,
+        "verify_positions_per_step": float(positions), "draft_positions_per_step": float(draft_positions),
+        "algorithmic_bytes_per_step": float(nbytes), "rotation_sets": len(sets),
+        "ms_per_step": ms_step,
+        "positions_per_s": positions / (ms_step * 1e-3),
+        "draft_positions_per_s": draft_positions / (ms_step * 1e-3),
+        "step_hbm_fraction": nbytes / (ms_step * 1e-3) / (HBM_PEAK_GBS * 1e9),
+        "kernel_ms": {"k_stats": {"mean": stats_ms, "p10": float(np.percentile(k_stats, 10)),
+                                  "p50": float(np.median(k_stats)), "p90": float(np.percentile(k_stats, 90))},
+                      "k_draw": float(np.mean(k_draw)), "k_commit": float(np.mean(k_commit)),
+                      "verify_call_p50": float(np.median(verify_ms))},
+        "stats_kernel_gbs": nbytes / (stats_ms * 1e-3) / 1e9,
+        "mean_accept_len": acc,
+        "status_faults": bad,
+    }
+
+
+def cpu_baseline(name: str, budget_s: float = 12.0) -> dict:
+    """The fp64 oracle on this host's cores, on the canonical input set of the timed workload."""
+    import numpy as np
+
+    import oracle
+    from draft_verification_acceptance_amd import workloads as W
+    w = W.FULL[name](seed={"chain_rejection": 2000, "block_greedy": 3000, "tree": 4000, "ragged": 5000}[name])
+    mode = w.modes[-1]
+    slots = W.verify_slots_for(w.total_rows)
+    seq = W.seq_lens_for(w.batch)
+    passes = 0
+    rows = 0
+    t0 = time.perf_counter()
+    while True:
+        if name == "tree":
+            o = oracle.verify_tree(w.target, w.parents, w.tokens, w.n_nodes, mode, u_accept=w.u_accept,
+                                   u_final=w.u_final, temperature=w.temperature)
+            offs = np.arange(w.batch + 1) * w.n_nodes
+            oracle.commit_indices(offs, o["accept_len"], o["accept_index"], slots, seq, w.n_nodes)
+        else:
+            o = oracle.verify_chain(w.target, w.offsets, w.draft_tokens, mode, draft=w.draft, u_accept=w.u_accept,
+                                    u_final=w.u_final, temperature=w.temperature, max_verify_len=w.max_verify_len)
+            oracle.commit_indices(w.offsets, o["accept_len"], o["accept_index"], slots, seq, w.max_verify_len)
+        passes += 1
+        rows += w.total_rows
+        if time.perf_counter() - t0 >= budget_s or passes >= 20:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": rows / dt, "unit": "positions/s", "cores": 1, "kind": "oracle",
+            "sample": f"{passes} full pass(es) over one input set of the timed workload ({w.batch} requests, "
+                      f"{w.total_rows} verify rows, fp64 numpy, one thread) incl. commit; {dt:.1f} s"}
+
+
+def load_traffic(name: str, stats_bytes: float):
+    """HBM traffic of k_stats from committed rocprofv3 counter runs, if taken on the current kernels."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("k_stats_hbm_bytes_per_launch")
+
+
+def copy_calibration():
+    """A plain copy of known size, for scaling rocprofv3's FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n, "copies": 3}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=["chain_rejection", "block_greedy", "tree",
+                                                                       "ragged"])
+    ap.add_argument("--mode", default=None)
+    ap.add_argument("--no-extra", action="store_true", help="skip the other full-size workloads")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the verify path shards by request with no exchange, so N GPUs "
+              "would each run this same step on B/N requests; N > 1 is not run.", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    main_res = run_workload(args.workload, args.mode, args.steps, args.warmup)
+    extra = {}
+    if not args.no_extra:
+        for name, mode in (("block_greedy", None), ("ragged", None), ("tree", "greedy"), ("tree", "target_only")):
+            if name == args.workload and (mode or "") == (args.mode or ""):
+                continue
+            r = run_workload(name, mode, max(50, args.steps // 2), args.warmup)
+            extra[f"{name}/{r['mode']}"] = {k: r[k] for k in ("verify_positions_per_step", "ms_per_step",
+                                                              "positions_per_s", "step_hbm_fraction",
+                                                              "stats_kernel_gbs", "kernel_ms", "mean_accept_len",
+                                                              "status_faults")}
+            torch.cuda.empty_cache()
+    stats_ms = main_res["kernel_ms"]["k_stats"]["mean"]
+    achieved = main_res["stats_kernel_gbs"]
+    traffic = load_traffic(main_res["workload"], main_res["algorithmic_bytes_per_step"])
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(main_res["workload"])
+    line = {
+        "metric": METRIC,
+        "value": main_res["positions_per_s"],
+        "unit": "positions/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": main_res["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded, shaped like the pages' workloads)",
+        "config": {"workload": f"{main_res['workload']}: B {main_res['batch']}, V {main_res['vocab']}, "
+                               f"{main_res['mode']}, {main_res['verify_positions_per_step']:.0f} verify rows/step",
+                   "mode": main_res["mode"], "batch": main_res["batch"], "vocab": main_res["vocab"],
+                   "verify_positions_per_step": main_res["verify_positions_per_step"],
+                   "draft_positions_per_step": main_res["draft_positions_per_step"],
+                   "rotation_sets": main_res["rotation_sets"], "parallelism": "none (one GPU)"},
+        "draft_positions_per_s": main_res["draft_positions_per_s"],
+        "step_hbm_fraction": main_res["step_hbm_fraction"],
+        "roofline": {"bound": "hbm", "kernel": "k_stats", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "algorithmic_bytes_per_launch": main_res["algorithmic_bytes_per_step"],
+                     "avg_launch_ms": stats_ms},
+        "kernel_ms": main_res["kernel_ms"],
+        "mean_accept_len": main_res["mean_accept_len"],
+        "status_faults": main_res["status_faults"],
+        "cpu_baseline": cpu,
+        "other_workloads": extra,
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -19,7 +19,7 @@ import torch
 __all__ = [
     "SpecError", "verify_chain", "verify_tree", "commit_indices", "workspace", "workspace_bytes",
     "workspace_init", "kernel_count", "status_string", "abi_version", "library_path", "HipEvents",
-    "MODES", "ST",
+    "MODES", "ST", "PreparedCall", "prepare_verify_chain", "prepare_verify_tree", "prepare_commit_indices",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -235,16 +235,32 @@ def _outputs(out, device, batch, rows, draft_rows, want_prob, want_resid):
     return out
 
 
-def verify_chain(target_logits: torch.Tensor, target_offsets: torch.Tensor, draft_tokens: torch.Tensor,
-                 mode: str = "greedy", *, draft_logits: torch.Tensor | None = None,
-                 u_accept: torch.Tensor | None = None, u_final: torch.Tensor | None = None,
-                 temperature: float = 1.0, max_verify_len: int | None = None, workspace_tensor=None,
-                 out: dict | None = None, accept_prob: bool = True, residual_mass: bool = True,
-                 events: HipEvents | None = None) -> dict:
-    """spec_verify_chain on torch tensors (launched on the current stream; asynchronous).
+class PreparedCall:
+    """A verify / commit call whose argument block is built once; run() launches it again on the current
+    stream of its device (same tensors, same workspace). Keeps every tensor it points at alive."""
 
-    target_logits [T_rows, V] bf16/fp32; target_offsets int32 [B+1]; draft-side int32 tokens, float32
-    uniforms and logits packed with m_b entries per request from off[b]-b. Returns the output tensors."""
+    def __init__(self, fn, args, outputs: dict, keep: list, device):
+        self._fn = fn
+        self._args = args
+        self.outputs = outputs
+        self._keep = keep
+        self._device = device
+
+    def run(self, events: "HipEvents | None" = None, stream: int | None = None) -> dict:
+        a = self._args
+        a.profile_events = events.pointer() if events is not None else None
+        a.n_profile_events = events.n if events is not None else 0
+        _check(self._fn(ctypes.byref(a), _stream(self._device) if stream is None else stream))
+        return self.outputs
+
+
+def prepare_verify_chain(target_logits: torch.Tensor, target_offsets: torch.Tensor, draft_tokens: torch.Tensor,
+                         mode: str = "greedy", *, draft_logits: torch.Tensor | None = None,
+                         u_accept: torch.Tensor | None = None, u_final: torch.Tensor | None = None,
+                         temperature: float = 1.0, max_verify_len: int | None = None, workspace_tensor=None,
+                         out: dict | None = None, accept_prob: bool = True,
+                         residual_mass: bool = True) -> PreparedCall:
+    """Checks and marshals the arguments of spec_verify_chain once (see verify_chain)."""
     lib = _lib()
     dev = target_logits.device
     if target_logits.dim() != 2:
@@ -264,6 +280,8 @@ def verify_chain(target_logits: torch.Tensor, target_offsets: torch.Tensor, draf
         _req(draft_logits, "draft_logits", target_logits.dtype, D * V, dev)
         _req(u_accept, "u_accept", torch.float32, D, dev)
         _req(u_final, "u_final", torch.float32, B, dev)
+    elif mode != "greedy":
+        raise SpecError(3, status_string(3))
     if workspace_tensor is None:
         workspace_tensor = workspace("chain", mode, T, V, B, max_verify_len, dev)
     o = _outputs(out, dev, B, T, D, accept_prob, residual_mass)
@@ -281,23 +299,33 @@ def verify_chain(target_logits: torch.Tensor, target_offsets: torch.Tensor, draf
     a.residual_mass = _ptr(o.get("residual_mass")) if residual_mass else None
     a.workspace = workspace_tensor.data_ptr()
     a.workspace_bytes = workspace_tensor.numel()
-    a.profile_events = events.pointer() if events is not None else None
-    a.n_profile_events = events.n if events is not None else 0
     a.total_rows, a.vocab, a.batch = T, V, B
     a.max_verify_len = int(max_verify_len)
     a.dtype = DTYPES[target_logits.dtype]
     a.mode = m
     a.temperature = float(temperature)
-    _check(lib.spec_verify_chain(ctypes.byref(a), _stream(dev)))
-    return o
+    keep = [target_logits, target_offsets, draft_tokens, draft_logits, u_accept, u_final, workspace_tensor]
+    return PreparedCall(lib.spec_verify_chain, a, o, keep, dev)
 
 
-def verify_tree(target_logits: torch.Tensor, parents: torch.Tensor, tokens: torch.Tensor, n_nodes: int,
-                mode: str = "greedy", *, u_accept=None, u_final=None, temperature: float = 1.0,
-                threshold_single: float = 1.0, threshold_acc: float = 1.0, workspace_tensor=None,
-                out: dict | None = None, accept_prob: bool = True, residual_mass: bool = True,
-                events: HipEvents | None = None) -> dict:
-    """spec_verify_tree on torch tensors: target_logits [B*N, V]; parents, tokens int32 [B*N]."""
+def verify_chain(target_logits: torch.Tensor, target_offsets: torch.Tensor, draft_tokens: torch.Tensor,
+                 mode: str = "greedy", *, events: "HipEvents | None" = None, **kw) -> dict:
+    """spec_verify_chain on torch tensors (launched on the current stream; asynchronous).
+
+    target_logits [T_rows, V] bf16/fp32; target_offsets int32 [B+1]; draft-side int32 tokens, float32
+    uniforms and logits packed with m_b entries per request from off[b]-b; max_verify_len bounds m_b + 1.
+    Keywords: draft_logits, u_accept, u_final, temperature, max_verify_len, workspace_tensor, out,
+    accept_prob, residual_mass. Returns the output tensors (accept_len, bonus, out_tokens, accept_index,
+    status, accept_prob, residual_mass)."""
+    return prepare_verify_chain(target_logits, target_offsets, draft_tokens, mode, **kw).run(events)
+
+
+def prepare_verify_tree(target_logits: torch.Tensor, parents: torch.Tensor, tokens: torch.Tensor, n_nodes: int,
+                        mode: str = "greedy", *, u_accept=None, u_final=None, temperature: float = 1.0,
+                        threshold_single: float = 1.0, threshold_acc: float = 1.0, workspace_tensor=None,
+                        out: dict | None = None, accept_prob: bool = True,
+                        residual_mass: bool = True) -> PreparedCall:
+    """Checks and marshals the arguments of spec_verify_tree once (see verify_tree)."""
     lib = _lib()
     dev = target_logits.device
     if target_logits.dim() != 2 or target_logits.dtype not in DTYPES:
@@ -313,6 +341,8 @@ def verify_tree(target_logits: torch.Tensor, parents: torch.Tensor, tokens: torc
     if mode == "target_only":
         _req(u_accept, "u_accept", torch.float32, rows, dev)
         _req(u_final, "u_final", torch.float32, B, dev)
+    elif mode != "greedy":
+        raise SpecError(3, status_string(3))
     if workspace_tensor is None:
         workspace_tensor = workspace("tree", mode, rows, V, B, N, dev)
     o = _outputs(out, dev, B, rows, rows, accept_prob, residual_mass)
@@ -326,23 +356,27 @@ def verify_tree(target_logits: torch.Tensor, parents: torch.Tensor, tokens: torc
     a.residual_mass = _ptr(o.get("residual_mass")) if residual_mass else None
     a.workspace = workspace_tensor.data_ptr()
     a.workspace_bytes = workspace_tensor.numel()
-    a.profile_events = events.pointer() if events is not None else None
-    a.n_profile_events = events.n if events is not None else 0
     a.vocab, a.batch, a.n_nodes = V, B, N
     a.dtype = DTYPES[target_logits.dtype]
     a.mode = MODES[mode]
     a.temperature = float(temperature)
     a.threshold_single, a.threshold_acc = float(threshold_single), float(threshold_acc)
-    _check(lib.spec_verify_tree(ctypes.byref(a), _stream(dev)))
-    return o
+    keep = [target_logits, parents, tokens, u_accept, u_final, workspace_tensor]
+    return PreparedCall(lib.spec_verify_tree, a, o, keep, dev)
 
 
-def commit_indices(row_offsets: torch.Tensor, accept_len: torch.Tensor, accept_index: torch.Tensor,
-                   verify_slots: torch.Tensor, seq_lens: torch.Tensor, *, max_verify_len: int,
-                   evict: bool = True, out: dict | None = None, events: HipEvents | None = None) -> dict:
-    """spec_commit_indices on torch tensors. Returns commit_offsets, src_slots, dst_pos, new_seq_lens,
-    status (and evict_offsets, evict_slots). src_slots / dst_pos are sized total_rows; the valid part is
-    commit_offsets[-1] entries long."""
+def verify_tree(target_logits: torch.Tensor, parents: torch.Tensor, tokens: torch.Tensor, n_nodes: int,
+                mode: str = "greedy", *, events: "HipEvents | None" = None, **kw) -> dict:
+    """spec_verify_tree on torch tensors: target_logits [B*N, V]; parents, tokens int32 [B*N]. Keywords:
+    u_accept, u_final, temperature, threshold_single, threshold_acc, workspace_tensor, out, accept_prob,
+    residual_mass."""
+    return prepare_verify_tree(target_logits, parents, tokens, n_nodes, mode, **kw).run(events)
+
+
+def prepare_commit_indices(row_offsets: torch.Tensor, accept_len: torch.Tensor, accept_index: torch.Tensor,
+                           verify_slots: torch.Tensor, seq_lens: torch.Tensor, *, max_verify_len: int,
+                           evict: bool = True, out: dict | None = None) -> PreparedCall:
+    """Checks and marshals the arguments of spec_commit_indices once (see commit_indices)."""
     lib = _lib()
     dev = row_offsets.device
     _req(row_offsets, "row_offsets", torch.int32, device=dev)
@@ -375,9 +409,17 @@ def commit_indices(row_offsets: torch.Tensor, accept_len: torch.Tensor, accept_i
     a.new_seq_lens, a.status = _ptr(o["new_seq_lens"]), _ptr(o["status"])
     a.evict_slots = _ptr(o.get("evict_slots")) if evict else None
     a.evict_offsets = _ptr(o.get("evict_offsets")) if evict else None
-    a.profile_events = events.pointer() if events is not None else None
-    a.n_profile_events = events.n if events is not None else 0
     a.total_rows, a.capacity, a.batch = T, T, B
     a.max_verify_len = int(max_verify_len)
-    _check(lib.spec_commit_indices(ctypes.byref(a), _stream(dev)))
-    return o
+    keep = [row_offsets, accept_len, accept_index, verify_slots, seq_lens]
+    return PreparedCall(lib.spec_commit_indices, a, o, keep, dev)
+
+
+def commit_indices(row_offsets: torch.Tensor, accept_len: torch.Tensor, accept_index: torch.Tensor,
+                   verify_slots: torch.Tensor, seq_lens: torch.Tensor, *, max_verify_len: int,
+                   evict: bool = True, out: dict | None = None, events: "HipEvents | None" = None) -> dict:
+    """spec_commit_indices on torch tensors. Returns commit_offsets, src_slots, dst_pos, new_seq_lens,
+    status (and evict_offsets, evict_slots). src_slots / dst_pos are sized total_rows; the valid part is
+    commit_offsets[-1] entries long."""
+    return prepare_commit_indices(row_offsets, accept_len, accept_index, verify_slots, seq_lens,
+                                  max_verify_len=max_verify_len, evict=evict, out=out).run(events)

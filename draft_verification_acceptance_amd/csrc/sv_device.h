@@ -67,17 +67,37 @@ __device__ __forceinline__ float sanitize_u(float u, bool& bad) {
   return fminf(fmaxf(u, 0.f), 0x1.fffffep-1f);
 }
 
-// Advance a per-request completion counter of this call (epoch in the high word, count in the low word;
-// a word left by another call restarts at 1). Returns the count after this increment.
+// Cross-workgroup hand-off without cache-wide fences. Partial results travel through agent-scope
+// atomic stores and loads (coherent across the XCDs' separate L2s) and a per-request completion counter;
+// the writer waits for its stores to complete before counting, so the workgroup that sees the final count
+// reads complete partials.
+__device__ __forceinline__ void store_agent(unsigned long long* p, unsigned long long v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ unsigned long long load_agent(unsigned long long* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Every memory operation this thread issued has completed (vmcnt = lgkmcnt = expcnt = 0); also keeps the
+// compiler from moving memory accesses across it.
+__device__ __forceinline__ void complete_memory_ops() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Advance a per-request completion counter of this call: a 64-bit word (epoch << 32 | count). A word
+// left by another call (other epoch) is restarted at 1 by one compare-and-swap; otherwise a single
+// atomic add. Returns the count after this increment.
 __device__ __forceinline__ uint32_t count_done(unsigned long long* c, uint32_t epoch) {
-  unsigned long long old = __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  while (true) {
-    const unsigned long long want =
-        uint32_t(old >> 32) == epoch ? old + 1ull : ((unsigned long long)epoch << 32) | 1ull;
-    const unsigned long long prev = atomicCAS(c, old, want);
-    if (prev == old) return uint32_t(want);
-    old = prev;
+  unsigned long long old = load_agent(c);
+  if (uint32_t(old >> 32) != epoch) {
+    const unsigned long long fresh = ((unsigned long long)epoch << 32) | 1ull;
+    if (atomicCAS(c, old, fresh) == old) return 1u;
+    // another workgroup of this call restarted it first: the word now carries this epoch
   }
+  return uint32_t(atomicAdd(c, 1ull)) + 1u;
 }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }

@@ -41,6 +41,20 @@ __device__ __forceinline__ void weight(const RowCtx& r, int64_t e, const int32_t
   }
 }
 
+// Segment sums are published and read as agent-scope 64-bit atomics (see complete_memory_ops).
+__device__ __forceinline__ void store_seg(float2* dst, float w, float pv) {
+  store_agent(reinterpret_cast<unsigned long long*>(dst),
+              (unsigned long long)__float_as_uint(w) | ((unsigned long long)__float_as_uint(pv) << 32));
+}
+
+struct SegView {
+  float2* base;
+  __device__ __forceinline__ float2 operator[](int s) const {
+    const unsigned long long v = load_agent(reinterpret_cast<unsigned long long*>(base + s));
+    return make_float2(__uint_as_float(uint32_t(v)), __uint_as_float(uint32_t(v >> 32)));
+  }
+};
+
 template <typename DT>
 __global__ __launch_bounds__(kThreads) void k_draw(DrawParams p) {
   __shared__ int32_t s_seen[kMaxLen];
@@ -96,20 +110,17 @@ __global__ __launch_bounds__(kThreads) void k_draw(DrawParams p) {
     }
     sw = wave_sum(sw);
     sp = wave_sum(sp);
-    if (lane == 0) p.seg[int64_t(b) * p.n_seg + s] = make_float2(sw, sp);
+    if (lane == 0) store_seg(p.seg + int64_t(b) * p.n_seg + s, sw, sp);
   }
 
+  complete_memory_ops();   // every wave's segment sums are stored before the workgroup is counted
   __syncthreads();
-  if (tid == 0) {
-    __threadfence();   // release this workgroup's segment sums
-    s_last = count_done(p.cnt2 + b, p.epoch) == uint32_t(p.S2);
-  }
+  if (tid == 0) s_last = count_done(p.cnt2 + b, p.epoch) == uint32_t(p.S2);
   __syncthreads();
   if (!s_last) return;
-  __threadfence();   // acquire the other workgroups' segment sums
 
   // ---- selection: float64 prefix over segments, then one segment token by token ----
-  const float2* seg = p.seg + int64_t(b) * p.n_seg;
+  SegView seg{p.seg + int64_t(b) * p.n_seg};
   const int R = (p.n_seg + kThreads - 1) / kThreads;
   const int r_lo = min(p.n_seg, tid * R);
   const int r_hi = min(p.n_seg, r_lo + R);

@@ -212,11 +212,30 @@ __device__ __forceinline__ float gather(const void* base, int64_t row, int64_t V
   return Elem<DT>::load(static_cast<const DT*>(base) + row * V, col);
 }
 
+// Partials are published and read as two agent-scope 64-bit atomics (see complete_memory_ops).
+__device__ __forceinline__ void store_part(Part* dst, const Part& v) {
+  unsigned long long* d = reinterpret_cast<unsigned long long*>(dst);
+  store_agent(d, (unsigned long long)__float_as_uint(v.a) | ((unsigned long long)__float_as_uint(v.b) << 32));
+  store_agent(d + 1, (unsigned long long)uint32_t(v.idx) | ((unsigned long long)v.flags << 32));
+}
+
+__device__ __forceinline__ Part load_part(const Part* src) {
+  unsigned long long* s = reinterpret_cast<unsigned long long*>(const_cast<Part*>(src));
+  const unsigned long long w0 = load_agent(s);
+  const unsigned long long w1 = load_agent(s + 1);
+  Part r;
+  r.a = __uint_as_float(uint32_t(w0));
+  r.b = __uint_as_float(uint32_t(w0 >> 32));
+  r.idx = int32_t(uint32_t(w1));
+  r.flags = uint32_t(w1 >> 32);
+  return r;
+}
+
 // Merge the S partials of one row slot.
 __device__ __forceinline__ Part merge_greedy(const Part* p, int S) {
-  Part r = p[0];
+  Part r = load_part(p);
   for (int c = 1; c < S; ++c) {
-    const Part q = p[c];
+    const Part q = load_part(p + c);
     if (better(q.a, q.idx, r.a, r.idx)) { r.a = q.a; r.idx = q.idx; }
     r.flags |= q.flags;
   }
@@ -224,9 +243,13 @@ __device__ __forceinline__ Part merge_greedy(const Part* p, int S) {
 }
 
 __device__ __forceinline__ void merge_sampling(const Part* p, int S, float& m, float& z) {
-  m = p[0].a;
-  z = p[0].b;
-  for (int c = 1; c < S; ++c) merge_mz(m, z, p[c].a, p[c].b);
+  const Part first = load_part(p);
+  m = first.a;
+  z = first.b;
+  for (int c = 1; c < S; ++c) {
+    const Part q = load_part(p + c);
+    merge_mz(m, z, q.a, q.b);
+  }
 }
 
 // A sampling row is usable iff its normaliser is a positive finite number (NaN: a NaN or +inf logit;
@@ -623,14 +646,13 @@ __global__ __launch_bounds__(kThreads) void k_stats(StatsParams p) {
   else chunk_argmax<DT>(base, lo, hi, s_part, red_f, red_i, red_u);
 
   if (threadIdx.x == 0) {
-    p.part[((size_t(b) * p.L + slot) * p.P + part) * p.S + chunk] = s_part;
-    __threadfence();   // release the partial before counting it
+    store_part(p.part + ((size_t(b) * p.L + slot) * p.P + part) * p.S + chunk, s_part);
+    complete_memory_ops();   // the partial is stored before it is counted
     const uint32_t expected = uint32_t((TREE ? len : (p.P == 2 ? 2 * len - 1 : len)) * p.S);
     s_last = count_done(p.cnt + b, p.epoch) == expected;
   }
   __syncthreads();
   if (!s_last) return;
-  __threadfence();   // acquire: the other workgroups' partials
   if (TREE) scan_tree<DT, SAMPLING>(p, b, smem);
   else if (SAMPLING) scan_chain_rejection<DT>(p, b, off0, int(len), smem);
   else scan_chain_greedy<DT>(p, b, off0, int(len), smem);

@@ -13,7 +13,7 @@ their order and notation:
 
 Verify rows are [a, d1 .. dm]: row j is the target's distribution for the token after d_j (row 0: after the
 anchor a), so row j-1 judges d_j and row m yields the bonus ([EAGLE→DFlash2] §1.1). Readings taken where
-the pages leave a step open are marked READING; all of them are listed in the repository's design notes.
+the pages leave a step open are marked READING.
 
 Pins: every function here is checked in tests/test_oracle_pins.py against values the pages print, closed
 forms, brute force and textbook special cases. No function is "parity unpinned".
