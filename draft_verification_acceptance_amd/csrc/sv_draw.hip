@@ -115,7 +115,7 @@ __global__ __launch_bounds__(kThreads) void k_draw(DrawParams p) {
 
   complete_memory_ops();   // every wave's segment sums are stored before the workgroup is counted
   __syncthreads();
-  if (tid == 0) s_last = count_done(p.cnt2 + b, p.epoch) == uint32_t(p.S2);
+  if (tid == 0) s_last = count_done(p.cnt2 + size_t(b) * kCounterWords, p.epoch) == uint32_t(p.S2);
   __syncthreads();
   if (!s_last) return;
 

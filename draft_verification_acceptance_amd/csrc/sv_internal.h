@@ -30,6 +30,11 @@ constexpr int kWave = 64;            // gfx950 wavefront size
 constexpr int kSeg = 512;            // tokens per draw segment (one wave: 8 tokens per lane)
 constexpr int kMaxLen = 1024;        // max verify rows per request (chain) / nodes per tree
 constexpr int64_t kMaxVocab = int64_t(1) << 22;
+// Per-request completion counters sit 256 bytes apart: a request's workgroups all update its counter at
+// the end of the kernel, and counters sharing a cache line would serialise every request's updates on
+// one memory channel while the logits stream saturates HBM.
+constexpr size_t kCounterStride = 256;
+constexpr size_t kCounterWords = kCounterStride / sizeof(unsigned long long);
 constexpr float kNear = 1e-5f;       // |u - alpha| / CDF-gap band reported as NEAR_*
 constexpr float kNearMass = 1e-6f;   // CDF-gap band in probability mass (gap * total weight)
 
@@ -94,8 +99,8 @@ inline Layout make_layout(int kind, int mode, int64_t total_rows, int64_t vocab,
   lo.S2 = (lo.n_seg + lo.spc - 1) / lo.spc;
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
   size_t o = 0;
-  lo.off_cnt = o;  o = up(o + sizeof(uint64_t) * size_t(batch));
-  lo.off_cnt2 = o; o = up(o + sizeof(uint64_t) * size_t(batch));
+  lo.off_cnt = o;  o = up(o + kCounterStride * size_t(batch));
+  lo.off_cnt2 = o; o = up(o + kCounterStride * size_t(batch));
   lo.off_part = o; o = up(o + sizeof(Part) * size_t(slots) * size_t(lo.S));
   lo.off_desc = o; o = up(o + sizeof(DrawDesc) * size_t(batch));
   lo.off_seg = o;  o = up(o + (sampling ? sizeof(float2) * size_t(batch) * size_t(lo.n_seg) : 0));

@@ -649,7 +649,7 @@ __global__ __launch_bounds__(kThreads) void k_stats(StatsParams p) {
     store_part(p.part + ((size_t(b) * p.L + slot) * p.P + part) * p.S + chunk, s_part);
     complete_memory_ops();   // the partial is stored before it is counted
     const uint32_t expected = uint32_t((TREE ? len : (p.P == 2 ? 2 * len - 1 : len)) * p.S);
-    s_last = count_done(p.cnt + b, p.epoch) == expected;
+    s_last = count_done(p.cnt + size_t(b) * kCounterWords, p.epoch) == expected;
   }
   __syncthreads();
   if (!s_last) return;
