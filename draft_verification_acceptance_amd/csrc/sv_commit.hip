@@ -4,8 +4,9 @@
 //   the accepted rows' slots move to contiguous positions after seq_lens ([SpecDec] "实现：共享的骨架",
 //   move_accept_tokens_to_target_kvcache); the other verify rows are listed for eviction (§8.2: rejected
 //   KV must stop being visible, when it is freed is the caller's choice).
-// Requests are handled in tiles of 1024 (thread per request for the scans, thread per (request, row) for
-// the gathers), so any batch size works in one launch.
+// Requests are handled in tiles of up to 1024 requests and 8192 verify rows: thread per request for the
+// scans, thread per verify row for the gathers, with the tile's accept_index entries staged in LDS for the
+// duplicate and eviction checks. Any batch size works in one launch.
 #include "sv_device.h"
 
 namespace sv {
@@ -36,22 +37,26 @@ __device__ __forceinline__ int64_t block_excl_scan_i64(int64_t v, int64_t* red, 
   return base + inc - v;
 }
 
+constexpr int kTileRows = 8192;   // verify rows whose accept_index entries are staged in LDS at once
+
 __global__ __launch_bounds__(kCommitThreads) void k_commit(spec_commit_args a) {
   __shared__ int64_t red[kCommitThreads / kWave];
-  __shared__ int32_t t_off[kCommitThreads];
+  __shared__ int32_t t_off[kCommitThreads + 1];
   __shared__ int32_t t_len[kCommitThreads];
   __shared__ int32_t t_r[kCommitThreads];
-  __shared__ int64_t t_co[kCommitThreads];
-  __shared__ int64_t t_eo[kCommitThreads];
+  __shared__ int32_t t_co[kCommitThreads];
+  __shared__ int32_t t_eo[kCommitThreads];
   __shared__ int32_t t_seq[kCommitThreads];
   __shared__ uint32_t t_st[kCommitThreads];
+  __shared__ int32_t s_ai[kTileRows];
+  __shared__ int s_nb;
 
   const int tid = threadIdx.x;
   const int B = a.batch;
   const int64_t T = a.total_rows;
   const int L = a.max_verify_len;
   int64_t carry_c = 0, carry_e = 0;
-  for (int t0 = 0; t0 < B; t0 += kCommitThreads) {
+  for (int t0 = 0; t0 < B; t0 += s_nb) {
     const int b = t0 + tid;
     int64_t clen = 0, elen = 0;
     int32_t off0 = 0, len = 0, r = 0, seq = 0;
@@ -60,7 +65,7 @@ __global__ __launch_bounds__(kCommitThreads) void k_commit(spec_commit_args a) {
       off0 = a.row_offsets[b];
       const int32_t off1 = a.row_offsets[b + 1];
       len = off1 - off0;
-      bool ok = off0 >= 0 && off1 > off0 && off1 <= T && len <= L;
+      bool ok = off0 >= b && off1 > off0 && off1 <= T - B + b + 1 && len <= L;
       if (b == 0 && off0 != 0) ok = false;
       if (b == B - 1 && off1 != T) ok = false;
       seq = a.seq_lens[b];
@@ -77,56 +82,95 @@ __global__ __launch_bounds__(kCommitThreads) void k_commit(spec_commit_args a) {
         elen = len - clen;
       }
     }
+    // This tile: as many of the next 1024 requests as have at most kTileRows rows in total (the rows
+    // of a valid batch are consecutive; at least one request always fits since len <= 1024).
+    int64_t tl;
+    const int64_t rows_before = block_excl_scan_i64(int64_t(len), red, tl);
+    const bool fits = b < B && rows_before + len <= kTileRows;
+    if (tid == 0) s_nb = 0;
+    __syncthreads();
+    if (fits) atomicMax(&s_nb, tid + 1);
+    __syncthreads();
+    const int nb = s_nb;
+    const bool in_tile = tid < nb;
     int64_t tc, te;
-    const int64_t co = carry_c + block_excl_scan_i64(clen, red, tc);
-    const int64_t eo = carry_e + block_excl_scan_i64(elen, red, te);
-    t_off[tid] = off0;
+    const int64_t co = carry_c + block_excl_scan_i64(in_tile ? clen : 0, red, tc);
+    const int64_t eo = carry_e + block_excl_scan_i64(in_tile ? elen : 0, red, te);
+    t_off[tid] = int32_t(rows_before);   // row index relative to the tile's first row
+    if (tid == nb - 1) t_off[nb] = int32_t(rows_before + len);
     t_len[tid] = len;
     t_r[tid] = r;
-    t_co[tid] = co;
-    t_eo[tid] = eo;
+    t_co[tid] = int32_t(co);
+    t_eo[tid] = int32_t(eo);
     t_seq[tid] = seq;
     t_st[tid] = st;
-    if (b < B) {
+    if (in_tile) {
       a.commit_offsets[b] = int32_t(co);
       a.new_seq_lens[b] = seq + int32_t(clen);
       if (a.evict_offsets) a.evict_offsets[b] = int32_t(eo);
     }
     __syncthreads();
-    const int nb = min(kCommitThreads, B - t0);
-    for (int64_t idx = tid; idx < int64_t(nb) * L; idx += kCommitThreads) {
-      const int lb = int(idx / L);
-      const int k = int(idx % L);
+    // Rows of the tile: global rows [row0, row0 + n_rows) (consecutive for valid offsets; requests with
+    // bad offsets own no rows).
+    const int n_rows = t_off[nb];
+    int32_t row0 = 0;
+    {
+      // first valid request's off0 minus its relative position gives the tile's first global row
+      __shared__ int32_t s_row0;
+      if (tid == 0) s_row0 = 0;
+      __syncthreads();
+      if (in_tile && len > 0 && t_off[tid] == 0) s_row0 = off0;
+      __syncthreads();
+      row0 = s_row0;
+    }
+    for (int i = tid; i < n_rows; i += kCommitThreads) s_ai[i] = row0 + i < T ? a.accept_index[row0 + i] : -1;
+    __syncthreads();
+    for (int i = tid; i < n_rows; i += kCommitThreads) {
+      // request owning relative row i: the last lb with t_off[lb] <= i and t_len[lb] > 0
+      int lo = 0, hi = nb - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (t_off[mid] <= i) lo = mid;
+        else hi = mid - 1;
+      }
+      int lb = lo;
+      while (lb > 0 && t_len[lb] == 0) --lb;
+      const int32_t rel0 = t_off[lb];
       const int32_t len_b = t_len[lb];
-      if (k >= len_b) continue;
-      const int32_t o0 = t_off[lb];
+      const int k = i - rel0;
+      if (k < 0 || k >= len_b) continue;
       const int32_t r_b = t_r[lb];
+      const int32_t o0 = row0 + rel0;
       const int32_t row = o0 + k;
+      if (row >= T) continue;   // only when the offsets are inconsistent (the batch reports BAD_OFFSETS)
       if (k <= r_b) {
-        const int32_t ai = a.accept_index[row];
-        bool valid = ai >= o0 && ai < o0 + len_b;
+        const int32_t ai = s_ai[i];
+        bool valid = ai >= o0 && ai < o0 + len_b && ai < T;
         for (int j = 0; j < k && valid; ++j)
-          if (a.accept_index[o0 + j] == ai) valid = false;   // listed twice
+          if (s_ai[rel0 + j] == ai) valid = false;   // listed twice
         if (!valid) atomicOr(&t_st[lb], SPEC_ST_BAD_ACCEPT);
-        a.src_slots[t_co[lb] + k] = valid ? a.verify_slots[ai] : int64_t(-1);
-        a.dst_pos[t_co[lb] + k] = t_seq[lb] + k;
+        if (int64_t(t_co[lb]) + k < a.capacity) {   // always true unless the offsets are inconsistent
+          a.src_slots[t_co[lb] + k] = valid ? a.verify_slots[ai] : int64_t(-1);
+          a.dst_pos[t_co[lb] + k] = t_seq[lb] + k;
+        }
       }
       if (a.evict_slots) {
         int below = 0;
         bool accepted = false;
         for (int j = 0; j <= r_b; ++j) {
-          const int32_t ai = a.accept_index[o0 + j];
+          const int32_t ai = s_ai[rel0 + j];
           below += ai < row;
           accepted |= ai == row;
         }
         if (!accepted) {
-          const int64_t pos = t_eo[lb] + (k - below);
-          if (pos >= t_eo[lb] && pos < t_eo[lb] + (len_b - r_b - 1)) a.evict_slots[pos] = a.verify_slots[row];
+          const int64_t pos = int64_t(t_eo[lb]) + (k - below);
+          if (pos >= t_eo[lb] && pos < int64_t(t_eo[lb]) + (len_b - r_b - 1) && pos < a.capacity)
+            a.evict_slots[pos] = a.verify_slots[row];
         }
       }
     }
     __syncthreads();
-    if (b < B) a.status[b] = t_st[tid];
+    if (in_tile) a.status[b] = t_st[tid];
     carry_c += tc;
     carry_e += te;
     __syncthreads();

@@ -9,8 +9,8 @@
 // step the last positive-weight token is taken. Weights summing to 0 fall back to p (flagged).
 //
 // Layout of the work: k_draw workgroup (b, c) covers a contiguous range of 512-token segments of request
-// b's row; each wave reduces whole segments (8 tokens per lane, coalesced 128-byte rows of loads) and
-// stores (sum w, sum p) per segment. The request's last workgroup takes a float64 prefix over the
+// b's row; each wave reduces whole segments (8 consecutive tokens per lane, 16-byte loads) and stores
+// (sum w, sum p) per segment. The request's last workgroup takes a float64 prefix over the
 // segments, then rescans the single segment holding u * Z in float64, token by token.
 #include "sv_device.h"
 
@@ -22,23 +22,58 @@ struct RowCtx {
   const void* xt;
   const void* xq;
   float coef, m_t, inv_zt, m_q, inv_zq;
+  bool vec;   // both rows 16-byte aligned: whole 8-token runs load as one (bf16) or two (fp32) vectors
 };
 
-// Weight of token e: w (residual / masked p) and p itself. Identical arithmetic in both passes.
+// The 8 logits of tokens [e, e+8) of one row (tokens past the end of the row read as -inf).
 template <typename DT>
-__device__ __forceinline__ void weight(const RowCtx& r, int64_t e, const int32_t* seen, int n_seen, float& w,
-                                       float& pv) {
-  const float x = Elem<DT>::load(static_cast<const DT*>(r.xt), e);
-  pv = exp2_fast(fmaf(x, r.coef, -r.m_t)) * r.inv_zt;
-  if (r.xq) {
-    const float y = Elem<DT>::load(static_cast<const DT*>(r.xq), e);
-    const float qv = exp2_fast(fmaf(y, r.coef, -r.m_q)) * r.inv_zq;
-    w = fmaxf(pv - qv, 0.f);
+__device__ __forceinline__ void load8(const void* base, int64_t e, int64_t V, bool vec, float* x) {
+  const DT* row = static_cast<const DT*>(base);
+  if (vec && e + 8 <= V) {
+    const uint4* vp = reinterpret_cast<const uint4*>(row + e);
+    constexpr int E = Elem<DT>::kPerVec;
+#pragma unroll
+    for (int v = 0; v < 8 / E; ++v) Elem<DT>::unpack(vp[v], x + v * E);
   } else {
-    w = pv;
-    for (int i = 0; i < n_seen; ++i)
-      if (seen[i] == e) w = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = e + j < V ? Elem<DT>::load(row, e + j) : -INFINITY;
   }
+}
+
+// Weights of tokens [e, e+8): w (residual [p - q]_+, or p with tried tokens zeroed) and p. The same
+// arithmetic serves the segment sums and the token-by-token search, so both see identical values.
+template <typename DT>
+__device__ __forceinline__ void weights8(const RowCtx& r, int64_t e, int64_t V, const int32_t* seen, int n_seen,
+                                         float* w, float* pv) {
+  float x[8];
+  load8<DT>(r.xt, e, V, r.vec, x);
+  if (r.xq) {
+    float y[8];
+    load8<DT>(r.xq, e, V, r.vec, y);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      pv[j] = exp2_fast(fmaf(x[j], r.coef, -r.m_t)) * r.inv_zt;
+      const float qv = exp2_fast(fmaf(y[j], r.coef, -r.m_q)) * r.inv_zq;
+      w[j] = fmaxf(pv[j] - qv, 0.f);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      pv[j] = exp2_fast(fmaf(x[j], r.coef, -r.m_t)) * r.inv_zt;
+      w[j] = pv[j];
+    }
+    for (int i = 0; i < n_seen; ++i) {
+      const int64_t d = int64_t(seen[i]) - e;
+      if (d >= 0 && d < 8) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (j == d) w[j] = 0.f;
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    if (e + j >= V) { w[j] = 0.f; pv[j] = 0.f; }
 }
 
 // Segment sums are published and read as agent-scope 64-bit atomics (see complete_memory_ops).
@@ -81,6 +116,7 @@ __global__ __launch_bounds__(kThreads) void k_draw(DrawParams p) {
   r.inv_zt = 1.f / d.l_t;
   r.m_q = d.m_q;
   r.inv_zq = 1.f / d.l_q;
+  r.vec = (reinterpret_cast<uintptr_t>(r.xt) & 15) == 0 && (reinterpret_cast<uintptr_t>(r.xq) & 15) == 0;
 
   const int s_begin = c * p.spc;
   const int s_end = min(p.n_seg, s_begin + p.spc);
@@ -96,21 +132,26 @@ __global__ __launch_bounds__(kThreads) void k_draw(DrawParams p) {
   __syncthreads();
   const int n_seen = s_nseen;
 
-  for (int s = s_begin + wv; s < s_end; s += kThreads / kWave) {
-    float sw = 0.f, sp = 0.f;
+  // Lane l of a wave owns tokens [s*512 + 8l, s*512 + 8l + 8) of segment s; two segments per trip.
+  constexpr int kW = kThreads / kWave;
+  for (int s = s_begin + wv; s < s_end; s += 2 * kW) {
+    const int s2 = s + kW;
+    float w0[8], p0[8], w1[8], p1[8];
+    weights8<DT>(r, int64_t(s) * kSeg + 8 * lane, p.V, s_seen, n_seen, w0, p0);
+    if (s2 < s_end) weights8<DT>(r, int64_t(s2) * kSeg + 8 * lane, p.V, s_seen, n_seen, w1, p1);
+    float sw = 0.f, sp = 0.f, sw1 = 0.f, sp1 = 0.f;
 #pragma unroll
-    for (int k = 0; k < kSeg / kWave; ++k) {
-      const int64_t e = int64_t(s) * kSeg + k * kWave + lane;
-      if (e < p.V) {
-        float w, pv;
-        weight<DT>(r, e, s_seen, n_seen, w, pv);
-        sw += w;
-        sp += pv;
-      }
-    }
+    for (int j = 0; j < 8; ++j) { sw += w0[j]; sp += p0[j]; }
     sw = wave_sum(sw);
     sp = wave_sum(sp);
     if (lane == 0) store_seg(p.seg + int64_t(b) * p.n_seg + s, sw, sp);
+    if (s2 < s_end) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) { sw1 += w1[j]; sp1 += p1[j]; }
+      sw1 = wave_sum(sw1);
+      sp1 = wave_sum(sp1);
+      if (lane == 0) store_seg(p.seg + int64_t(b) * p.n_seg + s2, sw1, sp1);
+    }
   }
 
   complete_memory_ops();   // every wave's segment sums are stored before the workgroup is counted
@@ -183,39 +224,50 @@ __global__ __launch_bounds__(kThreads) void k_draw(DrawParams p) {
   }
   __syncthreads();
   if (tid < kWave) {
-    const int ns = use_p ? 0 : s_nseen;
-    double carry = sel_excl;
-    int64_t x = -1;
-    double c_lo = 0.0, c_hi = 0.0;
-    int64_t last_e = -1;
-    double last_lo = 0.0, last_hi = 0.0;
-    for (int k = 0; k < kSeg / kWave; ++k) {
-      const int64_t e = g_lo + k * kWave + lane;
-      float w = 0.f, pv = 0.f;
-      if (e < p.V) weight<DT>(r, e, s_seen, ns, w, pv);
-      const double wd = double(use_p ? pv : w);
-      const double inc = carry + wave_inclusive_sum(wd);
-      const uint64_t hit = __ballot(wd > 0.0 && target < inc);
-      if (hit) {
-        const int f = __ffsll((unsigned long long)hit) - 1;
-        x = g_lo + k * kWave + f;
-        c_hi = __shfl(inc, f);
-        c_lo = __shfl(inc - wd, f);
-        break;
-      }
-      const uint64_t pos = __ballot(wd > 0.0);
-      if (pos) {
-        const int l = 63 - __clzll((long long)pos);
-        last_e = g_lo + k * kWave + l;
-        last_hi = __shfl(inc, l);
-        last_lo = __shfl(inc - wd, l);
-      }
-      carry = __shfl(inc, kWave - 1);
+    // Token by token in float64, ascending: lane l holds tokens g_lo + 8l .. g_lo + 8l + 7.
+    float w[8], pv[8];
+    weights8<DT>(r, g_lo + 8 * lane, p.V, s_seen, use_p ? 0 : s_nseen, w, pv);
+    double inc[8];
+    double run = 0.0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      run += double(use_p ? pv[j] : w[j]);
+      inc[j] = run;
     }
-    if (x < 0) {
-      x = last_e >= 0 ? last_e : g_lo;
-      c_hi = last_hi;
-      c_lo = last_lo;
+    const double lane_incl = wave_inclusive_sum(run);
+    const double base = sel_excl + (lane_incl - run);
+    int hit = -1, lastpos = -1;
+#pragma unroll
+    for (int j = 7; j >= 0; --j) {
+      const double wj = double(use_p ? pv[j] : w[j]);
+      if (wj > 0.0 && target < base + inc[j]) hit = j;
+      if (wj > 0.0 && lastpos < 0) lastpos = j;
+    }
+    const uint64_t hmask = __ballot(hit >= 0);
+    int64_t x;
+    double c_lo, c_hi;
+    if (hmask) {
+      const int f = __ffsll((unsigned long long)hmask) - 1;
+      const int j = __shfl(hit, f);
+      double hi = 0.0, wj = 0.0;
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (k == j) { hi = base + inc[k]; wj = double(use_p ? pv[k] : w[k]); }
+      c_hi = __shfl(hi, f);
+      c_lo = __shfl(hi - wj, f);
+      x = g_lo + 8 * f + j;
+    } else {
+      // rounding left u * Z past the segment: its last token with positive weight
+      const uint64_t pmask = __ballot(lastpos >= 0);
+      const int l = pmask ? 63 - __clzll((long long)pmask) : 0;
+      const int j = __shfl(lastpos, l);
+      double hi = 0.0, wj = 0.0;
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (k == j) { hi = base + inc[k]; wj = double(use_p ? pv[k] : w[k]); }
+      c_hi = __shfl(hi, l);
+      c_lo = __shfl(hi - wj, l);
+      x = g_lo + 8 * l + (j < 0 ? 0 : j);
     }
     if (lane == 0) {
       const double u = double(d.u);

@@ -92,8 +92,10 @@ inline Layout make_layout(int kind, int mode, int64_t total_rows, int64_t vocab,
   lo.chunk = chunk;
   lo.S = int32_t((vocab + chunk - 1) / chunk);
   lo.n_seg = int32_t((vocab + kSeg - 1) / kSeg);
+  // k_draw: ~2048 workgroups, each covering at least 16 segments (4 per wave).
   int64_t s2 = batch > 0 ? (2048 + batch - 1) / batch : 1;
-  if (s2 > lo.n_seg) s2 = lo.n_seg;
+  const int64_t max_s2 = (lo.n_seg + 15) / 16;
+  if (s2 > max_s2) s2 = max_s2;
   if (s2 < 1) s2 = 1;
   lo.spc = int32_t((lo.n_seg + s2 - 1) / s2);
   lo.S2 = (lo.n_seg + lo.spc - 1) / lo.spc;

@@ -620,7 +620,9 @@ __global__ __launch_bounds__(kThreads) void k_stats(StatsParams p) {
     off0 = p.offsets[b];
     const int64_t off1 = p.offsets[b + 1];
     len = off1 - off0;
-    bool ok = off0 >= 0 && off1 > off0 && off1 <= p.total_rows && len <= p.L;
+    // Besides its own range, a request checks the conditions every valid batch meets that keep its draft
+    // rows inside [0, total_rows - B): off[b] >= b and off[b+1] <= total_rows - B + b + 1.
+    bool ok = off0 >= b && off1 > off0 && off1 <= p.total_rows - p.B + b + 1 && len <= p.L;
     if (b == 0 && off0 != 0) ok = false;
     if (b == p.B - 1 && off1 != p.total_rows) ok = false;
     if (!ok) {

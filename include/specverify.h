@@ -82,8 +82,10 @@ typedef enum spec_kind { SPEC_KIND_CHAIN = 0, SPEC_KIND_TREE = 1, SPEC_KIND_COMM
 #define SPEC_ST_NONFINITE     (1u << 0) /* a NaN logit in one of the request's rows; in sampling modes also
                                            +inf, or a row whose logits are all -inf                         */
 #define SPEC_ST_BAD_TOKEN     (1u << 1) /* a draft / node token outside [0, vocab); it is never accepted    */
-#define SPEC_ST_BAD_OFFSETS   (1u << 2) /* off[b] / off[b+1] inconsistent: then the whole batch's outputs
-                                           are unspecified (no memory outside the given buffers is touched) */
+#define SPEC_ST_BAD_OFFSETS   (1u << 2) /* off[b] / off[b+1] fail the request's own checks (non-empty, at
+                                           most max_verify_len rows, b <= off[b], off[b+1] <= T - B + b + 1,
+                                           off[0] = 0, off[B] = T): the whole batch's outputs are then
+                                           unspecified (no memory outside the given buffers is touched)    */
 #define SPEC_ST_BAD_PARENT    (1u << 3) /* tree: parent[0] != -1 or parent[i] not in [0, i); such a node is
                                            nobody's child                                                   */
 #define SPEC_ST_BAD_UNIFORM   (1u << 4) /* a uniform that is NaN or outside [0,1); it is used as 0 if NaN,

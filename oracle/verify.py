@@ -171,8 +171,10 @@ def verify_chain(target: np.ndarray, offsets: np.ndarray, draft_tokens: np.ndarr
 
 
 def _chain_offsets_ok(offsets, b, T, B, max_len) -> bool:
+    """Request b's rows [off[b], off[b+1]) checked on their own: non-empty, at most max_len rows, and the
+    bounds every strictly increasing offsets array from 0 to T obeys (off[b] >= b, off[b+1] <= T-B+b+1)."""
     lo, hi = int(offsets[b]), int(offsets[b + 1])
-    ok = 0 <= lo < hi <= T and hi - lo <= max_len
+    ok = b <= lo < hi <= T - B + b + 1 and hi - lo <= max_len
     if b == 0 and lo != 0:
         ok = False
     if b == B - 1 and hi != T:

@@ -364,3 +364,25 @@ def test_commit_parity_chain_and_tree():
                                    dev(np.array([0, 1, 2, 3, 3, -1], np.int32)), dev(np.arange(6, dtype=np.int64)),
                                    dev(np.array([0, 0], np.int32)), max_verify_len=4))
     assert g2["status"][0] & oracle.ST_BAD_ACCEPT and g2["status"][1] & oracle.ST_BAD_ACCEPT
+
+
+def test_inconsistent_offsets_are_reported_and_stay_in_bounds():
+    # Offsets that describe no valid packing; every request checks its own bounds (draft rows inside
+    # [0, T - B)), reports BAD_OFFSETS, and the kernels touch nothing outside the given buffers.
+    rng = np.random.default_rng(21)
+    V, T, B = 300, 10, 3
+    tl = rng.normal(0, 1, (T, V)).astype(np.float32)
+    dl = rng.normal(0, 1, (T - B, V)).astype(np.float32)
+    toks = rng.integers(0, V, T - B).astype(np.int32)
+    for offs in ([0, 10, 5, 10], [0, 2, 2, 10], [1, 4, 7, 10], [0, 4, 7, 9]):
+        w = _chain_from(tl, dl, np.array(offs, np.int32), toks, rng.random(T - B), rng.random(B), 1.0, 16)
+        o = oracle_chain(w, "rejection")
+        for mode in ("greedy", "rejection"):
+            g = run_chain(w, mode)
+            for b in range(B):
+                assert bool(g["status"][b] & oracle.ST_BAD_OFFSETS) == bool(o["status"][b] & oracle.ST_BAD_OFFSETS)
+            assert np.any(g["status"] & oracle.ST_BAD_OFFSETS)
+        gc = np_out(dva.commit_indices(dev(np.array(offs, np.int32)), dev(np.zeros(B, np.int32)),
+                                       dev(np.arange(T, dtype=np.int32)), dev(np.arange(T, dtype=np.int64)),
+                                       dev(np.zeros(B, np.int32)), max_verify_len=16))
+        assert np.any(gc["status"] & oracle.ST_BAD_OFFSETS)
