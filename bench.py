@@ -218,16 +218,22 @@ def cpu_baseline(name: str, budget_s: float = 12.0) -> dict:
                       f"{w.total_rows} verify rows, fp64 numpy, one thread) incl. commit; {dt:.1f} s"}
 
 
-def load_traffic(name: str, stats_bytes: float):
-    """HBM traffic of k_stats from committed rocprofv3 counter runs, if taken on the current kernels."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{name}.json")
+def load_traffic(name: str):
+    """HBM bytes per k_stats launch from the committed rocprofv3 counter summary (profiles/), if the counters
+    were taken on the current kernel sources; None otherwise."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{name}.txt")
     if not os.path.exists(path):
         return None
+    vals = {}
     with open(path) as f:
-        t = json.load(f)
-    if t.get("kernel_source_hash") != kernel_source_hash():
+        for line in f:
+            if line.startswith("#") or ":" not in line:
+                continue
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_hash") != kernel_source_hash():
         return None
-    return t.get("k_stats_hbm_bytes_per_launch")
+    return float(vals["k_stats_hbm_bytes_per_launch"])
 
 
 def copy_calibration():
@@ -281,7 +287,7 @@ def main():
             torch.cuda.empty_cache()
     stats_ms = main_res["kernel_ms"]["k_stats"]["mean"]
     achieved = main_res["stats_kernel_gbs"]
-    traffic = load_traffic(main_res["workload"], main_res["algorithmic_bytes_per_step"])
+    traffic = load_traffic(main_res["workload"])
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(main_res["workload"])
