@@ -34,6 +34,13 @@ struct Elem<float> {
   }
 };
 
+// A 16-byte load that bypasses cache retention: every logit is read once per pass.
+__device__ __forceinline__ uint4 load_stream(const uint4* p) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // v_exp_f32: 2^x (inputs below -126 give 0 or a denormal; such masses never matter at fp32 resolution).
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 

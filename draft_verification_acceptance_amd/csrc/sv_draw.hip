@@ -33,7 +33,7 @@ __device__ __forceinline__ void load8(const void* base, int64_t e, int64_t V, bo
     const uint4* vp = reinterpret_cast<const uint4*>(row + e);
     constexpr int E = Elem<DT>::kPerVec;
 #pragma unroll
-    for (int v = 0; v < 8 / E; ++v) Elem<DT>::unpack(vp[v], x + v * E);
+    for (int v = 0; v < 8 / E; ++v) Elem<DT>::unpack(load_stream(vp + v), x + v * E);
   } else {
 #pragma unroll
     for (int j = 0; j < 8; ++j) x[j] = e + j < V ? Elem<DT>::load(row, e + j) : -INFINITY;

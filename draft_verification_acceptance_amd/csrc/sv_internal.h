@@ -81,8 +81,10 @@ inline Layout make_layout(int kind, int mode, int64_t total_rows, int64_t vocab,
   lo.L = L;
   lo.P = (kind == SPEC_KIND_CHAIN && mode == SPEC_MODE_REJECTION) ? 2 : 1;
   const int64_t slots = int64_t(batch) * L * lo.P;
-  // Aim at >= 2048 streaming workgroups (8 per CU on 256 CUs) with chunks of at least 8192 tokens.
-  int64_t s = slots > 0 ? (2048 + slots - 1) / slots : 1;
+  // One workgroup per row once there are >= 512 rows (measured best on MI355X: fewer partials and
+  // counter updates per request, long streams per workgroup); smaller batches split rows into chunks of
+  // at least 8192 tokens to keep ~512 workgroups streaming.
+  int64_t s = slots > 0 ? (512 + slots - 1) / slots : 1;
   int64_t max_s = vocab / 8192;
   if (max_s < 1) max_s = 1;
   if (s > max_s) s = max_s;

@@ -49,7 +49,7 @@ __device__ void chunk_argmax(const DT* __restrict__ row, int64_t lo, int64_t hi,
   for (; k + (kUnroll - 1) * kThreads < sp.nvec; k += kUnroll * kThreads) {
     uint4 q[kUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) q[u] = vp[k + u * kThreads];
+    for (int u = 0; u < kUnroll; ++u) q[u] = load_stream(vp + k + u * kThreads);
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       float x[E];
@@ -67,7 +67,7 @@ __device__ void chunk_argmax(const DT* __restrict__ row, int64_t lo, int64_t hi,
   }
   for (; k < sp.nvec; k += kThreads) {
     float x[E];
-    Elem<DT>::unpack(vp[k], x);
+    Elem<DT>::unpack(load_stream(vp + k), x);
     float vm = x[0];
 #pragma unroll
     for (int e = 1; e < E; ++e) vm = fmaxf(vm, x[e]);
@@ -142,7 +142,7 @@ __device__ void chunk_lse(const DT* __restrict__ row, int64_t lo, int64_t hi, fl
   for (; k + (kUnroll - 1) * kThreads < sp.nvec; k += kUnroll * kThreads) {
     uint4 q[kUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) q[u] = vp[k + u * kThreads];
+    for (int u = 0; u < kUnroll; ++u) q[u] = load_stream(vp + k + u * kThreads);
     float x[kUnroll * E];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) Elem<DT>::unpack(q[u], x + u * E);
@@ -158,7 +158,7 @@ __device__ void chunk_lse(const DT* __restrict__ row, int64_t lo, int64_t hi, fl
   }
   for (; k < sp.nvec; k += kThreads) {
     float x[E];
-    Elem<DT>::unpack(vp[k], x);
+    Elem<DT>::unpack(load_stream(vp + k), x);
     float vm = x[0];
 #pragma unroll
     for (int e = 1; e < E; ++e) vm = fmaxf(vm, x[e]);
