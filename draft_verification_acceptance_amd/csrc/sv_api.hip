@@ -52,6 +52,7 @@ void carve(StatsParams& p, DrawParams& d, const Layout& lo, void* ws) {
   p.desc = reinterpret_cast<DrawDesc*>(w + lo.off_desc);
   p.seen = reinterpret_cast<int32_t*>(w + lo.off_seen);
   d.cnt2 = reinterpret_cast<unsigned long long*>(w + lo.off_cnt2);
+  p.cnt2 = d.cnt2;
   d.desc = p.desc;
   d.seg = reinterpret_cast<float2*>(w + lo.off_seg);
   d.seen = p.seen;

@@ -5,8 +5,10 @@
 //   move_accept_tokens_to_target_kvcache); the other verify rows are listed for eviction (§8.2: rejected
 //   KV must stop being visible, when it is freed is the caller's choice).
 // Requests are handled in tiles of up to 1024 requests and 8192 verify rows: thread per request for the
-// scans, thread per verify row for the gathers, with the tile's accept_index entries staged in LDS for the
-// duplicate and eviction checks. Any batch size works in one launch.
+// scan, thread per verify row for the gathers. Each tile's window of accept_index and verify_slots entries
+// (the rows that follow the previous tile's) is loaded into LDS together with the request data, so that a
+// tile costs one round trip to memory; rows outside the window (only with inconsistent offsets) are read
+// from memory directly. Any batch size works in one launch.
 #include "sv_device.h"
 
 namespace sv {
@@ -14,51 +16,60 @@ namespace sv {
 namespace {
 
 constexpr int kCommitThreads = 1024;
+constexpr int kTileRows = 8192;                       // verify rows staged in LDS at once
+constexpr int kRowsPerThread = kTileRows / kCommitThreads;
 
-__device__ __forceinline__ int64_t block_excl_scan_i64(int64_t v, int64_t* red, int64_t& total) {
-  const int lane = lane_id();
-  const int w = threadIdx.x / kWave;
-  int64_t inc = v;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int64_t n = __shfl_up(inc, o);
-    if (lane >= o) inc += n;
+struct CommitTile {
+  int64_t w0;       // first global row of the staged window
+  int n_st;         // rows staged
+  const int32_t* s_ai;
+  const int64_t* s_vs;
+  const int32_t* accept_index;
+  const int64_t* verify_slots;
+  __device__ int32_t ai(int64_t row) const {
+    const int64_t i = row - w0;
+    return i >= 0 && i < n_st ? s_ai[i] : accept_index[row];
   }
-  __syncthreads();
-  if (lane == kWave - 1) red[w] = inc;
-  __syncthreads();
-  int64_t base = 0, tot = 0;
-  for (int i = 0; i < kCommitThreads / kWave; ++i) {
-    if (i < w) base += red[i];
-    tot += red[i];
+  __device__ int64_t vs(int64_t row) const {
+    const int64_t i = row - w0;
+    return i >= 0 && i < n_st ? s_vs[i] : verify_slots[row];
   }
-  __syncthreads();
-  total = tot;
-  return base + inc - v;
-}
-
-constexpr int kTileRows = 8192;   // verify rows whose accept_index entries are staged in LDS at once
+};
 
 __global__ __launch_bounds__(kCommitThreads) void k_commit(spec_commit_args a) {
-  __shared__ int64_t red[kCommitThreads / kWave];
-  __shared__ int32_t t_off[kCommitThreads + 1];
+  // Per request of the tile: inclusive prefix of (rows << 32 | committed rows), its rows, accept length,
+  // first row, seq_len and status.
+  __shared__ uint64_t red[kCommitThreads / kWave];
+  __shared__ uint64_t t_incl[kCommitThreads];
   __shared__ int32_t t_len[kCommitThreads];
   __shared__ int32_t t_r[kCommitThreads];
-  __shared__ int32_t t_co[kCommitThreads];
-  __shared__ int32_t t_eo[kCommitThreads];
+  __shared__ int32_t t_o0[kCommitThreads];
   __shared__ int32_t t_seq[kCommitThreads];
   __shared__ uint32_t t_st[kCommitThreads];
   __shared__ int32_t s_ai[kTileRows];
-  __shared__ int s_nb;
+  __shared__ int64_t s_vs[kTileRows];
 
   const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wv = tid / kWave;
   const int B = a.batch;
   const int64_t T = a.total_rows;
   const int L = a.max_verify_len;
-  int64_t carry_c = 0, carry_e = 0;
-  for (int t0 = 0; t0 < B; t0 += s_nb) {
+  int64_t carry_c = 0, carry_e = 0, w0 = 0;
+  for (int t0 = 0; t0 < B;) {
+    const int n_st = int(min(int64_t(kTileRows), max(int64_t(0), T - w0)));
+    // ---- one round of loads: the request and the window of rows after the previous tile's ----
+    int32_t ai_r[kRowsPerThread];
+    int64_t vs_r[kRowsPerThread];
+#pragma unroll
+    for (int j = 0; j < kRowsPerThread; ++j) {
+      const int i = tid + j * kCommitThreads;
+      if (i < n_st) {
+        ai_r[j] = a.accept_index[w0 + i];
+        vs_r[j] = a.verify_slots[w0 + i];
+      }
+    }
     const int b = t0 + tid;
-    int64_t clen = 0, elen = 0;
     int32_t off0 = 0, len = 0, r = 0, seq = 0;
     uint32_t st = 0;
     if (b < B) {
@@ -78,102 +89,105 @@ __global__ __launch_bounds__(kCommitThreads) void k_commit(spec_commit_args a) {
           st |= SPEC_ST_BAD_ACCEPT;
           r = r < 0 ? 0 : len - 1;
         }
-        clen = r + 1;
-        elen = len - clen;
       }
     }
-    // This tile: as many of the next 1024 requests as have at most kTileRows rows in total (the rows
-    // of a valid batch are consecutive; at least one request always fits since len <= 1024).
-    int64_t tl;
-    const int64_t rows_before = block_excl_scan_i64(int64_t(len), red, tl);
-    const bool fits = b < B && rows_before + len <= kTileRows;
-    if (tid == 0) s_nb = 0;
-    __syncthreads();
-    if (fits) atomicMax(&s_nb, tid + 1);
-    __syncthreads();
-    const int nb = s_nb;
-    const bool in_tile = tid < nb;
-    int64_t tc, te;
-    const int64_t co = carry_c + block_excl_scan_i64(in_tile ? clen : 0, red, tc);
-    const int64_t eo = carry_e + block_excl_scan_i64(in_tile ? elen : 0, red, te);
-    t_off[tid] = int32_t(rows_before);   // row index relative to the tile's first row
-    if (tid == nb - 1) t_off[nb] = int32_t(rows_before + len);
+    const uint64_t mine = (uint64_t(uint32_t(len)) << 32) | uint32_t(len > 0 ? r + 1 : 0);
+    uint64_t inc = mine;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const uint64_t n = __shfl_up(inc, o);
+      if (lane >= o) inc += n;
+    }
+    if (lane == kWave - 1) red[wv] = inc;
     t_len[tid] = len;
     t_r[tid] = r;
-    t_co[tid] = int32_t(co);
-    t_eo[tid] = int32_t(eo);
+    t_o0[tid] = off0;
     t_seq[tid] = seq;
     t_st[tid] = st;
-    if (in_tile) {
+#pragma unroll
+    for (int j = 0; j < kRowsPerThread; ++j) {
+      const int i = tid + j * kCommitThreads;
+      if (i < n_st) {
+        s_ai[i] = ai_r[j];
+        s_vs[i] = vs_r[j];
+      }
+    }
+    __syncthreads();
+    uint64_t base = 0;
+    for (int i = 0; i < wv; ++i) base += red[i];
+    const uint64_t incl = base + inc;
+    t_incl[tid] = incl;
+    __syncthreads();
+    // This tile: the longest prefix of the next min(1024, B - t0) requests with at most kTileRows rows
+    // (never empty, since a request has at most 1024 rows).
+    const int avail = min(kCommitThreads, B - t0);
+    int lo = 1, hi = avail;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if ((t_incl[mid - 1] >> 32) <= uint64_t(kTileRows)) lo = mid;
+      else hi = mid - 1;
+    }
+    const int nb = lo;
+    const uint64_t tile_tot = t_incl[nb - 1];
+    const int n_rows = int(tile_tot >> 32);
+    if (tid < nb) {
+      const int64_t co = carry_c + int64_t(uint32_t(incl - mine));
+      const int64_t eo = carry_e + int64_t((incl - mine) >> 32) - int64_t(uint32_t(incl - mine));
       a.commit_offsets[b] = int32_t(co);
-      a.new_seq_lens[b] = seq + int32_t(clen);
+      a.new_seq_lens[b] = seq + (len > 0 ? r + 1 : 0);
       if (a.evict_offsets) a.evict_offsets[b] = int32_t(eo);
     }
-    __syncthreads();
-    // Rows of the tile: global rows [row0, row0 + n_rows) (consecutive for valid offsets; requests with
-    // bad offsets own no rows).
-    const int n_rows = t_off[nb];
-    int32_t row0 = 0;
-    {
-      // first valid request's off0 minus its relative position gives the tile's first global row
-      __shared__ int32_t s_row0;
-      if (tid == 0) s_row0 = 0;
-      __syncthreads();
-      if (in_tile && len > 0 && t_off[tid] == 0) s_row0 = off0;
-      __syncthreads();
-      row0 = s_row0;
-    }
-    for (int i = tid; i < n_rows; i += kCommitThreads) s_ai[i] = row0 + i < T ? a.accept_index[row0 + i] : -1;
-    __syncthreads();
+    // ---- gathers, one thread per verify row of the tile ----
+    const CommitTile tw{w0, n_st, s_ai, s_vs, a.accept_index, a.verify_slots};
     for (int i = tid; i < n_rows; i += kCommitThreads) {
-      // request owning relative row i: the last lb with t_off[lb] <= i and t_len[lb] > 0
-      int lo = 0, hi = nb - 1;
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (t_off[mid] <= i) lo = mid;
-        else hi = mid - 1;
+      // owning request: the first lb whose inclusive row count exceeds i (it has rows)
+      int l2 = 0, h2 = nb - 1;
+      while (l2 < h2) {
+        const int mid = (l2 + h2) >> 1;
+        if ((t_incl[mid] >> 32) > uint64_t(i)) h2 = mid;
+        else l2 = mid + 1;
       }
-      int lb = lo;
-      while (lb > 0 && t_len[lb] == 0) --lb;
-      const int32_t rel0 = t_off[lb];
+      const int lb = l2;
+      const uint64_t inc_b = t_incl[lb];
       const int32_t len_b = t_len[lb];
-      const int k = i - rel0;
-      if (k < 0 || k >= len_b) continue;
       const int32_t r_b = t_r[lb];
-      const int32_t o0 = row0 + rel0;
-      const int32_t row = o0 + k;
-      if (row >= T) continue;   // only when the offsets are inconsistent (the batch reports BAD_OFFSETS)
+      const int k = i - (int(inc_b >> 32) - len_b);
+      const int64_t o0 = t_o0[lb];
+      const int64_t row = o0 + k;   // < T: the request's offsets passed their checks
+      const int64_t co_b = carry_c + int64_t(uint32_t(inc_b)) - (r_b + 1);
       if (k <= r_b) {
-        const int32_t ai = s_ai[i];
-        bool valid = ai >= o0 && ai < o0 + len_b && ai < T;
+        const int32_t ai = tw.ai(row);
+        bool valid = ai >= o0 && ai < o0 + len_b;
         for (int j = 0; j < k && valid; ++j)
-          if (s_ai[rel0 + j] == ai) valid = false;   // listed twice
+          if (tw.ai(o0 + j) == ai) valid = false;   // listed twice
         if (!valid) atomicOr(&t_st[lb], SPEC_ST_BAD_ACCEPT);
-        if (int64_t(t_co[lb]) + k < a.capacity) {   // always true unless the offsets are inconsistent
-          a.src_slots[t_co[lb] + k] = valid ? a.verify_slots[ai] : int64_t(-1);
-          a.dst_pos[t_co[lb] + k] = t_seq[lb] + k;
+        if (co_b + k < a.capacity) {   // always true unless the offsets are inconsistent
+          a.src_slots[co_b + k] = valid ? tw.vs(ai) : int64_t(-1);
+          a.dst_pos[co_b + k] = t_seq[lb] + k;
         }
       }
       if (a.evict_slots) {
         int below = 0;
         bool accepted = false;
         for (int j = 0; j <= r_b; ++j) {
-          const int32_t ai = s_ai[rel0 + j];
+          const int32_t ai = tw.ai(o0 + j);
           below += ai < row;
           accepted |= ai == row;
         }
         if (!accepted) {
-          const int64_t pos = int64_t(t_eo[lb]) + (k - below);
-          if (pos >= t_eo[lb] && pos < int64_t(t_eo[lb]) + (len_b - r_b - 1) && pos < a.capacity)
-            a.evict_slots[pos] = a.verify_slots[row];
+          const int64_t eo_b = carry_e + (int64_t(inc_b >> 32) - len_b) - (co_b - carry_c);
+          const int64_t pos = eo_b + (k - below);
+          if (pos >= eo_b && pos < eo_b + (len_b - r_b - 1) && pos < a.capacity) a.evict_slots[pos] = tw.vs(row);
         }
       }
     }
     __syncthreads();
-    if (in_tile) a.status[b] = t_st[tid];
-    carry_c += tc;
-    carry_e += te;
-    __syncthreads();
+    // Each thread reads back only its own status entry before the next tile rewrites the tile arrays.
+    if (tid < nb) a.status[b] = t_st[tid];
+    carry_c += int64_t(uint32_t(tile_tot));
+    carry_e += int64_t(tile_tot >> 32) - int64_t(uint32_t(tile_tot));
+    w0 += n_rows;
+    t0 += nb;
   }
   if (tid == 0) {
     a.commit_offsets[B] = int32_t(carry_c);

@@ -25,31 +25,48 @@ struct RowCtx {
   bool vec;   // both rows 16-byte aligned: whole 8-token runs load as one (bf16) or two (fp32) vectors
 };
 
-// The 8 logits of tokens [e, e+8) of one row (tokens past the end of the row read as -inf).
+// Raw 16-bit (bf16) or 32-bit (fp32) bit patterns of 8 consecutive logits: loaded first, unpacked later,
+// so that a wave can have every segment of its trip in flight at once.
+struct Raw8 {
+  uint4 a, b;   // bf16: a holds 8 values; fp32: a holds 4, b holds 4
+};
+
 template <typename DT>
-__device__ __forceinline__ void load8(const void* base, int64_t e, int64_t V, bool vec, float* x) {
+__device__ __forceinline__ void load_raw8(const void* base, int64_t e, int64_t V, bool vec, Raw8& w) {
   const DT* row = static_cast<const DT*>(base);
   if (vec && e + 8 <= V) {
     const uint4* vp = reinterpret_cast<const uint4*>(row + e);
-    constexpr int E = Elem<DT>::kPerVec;
+    w.a = load_stream(vp);
+    if (sizeof(DT) == 4) w.b = load_stream(vp + 1);
+    return;
+  }
+  // unaligned row or the row's last 8 tokens: element by element, -inf past the end
+  uint32_t v[8];
 #pragma unroll
-    for (int v = 0; v < 8 / E; ++v) Elem<DT>::unpack(load_stream(vp + v), x + v * E);
+  for (int j = 0; j < 8; ++j) {
+    if (sizeof(DT) == 2) v[j] = e + j < V ? uint32_t(reinterpret_cast<const uint16_t*>(row)[e + j]) : 0xFF80u;
+    else v[j] = e + j < V ? __float_as_uint(reinterpret_cast<const float*>(row)[e + j]) : 0xFF800000u;
+  }
+  if (sizeof(DT) == 2) {
+    w.a = make_uint4(v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16), v[6] | (v[7] << 16));
   } else {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) x[j] = e + j < V ? Elem<DT>::load(row, e + j) : -INFINITY;
+    w.a = make_uint4(v[0], v[1], v[2], v[3]);
+    w.b = make_uint4(v[4], v[5], v[6], v[7]);
   }
 }
 
-// Weights of tokens [e, e+8): w (residual [p - q]_+, or p with tried tokens zeroed) and p. The same
-// arithmetic serves the segment sums and the token-by-token search, so both see identical values.
 template <typename DT>
-__device__ __forceinline__ void weights8(const RowCtx& r, int64_t e, int64_t V, const int32_t* seen, int n_seen,
-                                         float* w, float* pv) {
-  float x[8];
-  load8<DT>(r.xt, e, V, r.vec, x);
+__device__ __forceinline__ void unpack_raw8(const Raw8& w, float* x) {
+  Elem<DT>::unpack(w.a, x);
+  if (sizeof(DT) == 4) Elem<DT>::unpack(w.b, x + 4);
+}
+
+// Weights of tokens [e, e+8) from their logits: w (residual [p - q]_+, or p with tried tokens zeroed) and
+// p. The same arithmetic serves the segment sums and the token-by-token search, so both see identical
+// values.
+__device__ __forceinline__ void weights8(const RowCtx& r, int64_t e, int64_t V, const float* x, const float* y,
+                                         const int32_t* seen, int n_seen, float* w, float* pv) {
   if (r.xq) {
-    float y[8];
-    load8<DT>(r.xq, e, V, r.vec, y);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       pv[j] = exp2_fast(fmaf(x[j], r.coef, -r.m_t)) * r.inv_zt;
@@ -74,6 +91,18 @@ __device__ __forceinline__ void weights8(const RowCtx& r, int64_t e, int64_t V, 
 #pragma unroll
   for (int j = 0; j < 8; ++j)
     if (e + j >= V) { w[j] = 0.f; pv[j] = 0.f; }
+}
+
+template <typename DT>
+__device__ __forceinline__ void load_weights8(const RowCtx& r, int64_t e, int64_t V, const int32_t* seen,
+                                              int n_seen, float* w, float* pv) {
+  Raw8 rt, rq;
+  load_raw8<DT>(r.xt, e, V, r.vec, rt);
+  if (r.xq) load_raw8<DT>(r.xq, e, V, r.vec, rq);
+  float x[8], y[8];
+  unpack_raw8<DT>(rt, x);
+  if (r.xq) unpack_raw8<DT>(rq, y);
+  weights8(r, e, V, x, y, seen, n_seen, w, pv);
 }
 
 // Segment sums are published and read as agent-scope 64-bit atomics (see complete_memory_ops).
@@ -132,31 +161,42 @@ __global__ __launch_bounds__(kThreads) void k_draw(DrawParams p) {
   __syncthreads();
   const int n_seen = s_nseen;
 
-  // Lane l of a wave owns tokens [s*512 + 8l, s*512 + 8l + 8) of segment s; two segments per trip.
+  // Lane l of a wave owns tokens [s*512 + 8l, s*512 + 8l + 8) of segment s. A trip covers kTrip segments
+  // per wave with all of their loads issued before any is used.
   constexpr int kW = kThreads / kWave;
-  for (int s = s_begin + wv; s < s_end; s += 2 * kW) {
-    const int s2 = s + kW;
-    float w0[8], p0[8], w1[8], p1[8];
-    weights8<DT>(r, int64_t(s) * kSeg + 8 * lane, p.V, s_seen, n_seen, w0, p0);
-    if (s2 < s_end) weights8<DT>(r, int64_t(s2) * kSeg + 8 * lane, p.V, s_seen, n_seen, w1, p1);
-    float sw = 0.f, sp = 0.f, sw1 = 0.f, sp1 = 0.f;
+  constexpr int kTrip = 4;
+  for (int s0 = s_begin + wv; s0 < s_end; s0 += kTrip * kW) {
+    Raw8 rt[kTrip], rq[kTrip];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) { sw += w0[j]; sp += p0[j]; }
-    sw = wave_sum(sw);
-    sp = wave_sum(sp);
-    if (lane == 0) store_seg(p.seg + int64_t(b) * p.n_seg + s, sw, sp);
-    if (s2 < s_end) {
+    for (int u = 0; u < kTrip; ++u) {
+      const int s = s0 + u * kW;
+      if (s < s_end) {
+        load_raw8<DT>(r.xt, int64_t(s) * kSeg + 8 * lane, p.V, r.vec, rt[u]);
+        if (r.xq) load_raw8<DT>(r.xq, int64_t(s) * kSeg + 8 * lane, p.V, r.vec, rq[u]);
+      }
+    }
 #pragma unroll
-      for (int j = 0; j < 8; ++j) { sw1 += w1[j]; sp1 += p1[j]; }
-      sw1 = wave_sum(sw1);
-      sp1 = wave_sum(sp1);
-      if (lane == 0) store_seg(p.seg + int64_t(b) * p.n_seg + s2, sw1, sp1);
+    for (int u = 0; u < kTrip; ++u) {
+      const int s = s0 + u * kW;
+      if (s >= s_end) break;
+      const int64_t e = int64_t(s) * kSeg + 8 * lane;
+      float x[8], y[8], w[8], pv[8];
+      unpack_raw8<DT>(rt[u], x);
+      if (r.xq) unpack_raw8<DT>(rq[u], y);
+      weights8(r, e, p.V, x, y, s_seen, n_seen, w, pv);
+      float sw = 0.f, sp = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) { sw += w[j]; sp += pv[j]; }
+      sw = wave_sum(sw);
+      sp = wave_sum(sp);
+      if (lane == 0) store_seg(p.seg + int64_t(b) * p.n_seg + s, sw, sp);
     }
   }
 
   complete_memory_ops();   // every wave's segment sums are stored before the workgroup is counted
   __syncthreads();
-  if (tid == 0) s_last = count_done(p.cnt2 + size_t(b) * kCounterWords, p.epoch) == uint32_t(p.S2);
+  // The request's scan armed this counter with the call's epoch and a zero count (previous kernel).
+  if (tid == 0) s_last = uint32_t(atomicAdd(p.cnt2 + size_t(b) * kCounterWords, 1ull)) + 1u == uint32_t(p.S2);
   __syncthreads();
   if (!s_last) return;
 
@@ -226,7 +266,7 @@ __global__ __launch_bounds__(kThreads) void k_draw(DrawParams p) {
   if (tid < kWave) {
     // Token by token in float64, ascending: lane l holds tokens g_lo + 8l .. g_lo + 8l + 7.
     float w[8], pv[8];
-    weights8<DT>(r, g_lo + 8 * lane, p.V, s_seen, use_p ? 0 : s_nseen, w, pv);
+    load_weights8<DT>(r, g_lo + 8 * lane, p.V, s_seen, use_p ? 0 : s_nseen, w, pv);
     double inc[8];
     double run = 0.0;
 #pragma unroll

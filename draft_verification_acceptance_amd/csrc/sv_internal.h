@@ -132,6 +132,7 @@ struct StatsParams {
   float* accept_prob;
   float* residual_mass;
   unsigned long long* cnt;
+  unsigned long long* cnt2;   // draw-pass counters, armed by each request's scan
   Part* part;
   DrawDesc* desc;
   int32_t* seen;

@@ -396,6 +396,7 @@ __device__ void scan_chain_rejection(const StatsParams& p, int b, int64_t off0, 
     d.status = s_flags;
     d.n_seen = 0;
     p.desc[b] = d;
+    p.cnt2[size_t(b) * kCounterWords] = (unsigned long long)p.epoch << 32;   // the draw pass counts from 0
     p.status[b] = s_flags;
   }
 }
@@ -585,6 +586,7 @@ __device__ void scan_tree(const StatsParams& p, int b, char* smem) {
       d.status = st;
       d.n_seen = s_nseen;
       p.desc[b] = d;
+    p.cnt2[size_t(b) * kCounterWords] = (unsigned long long)p.epoch << 32;   // the draw pass counts from 0
       s_flags = st;
     }
     p.status[b] = s_flags;

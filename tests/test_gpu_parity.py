@@ -382,7 +382,7 @@ def test_inconsistent_offsets_are_reported_and_stay_in_bounds():
             for b in range(B):
                 assert bool(g["status"][b] & oracle.ST_BAD_OFFSETS) == bool(o["status"][b] & oracle.ST_BAD_OFFSETS)
             assert np.any(g["status"] & oracle.ST_BAD_OFFSETS)
-        gc = np_out(dva.commit_indices(dev(np.array(offs, np.int32)), dev(np.zeros(B, np.int32)),
-                                       dev(np.arange(T, dtype=np.int32)), dev(np.arange(T, dtype=np.int64)),
-                                       dev(np.zeros(B, np.int32)), max_verify_len=16))
+        # the commit pass handles the requests whose own offsets pass exactly as the oracle does
+        gc = _commit_check(np.array(offs, np.int32), np.zeros(B, np.int32), np.arange(T, dtype=np.int32),
+                           np.arange(T, dtype=np.int64), np.zeros(B, np.int32), 16)
         assert np.any(gc["status"] & oracle.ST_BAD_OFFSETS)
