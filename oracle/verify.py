@@ -33,6 +33,7 @@ ST_ZERO_RESIDUAL = 1 << 6
 ST_NEAR_ALPHA = 1 << 7
 ST_NEAR_CDF = 1 << 8
 ST_BAD_ACCEPT = 1 << 9
+ST_BAD_Q = 1 << 10
 
 NEAR = 1e-5          # width of the "too close to call" band for accept tests and CDF steps
 NEAR_MASS = 1e-6     # the same band measured in probability mass for a draw (gap * Z), see near_cdf()
@@ -104,6 +105,26 @@ def accept_probability(pd: float, qd: float) -> float:
     return min(1.0, pd / qd)
 
 
+def sparse_q(ids: np.ndarray, probs: np.ndarray, V: int) -> tuple[np.ndarray, int]:
+    """Proposal q over the vocab from K (candidate id, probability) pairs: the candidate distribution is
+    scattered into target vocab coordinates and q is zero everywhere else ([EAGLE→DFlash2] §6.5, sampling
+    verify with the selector's candidate q; greedy rows carry a one-hot q). Returns (q, status bits).
+    READING: a repeated id adds its masses (top-K ids are distinct, so this only concerns malformed
+    input); an id outside [0, V) sets BAD_TOKEN and a negative or non-finite probability sets BAD_Q, and
+    such an entry is left out."""
+    q = np.zeros(V)
+    st = 0
+    for i, w in zip(np.asarray(ids).tolist(), np.asarray(probs, np.float64).tolist()):
+        if not 0 <= i < V:
+            st |= ST_BAD_TOKEN
+            continue
+        if not (np.isfinite(w) and w >= 0.0):
+            st |= ST_BAD_Q
+            continue
+        q[i] += w
+    return q, st
+
+
 def draw(w: np.ndarray, u: float) -> tuple[int, float, float]:
     """Inverse-CDF draw from nonnegative weights w ([EAGLE→DFlash2] §6.2, the selector's rule: the index is
     the number of cumulative probabilities that u has reached). Returns (token, gap, Z) where Z = sum w
@@ -149,24 +170,28 @@ def _sentinel_outputs(n_rows: int, n_draft: int, batch: int) -> dict:
 def verify_chain(target: np.ndarray, offsets: np.ndarray, draft_tokens: np.ndarray, mode: str, *,
                  draft: np.ndarray | None = None, u_accept: np.ndarray | None = None,
                  u_final: np.ndarray | None = None, temperature: float = 1.0,
-                 max_verify_len: int = 1024, requests=None) -> dict:
-    """Chain verify for mode "greedy" or "rejection".
+                 max_verify_len: int = 1024, requests=None, cand_ids: np.ndarray | None = None,
+                 cand_q: np.ndarray | None = None) -> dict:
+    """Chain verify for mode "greedy", "rejection" or "rejection_sparse".
 
     target [T_rows, V] (uint16 bf16 bits or float32); offsets [B+1]: request b owns target rows
     off[b]..off[b+1]-1 (ragged layout of [EAGLE→DFlash2] §5.6.5). Draft-side arrays hold m_b entries per
-    request from off[b]-b on; entry j is about d_{j+1}. `requests` limits the work to some requests (the
-    others keep sentinel values: -2 / NaN).
+    request from off[b]-b on; entry j is about d_{j+1}. "rejection" takes q_j = softmax(draft row / T);
+    "rejection_sparse" takes q_j from the K candidate pairs cand_ids[entry], cand_q[entry] ([D_rows, K]) of
+    sparse_q (the temperature then divides the target logits only: q arrives as probabilities).
+    `requests` limits the work to some requests (the others keep sentinel values: -2 / NaN).
 
     Returns accept_len, bonus, out_tokens, accept_index, status, accept_prob, residual_mass and flag_pos
     (oracle only: number of leading emitted tokens fixed before the first NEAR_* decision; r+1 if none).
     """
-    assert mode in ("greedy", "rejection")
+    assert mode in ("greedy", "rejection", "rejection_sparse")
     T, V = target.shape
     B = len(offsets) - 1
     out = _sentinel_outputs(T, max(T - B, 0), B)
+    cand = (cand_ids, cand_q) if mode == "rejection_sparse" else None
     for b in (range(B) if requests is None else requests):
         _chain_request(out, b, target, offsets, draft_tokens, mode, draft, u_accept, u_final,
-                       temperature, max_verify_len, T, V, B)
+                       temperature, max_verify_len, T, V, B, cand)
     return out
 
 
@@ -183,7 +208,7 @@ def _chain_offsets_ok(offsets, b, T, B, max_len) -> bool:
 
 
 def _chain_request(out, b, target, offsets, draft_tokens, mode, draft, u_accept, u_final, temperature,
-                   max_len, T, V, B):
+                   max_len, T, V, B, cand=None):
     out["evaluated"][b] = True
     if not _chain_offsets_ok(offsets, b, T, B, max_len):
         out["status"][b] = ST_BAD_OFFSETS
@@ -194,11 +219,11 @@ def _chain_request(out, b, target, offsets, draft_tokens, mode, draft, u_accept,
     off = int(offsets[b])
     m = int(offsets[b + 1]) - off - 1
     dr0 = off - b                      # first draft-side entry of this request
-    sampling = mode == "rejection"
+    sampling = mode != "greedy"
     st = 0
 
     t_rows = [decode_row(target[off + j]) for j in range(m + 1)]
-    s_rows = [decode_row(draft[dr0 + j]) for j in range(m)] if sampling else []
+    s_rows = [decode_row(draft[dr0 + j]) for j in range(m)] if mode == "rejection" else []
     for x in t_rows + s_rows:
         if row_nonfinite(x, sampling):
             st |= ST_NONFINITE
@@ -226,7 +251,14 @@ def _chain_request(out, b, target, offsets, draft_tokens, mode, draft, u_accept,
         if uf_bad or any(bad for _, bad in us):
             st |= ST_BAD_UNIFORM
         ps = [softmax_T(x, temperature) for x in t_rows]
-        qs = [softmax_T(x, temperature) for x in s_rows]
+        if cand is None:
+            qs = [softmax_T(x, temperature) for x in s_rows]
+        else:
+            qs = []
+            for j in range(m):
+                q, qst = sparse_q(cand[0][dr0 + j], cand[1][dr0 + j], V)
+                qs.append(q)
+                st |= qst
         r = m
         w = None
         for j in range(1, m + 1):

@@ -653,6 +653,184 @@ def test_edge_cases_statuses():
 
 
 # ----------------------------------------------------------------------------------------------------
+# sparse-q rejection ([EAGLE→DFlash2] §6.5: the selector's K-candidate q is scattered into vocab
+# coordinates, zero elsewhere; the residual still spans the whole vocab; greedy rows carry a one-hot q)
+# ----------------------------------------------------------------------------------------------------
+def chain_call_sparse(t_rows, ids_rows, q_rows, toks, us, uf, T):
+    t = np.asarray(t_rows, np.float32)
+    n = len(t)
+    return oracle.verify_chain(t, np.array([0, n], np.int32), np.asarray(toks, np.int32), "rejection_sparse",
+                               u_accept=np.asarray(us, np.float64), u_final=np.array([uf], np.float64),
+                               temperature=T, cand_ids=np.asarray(ids_rows).reshape(n - 1, -1),
+                               cand_q=np.asarray(q_rows, np.float64).reshape(n - 1, -1))
+
+
+def _top_candidates(s_logits, K, T):
+    """K highest draft logits (distinct ids, descending) and the softmax over just those K at T: the
+    selector's candidate set and its normalised conditional q."""
+    ids = np.argsort(-np.asarray(s_logits, np.float64), kind="stable")[:K]
+    return ids, _p(np.asarray(s_logits, np.float64)[ids], T)
+
+
+def test_sparse_full_support_equals_dense_rejection():
+    # K = V with q = softmax(draft / T): the same proposal as dense rejection, so every output agrees.
+    # The candidate order is a random permutation, so a scatter by candidate position would fail.
+    rng = np.random.default_rng(41)
+    V, T = 24, 0.8
+    lens = rng.integers(1, 7, 40)
+    offs = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    R, B = int(offs[-1]), len(lens)
+    tl = rng.normal(0, 1.5, (R, V)).astype(np.float32)
+    dl = np.concatenate([tl[offs[b]:offs[b + 1] - 1] for b in range(B)]) + rng.normal(0, 0.7, (R - B, V))
+    dl = dl.astype(np.float32)
+    q = np.stack([_p(x, T) for x in dl])
+    toks = np.array([rng.choice(V, p=qq) for qq in q], np.int32)
+    ids = np.stack([rng.permutation(V) for _ in range(R - B)]).astype(np.int32)
+    ua, uf = rng.random(R - B), rng.random(B)
+    od = oracle.verify_chain(tl, offs, toks, "rejection", draft=dl, u_accept=ua, u_final=uf, temperature=T)
+    osp = oracle.verify_chain(tl, offs, toks, "rejection_sparse", u_accept=ua, u_final=uf, temperature=T,
+                              cand_ids=ids, cand_q=np.take_along_axis(q, ids, 1))
+    for k in ("accept_len", "bonus", "out_tokens", "accept_index", "status"):
+        assert np.array_equal(od[k], osp[k]), k
+    assert np.allclose(od["accept_prob"], osp["accept_prob"], rtol=0, atol=1e-15)
+    assert np.allclose(od["residual_mass"], osp["residual_mass"], rtol=0, atol=1e-15)
+
+
+def test_sparse_one_hot_equals_tree_target_only_on_a_chain():
+    # Greedy rows: q = one-hot(d). Rejection with that q is the target-only rule on a chain-shaped tree
+    # (each node has one child), pinned separately by exact integration.
+    rng = np.random.default_rng(43)
+    V, m, B = 10, 4, 40
+    for T in (0.6, 1.0):
+        tl = rng.normal(0, 1.5, (B * (m + 1), V)).astype(np.float32)
+        toks = rng.integers(0, V, B * m).astype(np.int32)
+        for i in range(B * m):
+            if rng.random() < 0.6:
+                toks[i] = np.argmax(tl[(i // m) * (m + 1) + i % m])
+        ua, uf = rng.random(B * m), rng.random(B)
+        offs = (np.arange(B + 1) * (m + 1)).astype(np.int32)
+        osp = oracle.verify_chain(tl, offs, toks, "rejection_sparse", u_accept=ua, u_final=uf, temperature=T,
+                                  cand_ids=toks[:, None], cand_q=np.ones((B * m, 1)))
+        N = m + 1
+        parents = np.tile(np.arange(-1, N - 1), B)
+        tokens = np.concatenate([[0] + list(toks[b * m:(b + 1) * m]) for b in range(B)])
+        u_nodes = np.concatenate([list(ua[b * m:(b + 1) * m]) + [0.5] for b in range(B)])
+        ot = oracle.verify_tree(tl, parents, tokens, N, "target_only", u_accept=u_nodes, u_final=uf, temperature=T)
+        for k in ("accept_len", "bonus", "out_tokens", "accept_index", "residual_mass", "status"):
+            assert np.array_equal(osp[k], ot[k]), k
+
+
+def sparse_mass_decomposition_error(seed=7, V=6, K=3, T=0.9):
+    """One draft position with a K-candidate q: accept mass of v is min(p, q)(v), rejection mass
+    [p - q]_+(v) (equal to p(v) off the candidates), and the two add up to p(v)."""
+    rng = np.random.default_rng(seed)
+    t0 = rng.normal(0, 1.5, V).astype(np.float32)
+    t1 = rng.normal(0, 1.5, V).astype(np.float32)
+    ids, qc = _top_candidates(t0 + rng.normal(0, 1.0, V), K, T)
+    p = _p(t0, T)
+    q = np.zeros(V)
+    q[ids] = qc
+    A = np.zeros(V)
+    R = np.zeros(V)
+    for d, qd in zip(ids, qc):
+        def run(u1, uf):
+            return chain_call_sparse([t0, t1], [ids], [qc], [d], [u1], uf, T)
+        for a1, b1, acc in pieces(lambda u: int(run(u, 0.5)["accept_len"][0]) >= 1):
+            if acc:
+                A[d] += qd * (b1 - a1)
+            else:
+                m1 = 0.5 * (a1 + b1)
+                for af, bf, x in pieces(lambda u: int(run(m1, u)["bonus"][0])):
+                    R[x] += qd * (b1 - a1) * (bf - af)
+    off = np.setdiff1d(np.arange(V), ids)
+    assert np.all(R[off] > 0)          # tokens outside the candidates stay reachable
+    return max(np.max(np.abs(A - np.minimum(p, q))), np.max(np.abs(R - np.maximum(p - q, 0))),
+               np.max(np.abs(A + R - p)))
+
+
+def test_sparse_accept_plus_reject_mass_is_p():
+    assert sparse_mass_decomposition_error() < 1e-12
+
+
+def sparse_chain_integration_error(seed=0, V=4, K=2, T=1.0):
+    """Exact integration of one m = 2 round with K-candidate proposals (d ~ q over the candidates of the
+    row each draft came from) plus exact continuation: the 3-token distribution must be the target's."""
+    t, s = _tables(seed, V)
+
+    def p_true(prefix):
+        if len(prefix) == 0:
+            return _p(t[0], T)
+        if len(prefix) == 1:
+            return _p(t[1][prefix[0]], T)
+        return _p(t[2][prefix[0], prefix[1]], T)
+
+    target = np.zeros((V, V, V))
+    for a in range(V):
+        for b in range(V):
+            target[a, b] = p_true([])[a] * p_true([a])[b] * p_true([a, b])
+    spec = np.zeros((V, V, V))
+    ids0, q0 = _top_candidates(s[0], K, T)
+    for d1, w1 in zip(ids0, q0):
+        ids1, q1 = _top_candidates(s[1][d1], K, T)
+        for d2, w2 in zip(ids1, q1):
+            trows = [t[0], t[1][d1], t[2][d1, d2]]
+
+            def run(u1, u2, uf):
+                return chain_call_sparse(trows, [ids0, ids1], [q0, q1], [d1, d2], [u1, u2], uf, T)
+
+            for a1, b1, acc1 in pieces(lambda u: int(run(u, 0.5, 0.5)["accept_len"][0]) >= 1):
+                m1 = 0.5 * (a1 + b1)
+                regions = [(b1 - a1, m1, 0.5)] if not acc1 else [
+                    ((b1 - a1) * (b2 - a2), m1, 0.5 * (a2 + b2))
+                    for a2, b2, _ in pieces(lambda u: int(run(m1, u, 0.5)["accept_len"][0]) >= 2)]
+                for meas, u1, u2 in regions:
+                    for af, bf, _ in pieces(lambda u: int(run(u1, u2, u)["bonus"][0])):
+                        y = list(emitted(run(u1, u2, 0.5 * (af + bf))))
+                        mass = w1 * w2 * meas * (bf - af)
+                        if len(y) >= 3:
+                            spec[y[0], y[1], y[2]] += mass
+                        elif len(y) == 2:
+                            spec[y[0], y[1]] += mass * p_true(y)
+                        else:
+                            pa = p_true(y)
+                            for b in range(V):
+                                spec[y[0], b] += mass * pa[b] * p_true([y[0], b])
+    return float(np.max(np.abs(spec - target)))
+
+
+@pytest.mark.parametrize("seed,T", [(0, 1.0), (2, 0.6)])
+def test_sparse_rejection_exact_integration_is_lossless(seed, T):
+    assert sparse_chain_integration_error(seed, 4, 2, T) < 1e-12
+
+
+def test_sparse_duplicate_and_invalid_candidates():
+    rng = np.random.default_rng(47)
+    V = 16
+    tl = rng.normal(0, 1.5, (3, V)).astype(np.float32)
+    toks = np.array([3, 5], np.int32)
+    base_ids = np.array([[3, 7, 9], [5, 1, 2]])
+    base_q = np.array([[0.5, 0.3, 0.2], [0.6, 0.3, 0.1]])
+    ref = chain_call_sparse(tl, base_ids, base_q, toks, [0.4, 0.9], 0.3, 1.0)
+    # a repeated id adds its masses
+    dup = chain_call_sparse(tl, [[3, 7, 3, 9], [5, 1, 2, 2]], [[0.2, 0.3, 0.3, 0.2], [0.6, 0.3, 0.05, 0.05]],
+                            toks, [0.4, 0.9], 0.3, 1.0)
+    for k in ("accept_len", "bonus", "out_tokens", "status"):
+        assert np.array_equal(ref[k], dup[k]), k
+    assert np.allclose(ref["accept_prob"], dup["accept_prob"], rtol=0, atol=1e-15)
+    # entries with an id outside [0, V) or a negative / non-finite mass are reported and left out
+    for bad_id, bad_q, bit in ((V, 0.4, oracle.ST_BAD_TOKEN), (-1, 0.4, oracle.ST_BAD_TOKEN),
+                               (4, -0.1, oracle.ST_BAD_Q), (4, np.nan, oracle.ST_BAD_Q), (4, np.inf, oracle.ST_BAD_Q)):
+        o = chain_call_sparse(tl, np.concatenate([base_ids, [[bad_id], [4]]], 1),
+                              np.concatenate([base_q, [[bad_q], [0.0]]], 1), toks, [0.4, 0.9], 0.3, 1.0)
+        assert o["status"][0] & bit
+        for k in ("accept_len", "bonus", "out_tokens"):
+            assert np.array_equal(ref[k], o[k]), k
+    # a draft token that is no candidate has q(d) = 0
+    o = chain_call_sparse(tl, base_ids, base_q, [4, 5], [0.4, 0.9], 0.3, 1.0)
+    assert o["status"][0] & oracle.ST_ZERO_Q and o["accept_prob"][0] == 1.0
+
+
+# ----------------------------------------------------------------------------------------------------
 # planted mistakes: each plausible bug in the oracle must fail one of the pins above
 # ----------------------------------------------------------------------------------------------------
 def test_pins_catch_swapped_residual(monkeypatch):
@@ -709,6 +887,23 @@ def test_pins_catch_highest_index_ties(monkeypatch):
 def test_pins_catch_missing_temperature(monkeypatch):
     monkeypatch.setattr(ov, "softmax_T", lambda x, T: softmax(x))
     assert chain_integration_error(1, 4, 0.7) > 1e-3
+
+
+def test_pins_catch_residual_restricted_to_candidates(monkeypatch):
+    # a residual that drops the mass outside the candidate set makes those tokens unreachable
+    monkeypatch.setattr(ov, "residual_weights", lambda p, q: np.where(q > 0, np.maximum(p - q, 0.0), 0.0))
+    with pytest.raises(AssertionError):
+        sparse_mass_decomposition_error()
+    assert sparse_chain_integration_error(0, 4, 2, 1.0) > 1e-3
+
+
+def test_pins_catch_q_indexed_by_candidate_position(monkeypatch):
+    def bad_sparse_q(ids, probs, V):
+        q = np.zeros(V)
+        q[:len(probs)] = probs
+        return q, 0
+    monkeypatch.setattr(ov, "sparse_q", bad_sparse_q)
+    assert sparse_chain_integration_error(0, 4, 2, 1.0) > 1e-3
 
 
 def test_p_zero_is_never_accepted():
