@@ -13,7 +13,7 @@ roofline: the dominant kernel (k_stats, the logits stream) timed with HIP events
 it, against its algorithmic bytes (every target and draft row read once). cpu_baseline: the fp64 CPU
 oracle timed on this host on the same inputs.
 
-    python bench.py [--steps K] [--warmup W] [--workload chain_rejection|block_greedy|tree|ragged]
+    python bench.py [--steps K] [--warmup W] [--workload chain_rejection|block_greedy|tree|ragged|chain_sparse]
                     [--no-extra] [--no-cpu-baseline] [--copy-calibration]
 """
 from __future__ import annotations
@@ -67,7 +67,8 @@ def _dev(a):
 def build_sets(name: str):
     """Seeded input sets (seed 1000*k + i) until the live footprint exceeds 2x the Infinity Cache."""
     from draft_verification_acceptance_amd import workloads as W
-    base = {"tiny_chain": 1000, "chain_rejection": 2000, "block_greedy": 3000, "tree": 4000, "ragged": 5000}[name]
+    base = {"tiny_chain": 1000, "chain_rejection": 2000, "block_greedy": 3000, "tree": 4000, "ragged": 5000,
+            "chain_sparse": 6000}[name]
     sets = []
     total = 0
     i = 0
@@ -93,6 +94,9 @@ class ChainStep:
         if mode == "rejection":
             kw.update(draft_logits=_dev_logits(w.draft), u_accept=_dev(w.u_accept), u_final=_dev(w.u_final),
                       temperature=w.temperature)
+        elif mode == "rejection_sparse":
+            kw.update(cand_ids=_dev(w.cand_ids), cand_q=_dev(w.cand_q), u_accept=_dev(w.u_accept),
+                      u_final=_dev(w.u_final), temperature=w.temperature)
         self.verify = dva.prepare_verify_chain(t, offs, _dev(w.draft_tokens), mode, **kw)
         o = self.verify.outputs
         self.commit = dva.prepare_commit_indices(offs, o["accept_len"], o["accept_index"],
@@ -199,7 +203,8 @@ def cpu_baseline(name: str, budget_s: float = 12.0) -> dict:
 
     import oracle
     from draft_verification_acceptance_amd import workloads as W
-    w = W.FULL[name](seed={"chain_rejection": 2000, "block_greedy": 3000, "tree": 4000, "ragged": 5000}[name])
+    w = W.FULL[name](seed={"chain_rejection": 2000, "block_greedy": 3000, "tree": 4000, "ragged": 5000,
+                           "chain_sparse": 6000}[name])
     mode = w.modes[-1]
     slots = W.verify_slots_for(w.total_rows)
     seq = W.seq_lens_for(w.batch)
@@ -214,7 +219,8 @@ def cpu_baseline(name: str, budget_s: float = 12.0) -> dict:
             oracle.commit_indices(offs, o["accept_len"], o["accept_index"], slots, seq, w.n_nodes)
         else:
             o = oracle.verify_chain(w.target, w.offsets, w.draft_tokens, mode, draft=w.draft, u_accept=w.u_accept,
-                                    u_final=w.u_final, temperature=w.temperature, max_verify_len=w.max_verify_len)
+                                    u_final=w.u_final, temperature=w.temperature, max_verify_len=w.max_verify_len,
+                                    cand_ids=w.cand_ids, cand_q=w.cand_q)
             oracle.commit_indices(w.offsets, o["accept_len"], o["accept_index"], slots, seq, w.max_verify_len)
         passes += 1
         rows += w.total_rows
@@ -263,7 +269,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=["chain_rejection", "block_greedy", "tree",
-                                                                       "ragged"])
+                                                                       "ragged", "chain_sparse"])
     ap.add_argument("--mode", default=None)
     ap.add_argument("--no-extra", action="store_true", help="skip the other full-size workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -284,7 +290,8 @@ def main():
     main_res = run_workload(args.workload, args.mode, args.steps, args.warmup)
     extra = {}
     if not args.no_extra:
-        for name, mode in (("block_greedy", None), ("ragged", None), ("tree", "greedy"), ("tree", "target_only")):
+        for name, mode in (("block_greedy", None), ("ragged", None), ("tree", "greedy"), ("tree", "target_only"),
+                           ("chain_sparse", None)):
             if name == args.workload and (mode or "") == (args.mode or ""):
                 continue
             r = run_workload(name, mode, max(50, args.steps // 2), args.warmup)

@@ -25,8 +25,8 @@ __all__ = [
 _PKG = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_PKG, "libspecverify.so")
 
-ABI_VERSION = 1
-MODES = {"greedy": 0, "rejection": 1, "target_only": 2}
+ABI_VERSION = 2
+MODES = {"greedy": 0, "rejection": 1, "target_only": 2, "rejection_sparse": 3}
 KIND_CHAIN, KIND_TREE, KIND_COMMIT = 0, 1, 2
 DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 
@@ -43,6 +43,7 @@ class ST:
     NEAR_ALPHA = 1 << 7
     NEAR_CDF = 1 << 8
     BAD_ACCEPT = 1 << 9
+    BAD_Q = 1 << 10
 
 
 class SpecError(RuntimeError):
@@ -60,7 +61,8 @@ class ChainArgs(ctypes.Structure):
                 ("accept_index", _vp), ("status", _vp), ("accept_prob", _vp), ("residual_mass", _vp),
                 ("workspace", _vp), ("workspace_bytes", _sz), ("profile_events", _vp), ("total_rows", _i64),
                 ("vocab", _i64), ("batch", _i32), ("max_verify_len", _i32), ("dtype", _i32), ("mode", _i32),
-                ("temperature", _f32), ("n_profile_events", _i32)]
+                ("temperature", _f32), ("n_profile_events", _i32), ("cand_ids", _vp), ("cand_q", _vp),
+                ("n_cand", _i32), ("reserved", _i32)]
 
 
 class TreeArgs(ctypes.Structure):
@@ -258,8 +260,9 @@ def prepare_verify_chain(target_logits: torch.Tensor, target_offsets: torch.Tens
                          mode: str = "greedy", *, draft_logits: torch.Tensor | None = None,
                          u_accept: torch.Tensor | None = None, u_final: torch.Tensor | None = None,
                          temperature: float = 1.0, max_verify_len: int | None = None, workspace_tensor=None,
-                         out: dict | None = None, accept_prob: bool = True,
-                         residual_mass: bool = True) -> PreparedCall:
+                         out: dict | None = None, accept_prob: bool = True, residual_mass: bool = True,
+                         cand_ids: torch.Tensor | None = None,
+                         cand_q: torch.Tensor | None = None) -> PreparedCall:
     """Checks and marshals the arguments of spec_verify_chain once (see verify_chain)."""
     lib = _lib()
     dev = target_logits.device
@@ -276,12 +279,20 @@ def prepare_verify_chain(target_logits: torch.Tensor, target_offsets: torch.Tens
         raise ValueError("max_verify_len (upper bound on m_b + 1) is required")
     _req(draft_tokens, "draft_tokens", torch.int32, D, dev)
     m = MODES[mode]
+    K = 0
     if mode == "rejection":
         _req(draft_logits, "draft_logits", target_logits.dtype, D * V, dev)
-        _req(u_accept, "u_accept", torch.float32, D, dev)
-        _req(u_final, "u_final", torch.float32, B, dev)
+    elif mode == "rejection_sparse":
+        if cand_ids is None or cand_ids.dim() != 2 or cand_ids.shape[0] != D:
+            raise ValueError("cand_ids must be [total_rows - batch, K]")
+        K = int(cand_ids.shape[1])
+        _req(cand_ids, "cand_ids", torch.int32, D * K, dev)
+        _req(cand_q, "cand_q", torch.float32, D * K, dev)
     elif mode != "greedy":
         raise SpecError(3, status_string(3))
+    if mode != "greedy":
+        _req(u_accept, "u_accept", torch.float32, D, dev)
+        _req(u_final, "u_final", torch.float32, B, dev)
     if workspace_tensor is None:
         workspace_tensor = workspace("chain", mode, T, V, B, max_verify_len, dev)
     o = _outputs(out, dev, B, T, D, accept_prob, residual_mass)
@@ -304,7 +315,11 @@ def prepare_verify_chain(target_logits: torch.Tensor, target_offsets: torch.Tens
     a.dtype = DTYPES[target_logits.dtype]
     a.mode = m
     a.temperature = float(temperature)
-    keep = [target_logits, target_offsets, draft_tokens, draft_logits, u_accept, u_final, workspace_tensor]
+    a.cand_ids = _ptr(cand_ids) if K else None
+    a.cand_q = _ptr(cand_q) if K else None
+    a.n_cand = K
+    keep = [target_logits, target_offsets, draft_tokens, draft_logits, u_accept, u_final, cand_ids, cand_q,
+            workspace_tensor]
     return PreparedCall(lib.spec_verify_chain, a, o, keep, dev)
 
 
@@ -314,8 +329,8 @@ def verify_chain(target_logits: torch.Tensor, target_offsets: torch.Tensor, draf
 
     target_logits [T_rows, V] bf16/fp32; target_offsets int32 [B+1]; draft-side int32 tokens, float32
     uniforms and logits packed with m_b entries per request from off[b]-b; max_verify_len bounds m_b + 1.
-    Keywords: draft_logits, u_accept, u_final, temperature, max_verify_len, workspace_tensor, out,
-    accept_prob, residual_mass. Returns the output tensors (accept_len, bonus, out_tokens, accept_index,
+    Keywords: draft_logits (rejection), cand_ids / cand_q ([T_rows - B, K] int32 / float32, rejection_sparse),
+    u_accept, u_final, temperature, max_verify_len, workspace_tensor, out, accept_prob, residual_mass. Returns the output tensors (accept_len, bonus, out_tokens, accept_index,
     status, accept_prob, residual_mass)."""
     return prepare_verify_chain(target_logits, target_offsets, draft_tokens, mode, **kw).run(events)
 

@@ -80,6 +80,9 @@ spec_status launch_pair(int dtype, int mode, bool tree, StatsParams& p, DrawPara
   d.spc = lo.spc;
   d.n_seg = lo.n_seg;
   d.seen_stride = lo.L;
+  d.cand_ids = p.cand_ids;
+  d.cand_q = p.cand_q;
+  d.K = p.K;
   if (launch_draw(dtype, d, lo, stream) != hipSuccess) return SPEC_ELAUNCH;
   return record(ev, nev, 2, stream);
 }
@@ -121,7 +124,9 @@ size_t spec_workspace_bytes(int32_t kind, int32_t mode, int64_t total_rows, int6
                             int32_t max_verify_len) {
   if (kind == SPEC_KIND_COMMIT) return 0;
   if (batch < 0 || vocab < 1 || vocab > kMaxVocab || total_rows < batch) return 0;
-  if (mode != SPEC_MODE_GREEDY && mode != SPEC_MODE_REJECTION && mode != SPEC_MODE_TARGET_ONLY) return 0;
+  if (mode != SPEC_MODE_GREEDY && mode != SPEC_MODE_REJECTION && mode != SPEC_MODE_TARGET_ONLY &&
+      mode != SPEC_MODE_REJECTION_SPARSE)
+    return 0;
   int32_t L;
   if (kind == SPEC_KIND_CHAIN) {
     L = max_verify_len;
@@ -145,11 +150,15 @@ spec_status spec_verify_chain(const spec_chain_args* a, hipStream_t stream) {
   if (!a) return SPEC_EINVAL;
   if (a->dtype != SPEC_DTYPE_F32 && a->dtype != SPEC_DTYPE_BF16) return SPEC_EDTYPE;
   if (a->mode == SPEC_MODE_TARGET_ONLY) return SPEC_EUNSUPPORTED;
-  if (a->mode != SPEC_MODE_GREEDY && a->mode != SPEC_MODE_REJECTION) return SPEC_EINVAL;
+  if (a->mode != SPEC_MODE_GREEDY && a->mode != SPEC_MODE_REJECTION && a->mode != SPEC_MODE_REJECTION_SPARSE)
+    return SPEC_EINVAL;
   if (a->batch < 0 || a->vocab < 1 || a->vocab > kMaxVocab || a->total_rows < a->batch ||
       a->total_rows > INT32_MAX || a->max_verify_len < 1 || a->max_verify_len > kMaxLen)
     return SPEC_EINVAL;
-  const bool rej = a->mode == SPEC_MODE_REJECTION;
+  const bool dense = a->mode == SPEC_MODE_REJECTION;
+  const bool sparse = a->mode == SPEC_MODE_REJECTION_SPARSE;
+  const bool sampling = dense || sparse;
+  if (sparse && (a->n_cand < 1 || a->n_cand > kMaxCand)) return SPEC_EINVAL;
   if (bad_events(a->profile_events, a->n_profile_events, spec_kernel_count(SPEC_KIND_CHAIN, a->mode)))
     return SPEC_EINVAL;
   if (a->batch == 0) {
@@ -162,17 +171,22 @@ spec_status spec_verify_chain(const spec_chain_args* a, hipStream_t stream) {
       !a->accept_index || !a->status)
     return SPEC_EINVAL;
   if (D > 0 && !a->draft_tokens) return SPEC_EINVAL;
-  if (rej) {
-    if (!a->u_final || (D > 0 && (!a->draft_logits || !a->u_accept))) return SPEC_EINVAL;
+  if (sampling) {
+    if (!a->u_final || (D > 0 && !a->u_accept)) return SPEC_EINVAL;
     if (!(a->temperature > 0.f) || !isfinite(a->temperature)) return SPEC_EINVAL;
   }
+  if (dense && D > 0 && !a->draft_logits) return SPEC_EINVAL;
+  if (sparse && D > 0 && (!a->cand_ids || !a->cand_q)) return SPEC_EINVAL;
   const Layout lo = make_layout(SPEC_KIND_CHAIN, a->mode, a->total_rows, a->vocab, a->batch, a->max_verify_len);
   if (!a->workspace || a->workspace_bytes < lo.bytes) return SPEC_EWORKSPACE;
 
   StatsParams p{};
   DrawParams d{};
   p.target = a->target_logits;
-  p.draft = a->draft_logits;
+  p.draft = dense ? a->draft_logits : nullptr;
+  p.cand_ids = sparse ? a->cand_ids : nullptr;
+  p.cand_q = sparse ? a->cand_q : nullptr;
+  p.K = sparse ? a->n_cand : 0;
   p.offsets = a->target_offsets;
   p.draft_tokens = a->draft_tokens;
   p.u_accept = a->u_accept;
@@ -186,14 +200,15 @@ spec_status spec_verify_chain(const spec_chain_args* a, hipStream_t stream) {
   p.L = lo.L;
   p.P = lo.P;
   p.S = lo.S;
-  p.coef = rej ? float(kLog2e / double(a->temperature)) : 0.f;
+  p.coef = sampling ? float(kLog2e / double(a->temperature)) : 0.f;
   return launch_pair(a->dtype, a->mode, false, p, d, lo, a->profile_events, a->n_profile_events, stream);
 }
 
 spec_status spec_verify_tree(const spec_tree_args* a, hipStream_t stream) {
   if (!a) return SPEC_EINVAL;
   if (a->dtype != SPEC_DTYPE_F32 && a->dtype != SPEC_DTYPE_BF16) return SPEC_EDTYPE;
-  if (a->mode == SPEC_MODE_REJECTION) return SPEC_EUNSUPPORTED;   // classic p/q rejection needs topk = 1
+  // classic p/q rejection needs topk = 1 (a chain)
+  if (a->mode == SPEC_MODE_REJECTION || a->mode == SPEC_MODE_REJECTION_SPARSE) return SPEC_EUNSUPPORTED;
   if (a->mode != SPEC_MODE_GREEDY && a->mode != SPEC_MODE_TARGET_ONLY) return SPEC_EINVAL;
   const bool tgt = a->mode == SPEC_MODE_TARGET_ONLY;
   if (tgt && (a->threshold_single != 1.f || a->threshold_acc != 1.f)) return SPEC_EUNSUPPORTED;

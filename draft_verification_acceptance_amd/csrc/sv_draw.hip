@@ -4,6 +4,10 @@
 //   every draft accepted      w = p_m                           ([EAGLE→DFlash2] §1.1, bonus)
 //   tree target-only          w = p_cur with the tried child tokens set to 0 ([SpecDec]
 //                             "为什么结果不受 draft 影响", target-only sampling; leaf: w = p_cur)
+//   sparse q, rejection at j  w = [p_{j-1} - q_{j-1}]_+ where q_{j-1} is zero off its K candidates
+//                             ([EAGLE→DFlash2] §6.5), so w = p except at the candidates
+// The last two are one rule: w = [p - a]_+ with a per-token adjustment list a (a tried token carries
+// a = +inf, a candidate its probability, repeated ids adding up) and a = 0 elsewhere.
 // The token is the number of cumulative probabilities u has reached, i.e. the smallest v with
 // sum_{t<=v} w_t > u * sum w ([EAGLE→DFlash2] §6.2, inverse-CDF rule); if rounding leaves u past the last
 // step the last positive-weight token is taken. Weights summing to 0 fall back to p (flagged).
@@ -61,11 +65,12 @@ __device__ __forceinline__ void unpack_raw8(const Raw8& w, float* x) {
   if (sizeof(DT) == 4) Elem<DT>::unpack(w.b, x + 4);
 }
 
-// Weights of tokens [e, e+8) from their logits: w (residual [p - q]_+, or p with tried tokens zeroed) and
-// p. The same arithmetic serves the segment sums and the token-by-token search, so both see identical
-// values.
+// Weights of tokens [e, e+8) from their logits: w (residual [p - q]_+ from a draft row, or [p - a]_+ with
+// the adjustment list (seen, seen_a)) and p. The same arithmetic serves the segment sums and the
+// token-by-token search, so both see identical values.
 __device__ __forceinline__ void weights8(const RowCtx& r, int64_t e, int64_t V, const float* x, const float* y,
-                                         const int32_t* seen, int n_seen, float* w, float* pv) {
+                                         const int32_t* seen, const float* seen_a, int n_seen, float* w,
+                                         float* pv) {
   if (r.xq) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -74,19 +79,22 @@ __device__ __forceinline__ void weights8(const RowCtx& r, int64_t e, int64_t V, 
       w[j] = fmaxf(pv[j] - qv, 0.f);
     }
   } else {
+    float adj[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       pv[j] = exp2_fast(fmaf(x[j], r.coef, -r.m_t)) * r.inv_zt;
-      w[j] = pv[j];
+      adj[j] = 0.f;
     }
     for (int i = 0; i < n_seen; ++i) {
       const int64_t d = int64_t(seen[i]) - e;
       if (d >= 0 && d < 8) {
 #pragma unroll
         for (int j = 0; j < 8; ++j)
-          if (j == d) w[j] = 0.f;
+          if (j == d) adj[j] += seen_a[i];
       }
     }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) w[j] = adj[j] > 0.f ? fmaxf(pv[j] - adj[j], 0.f) : pv[j];
   }
 #pragma unroll
   for (int j = 0; j < 8; ++j)
@@ -95,14 +103,51 @@ __device__ __forceinline__ void weights8(const RowCtx& r, int64_t e, int64_t V, 
 
 template <typename DT>
 __device__ __forceinline__ void load_weights8(const RowCtx& r, int64_t e, int64_t V, const int32_t* seen,
-                                              int n_seen, float* w, float* pv) {
+                                              const float* seen_a, int n_seen, float* w, float* pv) {
   Raw8 rt, rq;
   load_raw8<DT>(r.xt, e, V, r.vec, rt);
   if (r.xq) load_raw8<DT>(r.xq, e, V, r.vec, rq);
   float x[8], y[8];
   unpack_raw8<DT>(rt, x);
   if (r.xq) unpack_raw8<DT>(rq, y);
-  weights8(r, e, V, x, y, seen, n_seen, w, pv);
+  weights8(r, e, V, x, y, seen, seen_a, n_seen, w, pv);
+}
+
+// The adjustment list entries whose token lies in [lo, hi), copied to LDS in list order (ids outside the
+// vocab and masses that are negative, zero or not finite are left out). Returns the count (uniform).
+__device__ int collect_adjust(const int32_t* ids, const float* as, int n, int64_t lo, int64_t hi, int32_t* s_t,
+                              float* s_a, int* s_wcnt) {
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wv = tid / kWave;
+  int total = 0;
+  for (int i0 = 0; i0 < n; i0 += kThreads) {
+    const int i = i0 + tid;
+    bool keep = false;
+    int32_t t = 0;
+    float a = INFINITY;   // tried tree tokens: removed entirely
+    if (i < n) {
+      t = ids[i];
+      if (as) a = as[i];
+      keep = t >= lo && t < hi && (as == nullptr || (a > 0.f && a < INFINITY));
+    }
+    const uint64_t mask = __ballot(keep);
+    if (lane == 0) s_wcnt[wv] = __popcll(mask);
+    __syncthreads();
+    int before = total, here = 0;
+    for (int w = 0; w < kThreads / kWave; ++w) {
+      if (w < wv) before += s_wcnt[w];
+      here += s_wcnt[w];
+    }
+    if (keep) {
+      const int pos = before + __popcll(mask & lanes_below(lane));
+      s_t[pos] = t;
+      s_a[pos] = a;
+    }
+    total += here;
+    __syncthreads();
+  }
+  return total;
 }
 
 // Segment sums are published and read as agent-scope 64-bit atomics (see complete_memory_ops).
@@ -121,8 +166,9 @@ struct SegView {
 
 template <typename DT>
 __global__ __launch_bounds__(kThreads) void k_draw(DrawParams p) {
-  __shared__ int32_t s_seen[kMaxLen];
-  __shared__ int s_nseen;
+  __shared__ int32_t s_seen[kMaxLen];   // adjustment list entries inside the current token range
+  __shared__ float s_seen_a[kMaxLen];
+  __shared__ int s_wcnt[kThreads / kWave];
   __shared__ double red_d[kThreads / kWave];
   __shared__ int red_i[kThreads / kWave];
   __shared__ int s_last;
@@ -139,7 +185,7 @@ __global__ __launch_bounds__(kThreads) void k_draw(DrawParams p) {
 
   RowCtx r;
   r.xt = static_cast<const DT*>(p.target) + int64_t(d.row_t) * p.V;
-  r.xq = d.row_q >= 0 ? static_cast<const DT*>(p.draft) + int64_t(d.row_q) * p.V : nullptr;
+  r.xq = d.row_q >= 0 && p.draft ? static_cast<const DT*>(p.draft) + int64_t(d.row_q) * p.V : nullptr;
   r.coef = d.coef;
   r.m_t = d.m_t;
   r.inv_zt = 1.f / d.l_t;
@@ -152,14 +198,12 @@ __global__ __launch_bounds__(kThreads) void k_draw(DrawParams p) {
   const int64_t e_lo = int64_t(s_begin) * kSeg;
   const int64_t e_hi = int64_t(s_end) * kSeg;
   // Tried tokens inside this workgroup's range (tree target-only; usually none).
-  if (tid == 0) s_nseen = 0;
-  __syncthreads();
-  for (int i = tid; i < d.n_seen; i += kThreads) {
-    const int32_t t = p.seen[int64_t(b) * p.seen_stride + i];
-    if (t >= e_lo && t < e_hi) s_seen[atomicAdd(&s_nseen, 1)] = t;
-  }
-  __syncthreads();
-  const int n_seen = s_nseen;
+  // The adjustment list: the sparse candidates of the draft row, or the tokens a tree walk tried.
+  const bool sparse = p.cand_ids != nullptr && d.row_q >= 0;
+  const int32_t* adj_ids = sparse ? p.cand_ids + int64_t(d.row_q) * p.K : p.seen + int64_t(b) * p.seen_stride;
+  const float* adj_a = sparse ? p.cand_q + int64_t(d.row_q) * p.K : nullptr;
+  const int n_adj = sparse ? p.K : d.n_seen;
+  const int n_seen = collect_adjust(adj_ids, adj_a, n_adj, e_lo, e_hi, s_seen, s_seen_a, s_wcnt);
 
   // Lane l of a wave owns tokens [s*512 + 8l, s*512 + 8l + 8) of segment s. A trip covers kTrip segments
   // per wave with all of their loads issued before any is used.
@@ -183,7 +227,7 @@ __global__ __launch_bounds__(kThreads) void k_draw(DrawParams p) {
       float x[8], y[8], w[8], pv[8];
       unpack_raw8<DT>(rt[u], x);
       if (r.xq) unpack_raw8<DT>(rq[u], y);
-      weights8(r, e, p.V, x, y, s_seen, n_seen, w, pv);
+      weights8(r, e, p.V, x, y, s_seen, s_seen_a, n_seen, w, pv);
       float sw = 0.f, sp = 0.f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) { sw += w[j]; sp += pv[j]; }
@@ -253,20 +297,14 @@ __global__ __launch_bounds__(kThreads) void k_draw(DrawParams p) {
     block_scan_d(loc, red_d, e2, i2, t2);
     sel_excl = t2;
   }
-  // Tried tokens inside the selected segment.
-  __syncthreads();
-  if (tid == 0) s_nseen = 0;
+  // Adjustment list entries inside the selected segment.
   __syncthreads();
   const int64_t g_lo = int64_t(sel) * kSeg;
-  for (int i = tid; i < d.n_seen; i += kThreads) {
-    const int32_t t = p.seen[int64_t(b) * p.seen_stride + i];
-    if (t >= g_lo && t < g_lo + kSeg) s_seen[atomicAdd(&s_nseen, 1)] = t;
-  }
-  __syncthreads();
+  const int n_sel = collect_adjust(adj_ids, adj_a, n_adj, g_lo, g_lo + kSeg, s_seen, s_seen_a, s_wcnt);
   if (tid < kWave) {
     // Token by token in float64, ascending: lane l holds tokens g_lo + 8l .. g_lo + 8l + 7.
     float w[8], pv[8];
-    load_weights8<DT>(r, g_lo + 8 * lane, p.V, s_seen, use_p ? 0 : s_nseen, w, pv);
+    load_weights8<DT>(r, g_lo + 8 * lane, p.V, s_seen, s_seen_a, use_p ? 0 : n_sel, w, pv);
     double inc[8];
     double run = 0.0;
 #pragma unroll

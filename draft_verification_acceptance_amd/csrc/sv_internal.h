@@ -1,9 +1,10 @@
 // Internal definitions shared by the HIP translation units of libspecverify (not part of the ABI).
 //
 // Workspace state across calls: every call gets a fresh nonzero 32-bit epoch from the host. Per-request
-// completion counters are 64-bit words (epoch << 32 | count) advanced by compare-and-swap, and a draw
-// descriptor is pending only while its state equals the epoch, so whatever a previous call (of any shape)
-// left in the workspace is never mistaken for this call's progress.
+// completion counters are 64-bit words (epoch << 32 | count): k_stats restarts a counter that carries an
+// older epoch by compare-and-swap, and each request's scan arms its k_draw counter with the epoch and a
+// zero count. A draw descriptor is pending only while its state equals the epoch, so whatever a previous
+// call (of any shape) left in the workspace is never mistaken for this call's progress.
 //
 // Data flow of one verify call (all on the caller's stream, no host synchronisation):
 //   k_stats   one workgroup per (request, row slot, target|draft, vocab chunk): streams its slice of a
@@ -12,7 +13,8 @@
 //             (device-scope counter) merges the partials and runs the request's accept scan / tree walk,
 //             writes every output it can, and for sampling modes leaves a draw descriptor.
 //   k_draw    sampling modes only: one workgroup per (request, vocab chunk) re-reads the single row (or
-//             target/draft row pair) the final token is drawn from and writes per-512-token segment sums;
+//             target/draft row pair) the final token is drawn from, with the per-token adjustments of a
+//             short list (tried tree tokens, sparse q candidates), and writes per-512-token segment sums;
 //             the last workgroup of the request locates the inverse-CDF step (fp64 prefix over segments,
 //             then inside one segment) and writes the token.
 //   k_commit  one workgroup: exclusive scan of accept_len + 1 and the slot gathers of the KV commit.
@@ -29,6 +31,7 @@ constexpr int kThreads = 256;        // threads per workgroup of k_stats / k_dra
 constexpr int kWave = 64;            // gfx950 wavefront size
 constexpr int kSeg = 512;            // tokens per draw segment (one wave: 8 tokens per lane)
 constexpr int kMaxLen = 1024;        // max verify rows per request (chain) / nodes per tree
+constexpr int kMaxCand = 1024;       // max candidates per draft row (sparse q)
 constexpr int64_t kMaxVocab = int64_t(1) << 22;
 // Per-request completion counters sit 256 bytes apart: a request's workgroups all update its counter at
 // the end of the kernel, and counters sharing a cache line would serialise every request's updates on
@@ -52,10 +55,10 @@ struct alignas(16) Part {
 struct alignas(16) DrawDesc {
   uint32_t state;    // == the call's epoch: a draw is pending for this call
   int32_t row_t;     // global target row the token is drawn from
-  int32_t row_q;     // draft row of the residual [p - q]_+, or -1 (draw from p)
+  int32_t row_q;     // draft row of the residual [p - q]_+ (logits, or sparse candidates), or -1 (from p)
   int32_t out_pos;   // out_tokens index of the drawn token
-  float m_t, l_t;    // target row: max (log2 units) and log2 of its normaliser
-  float m_q, l_q;    // draft row, same meaning
+  float m_t, l_t;    // target row: max m (log2 units) and normaliser z of softmax = exp2(x*coef - m) / z
+  float m_q, l_q;    // draft row, same meaning (dense rejection)
   float coef;        // log2(e) / temperature
   float u;           // sanitized u_final
   uint32_t status;   // request status bits so far
@@ -122,6 +125,8 @@ struct StatsParams {
   const int32_t* draft_tokens;
   const int32_t* parents;
   const int32_t* tokens;
+  const int32_t* cand_ids;    // sparse q: [draft rows, K]
+  const float* cand_q;
   const float* u_accept;
   const float* u_final;
   int32_t* accept_len;
@@ -140,6 +145,7 @@ struct StatsParams {
   int64_t total_rows;
   int64_t chunk;
   int32_t B, L, P, S;
+  int32_t K;                  // sparse q: candidates per draft row (0 otherwise)
   float coef;
   uint32_t epoch;
 };
@@ -155,8 +161,10 @@ struct DrawParams {
   DrawDesc* desc;
   float2* seg;
   const int32_t* seen;
+  const int32_t* cand_ids;    // sparse q: the candidates of desc.row_q adjust the draw
+  const float* cand_q;
   int64_t V;
-  int32_t B, S2, spc, n_seg, seen_stride;
+  int32_t B, S2, spc, n_seg, seen_stride, K;
   uint32_t epoch;
 };
 

@@ -301,7 +301,9 @@ __device__ void scan_chain_greedy(const StatsParams& p, int b, int64_t off0, int
   }
 }
 
-template <typename DT>
+// Dense rejection (q from draft logits) or SPARSE (q from K candidate (id, probability) pairs per draft row,
+// zero off the candidates: [EAGLE→DFlash2] §6.5).
+template <typename DT, bool SPARSE>
 __device__ void scan_chain_rejection(const StatsParams& p, int b, int64_t off0, int len, char* smem) {
   __shared__ int s_red[kThreads / kWave];
   __shared__ uint32_t s_flags;
@@ -325,12 +327,24 @@ __device__ void scan_chain_rejection(const StatsParams& p, int b, int64_t off0, 
     s_zt[j] = zz;
     if (z_bad(zz)) fl |= SPEC_ST_NONFINITE;
   }
-  for (int j = tid; j < m; j += kThreads) {
-    float mm, zz;
-    merge_sampling(p.part + ((size_t(b) * p.L + j) * p.P + 1) * p.S, p.S, mm, zz);
-    s_mq[j] = mm;
-    s_zq[j] = zz;
-    if (z_bad(zz)) fl |= SPEC_ST_NONFINITE;
+  if (!SPARSE) {
+    for (int j = tid; j < m; j += kThreads) {
+      float mm, zz;
+      merge_sampling(p.part + ((size_t(b) * p.L + j) * p.P + 1) * p.S, p.S, mm, zz);
+      s_mq[j] = mm;
+      s_zq[j] = zz;
+      if (z_bad(zz)) fl |= SPEC_ST_NONFINITE;
+    }
+  } else {
+    // every candidate entry of the request's draft rows: ids in [0, V), probabilities finite and >= 0
+    const int64_t n_ent = int64_t(m) * p.K;
+    const int64_t e0 = dr0 * int64_t(p.K);
+    for (int64_t i = tid; i < n_ent; i += kThreads) {
+      const int32_t id = p.cand_ids[e0 + i];
+      const float qv = p.cand_q[e0 + i];
+      if (id < 0 || int64_t(id) >= p.V) fl |= SPEC_ST_BAD_TOKEN;
+      else if (!(qv >= 0.f && qv < INFINITY)) fl |= SPEC_ST_BAD_Q;
+    }
   }
   __syncthreads();
   int fail = INT32_MAX;
@@ -343,7 +357,22 @@ __device__ void scan_chain_rejection(const StatsParams& p, int b, int64_t off0, 
     if (ubad) fl |= SPEC_ST_BAD_UNIFORM;
     float a = 0.f;
     uint8_t bits = 0;
-    if (ok) {
+    if (ok && SPARSE) {
+      const float gt = gather<DT>(p.target, off0 + j, p.V, d);
+      // q(d): the masses of the valid candidate entries with id d, in entry order
+      const int64_t cb = (dr0 + j) * int64_t(p.K);
+      float qd = 0.f;
+      for (int k = 0; k < p.K; ++k) {
+        const float qv = p.cand_q[cb + k];
+        if (p.cand_ids[cb + k] == d && qv >= 0.f && qv < INFINITY) qd += qv;
+      }
+      if (!(qd > 0.f)) {           // q(d) = 0: alpha = 1 if p(d) > 0 else 0
+        bits |= 4;
+        a = gt > -INFINITY ? 1.f : 0.f;
+      } else {
+        a = fminf(1.f, exp2_fast(fmaf(gt, p.coef, -s_mt[j])) / (s_zt[j] * qd));
+      }
+    } else if (ok) {
       const float gt = gather<DT>(p.target, off0 + j, p.V, d);
       const float gq = gather<DT>(p.draft, dr0 + j, p.V, d);
       if (gq == -INFINITY) {       // q(d) = 0: alpha = 1 if p(d) > 0 else 0
@@ -389,8 +418,8 @@ __device__ void scan_chain_rejection(const StatsParams& p, int b, int64_t off0, 
     d.out_pos = int32_t(off0 + r);
     d.m_t = s_mt[r];
     d.l_t = s_zt[r];
-    d.m_q = r < m ? s_mq[r] : 0.f;
-    d.l_q = r < m ? s_zq[r] : 1.f;
+    d.m_q = r < m && !SPARSE ? s_mq[r] : 0.f;
+    d.l_q = r < m && !SPARSE ? s_zq[r] : 1.f;
     d.coef = p.coef;
     d.u = uf;
     d.status = s_flags;
@@ -586,7 +615,7 @@ __device__ void scan_tree(const StatsParams& p, int b, char* smem) {
       d.status = st;
       d.n_seen = s_nseen;
       p.desc[b] = d;
-    p.cnt2[size_t(b) * kCounterWords] = (unsigned long long)p.epoch << 32;   // the draw pass counts from 0
+      p.cnt2[size_t(b) * kCounterWords] = (unsigned long long)p.epoch << 32;   // the draw pass counts from 0
       s_flags = st;
     }
     p.status[b] = s_flags;
@@ -658,7 +687,8 @@ __global__ __launch_bounds__(kThreads) void k_stats(StatsParams p) {
   __syncthreads();
   if (!s_last) return;
   if (TREE) scan_tree<DT, SAMPLING>(p, b, smem);
-  else if (SAMPLING) scan_chain_rejection<DT>(p, b, off0, int(len), smem);
+  else if (SAMPLING && p.P == 2) scan_chain_rejection<DT, false>(p, b, off0, int(len), smem);
+  else if (SAMPLING) scan_chain_rejection<DT, true>(p, b, off0, int(len), smem);
   else scan_chain_greedy<DT>(p, b, off0, int(len), smem);
 }
 

@@ -17,6 +17,11 @@ uniforms streams, so requests can be generated independently and in parallel):
                    as the verifier sees q); greedy block workload: a planted accepted prefix (see
                    block_greedy); trees: EAGLE-style top-c expansion (see tree);
   * uniforms       Generator.random(dtype=float32), in [0, 1).
+  * sparse q       (chain_sparse) the drafter's candidate set of a draft row is the top-K of its float32
+                   draft logits (distinct ids, descending, lowest id first among equal values) and q the
+                   softmax over just those K at T, stored as float32; a greedy request takes the first
+                   candidate with a one-hot q over the candidates, a sampling request draws d ~ q from the
+                   stored float32 q (float64 inverse CDF).
 """
 from __future__ import annotations
 
@@ -87,6 +92,8 @@ class ChainWorkload:
     max_verify_len: int
     planted_r: np.ndarray | None = None     # block_greedy only: accept length fixed by construction
     meta: dict = field(default_factory=dict)
+    cand_ids: np.ndarray | None = None      # chain_sparse only: int32 [T_rows - B, K]
+    cand_q: np.ndarray | None = None        # chain_sparse only: float32 [T_rows - B, K]
 
     @property
     def total_rows(self) -> int:
@@ -97,9 +104,11 @@ class ChainWorkload:
         return "bf16" if self.target.dtype == np.uint16 else "f32"
 
     def algorithmic_bytes(self, mode: str) -> int:
-        """Every target row (and draft row in rejection mode) read once."""
+        """Every target row (and draft row in rejection mode, or the candidate pairs in sparse mode) read
+        once."""
         rows = self.total_rows + (self.total_rows - self.batch if mode == "rejection" else 0)
-        return rows * self.vocab * self.target.itemsize
+        extra = self.cand_ids.nbytes + self.cand_q.nbytes if mode == "rejection_sparse" else 0
+        return rows * self.vocab * self.target.itemsize + extra
 
 
 @dataclass
@@ -194,6 +203,62 @@ def ragged(seed: int = 5000, batch: int = 512, m_max: int = 15, vocab: int = QWE
     return _chain_from_lengths("ragged", seed, kids, lens, vocab, bf16=True, planted=True, scale=3.0,
                                draft_sigma=0.8, temperature=temperature, modes=("rejection",),
                                max_len=m_max + 1, parallel=parallel)
+
+
+def top_candidates(x: np.ndarray, K: int) -> np.ndarray:
+    """Ids of the K largest entries of x, by descending value and ascending id among equal values."""
+    part = np.argpartition(-x, K - 1)[:K] if K < len(x) else np.arange(len(x))
+    kth = x[part].min()
+    pool = np.flatnonzero(x >= kth)                  # every id tied with the K-th value competes
+    order = np.lexsort((pool, -x[pool].astype(np.float64)))
+    return pool[order[:K]].astype(np.int32)
+
+
+def chain_sparse(seed: int = 6000, batch: int = 64, m: int = 7, vocab: int = QWEN_VOCAB, K: int = 16,
+                 temperature: float = 1.0, greedy_frac: float = 0.25, bf16: bool = True,
+                 ragged: bool = False, draft_sigma: float = 1.0, parallel: bool = True) -> ChainWorkload:
+    """Chain rejection with a sparse q (the DFlash 2 selector's K candidates): B 64, m 7, V 151,936, bf16
+    target as chain_rejection; per draft row the top-16 of draft logits target + N(0, 1) and q = softmax
+    over them at T 1.0; a quarter of the requests are greedy rows (one-hot q on the first candidate).
+    ragged=True draws each request's m from U{0..m} instead."""
+    kids = np.random.SeedSequence(seed).spawn(batch + 1)
+    s_struct = np.random.Generator(np.random.PCG64(kids[0]))
+    greedy = s_struct.random(batch) < greedy_frac
+    lens = s_struct.integers(0, m + 1, size=batch) + 1 if ragged else np.full(batch, m + 1, np.int64)
+    w = _chain_from_lengths("chain_sparse", seed, kids, lens, vocab, bf16=bf16, planted=True, scale=3.0,
+                            draft_sigma=None, temperature=temperature, modes=("rejection_sparse",),
+                            max_len=m + 1, parallel=parallel)
+    D = w.total_rows - batch
+    ids = np.empty((D, K), np.int32)
+    qs = np.empty((D, K), np.float32)
+
+    def one(b):
+        # streams 4 and 5 of request b (0..3 made its target rows and uniforms)
+        s_noise, s_tok = [np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed, spawn_key=(b + 1, i))))
+                          for i in (4, 5)]
+        lo, dlo = int(w.offsets[b]), int(w.offsets[b]) - b
+        for j in range(int(lens[b]) - 1):
+            t = bf16_to_f32(w.target[lo + j]) if bf16 else w.target[lo + j]
+            d = t + s_noise.standard_normal(vocab, dtype=np.float32) * np.float32(draft_sigma)
+            c = top_candidates(d, K)
+            ids[dlo + j] = c
+            if greedy[b]:
+                qs[dlo + j] = 0.0
+                qs[dlo + j, 0] = 1.0
+                w.draft_tokens[dlo + j] = c[0]
+            else:
+                z = d[c].astype(np.float64) / temperature
+                e = np.exp(z - z.max())
+                qs[dlo + j] = (e / e.sum()).astype(np.float32)
+                cdf = np.cumsum(qs[dlo + j].astype(np.float64))
+                u = float(s_tok.random(dtype=np.float32))
+                k = int(np.searchsorted(cdf, u * cdf[-1], side="right"))
+                w.draft_tokens[dlo + j] = c[min(k, K - 1)]
+
+    _pool_map(one, range(batch), parallel)
+    w.cand_ids, w.cand_q = ids, qs
+    w.meta["greedy_requests"] = int(greedy.sum())
+    return w
 
 
 def block_greedy(seed: int = 3000, batch: int = 32, block: int = 16, vocab: int = QWEN_VOCAB,
@@ -330,4 +395,5 @@ FULL = {
     "block_greedy": block_greedy,
     "tree": tree,
     "ragged": ragged,
+    "chain_sparse": chain_sparse,
 }

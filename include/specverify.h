@@ -43,7 +43,7 @@ extern "C" {
 typedef struct ihipStream_t* hipStream_t;
 typedef struct ihipEvent_t* hipEvent_t;
 
-#define SPEC_ABI_VERSION 1
+#define SPEC_ABI_VERSION 2
 
 /* Host-visible return codes. */
 typedef enum spec_status {
@@ -73,8 +73,20 @@ typedef enum spec_dtype { SPEC_DTYPE_F32 = 0, SPEC_DTYPE_BF16 = 1 } spec_dtype;
  *                `cur` add p_cur(token) of each child in ascending node order (a token already seen among
  *                earlier siblings adds nothing) into acc and accept the first child with u_cur < acc; if
  *                none is accepted draw from p_cur with the tried tokens zeroed; at a leaf draw from p_cur.
+ *   REJECTION_SPARSE
+ *                chain only: REJECTION where each draft row's q arrives as K (candidate id, probability)
+ *                pairs instead of draft logits: q is that candidate distribution scattered into vocab
+ *                coordinates and zero elsewhere, so [p-q]_+ still covers the whole vocab and tokens
+ *                outside the candidates remain reachable ([EAGLE→DFlash2] §6.5, sampling verify with the
+ *                selector's q; greedy rows carry a one-hot q, i.e. K = 1 with probability 1). A repeated id
+ *                adds its masses. The temperature divides the target logits only.
  */
-typedef enum spec_mode { SPEC_MODE_GREEDY = 0, SPEC_MODE_REJECTION = 1, SPEC_MODE_TARGET_ONLY = 2 } spec_mode;
+typedef enum spec_mode {
+  SPEC_MODE_GREEDY = 0,
+  SPEC_MODE_REJECTION = 1,
+  SPEC_MODE_TARGET_ONLY = 2,
+  SPEC_MODE_REJECTION_SPARSE = 3,
+} spec_mode;
 
 typedef enum spec_kind { SPEC_KIND_CHAIN = 0, SPEC_KIND_TREE = 1, SPEC_KIND_COMMIT = 2 } spec_kind;
 
@@ -97,9 +109,12 @@ typedef enum spec_kind { SPEC_KIND_CHAIN = 0, SPEC_KIND_TREE = 1, SPEC_KIND_COMM
 #define SPEC_ST_NEAR_CDF      (1u << 8) /* diagnostic: the final draw's u lies within 1e-5 of a CDF step, or
                                            that margin times the weights' total mass Z is below 1e-6        */
 #define SPEC_ST_BAD_ACCEPT    (1u << 9) /* commit: accept_len / accept_index outside the request's rows     */
+#define SPEC_ST_BAD_Q         (1u << 10) /* REJECTION_SPARSE: a candidate probability that is negative or not
+                                            finite; the entry is left out (an out-of-range candidate id
+                                            sets SPEC_ST_BAD_TOKEN and is left out too)                     */
 
 /*
- * Chain verify (GREEDY or REJECTION).
+ * Chain verify (GREEDY, REJECTION or REJECTION_SPARSE).
  *
  * Request b owns target rows [off[b], off[b+1]) (the ragged packing of [EAGLE→DFlash2] §5.6.5: verify
  * lens [4,2,6] -> offsets [0,4,6,12]); m_b = off[b+1] - off[b] - 1 >= 0 drafts. Draft-side arrays are
@@ -113,16 +128,16 @@ typedef enum spec_kind { SPEC_KIND_CHAIN = 0, SPEC_KIND_TREE = 1, SPEC_KIND_COMM
  *   out_tokens[off[b]+k]      k < r: d_{k+1}; k == r: bonus; k > r: -1
  *   accept_index[off[b]+k]    k <= r: off[b]+k (global verify row whose KV is committed); else -1
  *   status[b]                 SPEC_ST_* bits
- *   accept_prob[off[b]-b+j]   opt.: alpha_{j+1} where tested (REJECTION), else -1
- *   residual_mass[b]          opt.: sum of the final draw's weights (REJECTION), -1 in GREEDY
+ *   accept_prob[off[b]-b+j]   opt.: alpha_{j+1} where tested (sampling modes), else -1
+ *   residual_mass[b]          opt.: sum of the final draw's weights (sampling modes), -1 in GREEDY
  */
 typedef struct spec_chain_args {
   const void* target_logits;     /* [total_rows, vocab]                                   */
   const int32_t* target_offsets; /* [batch+1], off[0] = 0, off[batch] = total_rows           */
   const void* draft_logits;      /* [total_rows - batch, vocab]; REJECTION only (else NULL) */
   const int32_t* draft_tokens;   /* [total_rows - batch]                                   */
-  const float* u_accept;         /* [total_rows - batch]; REJECTION only                   */
-  const float* u_final;          /* [batch]; REJECTION only                                */
+  const float* u_accept;         /* [total_rows - batch]; sampling modes only              */
+  const float* u_final;          /* [batch]; sampling modes only                           */
   int32_t* accept_len;           /* [batch]                                                */
   int32_t* bonus;                /* [batch]                                                */
   int32_t* out_tokens;           /* [total_rows]                                           */
@@ -141,9 +156,14 @@ typedef struct spec_chain_args {
   int32_t max_verify_len;        /* upper bound on m_b + 1, 1..1024; a longer request is
                                     reported as SPEC_ST_BAD_OFFSETS                        */
   int32_t dtype;                 /* spec_dtype                                             */
-  int32_t mode;                  /* SPEC_MODE_GREEDY or SPEC_MODE_REJECTION                */
-  float temperature;             /* REJECTION: finite, > 0; logits are divided by it        */
+  int32_t mode;                  /* SPEC_MODE_GREEDY, _REJECTION or _REJECTION_SPARSE       */
+  float temperature;             /* sampling modes: finite, > 0; logits are divided by it    */
   int32_t n_profile_events;
+  /* REJECTION_SPARSE only (else NULL / 0): candidate k of draft row i sits at [i * n_cand + k]     */
+  const int32_t* cand_ids;       /* [total_rows - batch, n_cand] candidate token ids        */
+  const float* cand_q;           /* [total_rows - batch, n_cand] their probabilities        */
+  int32_t n_cand;                /* K, 1..1024                                             */
+  int32_t reserved;
 } spec_chain_args;
 
 /*

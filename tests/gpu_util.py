@@ -44,6 +44,9 @@ def run_chain(w, mode, *, target=None, draft=None, ws=None, **kw):
     if mode == "rejection":
         d = dev_logits(w.draft) if draft is None else draft
         args.update(draft_logits=d, u_accept=dev(w.u_accept), u_final=dev(w.u_final), temperature=w.temperature)
+    elif mode == "rejection_sparse":
+        args.update(cand_ids=dev(w.cand_ids, torch.int32), cand_q=dev(w.cand_q, torch.float32),
+                    u_accept=dev(w.u_accept), u_final=dev(w.u_final), temperature=w.temperature)
     args.update(kw)
     o = dva.verify_chain(t, dev(w.offsets, torch.int32), dev(w.draft_tokens, torch.int32), mode, **args)
     return np_out(o)
@@ -63,6 +66,9 @@ def oracle_chain(w, mode, requests=None):
     kw = dict(max_verify_len=w.max_verify_len, requests=requests)
     if mode == "rejection":
         kw.update(draft=w.draft, u_accept=w.u_accept, u_final=w.u_final, temperature=w.temperature)
+    elif mode == "rejection_sparse":
+        kw.update(cand_ids=w.cand_ids, cand_q=w.cand_q, u_accept=w.u_accept, u_final=w.u_final,
+                  temperature=w.temperature)
     return oracle.verify_chain(w.target, w.offsets, w.draft_tokens, mode, **kw)
 
 
@@ -125,7 +131,7 @@ def compare_chain(w, mode, o, g, requests=None):
     reqs = list(range(w.batch) if requests is None else requests)
     off = w.offsets
     ex, same = compare(o, g, lambda b: int(off[b]), lambda b: int(off[b + 1]), lambda b: int(off[b]) - b,
-                       lambda b: int(off[b + 1]) - b - 1, reqs, mode == "rejection")
+                       lambda b: int(off[b + 1]) - b - 1, reqs, mode != "greedy")
     check_exempt(len(reqs), ex, same, f"{w.name}/{mode}")
     return ex
 

@@ -69,7 +69,58 @@ def test_ragged_small_vocab():
     compare_chain(w, "rejection", o, g)
 
 
+@pytest.mark.parametrize("K,T,sigma", [(16, 1.0, 1.0), (1, 0.7, 1.0), (64, 0.5, 0.2)])
+def test_chain_sparse_small_vocab(K, T, sigma):
+    w = W.chain_sparse(seed=6001, vocab=20011, K=K, temperature=T, greedy_frac=0.3, batch=40, draft_sigma=sigma)
+    _say("chain_sparse V=20011", K, T, w.meta)
+    g = run_chain(w, "rejection_sparse")
+    o = oracle_chain(w, "rejection_sparse")
+    compare_chain(w, "rejection_sparse", o, g)
+    # tokens outside the candidates are emitted after rejections (the residual spans the vocab)
+    D = w.total_rows - w.batch
+    outside = 0
+    for b in range(w.batch):
+        r = int(o["accept_len"][b])
+        if r < 7:
+            outside += int(int(o["bonus"][b]) not in set(w.cand_ids[int(w.offsets[b]) - b + r].tolist()))
+    assert D > 0 and (outside > 0 or K == 64)
+
+
+def test_chain_sparse_fp32_and_ragged():
+    w = W.chain_sparse(seed=6002, vocab=999, K=8, temperature=0.8, greedy_frac=0.5, batch=24, bf16=False,
+                       ragged=True, parallel=False)
+    _say("chain_sparse fp32 V=999")
+    assert compare_chain(w, "rejection_sparse", oracle_chain(w, "rejection_sparse"), run_chain(w, "rejection_sparse")) <= 12
+    # duplicates, invalid entries and q(d) = 0 on the device as in the oracle
+    ids = w.cand_ids.copy()
+    q = w.cand_q.copy()
+    D = w.total_rows - w.batch
+    assert D >= 8
+    ids[0, 1] = ids[0, 0]                     # repeated id: masses add
+    ids[D // 4, 2] = w.vocab + 3              # out of range: BAD_TOKEN, left out
+    q[D // 2, 3] = -0.5                       # negative: BAD_Q, left out
+    q[D - 1, 0] = np.nan
+    w.draft_tokens[3] = int(np.setdiff1d(np.arange(w.vocab), ids[3])[0])   # not a candidate: q(d) = 0
+    w.cand_ids, w.cand_q = ids, q
+    o = oracle_chain(w, "rejection_sparse")
+    g = run_chain(w, "rejection_sparse")
+    assert np.any(o["status"] & oracle.ST_BAD_TOKEN) and np.any(o["status"] & oracle.ST_BAD_Q)
+    compare_chain(w, "rejection_sparse", o, g)
+
+
 # Full sizes, the benchmark's launch configuration; the oracle checks a sample of requests.
+def test_full_chain_sparse():
+    w = W.chain_sparse()
+    _say("chain_sparse full", w.meta)
+    g = run_chain(w, "rejection_sparse")
+    reqs = [0, 1, 17, 33, 50, 63]
+    o = oracle_chain(w, "rejection_sparse", reqs)
+    compare_chain(w, "rejection_sparse", o, g, reqs)
+    assert np.all((g["accept_len"] >= 0) & (g["accept_len"] <= 7))
+    assert not np.any(g["status"] & ~np.uint32(oracle.ST_NEAR_ALPHA | oracle.ST_NEAR_CDF))
+
+
+
 def test_full_chain_rejection():
     w = W.chain_rejection()
     _say("chain_rejection full")
