@@ -38,10 +38,14 @@ def _log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+STATS_SOURCES = ("sv_stats.hip", "sv_device.h", "sv_internal.h")   # what k_stats is compiled from
+
+
 def kernel_source_hash() -> str:
+    """Hash of the k_stats sources: counter summaries taken on other sources are not reused."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "draft_verification_acceptance_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in STATS_SOURCES:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
