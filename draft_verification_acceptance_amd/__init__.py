@@ -25,7 +25,7 @@ __all__ = [
 _PKG = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_PKG, "libspecverify.so")
 
-ABI_VERSION = 2
+ABI_VERSION = 3
 MODES = {"greedy": 0, "rejection": 1, "target_only": 2, "rejection_sparse": 3}
 KIND_CHAIN, KIND_TREE, KIND_COMMIT = 0, 1, 2
 DTYPES = {torch.float32: 0, torch.bfloat16: 1}
@@ -182,7 +182,8 @@ def _req(t: torch.Tensor, name: str, dtype, n=None, device=None):
 
 
 class HipEvents:
-    """Timing events created through the HIP runtime, recorded by the library between its kernels."""
+    """Timing events created through the HIP runtime. Passed to a library call (2 per kernel), events 2k and
+    2k+1 take the start and stop timestamps of the call's kernel k."""
 
     def __init__(self, n: int):
         self._hip = ctypes.CDLL("libamdhip64.so")

@@ -2,8 +2,6 @@
 // Nothing here allocates, synchronises or reads device memory.
 #include <math.h>
 
-#include <atomic>
-#include <chrono>
 
 #include "sv_internal.h"
 
@@ -13,29 +11,30 @@ namespace {
 
 constexpr double kLog2e = 1.4426950408889634;
 
-// Per-call epoch (never 0, the value of a zero-filled workspace); seeded from the clock so that a
-// workspace left by another process is not mistaken for this process's calls.
-uint32_t next_epoch() {
-  static std::atomic<uint32_t> ctr{uint32_t(std::chrono::steady_clock::now().time_since_epoch().count() * 2654435761u)};
-  uint32_t e;
-  do {
-    e = ctr.fetch_add(1u, std::memory_order_relaxed) + 1u;
-  } while (e == 0u);
-  return e;
+// The logits stream launches B x L x P x S workgroups and the draw B x S2: both within one grid dimension.
+bool grid_fits(const Layout& lo, int32_t batch) {
+  const int64_t stream_wgs = int64_t(batch) * lo.L * lo.P * lo.S;
+  const int64_t draw_wgs = int64_t(batch) * lo.S2;
+  return stream_wgs <= INT32_MAX && draw_wgs <= INT32_MAX;
 }
 
+// Profiling events: none, or a start / stop pair per kernel, taken from the kernel's own timestamps.
 bool bad_events(hipEvent_t* ev, int32_t n, int32_t kernels) {
   if (n == 0) return false;
-  return ev == nullptr || n != kernels + 1;
+  return ev == nullptr || n != 2 * kernels;
 }
 
-spec_status record(hipEvent_t* ev, int32_t n, int32_t i, hipStream_t stream) {
-  if (n == 0) return SPEC_OK;
-  return hipEventRecord(ev[i], stream) == hipSuccess ? SPEC_OK : SPEC_ELAUNCH;
+hipEvent_t ev_at(hipEvent_t* ev, int32_t n, int32_t i) { return n ? ev[i] : nullptr; }
+
+// Nothing to launch: every event is still recorded on the stream, so that it completes.
+spec_status record_all(hipEvent_t* ev, int32_t n, hipStream_t stream) {
+  for (int32_t i = 0; i < n; ++i)
+    if (hipEventRecord(ev[i], stream) != hipSuccess) return SPEC_ELAUNCH;
+  return SPEC_OK;
 }
 
 template <typename A>
-void fill_outputs(StatsParams& p, const A* a) {
+void fill_outputs(VerifyParams& p, const A* a) {
   p.accept_len = a->accept_len;
   p.bonus = a->bonus;
   p.out_tokens = a->out_tokens;
@@ -45,46 +44,28 @@ void fill_outputs(StatsParams& p, const A* a) {
   p.residual_mass = a->residual_mass;
 }
 
-void carve(StatsParams& p, DrawParams& d, const Layout& lo, void* ws) {
+void carve(VerifyParams& p, const Layout& lo, void* ws) {
   char* w = static_cast<char*>(ws);
-  p.cnt = reinterpret_cast<unsigned long long*>(w + lo.off_cnt);
+  p.cnt2 = reinterpret_cast<unsigned long long*>(w + lo.off_cnt2);
   p.part = reinterpret_cast<Part*>(w + lo.off_part);
-  p.desc = reinterpret_cast<DrawDesc*>(w + lo.off_desc);
-  p.seen = reinterpret_cast<int32_t*>(w + lo.off_seen);
-  d.cnt2 = reinterpret_cast<unsigned long long*>(w + lo.off_cnt2);
-  p.cnt2 = d.cnt2;
-  d.desc = p.desc;
-  d.seg = reinterpret_cast<float2*>(w + lo.off_seg);
-  d.seen = p.seen;
+  p.seg = reinterpret_cast<float2*>(w + lo.off_seg);
+  p.chunk = lo.chunk;
+  p.L = lo.L;
+  p.P = lo.P;
+  p.S = lo.S;
+  p.S2 = lo.S2;
+  p.spc = lo.spc;
+  p.n_seg = lo.n_seg;
 }
 
-spec_status launch_pair(int dtype, int mode, bool tree, StatsParams& p, DrawParams& d, const Layout& lo,
-                        hipEvent_t* ev, int32_t nev, hipStream_t stream) {
-  p.epoch = next_epoch();
-  d.epoch = p.epoch;
-  spec_status s = record(ev, nev, 0, stream);
-  if (s != SPEC_OK) return s;
-  if (launch_stats(dtype, mode, tree, p, lo, stream) != hipSuccess) return SPEC_ELAUNCH;
-  s = record(ev, nev, 1, stream);
-  if (s != SPEC_OK) return s;
-  if (mode == SPEC_MODE_GREEDY) return SPEC_OK;
-  d.target = p.target;
-  d.draft = p.draft;
-  d.bonus = p.bonus;
-  d.out_tokens = p.out_tokens;
-  d.status = p.status;
-  d.residual_mass = p.residual_mass;
-  d.V = p.V;
-  d.B = p.B;
-  d.S2 = lo.S2;
-  d.spc = lo.spc;
-  d.n_seg = lo.n_seg;
-  d.seen_stride = lo.L;
-  d.cand_ids = p.cand_ids;
-  d.cand_q = p.cand_q;
-  d.K = p.K;
-  if (launch_draw(dtype, d, lo, stream) != hipSuccess) return SPEC_ELAUNCH;
-  return record(ev, nev, 2, stream);
+// The two kernels of a verify call: the logits stream, then the greedy scans or the sampling draw.
+spec_status launch_pair(int dtype, int mode, VerifyParams& p, hipEvent_t* ev, int32_t nev, hipStream_t stream) {
+  if (launch_stats(dtype, mode, p, stream, ev_at(ev, nev, 0), ev_at(ev, nev, 1)) != hipSuccess)
+    return SPEC_ELAUNCH;
+  const hipError_t e = mode == SPEC_MODE_GREEDY
+                           ? launch_scan(dtype, p, stream, ev_at(ev, nev, 2), ev_at(ev, nev, 3))
+                           : launch_draw(dtype, mode, p, stream, ev_at(ev, nev, 2), ev_at(ev, nev, 3));
+  return e == hipSuccess ? SPEC_OK : SPEC_ELAUNCH;
 }
 
 }  // namespace
@@ -115,9 +96,10 @@ const char* spec_status_string(spec_status s) {
 }
 
 int32_t spec_kernel_count(int32_t kind, int32_t mode) {
+  (void)mode;
   if (kind == SPEC_KIND_COMMIT) return 1;
   if (kind != SPEC_KIND_CHAIN && kind != SPEC_KIND_TREE) return 0;
-  return mode == SPEC_MODE_GREEDY ? 1 : 2;
+  return 2;
 }
 
 size_t spec_workspace_bytes(int32_t kind, int32_t mode, int64_t total_rows, int64_t vocab, int32_t batch,
@@ -161,11 +143,7 @@ spec_status spec_verify_chain(const spec_chain_args* a, hipStream_t stream) {
   if (sparse && (a->n_cand < 1 || a->n_cand > kMaxCand)) return SPEC_EINVAL;
   if (bad_events(a->profile_events, a->n_profile_events, spec_kernel_count(SPEC_KIND_CHAIN, a->mode)))
     return SPEC_EINVAL;
-  if (a->batch == 0) {
-    for (int i = 0; i < a->n_profile_events; ++i)
-      if (record(a->profile_events, a->n_profile_events, i, stream) != SPEC_OK) return SPEC_ELAUNCH;
-    return SPEC_OK;
-  }
+  if (a->batch == 0) return record_all(a->profile_events, a->n_profile_events, stream);
   const int64_t D = a->total_rows - a->batch;
   if (!a->target_logits || !a->target_offsets || !a->accept_len || !a->bonus || !a->out_tokens ||
       !a->accept_index || !a->status)
@@ -178,10 +156,10 @@ spec_status spec_verify_chain(const spec_chain_args* a, hipStream_t stream) {
   if (dense && D > 0 && !a->draft_logits) return SPEC_EINVAL;
   if (sparse && D > 0 && (!a->cand_ids || !a->cand_q)) return SPEC_EINVAL;
   const Layout lo = make_layout(SPEC_KIND_CHAIN, a->mode, a->total_rows, a->vocab, a->batch, a->max_verify_len);
+  if (!grid_fits(lo, a->batch)) return SPEC_EINVAL;
   if (!a->workspace || a->workspace_bytes < lo.bytes) return SPEC_EWORKSPACE;
 
-  StatsParams p{};
-  DrawParams d{};
+  VerifyParams p{};
   p.target = a->target_logits;
   p.draft = dense ? a->draft_logits : nullptr;
   p.cand_ids = sparse ? a->cand_ids : nullptr;
@@ -192,16 +170,13 @@ spec_status spec_verify_chain(const spec_chain_args* a, hipStream_t stream) {
   p.u_accept = a->u_accept;
   p.u_final = a->u_final;
   fill_outputs(p, a);
-  carve(p, d, lo, a->workspace);
+  carve(p, lo, a->workspace);
   p.V = a->vocab;
   p.total_rows = a->total_rows;
-  p.chunk = lo.chunk;
   p.B = a->batch;
-  p.L = lo.L;
-  p.P = lo.P;
-  p.S = lo.S;
+  p.tree = 0;
   p.coef = sampling ? float(kLog2e / double(a->temperature)) : 0.f;
-  return launch_pair(a->dtype, a->mode, false, p, d, lo, a->profile_events, a->n_profile_events, stream);
+  return launch_pair(a->dtype, a->mode, p, a->profile_events, a->n_profile_events, stream);
 }
 
 spec_status spec_verify_tree(const spec_tree_args* a, hipStream_t stream) {
@@ -217,11 +192,7 @@ spec_status spec_verify_tree(const spec_tree_args* a, hipStream_t stream) {
     return SPEC_EINVAL;
   if (bad_events(a->profile_events, a->n_profile_events, spec_kernel_count(SPEC_KIND_TREE, a->mode)))
     return SPEC_EINVAL;
-  if (a->batch == 0) {
-    for (int i = 0; i < a->n_profile_events; ++i)
-      if (record(a->profile_events, a->n_profile_events, i, stream) != SPEC_OK) return SPEC_ELAUNCH;
-    return SPEC_OK;
-  }
+  if (a->batch == 0) return record_all(a->profile_events, a->n_profile_events, stream);
   if (!a->target_logits || !a->parents || !a->tokens || !a->accept_len || !a->bonus || !a->out_tokens ||
       !a->accept_index || !a->status)
     return SPEC_EINVAL;
@@ -231,10 +202,10 @@ spec_status spec_verify_tree(const spec_tree_args* a, hipStream_t stream) {
   }
   const int64_t rows = int64_t(a->batch) * a->n_nodes;
   const Layout lo = make_layout(SPEC_KIND_TREE, a->mode, rows, a->vocab, a->batch, a->n_nodes);
+  if (!grid_fits(lo, a->batch)) return SPEC_EINVAL;
   if (!a->workspace || a->workspace_bytes < lo.bytes) return SPEC_EWORKSPACE;
 
-  StatsParams p{};
-  DrawParams d{};
+  VerifyParams p{};
   p.target = a->target_logits;
   p.draft = nullptr;
   p.parents = a->parents;
@@ -242,16 +213,13 @@ spec_status spec_verify_tree(const spec_tree_args* a, hipStream_t stream) {
   p.u_accept = a->u_accept;
   p.u_final = a->u_final;
   fill_outputs(p, a);
-  carve(p, d, lo, a->workspace);
+  carve(p, lo, a->workspace);
   p.V = a->vocab;
   p.total_rows = rows;
-  p.chunk = lo.chunk;
   p.B = a->batch;
-  p.L = lo.L;
-  p.P = 1;
-  p.S = lo.S;
+  p.tree = 1;
   p.coef = tgt ? float(kLog2e / double(a->temperature)) : 0.f;
-  return launch_pair(a->dtype, a->mode, true, p, d, lo, a->profile_events, a->n_profile_events, stream);
+  return launch_pair(a->dtype, a->mode, p, a->profile_events, a->n_profile_events, stream);
 }
 
 spec_status spec_commit_indices(const spec_commit_args* a, hipStream_t stream) {
@@ -265,10 +233,10 @@ spec_status spec_commit_indices(const spec_commit_args* a, hipStream_t stream) {
                        !a->dst_pos || !a->new_seq_lens || !a->status))
     return SPEC_EINVAL;
   if ((a->evict_slots == nullptr) != (a->evict_offsets == nullptr)) return SPEC_EINVAL;
-  spec_status s = record(a->profile_events, a->n_profile_events, 0, stream);
-  if (s != SPEC_OK) return s;
-  if (launch_commit(*a, stream) != hipSuccess) return SPEC_ELAUNCH;
-  return record(a->profile_events, a->n_profile_events, 1, stream);
+  const int32_t n = a->n_profile_events;
+  if (launch_commit(*a, stream, ev_at(a->profile_events, n, 0), ev_at(a->profile_events, n, 1)) != hipSuccess)
+    return SPEC_ELAUNCH;
+  return SPEC_OK;
 }
 
 }  // extern "C"

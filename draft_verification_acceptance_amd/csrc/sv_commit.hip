@@ -203,9 +203,8 @@ __global__ void k_fill_zero(uint4* p, size_t n16, uint8_t* tail, size_t ntail) {
 
 }  // namespace
 
-hipError_t launch_commit(const spec_commit_args& a, hipStream_t stream) {
-  hipLaunchKernelGGL(k_commit, dim3(1), dim3(kCommitThreads), 0, stream, a);
-  return hipGetLastError();
+hipError_t launch_commit(const spec_commit_args& a, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+  return launch_kernel(k_commit, dim3(1), dim3(kCommitThreads), 0, stream, ev0, ev1, a);
 }
 
 hipError_t launch_fill_zero(void* ptr, size_t bytes, hipStream_t stream) {

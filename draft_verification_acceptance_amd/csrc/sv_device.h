@@ -94,19 +94,6 @@ __device__ __forceinline__ void complete_memory_ops() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-// Advance a per-request completion counter of this call: a 64-bit word (epoch << 32 | count). A word
-// left by another call (other epoch) is restarted at 1 by one compare-and-swap; otherwise a single
-// atomic add. Returns the count after this increment.
-__device__ __forceinline__ uint32_t count_done(unsigned long long* c, uint32_t epoch) {
-  unsigned long long old = load_agent(c);
-  if (uint32_t(old >> 32) != epoch) {
-    const unsigned long long fresh = ((unsigned long long)epoch << 32) | 1ull;
-    if (atomicCAS(c, old, fresh) == old) return 1u;
-    // another workgroup of this call restarted it first: the word now carries this epoch
-  }
-  return uint32_t(atomicAdd(c, 1ull)) + 1u;
-}
-
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
 __device__ __forceinline__ uint64_t lanes_below(int lane) {
@@ -132,7 +119,8 @@ __device__ __forceinline__ int wave_max_i(int v) {
   return v;
 }
 
-// Block-wide min over kThreads threads; every thread gets the result. `red` holds >= 4 ints of LDS.
+// Block-wide min over NT threads; every thread gets the result. `red` holds >= NT / 64 ints of LDS.
+template <int NT = kThreads>
 __device__ __forceinline__ int block_min_i(int v, int* red) {
   v = wave_min_i(v);
   __syncthreads();
@@ -140,11 +128,12 @@ __device__ __forceinline__ int block_min_i(int v, int* red) {
   __syncthreads();
   int r = red[0];
 #pragma unroll
-  for (int w = 1; w < kThreads / kWave; ++w) r = min(r, red[w]);
+  for (int w = 1; w < NT / kWave; ++w) r = min(r, red[w]);
   __syncthreads();
   return r;
 }
 
+template <int NT = kThreads>
 __device__ __forceinline__ int block_max_i(int v, int* red) {
   v = wave_max_i(v);
   __syncthreads();
@@ -152,7 +141,7 @@ __device__ __forceinline__ int block_max_i(int v, int* red) {
   __syncthreads();
   int r = red[0];
 #pragma unroll
-  for (int w = 1; w < kThreads / kWave; ++w) r = max(r, red[w]);
+  for (int w = 1; w < NT / kWave; ++w) r = max(r, red[w]);
   __syncthreads();
   return r;
 }

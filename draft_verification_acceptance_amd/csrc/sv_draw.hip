@@ -16,7 +16,7 @@
 // b's row; each wave reduces whole segments (8 consecutive tokens per lane, 16-byte loads) and stores
 // (sum w, sum p) per segment. The request's last workgroup takes a float64 prefix over the
 // segments, then rescans the single segment holding u * Z in float64, token by token.
-#include "sv_device.h"
+#include "sv_scan.h"
 
 namespace sv {
 
@@ -164,8 +164,9 @@ struct SegView {
   }
 };
 
-template <typename DT>
-__global__ __launch_bounds__(kThreads) void k_draw(DrawParams p) {
+template <typename DT, bool TREE, bool SPARSE>
+__global__ __launch_bounds__(kThreads) void k_draw(VerifyParams p) {
+  extern __shared__ __align__(16) char smem[];
   __shared__ int32_t s_seen[kMaxLen];   // adjustment list entries inside the current token range
   __shared__ float s_seen_a[kMaxLen];
   __shared__ int s_wcnt[kThreads / kWave];
@@ -180,27 +181,41 @@ __global__ __launch_bounds__(kThreads) void k_draw(DrawParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wv = tid / kWave;
-  const DrawDesc d = p.desc[b];
-  if (d.state != p.epoch) return;   // no draw pending for b in this call (bad offsets): all of b's workgroups agree
+
+  // The request's scan (every workgroup of the request computes the same plan; chunk 0 writes the outputs
+  // it determines).
+  const int nst = staged_parts(p.L, p.P, p.S);
+  Part* stage = nst ? reinterpret_cast<Part*>(smem) : nullptr;
+  char* rows = smem + size_t(nst) * sizeof(Part);
+  DrawPlan d;
+  if (TREE) {
+    d = scan_tree<DT, true>(p, b, rows, stage, c == 0);
+  } else {
+    int64_t off0, len;
+    if (!chain_request(p, b, off0, len)) {
+      if (c == 0 && tid == 0) write_bad_offsets(p, b);
+      return;   // no draw for b: all of b's workgroups agree
+    }
+    d = scan_chain_rejection<SPARSE>(p, b, off0, int(len), rows, stage, c == 0);
+  }
 
   RowCtx r;
   r.xt = static_cast<const DT*>(p.target) + int64_t(d.row_t) * p.V;
   r.xq = d.row_q >= 0 && p.draft ? static_cast<const DT*>(p.draft) + int64_t(d.row_q) * p.V : nullptr;
-  r.coef = d.coef;
+  r.coef = p.coef;
   r.m_t = d.m_t;
-  r.inv_zt = 1.f / d.l_t;
+  r.inv_zt = 1.f / d.z_t;
   r.m_q = d.m_q;
-  r.inv_zq = 1.f / d.l_q;
+  r.inv_zq = 1.f / d.z_q;
   r.vec = (reinterpret_cast<uintptr_t>(r.xt) & 15) == 0 && (reinterpret_cast<uintptr_t>(r.xq) & 15) == 0;
 
   const int s_begin = c * p.spc;
   const int s_end = min(p.n_seg, s_begin + p.spc);
   const int64_t e_lo = int64_t(s_begin) * kSeg;
   const int64_t e_hi = int64_t(s_end) * kSeg;
-  // Tried tokens inside this workgroup's range (tree target-only; usually none).
-  // The adjustment list: the sparse candidates of the draft row, or the tokens a tree walk tried.
-  const bool sparse = p.cand_ids != nullptr && d.row_q >= 0;
-  const int32_t* adj_ids = sparse ? p.cand_ids + int64_t(d.row_q) * p.K : p.seen + int64_t(b) * p.seen_stride;
+  // The adjustment list: the sparse candidates of the draft row, or the tokens the tree walk tried (LDS).
+  const bool sparse = SPARSE && d.row_q >= 0;
+  const int32_t* adj_ids = sparse ? p.cand_ids + int64_t(d.row_q) * p.K : d.seen;
   const float* adj_a = sparse ? p.cand_q + int64_t(d.row_q) * p.K : nullptr;
   const int n_adj = sparse ? p.K : d.n_seen;
   const int n_seen = collect_adjust(adj_ids, adj_a, n_adj, e_lo, e_hi, s_seen, s_seen_a, s_wcnt);
@@ -208,7 +223,7 @@ __global__ __launch_bounds__(kThreads) void k_draw(DrawParams p) {
   // Lane l of a wave owns tokens [s*512 + 8l, s*512 + 8l + 8) of segment s. A trip covers kTrip segments
   // per wave with all of their loads issued before any is used.
   constexpr int kW = kThreads / kWave;
-  constexpr int kTrip = 4;
+  constexpr int kTrip = SV_DRAW_TRIP;
   for (int s0 = s_begin + wv; s0 < s_end; s0 += kTrip * kW) {
     Raw8 rt[kTrip], rq[kTrip];
 #pragma unroll
@@ -239,7 +254,7 @@ __global__ __launch_bounds__(kThreads) void k_draw(DrawParams p) {
 
   complete_memory_ops();   // every wave's segment sums are stored before the workgroup is counted
   __syncthreads();
-  // The request's scan armed this counter with the call's epoch and a zero count (previous kernel).
+  // The logits stream of this call reset this counter to 0 (previous kernel).
   if (tid == 0) s_last = uint32_t(atomicAdd(p.cnt2 + size_t(b) * kCounterWords, 1ull)) + 1u == uint32_t(p.S2);
   __syncthreads();
   if (!s_last) return;
@@ -363,19 +378,23 @@ __global__ __launch_bounds__(kThreads) void k_draw(DrawParams p) {
 }
 
 template <typename DT>
-hipError_t launch_draw_t(const DrawParams& p, hipStream_t stream) {
+hipError_t launch_draw_t(int mode, const VerifyParams& p, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
   const int64_t blocks = int64_t(p.B) * p.S2;
   if (blocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL((k_draw<DT>), dim3(unsigned(blocks)), dim3(kThreads), 0, stream, p);
-  return hipGetLastError();
+  const size_t smem = scan_smem_bytes(p.tree != 0, true, p.L, p.P, p.S);
+  const dim3 grid{unsigned(blocks)}, block{unsigned(kThreads)};
+  if (p.tree) return launch_kernel(k_draw<DT, true, false>, grid, block, smem, stream, ev0, ev1, p);
+  if (mode == SPEC_MODE_REJECTION_SPARSE)
+    return launch_kernel(k_draw<DT, false, true>, grid, block, smem, stream, ev0, ev1, p);
+  return launch_kernel(k_draw<DT, false, false>, grid, block, smem, stream, ev0, ev1, p);
 }
 
 }  // namespace
 
-hipError_t launch_draw(int dtype, const DrawParams& p, const Layout& lo, hipStream_t stream) {
-  (void)lo;
-  if (dtype == SPEC_DTYPE_BF16) return launch_draw_t<uint16_t>(p, stream);
-  return launch_draw_t<float>(p, stream);
+hipError_t launch_draw(int dtype, int mode, const VerifyParams& p, hipStream_t stream, hipEvent_t ev0,
+                       hipEvent_t ev1) {
+  if (dtype == SPEC_DTYPE_BF16) return launch_draw_t<uint16_t>(mode, p, stream, ev0, ev1);
+  return launch_draw_t<float>(mode, p, stream, ev0, ev1);
 }
 
 }  // namespace sv

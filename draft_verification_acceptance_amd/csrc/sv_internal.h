@@ -1,25 +1,28 @@
 // Internal definitions shared by the HIP translation units of libspecverify (not part of the ABI).
 //
-// Workspace state across calls: every call gets a fresh nonzero 32-bit epoch from the host. Per-request
-// completion counters are 64-bit words (epoch << 32 | count): k_stats restarts a counter that carries an
-// older epoch by compare-and-swap, and each request's scan arms its k_draw counter with the epoch and a
-// zero count. A draw descriptor is pending only while its state equals the epoch, so whatever a previous
-// call (of any shape) left in the workspace is never mistaken for this call's progress.
+// Workspace state across calls: none is kept. The draw pass's per-request completion counters are reset
+// to 0 by the logits stream of the same call (a kernel boundary before the draw counts), and every other
+// workspace word a call reads was written earlier in that call, so whatever a previous call (of any shape)
+// left in the workspace does not matter, and a captured call replays correctly.
 //
 // Data flow of one verify call (all on the caller's stream, no host synchronisation):
 //   k_stats   one workgroup per (request, row slot, target|draft, vocab chunk): streams its slice of a
-//             logits row once from HBM and writes a 16-byte partial (greedy: max + lowest argmax;
-//             sampling: online max + sum of exp2). The workgroup that completes a request's last slice
-//             (device-scope counter) merges the partials and runs the request's accept scan / tree walk,
-//             writes every output it can, and for sampling modes leaves a draw descriptor.
-//   k_draw    sampling modes only: one workgroup per (request, vocab chunk) re-reads the single row (or
-//             target/draft row pair) the final token is drawn from, with the per-token adjustments of a
-//             short list (tried tree tokens, sparse q candidates), and writes per-512-token segment sums;
-//             the last workgroup of the request locates the inverse-CDF step (fp64 prefix over segments,
-//             then inside one segment) and writes the token.
+//             logits row once from HBM and stores a partial (greedy: max + lowest argmax; sampling: online
+//             max + sum of exp2, and the logit at the token the row judges). Nothing else: no counters and
+//             no waits, so the stream ends when its last loads land.
+//   k_scan    greedy only: one workgroup per request merges the request's partials and runs its accept
+//             scan (chain) or tree walk, and writes every output.
+//   k_draw    sampling modes: workgroup (request, vocab chunk) first runs the request's scan itself (it is
+//             small: one round of loads of partials, tokens and uniforms), which names the single row (or
+//             target/draft row pair) the final token is drawn from; chunk 0 writes the scan's outputs.
+//             Then it re-reads its slice of that row with the per-token adjustments of a short list (tried
+//             tree tokens, sparse q candidates) and stores per-512-token segment sums; the last workgroup
+//             of the request locates the inverse-CDF step (fp64 prefix over segments, then inside one
+//             segment) and writes the token and the status.
 //   k_commit  one workgroup: exclusive scan of accept_len + 1 and the slot gathers of the KV commit.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -27,8 +30,39 @@
 
 namespace sv {
 
-constexpr int kThreads = 256;        // threads per workgroup of k_stats / k_draw (4 wave64)
+// Launch shape of the logits stream (k_stats). Tuned on MI355X; each may be overridden at build time.
+#ifndef SV_STATS_THREADS
+#define SV_STATS_THREADS 256         // threads per k_stats workgroup
+#endif
+#ifndef SV_STATS_WGS
+#define SV_STATS_WGS 512             // streaming workgroups aimed for per call, sampling modes (rows are
+#endif                               // split into chunks)
+#ifndef SV_STATS_WGS_GREEDY
+#define SV_STATS_WGS_GREEDY 1024     // the same, greedy (less work per token: more loads in flight needed)
+#endif
+#ifndef SV_STATS_MIN_CHUNK
+#define SV_STATS_MIN_CHUNK 8192      // fewest tokens per chunk
+#endif
+#ifndef SV_STATS_UNROLL
+#define SV_STATS_UNROLL 4            // 16-byte loads in flight per thread per loop trip
+#endif
+
+#ifndef SV_DRAW_THREADS
+#define SV_DRAW_THREADS 256          // threads per workgroup of k_draw and k_scan
+#endif
+#ifndef SV_DRAW_TRIP
+#define SV_DRAW_TRIP 4               // draw segments each wave has in flight per trip
+#endif
+#ifndef SV_DRAW_WGS
+#define SV_DRAW_WGS 1024             // draw workgroups aimed for per call
+#endif
+
+constexpr int kThreads = SV_DRAW_THREADS;
+constexpr int kStatsThreads = SV_STATS_THREADS;
 constexpr int kWave = 64;            // gfx950 wavefront size
+// The request scan stages every partial of its request in LDS when there are at most this many (one load
+// round); the launch shape keeps row slots x parts x chunks within it.
+constexpr int kMaxStagedParts = 1024;
 constexpr int kSeg = 512;            // tokens per draw segment (one wave: 8 tokens per lane)
 constexpr int kMaxLen = 1024;        // max verify rows per request (chain) / nodes per tree
 constexpr int kMaxCand = 1024;       // max candidates per draft row (sparse q)
@@ -41,29 +75,26 @@ constexpr size_t kCounterWords = kCounterStride / sizeof(unsigned long long);
 constexpr float kNear = 1e-5f;       // |u - alpha| / CDF-gap band reported as NEAR_*
 constexpr float kNearMass = 1e-6f;   // CDF-gap band in probability mass (gap * total weight)
 
-// Partial statistics of one vocab chunk of one row (16 bytes).
+// Partial statistics of one vocab chunk of one row (32 bytes).
 //   greedy:   a = max logit, idx = lowest index attaining it (INT32_MAX if none), flags bit0 = NaN seen
-//   sampling: a = m = max of x*coef (log2 units), b = z = sum exp2(x*coef - m)
+//   sampling: a = m = max of x*coef (log2 units), b = z = sum exp2(x*coef - m);
+//             g = the row's logit at the token it judges (chain: d_{j+1}), read by the workgroup whose
+//             chunk holds that token (flags kPartGathered); sparse q, chunk 0 of a target row: q = q(d), the
+//             summed mass of the draft row's valid candidates with id d, and flags kPartBadCandId /
+//             kPartBadCandQ for its malformed candidate entries.
 struct alignas(16) Part {
   float a;
   float b;
   int32_t idx;
   uint32_t flags;
+  float g;
+  float q;
+  uint32_t pad0, pad1;
 };
-
-// What the final draw of a request needs; written by the request's scan, consumed by k_draw.
-struct alignas(16) DrawDesc {
-  uint32_t state;    // == the call's epoch: a draw is pending for this call
-  int32_t row_t;     // global target row the token is drawn from
-  int32_t row_q;     // draft row of the residual [p - q]_+ (logits, or sparse candidates), or -1 (from p)
-  int32_t out_pos;   // out_tokens index of the drawn token
-  float m_t, l_t;    // target row: max m (log2 units) and normaliser z of softmax = exp2(x*coef - m) / z
-  float m_q, l_q;    // draft row, same meaning (dense rejection)
-  float coef;        // log2(e) / temperature
-  float u;           // sanitized u_final
-  uint32_t status;   // request status bits so far
-  int32_t n_seen;    // tree TARGET_ONLY: number of tokens excluded from the draw (in the seen buffer)
-};
+constexpr uint32_t kPartNaN = 1u;
+constexpr uint32_t kPartGathered = 2u;
+constexpr uint32_t kPartBadCandId = 4u;
+constexpr uint32_t kPartBadCandQ = 8u;
 
 struct Layout {
   int32_t L = 0;         // row slots per request (chain: max_verify_len, tree: n_nodes)
@@ -73,7 +104,7 @@ struct Layout {
   int32_t S2 = 1;        // vocab chunks per request in k_draw
   int32_t spc = 1;       // segments per k_draw chunk
   int32_t n_seg = 0;     // segments per row
-  size_t off_cnt = 0, off_cnt2 = 0, off_part = 0, off_desc = 0, off_seg = 0, off_seen = 0;
+  size_t off_cnt2 = 0, off_part = 0, off_seg = 0;
   size_t bytes = 0;
 };
 
@@ -84,11 +115,13 @@ inline Layout make_layout(int kind, int mode, int64_t total_rows, int64_t vocab,
   lo.L = L;
   lo.P = (kind == SPEC_KIND_CHAIN && mode == SPEC_MODE_REJECTION) ? 2 : 1;
   const int64_t slots = int64_t(batch) * L * lo.P;
-  // One workgroup per row once there are >= 512 rows (measured best on MI355X: fewer partials and
-  // counter updates per request, long streams per workgroup); smaller batches split rows into chunks of
-  // at least 8192 tokens to keep ~512 workgroups streaming.
-  int64_t s = slots > 0 ? (512 + slots - 1) / slots : 1;
-  int64_t max_s = vocab / 8192;
+  // Rows are split into S chunks so that about SV_STATS_WGS(_GREEDY) workgroups stream, with at least
+  // SV_STATS_MIN_CHUNK tokens per chunk and all of a request's partials fitting the scan's LDS.
+  const int64_t wgs = sampling ? SV_STATS_WGS : SV_STATS_WGS_GREEDY;
+  int64_t s = slots > 0 ? (wgs + slots - 1) / slots : 1;
+  int64_t max_s = vocab / SV_STATS_MIN_CHUNK;
+  const int64_t lds_s = kMaxStagedParts / (int64_t(L) * lo.P);
+  if (max_s > lds_s) max_s = lds_s;
   if (max_s < 1) max_s = 1;
   if (s > max_s) s = max_s;
   if (s < 1) s = 1;
@@ -97,28 +130,26 @@ inline Layout make_layout(int kind, int mode, int64_t total_rows, int64_t vocab,
   lo.chunk = chunk;
   lo.S = int32_t((vocab + chunk - 1) / chunk);
   lo.n_seg = int32_t((vocab + kSeg - 1) / kSeg);
-  // k_draw: ~2048 workgroups, each covering at least 16 segments (4 per wave).
-  int64_t s2 = batch > 0 ? (2048 + batch - 1) / batch : 1;
-  const int64_t max_s2 = (lo.n_seg + 15) / 16;
+  // k_draw: ~SV_DRAW_WGS workgroups, each covering at least one segment per wave.
+  int64_t s2 = batch > 0 ? (SV_DRAW_WGS + batch - 1) / batch : 1;
+  const int64_t min_segs = kThreads / kWave;
+  const int64_t max_s2 = (lo.n_seg + min_segs - 1) / min_segs;
   if (s2 > max_s2) s2 = max_s2;
   if (s2 < 1) s2 = 1;
   lo.spc = int32_t((lo.n_seg + s2 - 1) / s2);
   lo.S2 = (lo.n_seg + lo.spc - 1) / lo.spc;
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
   size_t o = 0;
-  lo.off_cnt = o;  o = up(o + kCounterStride * size_t(batch));
-  lo.off_cnt2 = o; o = up(o + kCounterStride * size_t(batch));
+  lo.off_cnt2 = o; o = up(o + (sampling ? kCounterStride * size_t(batch) : 0));
   lo.off_part = o; o = up(o + sizeof(Part) * size_t(slots) * size_t(lo.S));
-  lo.off_desc = o; o = up(o + sizeof(DrawDesc) * size_t(batch));
   lo.off_seg = o;  o = up(o + (sampling ? sizeof(float2) * size_t(batch) * size_t(lo.n_seg) : 0));
-  lo.off_seen = o; o = up(o + ((kind == SPEC_KIND_TREE && sampling) ? sizeof(int32_t) * size_t(batch) * L : 0));
   lo.bytes = o;
   (void)total_rows;
   return lo;
 }
 
-// Kernel parameter block of k_stats (passed by value).
-struct StatsParams {
+// Kernel parameter block of k_stats, k_scan and k_draw (passed by value).
+struct VerifyParams {
   const void* target;
   const void* draft;
   const int32_t* offsets;
@@ -136,36 +167,17 @@ struct StatsParams {
   uint32_t* status;
   float* accept_prob;
   float* residual_mass;
-  unsigned long long* cnt;
-  unsigned long long* cnt2;   // draw-pass counters, armed by each request's scan
+  unsigned long long* cnt2;   // draw-pass counters, armed by the logits stream
   Part* part;
-  DrawDesc* desc;
-  int32_t* seen;
+  float2* seg;                // draw-pass segment sums
   int64_t V;
   int64_t total_rows;
   int64_t chunk;
   int32_t B, L, P, S;
   int32_t K;                  // sparse q: candidates per draft row (0 otherwise)
-  float coef;
-  uint32_t epoch;
-};
-
-struct DrawParams {
-  const void* target;
-  const void* draft;
-  int32_t* bonus;
-  int32_t* out_tokens;
-  uint32_t* status;
-  float* residual_mass;
-  unsigned long long* cnt2;
-  DrawDesc* desc;
-  float2* seg;
-  const int32_t* seen;
-  const int32_t* cand_ids;    // sparse q: the candidates of desc.row_q adjust the draw
-  const float* cand_q;
-  int64_t V;
-  int32_t B, S2, spc, n_seg, seen_stride, K;
-  uint32_t epoch;
+  int32_t S2, spc, n_seg;     // draw pass: workgroups per request, segments per workgroup, segments per row
+  float coef;                 // log2(e) / temperature (sampling modes)
+  int32_t tree;               // 1: tree verify (rows node-major, B * L of them)
 };
 
 struct CommitParams {
@@ -174,10 +186,25 @@ struct CommitParams {
 
 // Host-side launchers (each in the translation unit of its kernel). They return hipSuccess or the
 // launch error.
-hipError_t launch_stats(int dtype, int mode, bool tree, const StatsParams& p, const Layout& lo,
-                        hipStream_t stream);
-hipError_t launch_draw(int dtype, const DrawParams& p, const Layout& lo, hipStream_t stream);
-hipError_t launch_commit(const spec_commit_args& a, hipStream_t stream);
+// Launch `kernel` on `stream`. With ev0 / ev1 the launch goes through hipExtLaunchKernelGGL, which sets
+// the events to the kernel's own start and stop timestamps (what a kernel trace reports), not to points
+// between launches.
+template <typename P>
+hipError_t launch_kernel(void (*kernel)(P), dim3 grid, dim3 block, size_t smem, hipStream_t stream, hipEvent_t ev0,
+                         hipEvent_t ev1, const P& p) {
+  if (ev0 || ev1) hipExtLaunchKernelGGL(kernel, grid, block, uint32_t(smem), stream, ev0, ev1, 0u, p);
+  else hipLaunchKernelGGL(kernel, grid, block, smem, stream, p);
+  return hipGetLastError();
+}
+
+// ev0 / ev1: optional events that take the kernel's own start / stop timestamps.
+hipError_t launch_stats(int dtype, int mode, const VerifyParams& p, hipStream_t stream, hipEvent_t ev0,
+                        hipEvent_t ev1);
+// The second kernel of a verify call: k_scan (greedy) or k_draw (sampling modes).
+hipError_t launch_scan(int dtype, const VerifyParams& p, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
+hipError_t launch_draw(int dtype, int mode, const VerifyParams& p, hipStream_t stream, hipEvent_t ev0,
+                       hipEvent_t ev1);
+hipError_t launch_commit(const spec_commit_args& a, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
 hipError_t launch_fill_zero(void* ptr, size_t bytes, hipStream_t stream);
 
 }  // namespace sv

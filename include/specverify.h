@@ -25,9 +25,10 @@
  *     deterministic function of the inputs: one uniform per row under test (`u_accept`) and one per
  *     request for the single final draw (`u_final`).
  *   - A workspace (scratch device memory sized by spec_workspace_bytes) serves one call at a time; calls
- *     that overlap on one workspace race. Its contents between calls do not matter: every call tags its
- *     progress counters with a fresh per-call number, so one workspace can be reused by later calls of any
- *     shape it is large enough for. spec_workspace_init zero-fills one (optional).
+ *     that overlap on one workspace race. Its contents between calls do not matter: a call resets or
+ *     overwrites every word it reads, so one workspace can be reused by later calls of any shape it is
+ *     large enough for, and a call captured in a HIP graph replays correctly (no memset nodes are
+ *     recorded). spec_workspace_init zero-fills one (optional).
  */
 #ifndef SPECVERIFY_H
 #define SPECVERIFY_H
@@ -43,7 +44,7 @@ extern "C" {
 typedef struct ihipStream_t* hipStream_t;
 typedef struct ihipEvent_t* hipEvent_t;
 
-#define SPEC_ABI_VERSION 2
+#define SPEC_ABI_VERSION 3
 
 /* Host-visible return codes. */
 typedef enum spec_status {
@@ -147,9 +148,10 @@ typedef struct spec_chain_args {
   float* residual_mass;          /* optional [batch]                                       */
   void* workspace;               /* >= spec_workspace_bytes(SPEC_KIND_CHAIN, ...) bytes    */
   size_t workspace_bytes;
-  hipEvent_t* profile_events;    /* HOST array, optional: n_profile_events events recorded on
-                                    `stream` before the first kernel, between kernels and after
-                                    the last one (n = kernels + 1; see spec_kernel_count)      */
+  hipEvent_t* profile_events;    /* HOST array, optional: n_profile_events = 2 * kernels events
+                                    (see spec_kernel_count); events 2k and 2k+1 take the start
+                                    and stop timestamps of kernel k itself (its dispatch on
+                                    `stream`, as a kernel trace reports it)                    */
   int64_t total_rows;            /* T_rows = sum_b (m_b + 1)                                */
   int64_t vocab;                 /* V, 1 <= V <= 2^22                                       */
   int32_t batch;                 /* B >= 0 (B == 0: nothing is launched)                    */
