@@ -7,3 +7,4 @@ from .verify import (  # noqa: F401
     ST_NEAR_CDF, ST_NONFINITE, ST_ZERO_Q, ST_ZERO_RESIDUAL, argmax_lowest, commit_indices, decode_row,
     draw, sanitize_uniform, softmax_T, sparse_q, verify_chain, verify_tree,
 )
+from . import plan  # noqa: F401,E402  (DSpark verify-length planner and cap_trim)
