@@ -218,6 +218,48 @@ def run_workload(name: str, mode: str | None, steps: int, warmup: int) -> dict:
     }
 
 
+def run_planner(steps: int) -> dict:
+    """The verify-length planner at the ragged workload's shape (512 requests x 15 proposed drafts): the host
+    budget from lagged confidences and a synthetic SPS table, the device allocation kernel, and the accept
+    cutoff of a full-width verify. Latency-bound work (30 KB of confidences): times, not bandwidth."""
+    import numpy as np
+    import torch
+
+    import draft_verification_acceptance_amd as dva
+    from draft_verification_acceptance_amd import workloads as W
+    w = W.planner_inputs()
+    t0 = time.perf_counter()
+    reps = 50
+    for _ in range(reps):
+        K, theta = dva.plan_budget(w.conf_hist, w.sps_rows, w.sps)
+    host_us = (time.perf_counter() - t0) / reps * 1e6
+    conf = torch.from_numpy(w.conf).cuda()
+    plan = dva.prepare_plan_layout(conf, budget=K)
+    R, Wd = w.conf.shape
+    offs = torch.arange(0, (R + 1) * (Wd + 1), Wd + 1, dtype=torch.int32, device="cuda")
+    raw = torch.from_numpy(w.raw_accept_len).cuda()
+    toks = torch.zeros(R * (Wd + 1), dtype=torch.int32, device="cuda")
+    trim = dva.prepare_cap_trim(offs, plan.outputs["verify_lens"], raw, raw.clone(), toks)
+    for _ in range(10):
+        plan.run()
+        trim.run()
+    torch.cuda.synchronize()
+    ev_p = [dva.HipEvents(2) for _ in range(steps)]
+    ev_t = [dva.HipEvents(2) for _ in range(steps)]
+    for i in range(steps):
+        plan.run(ev_p[i])
+        trim.run(ev_t[i])
+    torch.cuda.synchronize()
+    kp = np.array([e.elapsed_ms(0, 1) for e in ev_p]) * 1e3
+    kt = np.array([e.elapsed_ms(0, 1) for e in ev_t]) * 1e3
+    vl = plan.outputs["verify_lens"].cpu().numpy()
+    return {"requests": int(R), "proposed_drafts": int(R * Wd), "budget": int(K),
+            "target_rows_planned": int(vl.sum()), "host_budget_us": host_us,
+            "plan_kernel_us": {"mean": float(kp.mean()), "p50": float(np.median(kp))},
+            "cap_trim_kernel_us": {"mean": float(kt.mean()), "p50": float(np.median(kt))},
+            "bound": "latency (one workgroup; 30 KB of confidences)"}
+
+
 def cpu_baseline(name: str, budget_s: float = 12.0) -> dict:
     """The fp64 oracle on this host's cores, on the canonical input set of the timed workload."""
     import numpy as np
@@ -322,6 +364,7 @@ def main():
                                                               "stats_kernel_gbs", "kernel_ms", "mean_accept_len",
                                                               "status_faults")}
             torch.cuda.empty_cache()
+        extra["planner"] = run_planner(max(50, args.steps // 2))
     stats_ms = main_res["kernel_ms"]["k_stats"]["mean"]
     achieved = main_res["stats_kernel_gbs"]
     traffic = load_traffic(main_res["workload"])

@@ -20,14 +20,16 @@ __all__ = [
     "SpecError", "verify_chain", "verify_tree", "commit_indices", "workspace", "workspace_bytes",
     "workspace_init", "kernel_count", "status_string", "abi_version", "library_path", "HipEvents",
     "MODES", "ST", "PreparedCall", "prepare_verify_chain", "prepare_verify_tree", "prepare_commit_indices",
+    "plan_layout", "prepare_plan_layout", "plan_budget", "cap_trim", "prepare_cap_trim",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_PKG, "libspecverify.so")
 
-ABI_VERSION = 3
+ABI_VERSION = 4
 MODES = {"greedy": 0, "rejection": 1, "target_only": 2, "rejection_sparse": 3}
-KIND_CHAIN, KIND_TREE, KIND_COMMIT = 0, 1, 2
+KIND_CHAIN, KIND_TREE, KIND_COMMIT, KIND_PLAN, KIND_CAP_TRIM = 0, 1, 2, 3, 4
+PLAN_MODES = {"topk": 0, "threshold": 1}
 DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 
 
@@ -44,6 +46,7 @@ class ST:
     NEAR_CDF = 1 << 8
     BAD_ACCEPT = 1 << 9
     BAD_Q = 1 << 10
+    BAD_CONF = 1 << 11
 
 
 class SpecError(RuntimeError):
@@ -82,6 +85,20 @@ class CommitArgs(ctypes.Structure):
                 ("max_verify_len", _i32), ("n_profile_events", _i32), ("reserved", _i32)]
 
 
+class PlanArgs(ctypes.Structure):
+    _fields_ = [("confidence", _vp), ("selected", _vp), ("verify_lens", _vp), ("offsets", _vp), ("row_index", _vp),
+                ("status", _vp), ("profile_events", _vp), ("batch", _i32), ("width", _i32), ("mode", _i32),
+                ("budget", _i32), ("min_verify_len", _i32), ("max_verify_len", _i32), ("survival_eps", _f32),
+                ("threshold", _f32), ("n_profile_events", _i32), ("reserved", _i32)]
+
+
+class CapTrimArgs(ctypes.Structure):
+    _fields_ = [("row_offsets", _vp), ("verify_lens", _vp), ("raw_accept_len", _vp), ("raw_bonus", _vp),
+                ("out_tokens", _vp), ("correct_len", _vp), ("cap_trim_lens", _vp), ("commit_lens", _vp),
+                ("block_accept_lens", _vp), ("bonus", _vp), ("status", _vp), ("profile_events", _vp),
+                ("total_rows", _i64), ("batch", _i32), ("n_profile_events", _i32)]
+
+
 _LIB = None
 
 
@@ -95,8 +112,15 @@ def _lib():
     lib.spec_verify_chain.argtypes = [ctypes.POINTER(ChainArgs), _vp]
     lib.spec_verify_tree.argtypes = [ctypes.POINTER(TreeArgs), _vp]
     lib.spec_commit_indices.argtypes = [ctypes.POINTER(CommitArgs), _vp]
-    for f in (lib.spec_verify_chain, lib.spec_verify_tree, lib.spec_commit_indices):
+    lib.spec_plan_layout.argtypes = [ctypes.POINTER(PlanArgs), _vp]
+    lib.spec_cap_trim.argtypes = [ctypes.POINTER(CapTrimArgs), _vp]
+    for f in (lib.spec_verify_chain, lib.spec_verify_tree, lib.spec_commit_indices, lib.spec_plan_layout,
+              lib.spec_cap_trim):
         f.restype = ctypes.c_int
+    _dp = ctypes.POINTER(ctypes.c_double)
+    lib.spec_plan_budget.argtypes = [ctypes.POINTER(ctypes.c_float), _i32, _i32, _dp, _dp, _i32, _f32,
+                                     ctypes.POINTER(_i32), _dp, ctypes.POINTER(_i32)]
+    lib.spec_plan_budget.restype = ctypes.c_int
     lib.spec_workspace_bytes.argtypes = [_i32, _i32, _i64, _i64, _i32, _i32]
     lib.spec_workspace_bytes.restype = _sz
     lib.spec_workspace_init.argtypes = [_vp, _sz, _vp]
@@ -111,7 +135,8 @@ def _lib():
     lib.spec_args_size.restype = _sz
     if lib.spec_abi_version() != ABI_VERSION:
         raise RuntimeError(f"libspecverify ABI {lib.spec_abi_version()} != binding ABI {ABI_VERSION}")
-    for kind, st in ((KIND_CHAIN, ChainArgs), (KIND_TREE, TreeArgs), (KIND_COMMIT, CommitArgs)):
+    for kind, st in ((KIND_CHAIN, ChainArgs), (KIND_TREE, TreeArgs), (KIND_COMMIT, CommitArgs), (KIND_PLAN, PlanArgs),
+                     (KIND_CAP_TRIM, CapTrimArgs)):
         if lib.spec_args_size(kind) != ctypes.sizeof(st):
             raise RuntimeError(f"argument struct {st.__name__} size mismatch with the library")
     _LIB = lib
@@ -127,7 +152,8 @@ def status_string(code: int) -> str:
 
 
 def kernel_count(kind: str, mode: str) -> int:
-    k = {"chain": KIND_CHAIN, "tree": KIND_TREE, "commit": KIND_COMMIT}[kind]
+    k = {"chain": KIND_CHAIN, "tree": KIND_TREE, "commit": KIND_COMMIT, "plan": KIND_PLAN,
+         "cap_trim": KIND_CAP_TRIM}[kind]
     return int(_lib().spec_kernel_count(k, MODES.get(mode, 0)))
 
 
@@ -439,3 +465,109 @@ def commit_indices(row_offsets: torch.Tensor, accept_len: torch.Tensor, accept_i
     commit_offsets[-1] entries long."""
     return prepare_commit_indices(row_offsets, accept_len, accept_index, verify_slots, seq_lens,
                                   max_verify_len=max_verify_len, evict=evict, out=out).run(events)
+
+
+# ----------------------------------------------------------------------------------------------------
+# verify-length planner and accept cutoff
+# ----------------------------------------------------------------------------------------------------
+def plan_budget(confidence_hist, sps_rows, sps, *, survival_eps: float = 0.0) -> tuple[int, list]:
+    """spec_plan_budget (host function): the verify budget K* from lagged confidences [batch, width] (a host
+    array: numpy or CPU tensor, float32) and an SPS table. Returns (K*, predicted throughput for K = 0..n)."""
+    import numpy as np
+    c = np.ascontiguousarray(confidence_hist.cpu().numpy() if isinstance(confidence_hist, torch.Tensor)
+                             else confidence_hist, dtype=np.float32)
+    if c.ndim != 2:
+        raise ValueError("confidence_hist must be [batch, width]")
+    R, W = c.shape
+    xs = np.ascontiguousarray(sps_rows, dtype=np.float64)
+    ys = np.ascontiguousarray(sps, dtype=np.float64)
+    if xs.shape != ys.shape or xs.ndim != 1:
+        raise ValueError("sps_rows and sps must be 1-D of equal length")
+    theta = np.zeros(R * W + 1, np.float64)
+    k, n = _i32(), _i32()
+    _dp = ctypes.POINTER(ctypes.c_double)
+    _check(_lib().spec_plan_budget(c.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), R, W, xs.ctypes.data_as(_dp),
+                                   ys.ctypes.data_as(_dp), len(xs), float(survival_eps), ctypes.byref(k),
+                                   theta.ctypes.data_as(_dp), ctypes.byref(n)))
+    return int(k.value), theta[:n.value + 1].tolist()
+
+
+def prepare_plan_layout(confidence: torch.Tensor, *, mode: str = "topk", budget: int = -1, threshold: float = 0.5,
+                        min_verify_len: int = 1, max_verify_len: int | None = None, survival_eps: float = 0.0,
+                        row_index: bool = True, out: dict | None = None) -> PreparedCall:
+    """Checks and marshals the arguments of spec_plan_layout once (see plan_layout)."""
+    lib = _lib()
+    dev = confidence.device
+    if confidence.dim() != 2:
+        raise ValueError("confidence must be [batch, width]")
+    _req(confidence, "confidence", torch.float32, device=dev)
+    R, W = confidence.shape
+    o = {} if out is None else out
+
+    def get(name, n, dtype):
+        t = o.get(name)
+        if t is None:
+            t = torch.empty(n, dtype=dtype, device=dev)
+            o[name] = t
+        return _req(t, name, dtype, n, dev)
+    get("selected", R, torch.int32)
+    get("verify_lens", R, torch.int32)
+    get("offsets", R + 1, torch.int32)
+    get("status", R, torch.int32)
+    if row_index:
+        get("row_index", R * (W + 1), torch.int64)
+    a = PlanArgs()
+    a.confidence = _ptr(confidence)
+    a.selected, a.verify_lens, a.offsets = _ptr(o["selected"]), _ptr(o["verify_lens"]), _ptr(o["offsets"])
+    a.row_index = _ptr(o.get("row_index")) if row_index else None
+    a.status = _ptr(o["status"])
+    a.batch, a.width, a.mode, a.budget = R, W, PLAN_MODES[mode], int(budget)
+    a.min_verify_len = int(min_verify_len)
+    a.max_verify_len = int(W + 1 if max_verify_len is None else max_verify_len)
+    a.survival_eps, a.threshold = float(survival_eps), float(threshold)
+    return PreparedCall(lib.spec_plan_layout, a, o, [confidence], dev)
+
+
+def plan_layout(confidence: torch.Tensor, *, events: "HipEvents | None" = None, **kw) -> dict:
+    """spec_plan_layout: per-request verify lengths from current confidences [batch, width] (float32). mode
+    "topk" verifies the `budget` entries of highest prefix survival (budget < 0: every draft), "threshold" the
+    drafts before the first confidence below `threshold`. Returns selected, verify_lens, offsets, status and
+    row_index (compact verify row -> r * (width + 1) + j)."""
+    return prepare_plan_layout(confidence, **kw).run(events)
+
+
+def prepare_cap_trim(row_offsets: torch.Tensor, verify_lens: torch.Tensor, raw_accept_len: torch.Tensor,
+                     raw_bonus: torch.Tensor, out_tokens: torch.Tensor, *, out: dict | None = None) -> PreparedCall:
+    """Checks and marshals the arguments of spec_cap_trim once (see cap_trim)."""
+    lib = _lib()
+    dev = row_offsets.device
+    _req(row_offsets, "row_offsets", torch.int32, device=dev)
+    B = row_offsets.numel() - 1
+    _req(verify_lens, "verify_lens", torch.int32, B, dev)
+    _req(raw_accept_len, "raw_accept_len", torch.int32, B, dev)
+    _req(raw_bonus, "raw_bonus", torch.int32, B, dev)
+    T = out_tokens.numel()
+    _req(out_tokens, "out_tokens", torch.int32, T, dev)
+    o = {} if out is None else out
+    for name in ("correct_len", "cap_trim_lens", "commit_lens", "block_accept_lens", "bonus", "status"):
+        if o.get(name) is None:
+            o[name] = torch.empty(B, dtype=torch.int32, device=dev)
+        _req(o[name], name, torch.int32, B, dev)
+    o["out_tokens"] = out_tokens
+    a = CapTrimArgs()
+    a.row_offsets, a.verify_lens = _ptr(row_offsets), _ptr(verify_lens)
+    a.raw_accept_len, a.raw_bonus, a.out_tokens = _ptr(raw_accept_len), _ptr(raw_bonus), _ptr(out_tokens)
+    a.correct_len, a.cap_trim_lens = _ptr(o["correct_len"]), _ptr(o["cap_trim_lens"])
+    a.commit_lens, a.block_accept_lens = _ptr(o["commit_lens"]), _ptr(o["block_accept_lens"])
+    a.bonus, a.status = _ptr(o["bonus"]), _ptr(o["status"])
+    a.total_rows, a.batch = T, B
+    keep = [row_offsets, verify_lens, raw_accept_len, raw_bonus, out_tokens]
+    return PreparedCall(lib.spec_cap_trim, a, o, keep, dev)
+
+
+def cap_trim(row_offsets, verify_lens, raw_accept_len, raw_bonus, out_tokens, *,
+             events: "HipEvents | None" = None, out: dict | None = None) -> dict:
+    """spec_cap_trim: cut a full-width verify's accepted prefix at each request's verify length. out_tokens is
+    rewritten in place. Returns correct_len, cap_trim_lens, commit_lens, block_accept_lens, bonus, status."""
+    return prepare_cap_trim(row_offsets, verify_lens, raw_accept_len, raw_bonus, out_tokens, out=out).run(events)
+

@@ -79,6 +79,8 @@ size_t spec_args_size(int32_t kind) {
     case SPEC_KIND_CHAIN: return sizeof(spec_chain_args);
     case SPEC_KIND_TREE: return sizeof(spec_tree_args);
     case SPEC_KIND_COMMIT: return sizeof(spec_commit_args);
+    case SPEC_KIND_PLAN: return sizeof(spec_plan_args);
+    case SPEC_KIND_CAP_TRIM: return sizeof(spec_cap_trim_args);
     default: return 0;
   }
 }
@@ -97,7 +99,7 @@ const char* spec_status_string(spec_status s) {
 
 int32_t spec_kernel_count(int32_t kind, int32_t mode) {
   (void)mode;
-  if (kind == SPEC_KIND_COMMIT) return 1;
+  if (kind == SPEC_KIND_COMMIT || kind == SPEC_KIND_PLAN || kind == SPEC_KIND_CAP_TRIM) return 1;
   if (kind != SPEC_KIND_CHAIN && kind != SPEC_KIND_TREE) return 0;
   return 2;
 }
@@ -235,6 +237,51 @@ spec_status spec_commit_indices(const spec_commit_args* a, hipStream_t stream) {
   if ((a->evict_slots == nullptr) != (a->evict_offsets == nullptr)) return SPEC_EINVAL;
   const int32_t n = a->n_profile_events;
   if (launch_commit(*a, stream, ev_at(a->profile_events, n, 0), ev_at(a->profile_events, n, 1)) != hipSuccess)
+    return SPEC_ELAUNCH;
+  return SPEC_OK;
+}
+
+spec_status spec_plan_layout(const spec_plan_args* a, hipStream_t stream) {
+  if (!a) return SPEC_EINVAL;
+  if (a->mode != SPEC_PLAN_TOPK && a->mode != SPEC_PLAN_THRESHOLD) return SPEC_EINVAL;
+  if (a->batch < 0 || a->batch >= (1 << 20) || a->width < 0 || a->width > 4095) return SPEC_EINVAL;
+  if (int64_t(a->batch) * (int64_t(a->width) + 1) > INT32_MAX) return SPEC_EINVAL;
+  if (a->min_verify_len < 1 || a->max_verify_len < a->min_verify_len || a->max_verify_len > a->width + 1)
+    return SPEC_EINVAL;   // at most the anchor and every draft: row_index holds batch*(width+1) rows
+  if (!(a->survival_eps >= 0.f) || a->threshold != a->threshold) return SPEC_EINVAL;
+  if (bad_events(a->profile_events, a->n_profile_events, 1)) return SPEC_EINVAL;
+  if (!a->offsets) return SPEC_EINVAL;
+  if (a->batch > 0 && (!a->selected || !a->verify_lens || (a->width > 0 && !a->confidence))) return SPEC_EINVAL;
+  const int32_t n = a->n_profile_events;
+  if (launch_plan(*a, stream, ev_at(a->profile_events, n, 0), ev_at(a->profile_events, n, 1)) != hipSuccess)
+    return SPEC_ELAUNCH;
+  return SPEC_OK;
+}
+
+spec_status spec_plan_budget(const float* conf, int32_t batch, int32_t width, const double* sps_rows,
+                             const double* sps, int32_t n_sps, float survival_eps, int32_t* budget, double* theta,
+                             int32_t* n_entries) {
+  if (batch < 0 || width < 0 || n_sps < 1 || !sps_rows || !sps || !budget) return SPEC_EINVAL;
+  if (int64_t(batch) * width > INT32_MAX - 1) return SPEC_EINVAL;
+  if (int64_t(batch) * width > 0 && !conf) return SPEC_EINVAL;
+  if (!(survival_eps >= 0.f)) return SPEC_EINVAL;
+  for (int32_t i = 0; i < n_sps; ++i) {
+    if (!isfinite(sps_rows[i]) || !isfinite(sps[i])) return SPEC_EINVAL;
+    if (i > 0 && !(sps_rows[i] > sps_rows[i - 1])) return SPEC_EINVAL;
+  }
+  return plan_budget_host(conf, batch, width, sps_rows, sps, n_sps, survival_eps, budget, theta, n_entries);
+}
+
+spec_status spec_cap_trim(const spec_cap_trim_args* a, hipStream_t stream) {
+  if (!a) return SPEC_EINVAL;
+  if (a->batch < 0 || a->total_rows < 0 || a->total_rows > INT32_MAX) return SPEC_EINVAL;
+  if (bad_events(a->profile_events, a->n_profile_events, 1)) return SPEC_EINVAL;
+  if (a->batch == 0) return record_all(a->profile_events, a->n_profile_events, stream);
+  if (!a->row_offsets || !a->verify_lens || !a->raw_accept_len || !a->raw_bonus || !a->out_tokens ||
+      !a->correct_len || !a->cap_trim_lens || !a->commit_lens || !a->block_accept_lens || !a->bonus || !a->status)
+    return SPEC_EINVAL;
+  const int32_t n = a->n_profile_events;
+  if (launch_cap_trim(*a, stream, ev_at(a->profile_events, n, 0), ev_at(a->profile_events, n, 1)) != hipSuccess)
     return SPEC_ELAUNCH;
   return SPEC_OK;
 }

@@ -17,6 +17,11 @@ uniforms streams, so requests can be generated independently and in parallel):
                    as the verifier sees q); greedy block workload: a planted accepted prefix (see
                    block_greedy); trees: EAGLE-style top-c expansion (see tree);
   * uniforms       Generator.random(dtype=float32), in [0, 1).
+  * planner        (planner_inputs) per-request draft quality q_r ~ Beta(4, 1.5); current confidence
+                   c_{r,j} = clip(q_r * 0.97^j + N(0, 0.05^2), 0, 1) (later positions a little less sure);
+                   the lagged history = clip(c + N(0, 0.05^2), 0, 1); SPS table (rows -> steps/s) points
+                   512:100, 2048:95, 4096:70, 8192:35 (flat at low load, falling at high load, the shape
+                   the DSpark page describes); raw accept lengths of a full-width verify ~ U{0..W}.
   * sparse q       (chain_sparse) the drafter's candidate set of a draft row is the top-K of its float32
                    draft logits (distinct ids, descending, lowest id first among equal values) and q the
                    softmax over just those K at T, stored as float32; a greedy request takes the first
@@ -386,6 +391,27 @@ def verify_slots_for(total_rows: int, seed: int = 7) -> np.ndarray:
 def seq_lens_for(batch: int, seed: int = 8) -> np.ndarray:
     rng = np.random.Generator(np.random.PCG64(seed))
     return rng.integers(16, 4096, size=batch).astype(np.int32)
+
+
+@dataclass
+class PlannerInputs:
+    conf: np.ndarray            # [R, W] float32 current confidences
+    conf_hist: np.ndarray       # [R, W] float32 lagged confidences (the host budget's history)
+    sps_rows: np.ndarray        # SPS table: target rows ...
+    sps: np.ndarray             # ... and steps per second there
+    raw_accept_len: np.ndarray  # [R] int32 accept lengths of a full-width verify (for the cutoff)
+
+
+def planner_inputs(seed: int = 7000, batch: int = 512, width: int = 15) -> PlannerInputs:
+    """Confidences for the verify-length planner at the ragged workload's shape (see the module recipe)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    q = rng.beta(4.0, 1.5, batch)
+    decay = 0.97 ** np.arange(width)
+    conf = np.clip(q[:, None] * decay[None, :] + rng.normal(0, 0.05, (batch, width)), 0, 1).astype(np.float32)
+    hist = np.clip(conf + rng.normal(0, 0.05, (batch, width)), 0, 1).astype(np.float32)
+    raw = rng.integers(0, width + 1, batch).astype(np.int32)
+    return PlannerInputs(conf, hist, np.array([512.0, 2048.0, 4096.0, 8192.0]), np.array([100.0, 95.0, 70.0, 35.0]),
+                         raw)
 
 
 # Full-size workloads (name -> builder); each builder's defaults are the full shapes.

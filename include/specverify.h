@@ -44,7 +44,7 @@ extern "C" {
 typedef struct ihipStream_t* hipStream_t;
 typedef struct ihipEvent_t* hipEvent_t;
 
-#define SPEC_ABI_VERSION 3
+#define SPEC_ABI_VERSION 4
 
 /* Host-visible return codes. */
 typedef enum spec_status {
@@ -89,7 +89,13 @@ typedef enum spec_mode {
   SPEC_MODE_REJECTION_SPARSE = 3,
 } spec_mode;
 
-typedef enum spec_kind { SPEC_KIND_CHAIN = 0, SPEC_KIND_TREE = 1, SPEC_KIND_COMMIT = 2 } spec_kind;
+typedef enum spec_kind {
+  SPEC_KIND_CHAIN = 0,
+  SPEC_KIND_TREE = 1,
+  SPEC_KIND_COMMIT = 2,
+  SPEC_KIND_PLAN = 3,
+  SPEC_KIND_CAP_TRIM = 4,
+} spec_kind;
 
 /* Per-request status bits (output `status[b]`). */
 #define SPEC_ST_NONFINITE     (1u << 0) /* a NaN logit in one of the request's rows; in sampling modes also
@@ -113,6 +119,8 @@ typedef enum spec_kind { SPEC_KIND_CHAIN = 0, SPEC_KIND_TREE = 1, SPEC_KIND_COMM
 #define SPEC_ST_BAD_Q         (1u << 10) /* REJECTION_SPARSE: a candidate probability that is negative or not
                                             finite; the entry is left out (an out-of-range candidate id
                                             sets SPEC_ST_BAD_TOKEN and is left out too)                     */
+#define SPEC_ST_BAD_CONF      (1u << 11) /* planner: a confidence that is NaN (used as 0) or outside [0, 1]
+                                            (clamped into it)                                               */
 
 /*
  * Chain verify (GREEDY, REJECTION or REJECTION_SPARSE).
@@ -240,6 +248,94 @@ typedef struct spec_commit_args {
   int32_t n_profile_events;
   int32_t reserved;
 } spec_commit_args;
+
+/*
+ * Verify-length planner, device side: how many of each request's W proposed drafts this round verifies
+ * ([EAGLE→DFlash2] §5.6.4 device allocation, §5.6.5 ragged layout; [DSpark] confidence truncation).
+ *
+ * confidence[r*W + j] = c_{r,j}, the draft head's estimate that draft j+1 of request r survives given that
+ * draft j did; the prefix survival is A_{r,j} = c_{r,0} * .. * c_{r,j} (float32 products in position order).
+ *   SPEC_PLAN_TOPK       rank every (r, j) with A_{r,j} >= survival_eps by A descending, then position j
+ *                        ascending, then request r ascending; the first `budget` of them are verified, so
+ *                        request r verifies selected[r] drafts (a prefix, since A falls along j). budget < 0
+ *                        means no budget: every request verifies all W drafts.
+ *   SPEC_PLAN_THRESHOLD  request r verifies the drafts before its first position with c_{r,j} < threshold
+ *                        (all W if none).
+ * Then verify_lens[r] = clamp(1 + selected[r], min_verify_len, max_verify_len) (the anchor row plus the
+ * drafts), offsets = [0, verify_lens[0], ..] (exclusive prefix sum, total offsets[batch]; the layout
+ * spec_verify_chain takes), and row_index[offsets[r] + j] = r*(W+1) + j maps each compact verify row to its
+ * place in the uniform (W+1)-wide block [anchor, d_1 .. d_W] of request r. One workgroup, one kernel.
+ * A NaN confidence counts as 0 and one outside [0, 1] is clamped into it (SPEC_ST_BAD_CONF).
+ */
+typedef enum spec_plan_mode { SPEC_PLAN_TOPK = 0, SPEC_PLAN_THRESHOLD = 1 } spec_plan_mode;
+
+typedef struct spec_plan_args {
+  const float* confidence;     /* [batch, width]                                                  */
+  int32_t* selected;           /* [batch] drafts verified beyond the anchor                        */
+  int32_t* verify_lens;        /* [batch]                                                         */
+  int32_t* offsets;            /* [batch+1]                                                       */
+  int64_t* row_index;          /* optional [batch*(width+1)]; entries past offsets[batch] untouched */
+  uint32_t* status;            /* optional [batch]: SPEC_ST_BAD_CONF                               */
+  hipEvent_t* profile_events;  /* HOST array, optional (2 events: the kernel's start / stop)        */
+  int32_t batch;               /* R, 0..2^20-1                                                    */
+  int32_t width;               /* W drafts proposed per request, 0..4095                           */
+  int32_t mode;                /* spec_plan_mode                                                  */
+  int32_t budget;              /* TOPK: drafts to verify over the batch (K); < 0: all of them       */
+  int32_t min_verify_len;      /* 1 <= min_verify_len <= max_verify_len <= width + 1               */
+  int32_t max_verify_len;
+  float survival_eps;          /* TOPK: entries with survival below it are never selected (>= 0)   */
+  float threshold;             /* THRESHOLD                                                       */
+  int32_t n_profile_events;
+  int32_t reserved;
+} spec_plan_args;
+
+spec_status spec_plan_layout(const spec_plan_args* args, hipStream_t stream);
+
+/*
+ * Verify-length planner, host side: the budget K ([EAGLE→DFlash2] §5.6.3; [DSpark] Hardware-Aware Prefix
+ * Scheduler). From lagged confidences (HOST memory, [batch, width]) it takes the survival products as
+ * spec_plan_layout does, drops those below survival_eps, sorts the rest descending a_1 >= .. >= a_n and
+ * returns K* = argmax over 0 <= K <= n of (batch + a_1 + .. + a_K) * SPS(batch + K) (the smallest K among
+ * equal values), where SPS(M), the engine's steps per second at M target rows, is linear between the
+ * table points (sps_rows ascending, sps) and the nearest end value outside them. theta (optional, at least
+ * batch*width + 1 doubles) receives the predicted throughput of K = 0 .. n, n_entries (optional) n.
+ * Pure host function; SPEC_EINVAL for bad sizes, null pointers or a table whose rows do not increase.
+ */
+spec_status spec_plan_budget(const float* confidence_hist, int32_t batch, int32_t width, const double* sps_rows,
+                             const double* sps, int32_t n_sps, float survival_eps, int32_t* budget,
+                             double* theta, int32_t* n_entries);
+
+/*
+ * Accept cutoff of a verify run over the full proposal width ([EAGLE→DFlash2] §5.6.6: the accept kernel's
+ * cap_trim / commit_lens / block_accept_lens). For request b with rows [row_offsets[b], row_offsets[b+1])
+ * of a full-width verify (raw_accept_len, raw_bonus, out_tokens from spec_verify_chain) and the plan's
+ * verify_lens[b]:
+ *   ell = verify_lens[b] - 1, correct_len = min(raw, ell), cap_trim_lens = raw - correct_len,
+ *   commit_lens = correct_len + 1, block_accept_lens = commit_lens + cap_trim_lens.
+ * A cut request (cap_trim_lens > 0) emits the token at position ell (the accepted draft d_{ell+1}) as its
+ * bonus and its out_tokens after position ell become -1; otherwise bonus = raw_bonus. Requests whose rows
+ * or lengths are invalid get SPEC_ST_BAD_ACCEPT, -1 outputs and untouched tokens. Feed correct_len to
+ * spec_commit_indices as the accept length.
+ */
+typedef struct spec_cap_trim_args {
+  const int32_t* row_offsets;     /* [batch+1] rows of the full-width verify                        */
+  const int32_t* verify_lens;     /* [batch]                                                        */
+  const int32_t* raw_accept_len;  /* [batch]                                                        */
+  const int32_t* raw_bonus;       /* [batch]                                                        */
+  int32_t* out_tokens;            /* [total_rows], read and rewritten in place                      */
+  int32_t* correct_len;           /* [batch]                                                        */
+  int32_t* cap_trim_lens;         /* [batch]                                                        */
+  int32_t* commit_lens;           /* [batch]                                                        */
+  int32_t* block_accept_lens;     /* [batch]                                                        */
+  int32_t* bonus;                 /* [batch]                                                        */
+  uint32_t* status;               /* [batch]                                                        */
+  hipEvent_t* profile_events;     /* HOST array, optional (2 events)                                */
+  int64_t total_rows;
+  int32_t batch;
+  int32_t n_profile_events;
+} spec_cap_trim_args;
+
+spec_status spec_cap_trim(const spec_cap_trim_args* args, hipStream_t stream);
 
 spec_status spec_verify_chain(const spec_chain_args* args, hipStream_t stream);
 spec_status spec_verify_tree(const spec_tree_args* args, hipStream_t stream);

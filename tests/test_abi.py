@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_struct_sizes():
     lib = dva._lib()        # raises on ABI or struct-size mismatch
-    assert dva.abi_version() == 3
+    assert dva.abi_version() == 4
     assert lib.spec_args_size(0) == ctypes.sizeof(dva.ChainArgs) == 192
     assert lib.spec_args_size(1) == ctypes.sizeof(dva.TreeArgs)
     assert lib.spec_args_size(2) == ctypes.sizeof(dva.CommitArgs)
@@ -124,3 +124,55 @@ def test_tree_and_commit_host_checks():
     assert lib.spec_commit_indices(ctypes.byref(c), None) == 1                # capacity < total_rows
     c.capacity = 10
     assert lib.spec_commit_indices(ctypes.byref(c), None) == 1                # null pointers
+
+
+def test_plan_and_cap_trim_argument_checks():
+    lib = dva._lib()
+    assert lib.spec_args_size(3) == ctypes.sizeof(dva.PlanArgs)
+    assert lib.spec_args_size(4) == ctypes.sizeof(dva.CapTrimArgs)
+    assert dva.kernel_count("plan", "topk") == 1 and dva.kernel_count("cap_trim", "greedy") == 1
+    fake = 1 << 40                                                            # never dereferenced
+
+    def plan(**kw):
+        a = dva.PlanArgs()
+        base = dict(confidence=fake, selected=fake, verify_lens=fake, offsets=fake, batch=4, width=7, mode=0,
+                    budget=3, min_verify_len=1, max_verify_len=8, survival_eps=0.0, threshold=0.5)
+        base.update(kw)
+        for k, v in base.items():
+            setattr(a, k, v)
+        return lib.spec_plan_layout(ctypes.byref(a), None)
+    assert plan(mode=2) == 1                                                  # unknown mode
+    assert plan(max_verify_len=9) == 1                                        # more rows than anchor + drafts
+    assert plan(min_verify_len=0) == 1
+    assert plan(min_verify_len=5, max_verify_len=4) == 1
+    assert plan(width=4096) == 1
+    assert plan(batch=1 << 20) == 1
+    assert plan(offsets=None) == 1
+    assert plan(confidence=None) == 1
+    assert plan(survival_eps=-1.0) == 1
+    assert plan(n_profile_events=2) == 1                                      # events array missing
+
+    def trim(**kw):
+        a = dva.CapTrimArgs()
+        base = dict(row_offsets=fake, verify_lens=fake, raw_accept_len=fake, raw_bonus=fake, out_tokens=fake,
+                    correct_len=fake, cap_trim_lens=fake, commit_lens=fake, block_accept_lens=fake, bonus=fake,
+                    status=fake, total_rows=16, batch=2)
+        base.update(kw)
+        for k, v in base.items():
+            setattr(a, k, v)
+        return lib.spec_cap_trim(ctypes.byref(a), None)
+    assert trim(out_tokens=None) == 1
+    assert trim(batch=-1) == 1
+    assert trim(total_rows=-1) == 1
+
+
+def test_plan_budget_host_argument_checks():
+    import numpy as np
+    c = np.full((2, 3), 0.5, np.float32)
+    with pytest.raises(dva.SpecError):
+        dva.plan_budget(c, [1.0, 1.0], [5.0, 4.0])                           # rows must increase
+    with pytest.raises(dva.SpecError):
+        dva.plan_budget(c, [1.0, 2.0], [5.0, float("nan")])
+    with pytest.raises(dva.SpecError):
+        dva.plan_budget(c, [1.0, 2.0], [5.0, 4.0], survival_eps=-0.5)
+    assert dva.plan_budget(np.zeros((0, 3), np.float32), [1.0], [5.0]) == (0, [0.0])

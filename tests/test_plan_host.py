@@ -1,0 +1,52 @@
+"""The library's host budget function (spec_plan_budget) against the oracle: it is host code, so these run
+on the CPU. The budget is an integer decided by float comparisons; both sides take the survival products in
+float32 in position order and the sums and the throughput model in float64, so K* and every predicted
+throughput must agree exactly."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import draft_verification_acceptance_amd as dva
+from oracle import plan as op
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+pytestmark = pytest.mark.skipif(not os.path.exists(dva.library_path), reason="libspecverify.so not built")
+
+
+def test_host_budget_worked_example():
+    with open(os.path.join(GOLDEN, "dspark_budget_k4.json")) as f:
+        g = json.load(f)
+    A = np.asarray(g["history_survival"], np.float32)
+    # confidences whose float32 running products are the table's survival values
+    conf = np.empty_like(A)
+    for r in range(A.shape[0]):
+        prev = np.float32(1.0)
+        for j in range(A.shape[1]):
+            conf[r, j] = np.float32(A[r, j] / prev)
+            prev = np.float32(prev * conf[r, j])
+    K, theta = dva.plan_budget(conf, g["sps_rows"], g["sps"])
+    assert K == g["K_star"]
+    assert np.allclose(theta, g["predicted_tokens_per_s"], atol=1e-4)
+    Ko, tho = op.plan_budget(conf, g["sps_rows"], g["sps"])
+    assert K == Ko and np.array_equal(np.asarray(theta), tho)
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_host_budget_matches_oracle(seed):
+    rng = np.random.default_rng(seed)
+    R, W = int(rng.integers(1, 64)), int(rng.integers(1, 16))
+    conf = rng.beta(4, 1.5, (R, W)).astype(np.float32)
+    if seed % 4 == 0:
+        conf[rng.random((R, W)) < 0.05] = np.nan                  # sanitised as 0
+    if seed % 5 == 0:
+        conf = np.round(conf * 4) / 4                               # exact ties in the sort
+    n_pts = int(rng.integers(1, 6))
+    rows = np.sort(rng.choice(np.arange(1, R * (W + 1) + 4), n_pts, replace=False)).astype(np.float64)
+    sps = np.sort(rng.uniform(10, 200, n_pts))[::-1].copy()
+    eps = float(rng.choice([0.0, 0.05, 0.3]))
+    K, theta = dva.plan_budget(conf, rows, sps, survival_eps=eps)
+    Ko, tho = op.plan_budget(conf, rows, sps, eps)
+    assert K == Ko
+    assert np.array_equal(np.asarray(theta), tho)
