@@ -8,3 +8,5 @@ from .verify import (  # noqa: F401
     draw, sanitize_uniform, softmax_T, sparse_q, verify_chain, verify_tree,
 )
 from . import plan  # noqa: F401,E402  (DSpark verify-length planner and cap_trim)
+from . import kv  # noqa: F401,E402  (KV data move of the commit)
+from . import tree_build  # noqa: F401,E402  (EAGLE-2 draft-tree construction)
