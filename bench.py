@@ -260,6 +260,50 @@ def run_planner(steps: int) -> dict:
             "bound": "latency (one workgroup; 30 KB of confidences)"}
 
 
+def run_tree_round(steps: int) -> dict:
+    """The steps on either side of a tree verify at the EAGLE tree workload's shape: draft-tree construction
+    (B 32, topk 8, 8 steps: 456 candidates -> 64 nodes) and the KV data move of the accepted paths over 64
+    KV buffers of 2 KB rows (K and V of 32 layers x 8 KV heads x 128 dims, bf16: a Llama-3-8B-sized cache).
+    Tree build is latency work; the move's bytes are 2 x moved rows x 2 KB x 64 buffers."""
+    import numpy as np
+    import torch
+
+    import draft_verification_acceptance_amd as dva
+    from draft_verification_acceptance_amd import workloads as W
+    w = W.tree_round_inputs()
+    d = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()  # noqa: E731
+    build = dva.prepare_tree_build(d(w.anchors), d(w.draft_tokens), d(w.draft_probs), d(w.seq_lens), w.n_nodes)
+    n_buf, row_elems = 64, 1024
+    bufs = [torch.empty((w.n_slots, row_elems), dtype=torch.bfloat16, device="cuda").normal_() for _ in range(n_buf)]
+    move = dva.prepare_kv_move(bufs, d(w.commit_offsets), d(w.src_slots), d(w.dst_pos), d(w.req_to_token),
+                               d(np.arange(len(w.anchors), dtype=np.int32)))
+    for _ in range(10):
+        build.run()
+        move.run()
+    torch.cuda.synchronize()
+    eb = [dva.HipEvents(2) for _ in range(steps)]
+    em = [dva.HipEvents(2) for _ in range(steps)]
+    for i in range(steps):
+        build.run(eb[i])
+        move.run(em[i])
+    torch.cuda.synchronize()
+    kb = np.array([e.elapsed_ms(0, 1) for e in eb]) * 1e3
+    km = np.array([e.elapsed_ms(0, 1) for e in em]) * 1e3
+    moved = int(np.count_nonzero(w.src_slots != w.req_to_token[np.repeat(np.arange(len(w.anchors)),
+                                                                         np.diff(w.commit_offsets)), w.dst_pos]))
+    move_bytes = 2 * moved * row_elems * 2 * n_buf
+    del bufs
+    torch.cuda.empty_cache()
+    return {"tree_build": {"requests": len(w.anchors), "candidates": int(8 + 7 * 64), "nodes": w.n_nodes,
+                           "kernel_us": {"mean": float(kb.mean()), "p50": float(np.median(kb))},
+                           "bound": "latency (one workgroup per request)"},
+            "kv_move": {"commit_entries": int(w.src_slots.size), "rows_moved": moved, "buffers": n_buf,
+                        "row_bytes": row_elems * 2, "bytes": move_bytes,
+                        "kernel_us": {"mean": float(km.mean()), "p50": float(np.median(km))},
+                        "gbs": move_bytes / (float(km.mean()) * 1e-6) / 1e9,
+                        "bound": "hbm copy, latency-bound at this size"}}
+
+
 def cpu_baseline(name: str, budget_s: float = 12.0) -> dict:
     """The fp64 oracle on this host's cores, on the canonical input set of the timed workload."""
     import numpy as np
@@ -365,6 +409,7 @@ def main():
                                                               "status_faults")}
             torch.cuda.empty_cache()
         extra["planner"] = run_planner(max(50, args.steps // 2))
+        extra["tree_round"] = run_tree_round(max(50, args.steps // 2))
     stats_ms = main_res["kernel_ms"]["k_stats"]["mean"]
     achieved = main_res["stats_kernel_gbs"]
     traffic = load_traffic(main_res["workload"])

@@ -20,15 +20,16 @@ __all__ = [
     "SpecError", "verify_chain", "verify_tree", "commit_indices", "workspace", "workspace_bytes",
     "workspace_init", "kernel_count", "status_string", "abi_version", "library_path", "HipEvents",
     "MODES", "ST", "PreparedCall", "prepare_verify_chain", "prepare_verify_tree", "prepare_commit_indices",
-    "plan_layout", "prepare_plan_layout", "plan_budget", "cap_trim", "prepare_cap_trim",
+    "plan_layout", "prepare_plan_layout", "plan_budget", "cap_trim", "prepare_cap_trim", "kv_move",
+    "prepare_kv_move", "tree_build", "prepare_tree_build",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_PKG, "libspecverify.so")
 
-ABI_VERSION = 4
+ABI_VERSION = 5
 MODES = {"greedy": 0, "rejection": 1, "target_only": 2, "rejection_sparse": 3}
-KIND_CHAIN, KIND_TREE, KIND_COMMIT, KIND_PLAN, KIND_CAP_TRIM = 0, 1, 2, 3, 4
+KIND_CHAIN, KIND_TREE, KIND_COMMIT, KIND_PLAN, KIND_CAP_TRIM, KIND_KV_MOVE, KIND_TREE_BUILD = 0, 1, 2, 3, 4, 5, 6
 PLAN_MODES = {"topk": 0, "threshold": 1}
 DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 
@@ -47,6 +48,7 @@ class ST:
     BAD_ACCEPT = 1 << 9
     BAD_Q = 1 << 10
     BAD_CONF = 1 << 11
+    BAD_SLOT = 1 << 12
 
 
 class SpecError(RuntimeError):
@@ -99,6 +101,20 @@ class CapTrimArgs(ctypes.Structure):
                 ("total_rows", _i64), ("batch", _i32), ("n_profile_events", _i32)]
 
 
+class KvMoveArgs(ctypes.Structure):
+    _fields_ = [("buffers", _vp), ("commit_offsets", _vp), ("src_slots", _vp), ("dst_pos", _vp),
+                ("req_to_token", _vp), ("req_pool_indices", _vp), ("status", _vp), ("profile_events", _vp),
+                ("n_slots", _i64), ("max_context", _i64), ("n_req_rows", _i64), ("capacity", _i64),
+                ("row_bytes", _i32), ("n_buffers", _i32), ("batch", _i32), ("n_profile_events", _i32)]
+
+
+class TreeBuildArgs(ctypes.Structure):
+    _fields_ = [("anchors", _vp), ("draft_tokens", _vp), ("draft_probs", _vp), ("seq_lens", _vp), ("tokens", _vp),
+                ("parents", _vp), ("positions", _vp), ("mask", _vp), ("first_child", _vp), ("next_sibling", _vp),
+                ("cand_index", _vp), ("status", _vp), ("profile_events", _vp), ("batch", _i32), ("n_steps", _i32),
+                ("topk", _i32), ("n_nodes", _i32), ("n_profile_events", _i32), ("reserved", _i32)]
+
+
 _LIB = None
 
 
@@ -114,8 +130,10 @@ def _lib():
     lib.spec_commit_indices.argtypes = [ctypes.POINTER(CommitArgs), _vp]
     lib.spec_plan_layout.argtypes = [ctypes.POINTER(PlanArgs), _vp]
     lib.spec_cap_trim.argtypes = [ctypes.POINTER(CapTrimArgs), _vp]
+    lib.spec_kv_move.argtypes = [ctypes.POINTER(KvMoveArgs), _vp]
+    lib.spec_tree_build.argtypes = [ctypes.POINTER(TreeBuildArgs), _vp]
     for f in (lib.spec_verify_chain, lib.spec_verify_tree, lib.spec_commit_indices, lib.spec_plan_layout,
-              lib.spec_cap_trim):
+              lib.spec_cap_trim, lib.spec_kv_move, lib.spec_tree_build):
         f.restype = ctypes.c_int
     _dp = ctypes.POINTER(ctypes.c_double)
     lib.spec_plan_budget.argtypes = [ctypes.POINTER(ctypes.c_float), _i32, _i32, _dp, _dp, _i32, _f32,
@@ -136,7 +154,7 @@ def _lib():
     if lib.spec_abi_version() != ABI_VERSION:
         raise RuntimeError(f"libspecverify ABI {lib.spec_abi_version()} != binding ABI {ABI_VERSION}")
     for kind, st in ((KIND_CHAIN, ChainArgs), (KIND_TREE, TreeArgs), (KIND_COMMIT, CommitArgs), (KIND_PLAN, PlanArgs),
-                     (KIND_CAP_TRIM, CapTrimArgs)):
+                     (KIND_CAP_TRIM, CapTrimArgs), (KIND_KV_MOVE, KvMoveArgs), (KIND_TREE_BUILD, TreeBuildArgs)):
         if lib.spec_args_size(kind) != ctypes.sizeof(st):
             raise RuntimeError(f"argument struct {st.__name__} size mismatch with the library")
     _LIB = lib
@@ -153,7 +171,7 @@ def status_string(code: int) -> str:
 
 def kernel_count(kind: str, mode: str) -> int:
     k = {"chain": KIND_CHAIN, "tree": KIND_TREE, "commit": KIND_COMMIT, "plan": KIND_PLAN,
-         "cap_trim": KIND_CAP_TRIM}[kind]
+         "cap_trim": KIND_CAP_TRIM, "kv_move": KIND_KV_MOVE, "tree_build": KIND_TREE_BUILD}[kind]
     return int(_lib().spec_kernel_count(k, MODES.get(mode, 0)))
 
 
@@ -570,4 +588,92 @@ def cap_trim(row_offsets, verify_lens, raw_accept_len, raw_bonus, out_tokens, *,
     """spec_cap_trim: cut a full-width verify's accepted prefix at each request's verify length. out_tokens is
     rewritten in place. Returns correct_len, cap_trim_lens, commit_lens, block_accept_lens, bonus, status."""
     return prepare_cap_trim(row_offsets, verify_lens, raw_accept_len, raw_bonus, out_tokens, out=out).run(events)
+
+
+# ----------------------------------------------------------------------------------------------------
+# the steps on either side of a tree verify: KV data move of the commit, draft-tree construction
+# ----------------------------------------------------------------------------------------------------
+def prepare_kv_move(buffers, commit_offsets: torch.Tensor, src_slots: torch.Tensor, dst_pos: torch.Tensor,
+                    req_to_token: torch.Tensor, req_pool_indices: torch.Tensor) -> PreparedCall:
+    """Checks and marshals the arguments of spec_kv_move once (see kv_move)."""
+    lib = _lib()
+    if not buffers:
+        raise ValueError("at least one KV buffer is required")
+    dev = buffers[0].device
+    n_slots = buffers[0].shape[0]
+    row_bytes = buffers[0][0].numel() * buffers[0].element_size() if n_slots else 0
+    for t in buffers:
+        if not (t.is_cuda and t.is_contiguous() and t.device == dev and t.shape[0] == n_slots):
+            raise ValueError("KV buffers must be contiguous GPU tensors of equal slot count on one device")
+        if t[0].numel() * t.element_size() != row_bytes:
+            raise ValueError("KV buffers must have equal row bytes")
+    addrs = torch.tensor([t.data_ptr() for t in buffers], dtype=torch.int64, device=dev)
+    _req(commit_offsets, "commit_offsets", torch.int32, device=dev)
+    B = commit_offsets.numel() - 1
+    _req(src_slots, "src_slots", torch.int64, device=dev)
+    _req(dst_pos, "dst_pos", torch.int32, src_slots.numel(), dev)
+    _req(req_pool_indices, "req_pool_indices", torch.int32, B, dev)
+    if req_to_token.dim() != 2:
+        raise ValueError("req_to_token must be [rows, max_context]")
+    _req(req_to_token, "req_to_token", torch.int64, device=dev)
+    o = {"status": torch.empty(B, dtype=torch.int32, device=dev)}
+    a = KvMoveArgs()
+    a.buffers, a.commit_offsets = addrs.data_ptr(), _ptr(commit_offsets)
+    a.src_slots, a.dst_pos = _ptr(src_slots), _ptr(dst_pos)
+    a.req_to_token, a.req_pool_indices, a.status = _ptr(req_to_token), _ptr(req_pool_indices), _ptr(o["status"])
+    a.n_slots, a.max_context, a.n_req_rows = n_slots, req_to_token.shape[1], req_to_token.shape[0]
+    a.capacity, a.row_bytes, a.n_buffers, a.batch = src_slots.numel(), row_bytes, len(buffers), B
+    keep = [addrs, commit_offsets, src_slots, dst_pos, req_to_token, req_pool_indices] + list(buffers)
+    return PreparedCall(lib.spec_kv_move, a, o, keep, dev)
+
+
+def kv_move(buffers, commit_offsets, src_slots, dst_pos, req_to_token, req_pool_indices, *,
+            events: "HipEvents | None" = None) -> dict:
+    """spec_kv_move: move the committed rows of every KV buffer (list of [n_slots, ...] GPU tensors, equal row
+    bytes, a multiple of 16) to the slots of positions dst_pos through req_to_token. In place. Returns status."""
+    return prepare_kv_move(buffers, commit_offsets, src_slots, dst_pos, req_to_token, req_pool_indices).run(events)
+
+
+def prepare_tree_build(anchors: torch.Tensor, draft_tokens: torch.Tensor, draft_probs: torch.Tensor,
+                       seq_lens: torch.Tensor, n_nodes: int, *, mask: bool = True,
+                       out: dict | None = None) -> PreparedCall:
+    """Checks and marshals the arguments of spec_tree_build once (see tree_build)."""
+    lib = _lib()
+    dev = anchors.device
+    if draft_tokens.dim() != 4 or draft_tokens.shape[2] != draft_tokens.shape[3]:
+        raise ValueError("draft_tokens must be [batch, n_steps, topk, topk]")
+    B, S, k, _ = draft_tokens.shape
+    _req(anchors, "anchors", torch.int32, B, dev)
+    _req(draft_tokens, "draft_tokens", torch.int32, device=dev)
+    _req(draft_probs, "draft_probs", torch.float32, B * S * k * k, dev)
+    _req(seq_lens, "seq_lens", torch.int32, B, dev)
+    N = int(n_nodes)
+    o = {} if out is None else out
+    for name in ("tokens", "parents", "positions", "first_child", "next_sibling", "cand_index"):
+        if o.get(name) is None:
+            o[name] = torch.empty(B * N, dtype=torch.int32, device=dev)
+        _req(o[name], name, torch.int32, B * N, dev)
+    if o.get("status") is None:
+        o["status"] = torch.empty(B, dtype=torch.int32, device=dev)
+    if mask and o.get("mask") is None:
+        o["mask"] = torch.empty(B * N * N, dtype=torch.uint8, device=dev)
+    a = TreeBuildArgs()
+    a.anchors, a.draft_tokens, a.draft_probs, a.seq_lens = (_ptr(anchors), _ptr(draft_tokens), _ptr(draft_probs),
+                                                           _ptr(seq_lens))
+    a.tokens, a.parents, a.positions = _ptr(o["tokens"]), _ptr(o["parents"]), _ptr(o["positions"])
+    a.mask = _ptr(o.get("mask")) if mask else None
+    a.first_child, a.next_sibling, a.cand_index = (_ptr(o["first_child"]), _ptr(o["next_sibling"]),
+                                                   _ptr(o["cand_index"]))
+    a.status = _ptr(o["status"])
+    a.batch, a.n_steps, a.topk, a.n_nodes = B, S, k, N
+    return PreparedCall(lib.spec_tree_build, a, o, [anchors, draft_tokens, draft_probs, seq_lens], dev)
+
+
+def tree_build(anchors, draft_tokens, draft_probs, seq_lens, n_nodes: int, *, mask: bool = True,
+               events: "HipEvents | None" = None, out: dict | None = None) -> dict:
+    """spec_tree_build: EAGLE-2 draft trees of n_nodes nodes from the draft's per-step top-k children
+    (draft_tokens int32 / draft_probs float32 [batch, n_steps, topk, topk]). Returns tokens, parents,
+    positions, mask ([batch * n_nodes * n_nodes] uint8), first_child, next_sibling, cand_index ([batch *
+    n_nodes] int32 each; tokens and parents feed verify_tree) and status."""
+    return prepare_tree_build(anchors, draft_tokens, draft_probs, seq_lens, n_nodes, mask=mask, out=out).run(events)
 

@@ -81,6 +81,8 @@ size_t spec_args_size(int32_t kind) {
     case SPEC_KIND_COMMIT: return sizeof(spec_commit_args);
     case SPEC_KIND_PLAN: return sizeof(spec_plan_args);
     case SPEC_KIND_CAP_TRIM: return sizeof(spec_cap_trim_args);
+    case SPEC_KIND_KV_MOVE: return sizeof(spec_kv_move_args);
+    case SPEC_KIND_TREE_BUILD: return sizeof(spec_tree_build_args);
     default: return 0;
   }
 }
@@ -99,7 +101,9 @@ const char* spec_status_string(spec_status s) {
 
 int32_t spec_kernel_count(int32_t kind, int32_t mode) {
   (void)mode;
-  if (kind == SPEC_KIND_COMMIT || kind == SPEC_KIND_PLAN || kind == SPEC_KIND_CAP_TRIM) return 1;
+  if (kind == SPEC_KIND_COMMIT || kind == SPEC_KIND_PLAN || kind == SPEC_KIND_CAP_TRIM || kind == SPEC_KIND_KV_MOVE ||
+      kind == SPEC_KIND_TREE_BUILD)
+    return 1;
   if (kind != SPEC_KIND_CHAIN && kind != SPEC_KIND_TREE) return 0;
   return 2;
 }
@@ -286,4 +290,38 @@ spec_status spec_cap_trim(const spec_cap_trim_args* a, hipStream_t stream) {
   return SPEC_OK;
 }
 
+spec_status spec_kv_move(const spec_kv_move_args* a, hipStream_t stream) {
+  if (!a) return SPEC_EINVAL;
+  if (a->batch < 0 || a->n_buffers < 1 || a->n_buffers > 65535 || a->row_bytes < 16 || a->row_bytes % 16 ||
+      a->row_bytes > (1 << 20) || a->n_slots < 0 || a->max_context < 0 || a->n_req_rows < 0 || a->capacity < 0)
+    return SPEC_EINVAL;
+  if (int64_t(a->batch) * a->n_buffers * ((a->row_bytes / 16 + 255) / 256) > INT32_MAX) return SPEC_EINVAL;
+  if (bad_events(a->profile_events, a->n_profile_events, 1)) return SPEC_EINVAL;
+  if (a->batch == 0) return record_all(a->profile_events, a->n_profile_events, stream);
+  if (!a->buffers || !a->commit_offsets || !a->req_pool_indices || (a->n_req_rows > 0 && !a->req_to_token) ||
+      (a->capacity > 0 && (!a->src_slots || !a->dst_pos)))
+    return SPEC_EINVAL;
+  const int32_t n = a->n_profile_events;
+  if (launch_kv_move(*a, stream, ev_at(a->profile_events, n, 0), ev_at(a->profile_events, n, 1)) != hipSuccess)
+    return SPEC_ELAUNCH;
+  return SPEC_OK;
+}
+
+spec_status spec_tree_build(const spec_tree_build_args* a, hipStream_t stream) {
+  if (!a) return SPEC_EINVAL;
+  if (a->batch < 0 || a->n_steps < 1 || a->topk < 1 || a->topk > 64) return SPEC_EINVAL;
+  const int64_t n_cand = int64_t(a->topk) + int64_t(a->n_steps - 1) * a->topk * a->topk;
+  if (n_cand > 4096 || a->n_nodes < 1 || a->n_nodes > 1024 || a->n_nodes > n_cand + 1) return SPEC_EINVAL;
+  if (bad_events(a->profile_events, a->n_profile_events, 1)) return SPEC_EINVAL;
+  if (a->batch == 0) return record_all(a->profile_events, a->n_profile_events, stream);
+  if (!a->anchors || !a->draft_tokens || !a->draft_probs || !a->seq_lens || !a->tokens || !a->parents ||
+      !a->positions || !a->status)
+    return SPEC_EINVAL;
+  const int32_t n = a->n_profile_events;
+  if (launch_tree_build(*a, stream, ev_at(a->profile_events, n, 0), ev_at(a->profile_events, n, 1)) != hipSuccess)
+    return SPEC_ELAUNCH;
+  return SPEC_OK;
+}
+
 }  // extern "C"
+

@@ -207,6 +207,9 @@ hipError_t launch_draw(int dtype, int mode, const VerifyParams& p, hipStream_t s
 hipError_t launch_commit(const spec_commit_args& a, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
 hipError_t launch_plan(const spec_plan_args& a, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
 hipError_t launch_cap_trim(const spec_cap_trim_args& a, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
+hipError_t launch_kv_move(const spec_kv_move_args& a, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
+hipError_t launch_tree_build(const spec_tree_build_args& a, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
+size_t tree_build_smem(int topk, int n_steps, int n_nodes, bool* q_cached);
 spec_status plan_budget_host(const float* conf, int32_t R, int32_t W, const double* sps_rows, const double* sps,
                              int32_t n_sps, float eps, int32_t* budget, double* theta, int32_t* n_entries);
 hipError_t launch_fill_zero(void* ptr, size_t bytes, hipStream_t stream);

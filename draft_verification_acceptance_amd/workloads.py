@@ -22,6 +22,9 @@ uniforms streams, so requests can be generated independently and in parallel):
                    the lagged history = clip(c + N(0, 0.05^2), 0, 1); SPS table (rows -> steps/s) points
                    512:100, 2048:95, 4096:70, 8192:35 (flat at low load, falling at high load, the shape
                    the DSpark page describes); raw accept lengths of a full-width verify ~ U{0..W}.
+  * tree round     (tree_round_inputs) draft top-k children per step: token ids uniform, probabilities a
+                   sorted Dirichlet(0.7) top-k slice; accepted paths: the root and U{0..4} increasing node
+                   ids; req_to_token a shuffled slot table, node i of request b at position seq_len + i.
   * sparse q       (chain_sparse) the drafter's candidate set of a draft row is the top-K of its float32
                    draft logits (distinct ids, descending, lowest id first among equal values) and q the
                    softmax over just those K at T, stored as float32; a greedy request takes the first
@@ -412,6 +415,46 @@ def planner_inputs(seed: int = 7000, batch: int = 512, width: int = 15) -> Plann
     raw = rng.integers(0, width + 1, batch).astype(np.int32)
     return PlannerInputs(conf, hist, np.array([512.0, 2048.0, 4096.0, 8192.0]), np.array([100.0, 95.0, 70.0, 35.0]),
                          raw)
+
+
+@dataclass
+class TreeRoundInputs:
+    anchors: np.ndarray         # [B] int32
+    draft_tokens: np.ndarray    # [B, S, k, k] int32
+    draft_probs: np.ndarray     # [B, S, k, k] float32
+    seq_lens: np.ndarray        # [B] int32
+    n_nodes: int
+    commit_offsets: np.ndarray  # [B+1] int32: accepted paths of the tree (commit lists)
+    src_slots: np.ndarray       # int64
+    dst_pos: np.ndarray         # int32
+    req_to_token: np.ndarray    # [B, max_context] int64
+    n_slots: int
+
+
+def tree_round_inputs(seed: int = 8000, batch: int = 32, steps: int = 8, topk: int = 8, n_nodes: int = 64,
+                      vocab: int = LLAMA3_VOCAB, context: int = 256) -> TreeRoundInputs:
+    """The draft side and the commit side of a tree round at the EAGLE tree workload's shape (B 32, 64 nodes,
+    topk 8, 8 steps): the draft's per-step top-k children with probabilities drawn as top-k slices of a
+    Dirichlet(0.7) softmax, and accepted paths (a root plus U{0..4} increasing node ids) to move, with slots of
+    a shuffled req_to_token table (context positions per request, nodes at seq_len + i)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    toks = rng.integers(0, vocab, (batch, steps, topk, topk)).astype(np.int32)
+    probs = np.sort(rng.dirichlet(np.ones(topk) * 0.7, (batch, steps, topk)), axis=-1)[..., ::-1]
+    probs = np.ascontiguousarray(probs, dtype=np.float32)
+    anchors = rng.integers(0, vocab, batch).astype(np.int32)
+    seq = rng.integers(16, context - n_nodes - 1, batch).astype(np.int32)
+    n_slots = batch * context
+    r2t = rng.permutation(n_slots).reshape(batch, context).astype(np.int64)
+    offs, src, dst = [0], [], []
+    for b in range(batch):
+        r = int(rng.integers(0, 5))
+        path = [0] + sorted(rng.choice(np.arange(1, n_nodes), r, replace=False).tolist())
+        for k, node in enumerate(path):
+            src.append(int(r2t[b, seq[b] + node]))
+            dst.append(int(seq[b]) + k)
+        offs.append(len(src))
+    return TreeRoundInputs(anchors, toks, probs, seq, n_nodes, np.array(offs, np.int32), np.array(src, np.int64),
+                           np.array(dst, np.int32), r2t, n_slots)
 
 
 # Full-size workloads (name -> builder); each builder's defaults are the full shapes.

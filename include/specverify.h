@@ -44,7 +44,7 @@ extern "C" {
 typedef struct ihipStream_t* hipStream_t;
 typedef struct ihipEvent_t* hipEvent_t;
 
-#define SPEC_ABI_VERSION 4
+#define SPEC_ABI_VERSION 5
 
 /* Host-visible return codes. */
 typedef enum spec_status {
@@ -95,6 +95,8 @@ typedef enum spec_kind {
   SPEC_KIND_COMMIT = 2,
   SPEC_KIND_PLAN = 3,
   SPEC_KIND_CAP_TRIM = 4,
+  SPEC_KIND_KV_MOVE = 5,
+  SPEC_KIND_TREE_BUILD = 6,
 } spec_kind;
 
 /* Per-request status bits (output `status[b]`). */
@@ -119,8 +121,10 @@ typedef enum spec_kind {
 #define SPEC_ST_BAD_Q         (1u << 10) /* REJECTION_SPARSE: a candidate probability that is negative or not
                                             finite; the entry is left out (an out-of-range candidate id
                                             sets SPEC_ST_BAD_TOKEN and is left out too)                     */
-#define SPEC_ST_BAD_CONF      (1u << 11) /* planner: a confidence that is NaN (used as 0) or outside [0, 1]
-                                            (clamped into it)                                               */
+#define SPEC_ST_BAD_CONF      (1u << 11) /* planner / tree build: a confidence or draft probability that is NaN
+                                            (used as 0) or outside [0, 1] (clamped into it)                 */
+#define SPEC_ST_BAD_SLOT      (1u << 12) /* KV move: a slot, position, request row or commit range outside the
+                                            given tables; the entry (or the request's range) is skipped     */
 
 /*
  * Chain verify (GREEDY, REJECTION or REJECTION_SPARSE).
@@ -336,6 +340,80 @@ typedef struct spec_cap_trim_args {
 } spec_cap_trim_args;
 
 spec_status spec_cap_trim(const spec_cap_trim_args* args, hipStream_t stream);
+
+/*
+ * KV data move of a commit ([EAGLE→DFlash2] §8.2: a tree's accepted path is not contiguous in the flattened
+ * tree, so its KV is compacted to the positions after seq_lens; the engineering note on
+ * move_accept_tokens_to_target_kvcache: the accepted tokens' KV moves to the contiguous positions after
+ * seq_lens, rejected slots are overwritten later). Takes the lists of spec_commit_indices. For request b,
+ * entries e = commit_offsets[b] .. commit_offsets[b+1]-1 are moved in that order (path order):
+ *   dst_slot = req_to_token[req_pool_indices[b] * max_context + dst_pos[e]],
+ *   for every buffer: row dst_slot <- row src_slots[e]   (nothing when src == dst, e.g. a chain).
+ * For a tree path this equals reading every source before writing any destination. Buffers are raw bytes:
+ * buffers[i] is the device base address of buffer i, [n_slots, row_bytes] (e.g. K and V of every layer of
+ * the target and of the draft). An entry outside the tables, or a request whose commit range is outside
+ * [0, capacity], is skipped and sets SPEC_ST_BAD_SLOT.
+ */
+typedef struct spec_kv_move_args {
+  const uint64_t* buffers;          /* device [n_buffers] base addresses                               */
+  const int32_t* commit_offsets;    /* [batch+1]                                                       */
+  const int64_t* src_slots;         /* [capacity]                                                      */
+  const int32_t* dst_pos;           /* [capacity]                                                      */
+  const int64_t* req_to_token;      /* [n_req_rows, max_context] slot of each (request row, position)   */
+  const int32_t* req_pool_indices;  /* [batch] row of req_to_token of each request                     */
+  uint32_t* status;                 /* optional [batch]                                                */
+  hipEvent_t* profile_events;       /* HOST array, optional (2 events)                                 */
+  int64_t n_slots;
+  int64_t max_context;
+  int64_t n_req_rows;
+  int64_t capacity;                 /* entries of src_slots / dst_pos                                  */
+  int32_t row_bytes;                /* bytes per slot per buffer: a multiple of 16, 16 .. 2^20         */
+  int32_t n_buffers;                /* 1 .. 65535                                                      */
+  int32_t batch;
+  int32_t n_profile_events;
+} spec_kv_move_args;
+
+spec_status spec_kv_move(const spec_kv_move_args* args, hipStream_t stream);
+
+/*
+ * EAGLE-2 dynamic draft-tree construction ([EAGLE→DFlash2] §2.3–§2.4; [SpecDec] EAGLE tree build: topk^2 ->
+ * topk per step, then the best n_nodes - 1 nodes plus the root). Per request: the draft's top-k children of
+ * each frontier node at each of S steps, draft_tokens / draft_probs [batch, S, topk, topk] (step s, frontier
+ * slot f, child rank c; step 0 expands the root only, slot 0). A candidate's score is the float32 product of
+ * the probabilities along its path; candidate ids are c at step 0 and topk + (s-1) topk^2 + f topk + c at
+ * step s. Every selection ranks by score descending, then candidate id ascending: the frontier after step s is
+ * the top topk of step s's candidates (frontier slot = rank), and the tree's nodes are the root (node 0, token
+ * = anchors[b]) and the top n_nodes - 1 of all candidates, in candidate-id order (a parent precedes its
+ * children; the ancestor closure holds since a child never outranks its parent).
+ * Outputs, [batch, n_nodes] unless noted: tokens, parents (root -1; the input spec_verify_tree takes),
+ * positions = seq_lens[b] + depth (depth, not the flattened index), mask [batch, n_nodes, n_nodes] uint8
+ * (mask[i][j] = 1 iff j is i or an ancestor of i: a node sees the committed history, its ancestors and
+ * itself), first_child / next_sibling (-1 if none), cand_index (candidate id of each node, -1 for the root),
+ * status (SPEC_ST_BAD_CONF). One workgroup per request.
+ */
+typedef struct spec_tree_build_args {
+  const int32_t* anchors;           /* [batch]                                                        */
+  const int32_t* draft_tokens;      /* [batch, n_steps, topk, topk]                                   */
+  const float* draft_probs;         /* [batch, n_steps, topk, topk]                                   */
+  const int32_t* seq_lens;          /* [batch]                                                        */
+  int32_t* tokens;                  /* [batch, n_nodes]                                               */
+  int32_t* parents;                 /* [batch, n_nodes]                                               */
+  int32_t* positions;               /* [batch, n_nodes]                                               */
+  uint8_t* mask;                    /* optional [batch, n_nodes, n_nodes]                             */
+  int32_t* first_child;             /* optional [batch, n_nodes]                                      */
+  int32_t* next_sibling;            /* optional [batch, n_nodes]                                      */
+  int32_t* cand_index;              /* optional [batch, n_nodes]                                      */
+  uint32_t* status;                 /* [batch]                                                        */
+  hipEvent_t* profile_events;       /* HOST array, optional (2 events)                                */
+  int32_t batch;
+  int32_t n_steps;                  /* S >= 1                                                         */
+  int32_t topk;                     /* 1 .. 64; topk + (S-1) topk^2 candidates, at most 4096            */
+  int32_t n_nodes;                  /* 1 .. min(1024, candidates + 1)                                 */
+  int32_t n_profile_events;
+  int32_t reserved;
+} spec_tree_build_args;
+
+spec_status spec_tree_build(const spec_tree_build_args* args, hipStream_t stream);
 
 spec_status spec_verify_chain(const spec_chain_args* args, hipStream_t stream);
 spec_status spec_verify_tree(const spec_tree_args* args, hipStream_t stream);

@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_struct_sizes():
     lib = dva._lib()        # raises on ABI or struct-size mismatch
-    assert dva.abi_version() == 4
+    assert dva.abi_version() == 5
     assert lib.spec_args_size(0) == ctypes.sizeof(dva.ChainArgs) == 192
     assert lib.spec_args_size(1) == ctypes.sizeof(dva.TreeArgs)
     assert lib.spec_args_size(2) == ctypes.sizeof(dva.CommitArgs)
