@@ -62,6 +62,19 @@ def row_nonfinite(x: np.ndarray, sampling: bool) -> bool:
     return False
 
 
+def mask_row(x: np.ndarray, words) -> np.ndarray:
+    """Vocab (grammar) mask on one target row ([EAGLE→DFlash2] §5.6.6 and §8.4: the grammar mask is applied to
+    the target logits after the target forward and before acceptance, and sampling reads the masked
+    distribution). `words` holds the row's allowed-token bits: token v is allowed iff bit (v mod 32) of word
+    v // 32 is 1 (READING: the packed bitmask layout; None = every token allowed). A masked logit becomes -inf
+    whatever its value, so a NaN or +inf there no longer counts."""
+    if words is None:
+        return x
+    v = np.arange(len(x))
+    allowed = (np.asarray(words, np.uint64)[v >> 5] >> (v & 31).astype(np.uint64)) & np.uint64(1)
+    return np.where(allowed == 1, x, -np.inf)
+
+
 def softmax_T(x: np.ndarray, temperature: float) -> np.ndarray:
     """p = softmax(x / T) in float64 ([EAGLE→DFlash2] §1.2: p_j, q_j are the distributions actually used,
     READING: the same temperature divides target and draft logits). -inf entries get p = 0."""
@@ -150,6 +163,32 @@ def near_cdf(gap: float, Z: float) -> bool:
     return gap < NEAR or gap * Z < NEAR_MASS
 
 
+def sample_then_match(ps: list, toks: list, tok_ok: list, us: list) -> tuple[int, int, list, int | None]:
+    """Sample-then-match over one request's rows ([DFlash] decode loop, step 4: each draft token is compared
+    with a sample of the target posterior at its position, the accept length is the longest matching prefix,
+    and the first mismatch is replaced by that sample; [EAGLE→DFlash2] §1.2: sampling the target
+    independently and matching the prefix is a different implementation from p/q rejection). Every emitted
+    token is a draw from its row's p, so the output follows the target.
+    ps[j] = p_j (rows 0..m), toks[j] = d_{j+1}, us[j] = the uniform of row j.
+    READING: row j's sample is draw(p_j, us[j]) with us[j] = the uniform of d_{j+1}'s test for j < m and
+    u_final for row m; the compared positions report p_j(d_{j+1}) as their accept probability; there is no
+    residual. Returns (r, emitted sample at row r, accept probabilities of the compared positions, index of
+    the first sample too close to a CDF step or None)."""
+    m = len(toks)
+    alphas = []
+    near = None
+    for j in range(m + 1):
+        t, gap, Z = draw(ps[j], us[j])
+        if near_cdf(gap, Z) and near is None:
+            near = j
+        if j < m:
+            alphas.append(ps[j][toks[j]] if tok_ok[j] else 0.0)
+            if tok_ok[j] and t == toks[j]:
+                continue
+        return j, t, alphas, near
+    raise AssertionError("unreachable")
+
+
 def _sentinel_outputs(n_rows: int, n_draft: int, batch: int) -> dict:
     return {
         "accept_len": np.full(batch, -2, np.int64),
@@ -171,27 +210,29 @@ def verify_chain(target: np.ndarray, offsets: np.ndarray, draft_tokens: np.ndarr
                  draft: np.ndarray | None = None, u_accept: np.ndarray | None = None,
                  u_final: np.ndarray | None = None, temperature: float = 1.0,
                  max_verify_len: int = 1024, requests=None, cand_ids: np.ndarray | None = None,
-                 cand_q: np.ndarray | None = None) -> dict:
-    """Chain verify for mode "greedy", "rejection" or "rejection_sparse".
+                 cand_q: np.ndarray | None = None, vocab_mask: np.ndarray | None = None) -> dict:
+    """Chain verify for mode "greedy", "rejection", "rejection_sparse" or "sample_match".
 
     target [T_rows, V] (uint16 bf16 bits or float32); offsets [B+1]: request b owns target rows
     off[b]..off[b+1]-1 (ragged layout of [EAGLE→DFlash2] §5.6.5). Draft-side arrays hold m_b entries per
     request from off[b]-b on; entry j is about d_{j+1}. "rejection" takes q_j = softmax(draft row / T);
     "rejection_sparse" takes q_j from the K candidate pairs cand_ids[entry], cand_q[entry] ([D_rows, K]) of
     sparse_q (the temperature then divides the target logits only: q arrives as probabilities).
+    "sample_match" draws a sample from every target row and accepts while it equals the draft token.
+    vocab_mask [T_rows, ceil(V/32)] (optional) masks the target rows (mask_row); draft rows are not masked.
     `requests` limits the work to some requests (the others keep sentinel values: -2 / NaN).
 
     Returns accept_len, bonus, out_tokens, accept_index, status, accept_prob, residual_mass and flag_pos
     (oracle only: number of leading emitted tokens fixed before the first NEAR_* decision; r+1 if none).
     """
-    assert mode in ("greedy", "rejection", "rejection_sparse")
+    assert mode in ("greedy", "rejection", "rejection_sparse", "sample_match")
     T, V = target.shape
     B = len(offsets) - 1
     out = _sentinel_outputs(T, max(T - B, 0), B)
     cand = (cand_ids, cand_q) if mode == "rejection_sparse" else None
     for b in (range(B) if requests is None else requests):
         _chain_request(out, b, target, offsets, draft_tokens, mode, draft, u_accept, u_final,
-                       temperature, max_verify_len, T, V, B, cand)
+                       temperature, max_verify_len, T, V, B, cand, vocab_mask)
     return out
 
 
@@ -208,7 +249,7 @@ def _chain_offsets_ok(offsets, b, T, B, max_len) -> bool:
 
 
 def _chain_request(out, b, target, offsets, draft_tokens, mode, draft, u_accept, u_final, temperature,
-                   max_len, T, V, B, cand=None):
+                   max_len, T, V, B, cand=None, vocab_mask=None):
     out["evaluated"][b] = True
     if not _chain_offsets_ok(offsets, b, T, B, max_len):
         out["status"][b] = ST_BAD_OFFSETS
@@ -222,11 +263,14 @@ def _chain_request(out, b, target, offsets, draft_tokens, mode, draft, u_accept,
     sampling = mode != "greedy"
     st = 0
 
-    t_rows = [decode_row(target[off + j]) for j in range(m + 1)]
+    t_rows = [mask_row(decode_row(target[off + j]), None if vocab_mask is None else vocab_mask[off + j])
+              for j in range(m + 1)]
     s_rows = [decode_row(draft[dr0 + j]) for j in range(m)] if mode == "rejection" else []
     for x in t_rows + s_rows:
         if row_nonfinite(x, sampling):
             st |= ST_NONFINITE
+    if vocab_mask is not None and any(np.isneginf(x).all() for x in t_rows):
+        st |= ST_NONFINITE     # READING: a masked row with no allowed finite logit, in every mode
     toks = [int(draft_tokens[dr0 + j]) for j in range(m)]      # toks[j-1] = d_j
     tok_ok = [0 <= d < V for d in toks]
     if not all(tok_ok):
@@ -245,6 +289,16 @@ def _chain_request(out, b, target, offsets, draft_tokens, mode, draft, u_accept,
             else:
                 break
         x = argmax_lowest(t_rows[r])
+    elif mode == "sample_match":
+        us = [sanitize_uniform(u_accept[dr0 + j]) for j in range(m)] + [sanitize_uniform(u_final[b])]
+        if any(bad for _, bad in us):
+            st |= ST_BAD_UNIFORM
+        ps = [softmax_T(x, temperature) for x in t_rows]
+        r, x, a, near = sample_then_match(ps, toks, tok_ok, [u for u, _ in us])
+        alphas[:len(a)] = a
+        if near is not None:
+            st |= ST_NEAR_CDF
+            flag_pos = near
     else:
         us = [sanitize_uniform(u_accept[dr0 + j]) for j in range(m)]
         uf, uf_bad = sanitize_uniform(u_final[b])
@@ -309,12 +363,13 @@ def _chain_request(out, b, target, offsets, draft_tokens, mode, draft, u_accept,
 # ----------------------------------------------------------------------------------------------------
 def verify_tree(target: np.ndarray, parents: np.ndarray, tokens: np.ndarray, n_nodes: int, mode: str, *,
                 u_accept: np.ndarray | None = None, u_final: np.ndarray | None = None,
-                temperature: float = 1.0, requests=None) -> dict:
+                temperature: float = 1.0, requests=None, vocab_mask: np.ndarray | None = None) -> dict:
     """Tree verify for mode "greedy" or "target_only".
 
     Request b owns rows b*N .. b*N+N-1; node 0 is the anchor, node i > 0 has parent in [0, i) and token
     tokens[b*N+i]. Row i is the target distribution after the path to node i (tree attention,
-    [EAGLE→DFlash2] §2.4). Children are examined in ascending node index (READING).
+    [EAGLE→DFlash2] §2.4). Children are examined in ascending node index (READING). vocab_mask [B*N,
+    ceil(V/32)] (optional) masks every node row (mask_row).
     """
     assert mode in ("greedy", "target_only")
     rows, V = target.shape
@@ -322,19 +377,22 @@ def verify_tree(target: np.ndarray, parents: np.ndarray, tokens: np.ndarray, n_n
     B = rows // N
     out = _sentinel_outputs(rows, rows, B)
     for b in (range(B) if requests is None else requests):
-        _tree_request(out, b, target, parents, tokens, N, mode, u_accept, u_final, temperature, V)
+        _tree_request(out, b, target, parents, tokens, N, mode, u_accept, u_final, temperature, V, vocab_mask)
     return out
 
 
-def _tree_request(out, b, target, parents, tokens, N, mode, u_accept, u_final, temperature, V):
+def _tree_request(out, b, target, parents, tokens, N, mode, u_accept, u_final, temperature, V, vocab_mask=None):
     out["evaluated"][b] = True
     base = b * N
     sampling = mode == "target_only"
     st = 0
-    rows = [decode_row(target[base + i]) for i in range(N)]
+    rows = [mask_row(decode_row(target[base + i]), None if vocab_mask is None else vocab_mask[base + i])
+            for i in range(N)]
     for x in rows:
         if row_nonfinite(x, sampling):
             st |= ST_NONFINITE
+    if vocab_mask is not None and any(np.isneginf(x).all() for x in rows):
+        st |= ST_NONFINITE
     par = [int(parents[base + i]) for i in range(N)]
     tok = [int(tokens[base + i]) for i in range(N)]
     if par[0] != -1:
