@@ -27,8 +27,8 @@ __all__ = [
 _PKG = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_PKG, "libspecverify.so")
 
-ABI_VERSION = 5
-MODES = {"greedy": 0, "rejection": 1, "target_only": 2, "rejection_sparse": 3}
+ABI_VERSION = 6
+MODES = {"greedy": 0, "rejection": 1, "target_only": 2, "rejection_sparse": 3, "sample_match": 4}
 KIND_CHAIN, KIND_TREE, KIND_COMMIT, KIND_PLAN, KIND_CAP_TRIM, KIND_KV_MOVE, KIND_TREE_BUILD = 0, 1, 2, 3, 4, 5, 6
 PLAN_MODES = {"topk": 0, "threshold": 1}
 DTYPES = {torch.float32: 0, torch.bfloat16: 1}
@@ -67,7 +67,7 @@ class ChainArgs(ctypes.Structure):
                 ("workspace", _vp), ("workspace_bytes", _sz), ("profile_events", _vp), ("total_rows", _i64),
                 ("vocab", _i64), ("batch", _i32), ("max_verify_len", _i32), ("dtype", _i32), ("mode", _i32),
                 ("temperature", _f32), ("n_profile_events", _i32), ("cand_ids", _vp), ("cand_q", _vp),
-                ("n_cand", _i32), ("reserved", _i32)]
+                ("n_cand", _i32), ("reserved", _i32), ("vocab_mask", _vp)]
 
 
 class TreeArgs(ctypes.Structure):
@@ -76,7 +76,7 @@ class TreeArgs(ctypes.Structure):
                 ("accept_prob", _vp), ("residual_mass", _vp), ("workspace", _vp), ("workspace_bytes", _sz),
                 ("profile_events", _vp), ("vocab", _i64), ("batch", _i32), ("n_nodes", _i32), ("dtype", _i32),
                 ("mode", _i32), ("temperature", _f32), ("threshold_single", _f32), ("threshold_acc", _f32),
-                ("n_profile_events", _i32)]
+                ("n_profile_events", _i32), ("vocab_mask", _vp)]
 
 
 class CommitArgs(ctypes.Structure):
@@ -306,8 +306,8 @@ def prepare_verify_chain(target_logits: torch.Tensor, target_offsets: torch.Tens
                          u_accept: torch.Tensor | None = None, u_final: torch.Tensor | None = None,
                          temperature: float = 1.0, max_verify_len: int | None = None, workspace_tensor=None,
                          out: dict | None = None, accept_prob: bool = True, residual_mass: bool = True,
-                         cand_ids: torch.Tensor | None = None,
-                         cand_q: torch.Tensor | None = None) -> PreparedCall:
+                         cand_ids: torch.Tensor | None = None, cand_q: torch.Tensor | None = None,
+                         vocab_mask: torch.Tensor | None = None) -> PreparedCall:
     """Checks and marshals the arguments of spec_verify_chain once (see verify_chain)."""
     lib = _lib()
     dev = target_logits.device
@@ -333,8 +333,10 @@ def prepare_verify_chain(target_logits: torch.Tensor, target_offsets: torch.Tens
         K = int(cand_ids.shape[1])
         _req(cand_ids, "cand_ids", torch.int32, D * K, dev)
         _req(cand_q, "cand_q", torch.float32, D * K, dev)
-    elif mode != "greedy":
+    elif mode not in ("greedy", "sample_match"):
         raise SpecError(3, status_string(3))
+    if vocab_mask is not None:
+        _req(vocab_mask, "vocab_mask", torch.int32, T * ((V + 31) // 32), dev)
     if mode != "greedy":
         _req(u_accept, "u_accept", torch.float32, D, dev)
         _req(u_final, "u_final", torch.float32, B, dev)
@@ -363,8 +365,9 @@ def prepare_verify_chain(target_logits: torch.Tensor, target_offsets: torch.Tens
     a.cand_ids = _ptr(cand_ids) if K else None
     a.cand_q = _ptr(cand_q) if K else None
     a.n_cand = K
+    a.vocab_mask = _ptr(vocab_mask)
     keep = [target_logits, target_offsets, draft_tokens, draft_logits, u_accept, u_final, cand_ids, cand_q,
-            workspace_tensor]
+            vocab_mask, workspace_tensor]
     return PreparedCall(lib.spec_verify_chain, a, o, keep, dev)
 
 
@@ -375,16 +378,18 @@ def verify_chain(target_logits: torch.Tensor, target_offsets: torch.Tensor, draf
     target_logits [T_rows, V] bf16/fp32; target_offsets int32 [B+1]; draft-side int32 tokens, float32
     uniforms and logits packed with m_b entries per request from off[b]-b; max_verify_len bounds m_b + 1.
     Keywords: draft_logits (rejection), cand_ids / cand_q ([T_rows - B, K] int32 / float32, rejection_sparse),
-    u_accept, u_final, temperature, max_verify_len, workspace_tensor, out, accept_prob, residual_mass. Returns the output tensors (accept_len, bonus, out_tokens, accept_index,
-    status, accept_prob, residual_mass)."""
+    u_accept, u_final, temperature, max_verify_len, workspace_tensor, out, accept_prob, residual_mass,
+    vocab_mask (int32 [T_rows, ceil(V/32)] allowed-token bits of the target rows, bit v % 32 of word v // 32).
+    Modes: greedy, rejection, rejection_sparse, sample_match. Returns the output tensors (accept_len, bonus,
+    out_tokens, accept_index, status, accept_prob, residual_mass)."""
     return prepare_verify_chain(target_logits, target_offsets, draft_tokens, mode, **kw).run(events)
 
 
 def prepare_verify_tree(target_logits: torch.Tensor, parents: torch.Tensor, tokens: torch.Tensor, n_nodes: int,
                         mode: str = "greedy", *, u_accept=None, u_final=None, temperature: float = 1.0,
                         threshold_single: float = 1.0, threshold_acc: float = 1.0, workspace_tensor=None,
-                        out: dict | None = None, accept_prob: bool = True,
-                        residual_mass: bool = True) -> PreparedCall:
+                        out: dict | None = None, accept_prob: bool = True, residual_mass: bool = True,
+                        vocab_mask: torch.Tensor | None = None) -> PreparedCall:
     """Checks and marshals the arguments of spec_verify_tree once (see verify_tree)."""
     lib = _lib()
     dev = target_logits.device
@@ -403,6 +408,8 @@ def prepare_verify_tree(target_logits: torch.Tensor, parents: torch.Tensor, toke
         _req(u_final, "u_final", torch.float32, B, dev)
     elif mode != "greedy":
         raise SpecError(3, status_string(3))
+    if vocab_mask is not None:
+        _req(vocab_mask, "vocab_mask", torch.int32, rows * ((V + 31) // 32), dev)
     if workspace_tensor is None:
         workspace_tensor = workspace("tree", mode, rows, V, B, N, dev)
     o = _outputs(out, dev, B, rows, rows, accept_prob, residual_mass)
@@ -421,7 +428,8 @@ def prepare_verify_tree(target_logits: torch.Tensor, parents: torch.Tensor, toke
     a.mode = MODES[mode]
     a.temperature = float(temperature)
     a.threshold_single, a.threshold_acc = float(threshold_single), float(threshold_acc)
-    keep = [target_logits, parents, tokens, u_accept, u_final, workspace_tensor]
+    a.vocab_mask = _ptr(vocab_mask)
+    keep = [target_logits, parents, tokens, u_accept, u_final, vocab_mask, workspace_tensor]
     return PreparedCall(lib.spec_verify_tree, a, o, keep, dev)
 
 
@@ -429,7 +437,7 @@ def verify_tree(target_logits: torch.Tensor, parents: torch.Tensor, tokens: torc
                 mode: str = "greedy", *, events: "HipEvents | None" = None, **kw) -> dict:
     """spec_verify_tree on torch tensors: target_logits [B*N, V]; parents, tokens int32 [B*N]. Keywords:
     u_accept, u_final, temperature, threshold_single, threshold_acc, workspace_tensor, out, accept_prob,
-    residual_mass."""
+    residual_mass, vocab_mask (int32 [B*N, ceil(V/32)], as for verify_chain)."""
     return prepare_verify_tree(target_logits, parents, tokens, n_nodes, mode, **kw).run(events)
 
 

@@ -58,13 +58,15 @@ void carve(VerifyParams& p, const Layout& lo, void* ws) {
   p.n_seg = lo.n_seg;
 }
 
-// The two kernels of a verify call: the logits stream, then the greedy scans or the sampling draw.
+// The two kernels of a verify call: the logits stream, then the greedy scans, the sample-then-match
+// draws or the sampling draw.
 spec_status launch_pair(int dtype, int mode, VerifyParams& p, hipEvent_t* ev, int32_t nev, hipStream_t stream) {
   if (launch_stats(dtype, mode, p, stream, ev_at(ev, nev, 0), ev_at(ev, nev, 1)) != hipSuccess)
     return SPEC_ELAUNCH;
-  const hipError_t e = mode == SPEC_MODE_GREEDY
-                           ? launch_scan(dtype, p, stream, ev_at(ev, nev, 2), ev_at(ev, nev, 3))
-                           : launch_draw(dtype, mode, p, stream, ev_at(ev, nev, 2), ev_at(ev, nev, 3));
+  hipEvent_t e0 = ev_at(ev, nev, 2), e1 = ev_at(ev, nev, 3);
+  const hipError_t e = mode == SPEC_MODE_GREEDY         ? launch_scan(dtype, p, stream, e0, e1)
+                       : mode == SPEC_MODE_SAMPLE_MATCH ? launch_match(dtype, p, stream, e0, e1)
+                                                        : launch_draw(dtype, mode, p, stream, e0, e1);
   return e == hipSuccess ? SPEC_OK : SPEC_ELAUNCH;
 }
 
@@ -113,7 +115,7 @@ size_t spec_workspace_bytes(int32_t kind, int32_t mode, int64_t total_rows, int6
   if (kind == SPEC_KIND_COMMIT) return 0;
   if (batch < 0 || vocab < 1 || vocab > kMaxVocab || total_rows < batch) return 0;
   if (mode != SPEC_MODE_GREEDY && mode != SPEC_MODE_REJECTION && mode != SPEC_MODE_TARGET_ONLY &&
-      mode != SPEC_MODE_REJECTION_SPARSE)
+      mode != SPEC_MODE_REJECTION_SPARSE && mode != SPEC_MODE_SAMPLE_MATCH)
     return 0;
   int32_t L;
   if (kind == SPEC_KIND_CHAIN) {
@@ -138,14 +140,15 @@ spec_status spec_verify_chain(const spec_chain_args* a, hipStream_t stream) {
   if (!a) return SPEC_EINVAL;
   if (a->dtype != SPEC_DTYPE_F32 && a->dtype != SPEC_DTYPE_BF16) return SPEC_EDTYPE;
   if (a->mode == SPEC_MODE_TARGET_ONLY) return SPEC_EUNSUPPORTED;
-  if (a->mode != SPEC_MODE_GREEDY && a->mode != SPEC_MODE_REJECTION && a->mode != SPEC_MODE_REJECTION_SPARSE)
+  if (a->mode != SPEC_MODE_GREEDY && a->mode != SPEC_MODE_REJECTION && a->mode != SPEC_MODE_REJECTION_SPARSE &&
+      a->mode != SPEC_MODE_SAMPLE_MATCH)
     return SPEC_EINVAL;
   if (a->batch < 0 || a->vocab < 1 || a->vocab > kMaxVocab || a->total_rows < a->batch ||
       a->total_rows > INT32_MAX || a->max_verify_len < 1 || a->max_verify_len > kMaxLen)
     return SPEC_EINVAL;
   const bool dense = a->mode == SPEC_MODE_REJECTION;
   const bool sparse = a->mode == SPEC_MODE_REJECTION_SPARSE;
-  const bool sampling = dense || sparse;
+  const bool sampling = a->mode != SPEC_MODE_GREEDY;
   if (sparse && (a->n_cand < 1 || a->n_cand > kMaxCand)) return SPEC_EINVAL;
   if (bad_events(a->profile_events, a->n_profile_events, spec_kernel_count(SPEC_KIND_CHAIN, a->mode)))
     return SPEC_EINVAL;
@@ -182,14 +185,17 @@ spec_status spec_verify_chain(const spec_chain_args* a, hipStream_t stream) {
   p.B = a->batch;
   p.tree = 0;
   p.coef = sampling ? float(kLog2e / double(a->temperature)) : 0.f;
+  p.mask = a->vocab_mask;
+  p.mask_words = (a->vocab + 31) / 32;
   return launch_pair(a->dtype, a->mode, p, a->profile_events, a->n_profile_events, stream);
 }
 
 spec_status spec_verify_tree(const spec_tree_args* a, hipStream_t stream) {
   if (!a) return SPEC_EINVAL;
   if (a->dtype != SPEC_DTYPE_F32 && a->dtype != SPEC_DTYPE_BF16) return SPEC_EDTYPE;
-  // classic p/q rejection needs topk = 1 (a chain)
-  if (a->mode == SPEC_MODE_REJECTION || a->mode == SPEC_MODE_REJECTION_SPARSE) return SPEC_EUNSUPPORTED;
+  // classic p/q rejection needs topk = 1 (a chain); sample-then-match is a chain rule
+  if (a->mode == SPEC_MODE_REJECTION || a->mode == SPEC_MODE_REJECTION_SPARSE || a->mode == SPEC_MODE_SAMPLE_MATCH)
+    return SPEC_EUNSUPPORTED;
   if (a->mode != SPEC_MODE_GREEDY && a->mode != SPEC_MODE_TARGET_ONLY) return SPEC_EINVAL;
   const bool tgt = a->mode == SPEC_MODE_TARGET_ONLY;
   if (tgt && (a->threshold_single != 1.f || a->threshold_acc != 1.f)) return SPEC_EUNSUPPORTED;
@@ -225,6 +231,8 @@ spec_status spec_verify_tree(const spec_tree_args* a, hipStream_t stream) {
   p.B = a->batch;
   p.tree = 1;
   p.coef = tgt ? float(kLog2e / double(a->temperature)) : 0.f;
+  p.mask = a->vocab_mask;
+  p.mask_words = (a->vocab + 31) / 32;
   return launch_pair(a->dtype, a->mode, p, a->profile_events, a->n_profile_events, stream);
 }
 

@@ -96,6 +96,18 @@ __device__ __forceinline__ void complete_memory_ops() {
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
+// Vocab mask rows: bit (v % 32) of word v / 32 is 1 iff token v is allowed. mask_bits8 returns the bits
+// of tokens [v, v + 8) (bit i = token v + i) for v < V; the words past the row are not read.
+__device__ __forceinline__ uint32_t mask_bits8(const uint32_t* mrow, int64_t v, int64_t nwords) {
+  const int64_t w = v >> 5;
+  const uint32_t sh = uint32_t(v & 31);
+  uint32_t bits = mrow[w] >> sh;
+  if (sh > 24 && w + 1 < nwords) bits |= mrow[w + 1] << (32u - sh);
+  return bits;
+}
+
+__device__ __forceinline__ bool mask_allows(const uint32_t* mrow, int64_t v) { return (mrow[v >> 5] >> (v & 31)) & 1u; }
+
 __device__ __forceinline__ uint64_t lanes_below(int lane) {
   return lane == 0 ? 0ull : (~0ull >> (64 - lane));
 }

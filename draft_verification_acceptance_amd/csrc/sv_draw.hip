@@ -8,6 +8,7 @@
 //                             ([EAGLE→DFlash2] §6.5), so w = p except at the candidates
 // The last two are one rule: w = [p - a]_+ with a per-token adjustment list a (a tried token carries
 // a = +inf, a candidate its probability, repeated ids adding up) and a = 0 elsewhere.
+// With a vocab mask the target row's disallowed tokens have p = 0 (so w = 0).
 // The token is the number of cumulative probabilities u has reached, i.e. the smallest v with
 // sum_{t<=v} w_t > u * sum w ([EAGLE→DFlash2] §6.2, inverse-CDF rule); if rounding leaves u past the last
 // step the last positive-weight token is taken. Weights summing to 0 fall back to p (flagged).
@@ -25,6 +26,8 @@ namespace {
 struct RowCtx {
   const void* xt;
   const void* xq;
+  const uint32_t* mt;   // vocab mask of the target row, or NULL
+  int64_t mw;           // its words
   float coef, m_t, inv_zt, m_q, inv_zq;
   bool vec;   // both rows 16-byte aligned: whole 8-token runs load as one (bf16) or two (fp32) vectors
 };
@@ -68,9 +71,13 @@ __device__ __forceinline__ void unpack_raw8(const Raw8& w, float* x) {
 // Weights of tokens [e, e+8) from their logits: w (residual [p - q]_+ from a draft row, or [p - a]_+ with
 // the adjustment list (seen, seen_a)) and p. The same arithmetic serves the segment sums and the
 // token-by-token search, so both see identical values.
-__device__ __forceinline__ void weights8(const RowCtx& r, int64_t e, int64_t V, const float* x, const float* y,
+__device__ __forceinline__ void weights8(const RowCtx& r, int64_t e, int64_t V, const float* x_in, const float* y,
                                          const int32_t* seen, const float* seen_a, int n_seen, float* w,
                                          float* pv) {
+  float x[8];   // the target logits, disallowed ones (vocab mask) at -inf
+  const uint32_t mb = r.mt && e < V ? mask_bits8(r.mt, e, r.mw) : ~0u;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) x[j] = (mb >> j) & 1u ? x_in[j] : -INFINITY;
   if (r.xq) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -202,6 +209,8 @@ __global__ __launch_bounds__(kThreads) void k_draw(VerifyParams p) {
   RowCtx r;
   r.xt = static_cast<const DT*>(p.target) + int64_t(d.row_t) * p.V;
   r.xq = d.row_q >= 0 && p.draft ? static_cast<const DT*>(p.draft) + int64_t(d.row_q) * p.V : nullptr;
+  r.mt = p.mask ? p.mask + int64_t(d.row_t) * p.mask_words : nullptr;
+  r.mw = p.mask_words;
   r.coef = p.coef;
   r.m_t = d.m_t;
   r.inv_zt = 1.f / d.z_t;

@@ -178,6 +178,8 @@ struct VerifyParams {
   int32_t S2, spc, n_seg;     // draw pass: workgroups per request, segments per workgroup, segments per row
   float coef;                 // log2(e) / temperature (sampling modes)
   int32_t tree;               // 1: tree verify (rows node-major, B * L of them)
+  const uint32_t* mask;       // vocab mask of the target rows, [rows, mask_words], or NULL
+  int64_t mask_words;         // ceil(V / 32)
 };
 
 struct CommitParams {
@@ -204,6 +206,8 @@ hipError_t launch_stats(int dtype, int mode, const VerifyParams& p, hipStream_t 
 hipError_t launch_scan(int dtype, const VerifyParams& p, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
 hipError_t launch_draw(int dtype, int mode, const VerifyParams& p, hipStream_t stream, hipEvent_t ev0,
                        hipEvent_t ev1);
+// The second kernel of a sample-then-match call: per request, one sample per row and the match scan.
+hipError_t launch_match(int dtype, const VerifyParams& p, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
 hipError_t launch_commit(const spec_commit_args& a, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
 hipError_t launch_plan(const spec_plan_args& a, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
 hipError_t launch_cap_trim(const spec_cap_trim_args& a, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);

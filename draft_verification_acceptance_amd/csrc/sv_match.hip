@@ -1,0 +1,328 @@
+// k_match: the second kernel of a sample-then-match verify. Every target row j draws its own token t_j from
+// p_j by inverse CDF with its uniform; d_{j+1} is accepted while it equals t_j, and the first mismatch (or
+// row m) emits t_j ([DFlash] decode loop, step 4: compare each draft token with a sample of the posterior,
+// longest matching prefix, the first mismatch replaced by the posterior's sample; [EAGLE→DFlash2] §1.2:
+// independent target sampling then prefix matching is a different implementation from p/q rejection).
+//
+// One workgroup of 1024 threads per request, one wave per row, 16 rows at a time in row order; the request
+// stops after the first group of rows that holds a mismatch. A draw does not read the whole row: the
+// stream's partials give every vocab chunk's mass z_c 2^(m_c - m), so the chunk holding u * Z is known at
+// once; the wave then narrows that chunk down (each lane sums a contiguous range of it in float64, a wave
+// scan picks the lane whose range holds the target, and so on until a lane holds at most 8 tokens). Only
+// that chunk of the row is read (about 16 KB at a 152k vocab); the narrower levels hit the cache.
+#include "sv_scan.h"
+
+namespace sv {
+
+namespace {
+
+constexpr int kMatchThreads = 1024;
+constexpr int kMatchWaves = kMatchThreads / kWave;
+// 8-token runs in flight per lane while a range is summed (32 VGPRs of raw words for either type)
+template <typename DT>
+constexpr int sum_unroll() {
+  return sizeof(DT) == 2 ? 6 : 4;
+}
+
+// Raw bits of the logits of tokens [e, e + 8) of a row (bf16: one 16-byte word, fp32: two), -inf from `end`
+// on: vector loads when the run is whole and aligned, element by element otherwise. Plain (cached) loads:
+// the narrower levels of a draw read the same bytes again.
+struct Raw8 {
+  uint4 a, b;
+};
+
+template <typename DT>
+__device__ __forceinline__ void load_raw8(const DT* row, int e, int end, Raw8& w) {
+  if (e + 8 <= end && (reinterpret_cast<uintptr_t>(row + e) & 15) == 0) {
+    const uint4* vp = reinterpret_cast<const uint4*>(row + e);
+    w.a = vp[0];
+    if (sizeof(DT) == 4) w.b = vp[1];
+    return;
+  }
+  uint32_t v[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if (sizeof(DT) == 2) v[j] = e + j < end ? uint32_t(reinterpret_cast<const uint16_t*>(row)[e + j]) : 0xFF80u;
+    else v[j] = e + j < end ? __float_as_uint(reinterpret_cast<const float*>(row)[e + j]) : 0xFF800000u;
+  }
+  if (sizeof(DT) == 2) {
+    w.a = make_uint4(v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16), v[6] | (v[7] << 16));
+  } else {
+    w.a = make_uint4(v[0], v[1], v[2], v[3]);
+    w.b = make_uint4(v[4], v[5], v[6], v[7]);
+  }
+}
+
+// The weights exp2(x * coef - m) of the run at e (0 where the vocab mask disallows or past the row).
+template <typename DT>
+__device__ __forceinline__ void weights8(const Raw8& r, int e, float coef, float m, const uint32_t* mrow, int64_t mw,
+                                         float* w) {
+  float x[8];
+  Elem<DT>::unpack(r.a, x);
+  if (sizeof(DT) == 4) Elem<DT>::unpack(r.b, x + 4);
+  const uint32_t mb = mrow ? mask_bits8(mrow, e, mw) : ~0u;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) w[j] = (mb >> j) & 1u ? exp2_fast(fmaf(x[j], coef, -m)) : 0.f;
+}
+
+// Sum of the weights of tokens [la, lb), ascending, in float64 (sum_unroll runs in flight).
+template <typename DT>
+__device__ double range_sum(const DT* row, int la, int lb, float coef, float m, const uint32_t* mrow, int64_t mw) {
+  constexpr int kSumUnroll = sum_unroll<DT>();
+  double s = 0.0;
+  for (int e0 = la; e0 < lb; e0 += 8 * kSumUnroll) {
+    Raw8 r[kSumUnroll];
+#pragma unroll
+    for (int u = 0; u < kSumUnroll; ++u)
+      if (e0 + 8 * u < lb) load_raw8<DT>(row, e0 + 8 * u, lb, r[u]);
+#pragma unroll
+    for (int u = 0; u < kSumUnroll; ++u) {
+      const int e = e0 + 8 * u;
+      if (e >= lb) break;
+      float w[8];
+      weights8<DT>(r[u], e, coef, m, mrow, mw, w);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) s += double(w[j]);
+    }
+  }
+  return s;
+}
+
+// Inverse-CDF draw inside tokens [a, a + n) of a row (one wave, every lane active): t = the target mass
+// measured from a. Returns the token (the first whose cumulative weight exceeds t; if rounding leaves t past
+// the range, the last token with positive weight); cum = the mass before it, measured from a; w_tok = its
+// weight.
+template <typename DT>
+__device__ int wave_draw(const DT* row, int a, int n, double t, float coef, float m, const uint32_t* mrow, int64_t mw,
+                         double& cum, double& w_tok) {
+  const int lane = lane_id();
+  cum = 0.0;
+  w_tok = 0.0;
+  while (n > 0) {
+    int per = (n + kWave - 1) / kWave;
+    if (per > 8) per = (per + 7) / 8 * 8;   // 8-token runs stay 16-byte aligned
+    const int la = a + min(n, lane * per);
+    const int lb = a + min(n, (lane + 1) * per);
+    float wl[8];
+    double s = 0.0;
+    if (per <= 8) {
+      if (la < lb) {
+        Raw8 r;
+        load_raw8<DT>(row, la, lb, r);
+        weights8<DT>(r, la, coef, m, mrow, mw, wl);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) wl[j] = 0.f;
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) s += double(wl[j]);
+    } else {
+      s = range_sum<DT>(row, la, lb, coef, m, mrow, mw);
+    }
+    const double incl = wave_inclusive_sum(s);
+    const double excl = incl - s;
+    const uint64_t hit = __ballot(s > 0.0 && t < incl);
+    int f;
+    if (hit) {
+      f = __ffsll((unsigned long long)hit) - 1;
+    } else {
+      const uint64_t pos = __ballot(s > 0.0);
+      f = pos ? 63 - __clzll((long long)pos) : 0;
+    }
+    const double ex_f = __shfl(excl, f);
+    t -= ex_f;
+    cum += ex_f;
+    if (per <= 8) {
+      // lane f holds the token among its (at most 8) weights
+      int pick = 0;
+      double before = 0.0, wp = 0.0;
+      if (lane == f) {
+        int first = -1, last = -1;
+        double acc = 0.0, b_first = 0.0, b_last = 0.0, w_first = 0.0, w_last = 0.0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const double wj = double(wl[j]);
+          if (wj > 0.0) {
+            if (first < 0 && t < acc + wj) { first = j; b_first = acc; w_first = wj; }
+            last = j;
+            b_last = acc;
+            w_last = wj;
+          }
+          acc += wj;
+        }
+        if (first >= 0) { pick = first; before = b_first; wp = w_first; }
+        else if (last >= 0) { pick = last; before = b_last; wp = w_last; }
+      }
+      const int tok = __shfl(la + pick, f);
+      cum += __shfl(before, f);
+      w_tok = __shfl(wp, f);
+      return tok;
+    }
+    a = __shfl(la, f);
+    n = __shfl(lb, f) - a;
+  }
+  return a;
+}
+
+template <typename DT>
+__global__ __launch_bounds__(kMatchThreads) void k_match(VerifyParams p) {
+  __shared__ int32_t s_d[kMaxLen];     // d_{j+1} per row j < m
+  __shared__ int32_t s_t[kMaxLen];     // the sample t_j of row j
+  __shared__ float s_u[kMaxLen];       // sanitized uniform of row j
+  __shared__ float s_m[kMaxLen];       // merged row max (log2 units)
+  __shared__ float s_z[kMaxLen];       // merged row normaliser
+  __shared__ float s_g[kMaxLen];       // row j's logit at d_{j+1} (gathered while streaming)
+  __shared__ uint8_t s_near[kMaxLen];
+  __shared__ uint32_t s_flags;
+  __shared__ int s_r, s_stop;
+
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wv = tid / kWave;
+  int64_t off0, len64;
+  if (!chain_request(p, b, off0, len64)) {
+    if (tid == 0) write_bad_offsets(p, b);
+    return;
+  }
+  const int len = int(len64);
+  const int m = len - 1;
+  const int64_t dr0 = off0 - b;
+  const int S = p.S;
+  const Part* gp = p.part + size_t(b) * p.L * S;   // P = 1: target rows only
+
+  // Load round: per row its draft token, uniform and merged partials.
+  if (tid == 0) {
+    s_flags = 0;
+    s_r = m;
+    s_stop = 0;
+  }
+  __syncthreads();
+  uint32_t fl = 0;
+  for (int j = tid; j < len; j += kMatchThreads) {
+    const int32_t d = j < m ? p.draft_tokens[dr0 + j] : -1;
+    const float u_raw = j < m ? p.u_accept[dr0 + j] : p.u_final[b];
+    const RowStats r = merge_sampling(ReqParts{nullptr, gp, true}, j * S, S);
+    if (j < m && !(d >= 0 && int64_t(d) < p.V)) fl |= SPEC_ST_BAD_TOKEN;
+    bool ubad = false;
+    s_u[j] = sanitize_u(u_raw, ubad);
+    if (ubad) fl |= SPEC_ST_BAD_UNIFORM;
+    if (z_bad(r.z)) fl |= SPEC_ST_NONFINITE;
+    s_d[j] = d;
+    s_m[j] = r.m;
+    s_z[j] = r.z;
+    s_g[j] = r.g;
+  }
+  if (fl) atomicOr(&s_flags, fl);
+  __syncthreads();
+
+  for (int j0 = 0; j0 < len; j0 += kMatchWaves) {
+    const int j = j0 + wv;
+    if (j < len) {
+      // Chunk masses z_c 2^(m_c - m) in float64 (lane c), their total and the chunk holding u * Z.
+      const float M = s_m[j];
+      const Part* rp = gp + size_t(j) * S;
+      double Z = 0.0;
+      for (int c0 = 0; c0 < S; c0 += kWave) {
+        const int c = c0 + lane;
+        double mass = 0.0;
+        if (c < S) {
+          const Part pt = load_part(rp + c, true);
+          if (pt.b > 0.f) mass = double(pt.b) * exp2(double(pt.a) - double(M));
+        }
+        Z += wave_sum(mass);
+      }
+      const double T = double(s_u[j]) * Z;
+      int csel = -1, clast = -1;
+      double cum0 = 0.0, cum_last = 0.0, carry = 0.0;
+      for (int c0 = 0; c0 < S && csel < 0; c0 += kWave) {
+        const int c = c0 + lane;
+        double mass = 0.0;
+        if (c < S) {
+          const Part pt = load_part(rp + c, true);
+          if (pt.b > 0.f) mass = double(pt.b) * exp2(double(pt.a) - double(M));
+        }
+        const double incl = carry + wave_inclusive_sum(mass);
+        const uint64_t hit = __ballot(mass > 0.0 && T < incl);
+        if (hit) {
+          const int f = __ffsll((unsigned long long)hit) - 1;
+          csel = c0 + f;
+          cum0 = __shfl(incl - mass, f);
+        }
+        const uint64_t pos = __ballot(mass > 0.0);
+        if (pos) {
+          const int f = 63 - __clzll((long long)pos);
+          clast = c0 + f;
+          cum_last = __shfl(incl - mass, f);
+        }
+        carry = __shfl(incl, kWave - 1);
+      }
+      if (csel < 0) {   // rounding left u * Z past every chunk (or nothing has mass)
+        csel = clast < 0 ? 0 : clast;
+        cum0 = clast < 0 ? 0.0 : cum_last;
+      }
+      const int a = int(int64_t(csel) * p.chunk);
+      const int n = int(min(p.V, int64_t(csel + 1) * p.chunk)) - a;
+      const DT* row = static_cast<const DT*>(p.target) + (off0 + j) * p.V;
+      const uint32_t* mrow = p.mask ? p.mask + (off0 + j) * p.mask_words : nullptr;
+      double cum1, w_tok;
+      const int tok = wave_draw<DT>(row, a, n, T - cum0, p.coef, M, mrow, p.mask_words, cum1, w_tok);
+      if (lane == 0) {
+        // Too close to call: u within 1e-5 of a step of the normalised CDF.
+        const double u = double(s_u[j]);
+        const double lo = (cum0 + cum1) / Z;
+        const double gap = fmin(u - lo, lo + w_tok / Z - u);
+        s_t[j] = tok;
+        s_near[j] = !(gap >= double(kNear));
+      }
+    }
+    __syncthreads();
+    if (tid == 0) {
+      for (int jj = j0; jj < min(len, j0 + kMatchWaves); ++jj) {
+        const int32_t d = s_d[jj];
+        if (jj == m || !(d >= 0 && int64_t(d) < p.V && d == s_t[jj])) {
+          s_r = jj;
+          s_stop = 1;
+          break;
+        }
+      }
+    }
+    __syncthreads();
+    if (s_stop) break;
+  }
+
+  const int r = s_r;
+  const int32_t bonus = s_t[r];
+  uint32_t near = 0;
+  for (int k = tid; k < len; k += kMatchThreads) {
+    p.out_tokens[off0 + k] = k < r ? s_d[k] : (k == r ? bonus : -1);
+    p.accept_index[off0 + k] = k <= r ? int32_t(off0 + k) : -1;
+    if (k <= r && s_near[k]) near = SPEC_ST_NEAR_CDF;
+    if (k < m && p.accept_prob) {
+      // p_k(d_{k+1}) where compared: the same fp32 arithmetic as the rejection scans
+      const int32_t d = s_d[k];
+      float pk = -1.f;
+      if (k <= r) pk = d >= 0 && int64_t(d) < p.V ? exp2_fast(fmaf(s_g[k], p.coef, -s_m[k])) / s_z[k] : 0.f;
+      p.accept_prob[dr0 + k] = pk;
+    }
+  }
+  if (near) atomicOr(&s_flags, near);
+  __syncthreads();
+  if (tid == 0) {
+    p.accept_len[b] = r;
+    p.bonus[b] = bonus;
+    p.status[b] = s_flags;
+    if (p.residual_mass) p.residual_mass[b] = -1.f;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_match(int dtype, const VerifyParams& p, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+  if (p.B <= 0) return hipSuccess;
+  const dim3 grid{unsigned(p.B)}, block{unsigned(kMatchThreads)};
+  if (dtype == SPEC_DTYPE_BF16) return launch_kernel(k_match<uint16_t>, grid, block, 0, stream, ev0, ev1, p);
+  return launch_kernel(k_match<float>, grid, block, 0, stream, ev0, ev1, p);
+}
+
+}  // namespace sv

@@ -180,6 +180,7 @@ __device__ void scan_chain_greedy(const VerifyParams& p, int b, int64_t off0, in
     const Part r = merge_greedy(rp, j * p.S, p.S);
     s_arg[j] = r.idx;
     if (r.flags & kPartNaN) fl |= SPEC_ST_NONFINITE;
+    if (p.mask && r.a == -INFINITY) fl |= SPEC_ST_NONFINITE;   // the mask left no finite logit
     if (j < m) {   // test of d_{j+1} against row j
       const int32_t d = s_d[j];
       const bool ok = d >= 0 && int64_t(d) < p.V;
@@ -389,6 +390,7 @@ __device__ DrawPlan scan_tree(const VerifyParams& p, int b, char* smem, Part* st
       const Part r = merge_greedy(rp, i * p.S, p.S);
       s_arg[i] = r.idx;
       if (r.flags & kPartNaN) fl |= SPEC_ST_NONFINITE;
+      if (p.mask && r.a == -INFINITY) fl |= SPEC_ST_NONFINITE;   // the mask left no finite logit
     }
     const int32_t par = s_par[i];
     const int32_t tok = s_tok[i];
@@ -413,7 +415,8 @@ __device__ DrawPlan scan_tree(const VerifyParams& p, int b, char* smem, Part* st
       const int32_t tok = s_tok[i];
       float pv = 0.f;
       if (i > 0 && par >= 0 && tok >= 0) {
-        const float g = Elem<DT>::load(static_cast<const DT*>(p.target) + (base + par) * p.V, tok);
+        float g = Elem<DT>::load(static_cast<const DT*>(p.target) + (base + par) * p.V, tok);
+        if (p.mask && !mask_allows(p.mask + (base + par) * p.mask_words, tok)) g = -INFINITY;
         pv = exp2_fast(fmaf(g, p.coef, -s_m[par])) / s_z[par];
       }
       s_pv[i] = pv;

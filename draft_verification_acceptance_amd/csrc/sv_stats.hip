@@ -9,6 +9,8 @@
 //             ([EAGLE→DFlash2] §1.2: p_j and q_j are the distributions actually used), and for a chain the
 //             logit at the token the row judges; sparse q ([EAGLE→DFlash2] §6.5): also q(d) from the draft
 //             row's candidates.
+// A vocab mask ([EAGLE→DFlash2] §5.6.6, §8.4: applied to the target logits after the forward, before
+// acceptance) turns the disallowed logits of a target row into -inf as they stream.
 #include "sv_scan.h"
 
 namespace sv {
@@ -42,28 +44,38 @@ __device__ __forceinline__ Split split_chunk(const DT* row, int64_t lo, int64_t 
 // unaligned head and tail elements (rows whose byte offset is not a multiple of 16) are loaded before the
 // stream and folded in after it.
 
-// Greedy partial of row[lo, hi) reduced over the workgroup (result valid in thread 0).
-template <typename DT>
+// Greedy partial of row[lo, hi) reduced over the workgroup (result valid in thread 0). MASK: the row's vocab
+// mask `mrow` (nw words) turns disallowed logits into -inf as they are unpacked (one 4-byte mask load per
+// 16-byte logits load, issued with it).
+template <typename DT, bool MASK>
 __device__ __forceinline__ void chunk_argmax(const DT* __restrict__ row, int64_t lo, int64_t hi, Part& out,
-                                             float* red_f, int* red_i, uint32_t* red_u) {
+                                             float* red_f, int* red_i, uint32_t* red_u, const uint32_t* mrow,
+                                             int64_t nw) {
   constexpr int E = Elem<DT>::kPerVec;
   const int tid = threadIdx.x;
   const Split sp = split_chunk(row, lo, hi);
   const uint4* __restrict__ vp = reinterpret_cast<const uint4*>(row + sp.body_lo);
   const bool has_h = tid < sp.head;
   const bool has_t = tid < hi - sp.body_hi;
-  const float vh = has_h ? Elem<DT>::load(row, lo + tid) : 0.f;
-  const float vt = has_t ? Elem<DT>::load(row, sp.body_hi + tid) : 0.f;
+  float vh = has_h ? Elem<DT>::load(row, lo + tid) : 0.f;
+  float vt = has_t ? Elem<DT>::load(row, sp.body_hi + tid) : 0.f;
+  if (MASK && has_h && !mask_allows(mrow, lo + tid)) vh = -INFINITY;
+  if (MASK && has_t && !mask_allows(mrow, sp.body_hi + tid)) vt = -INFINITY;
 
   // Per thread: the largest vector maximum, the first vector attaining it and that vector's raw bits (the
   // lowest index inside it is recovered at the end without another load).
   float best = -INFINITY;
   int64_t bestk = -1;
   uint4 bestq = make_uint4(0u, 0u, 0u, 0u);
+  uint32_t bestmb = ~0u;
   bool nan = false;
-  auto consume = [&](const uint4& qv, int64_t kk) {
+  auto consume = [&](const uint4& qv, int64_t kk, uint32_t mb) {
     float x[E];
     Elem<DT>::unpack(qv, x);
+    if (MASK) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) x[e] = (mb >> e) & 1u ? x[e] : -INFINITY;
+    }
     float vm = x[0];
 #pragma unroll
     for (int e = 1; e < E; ++e) vm = fmaxf(vm, x[e]);
@@ -73,29 +85,41 @@ __device__ __forceinline__ void chunk_argmax(const DT* __restrict__ row, int64_t
       best = vm;
       bestk = kk;
       bestq = qv;
+      bestmb = mb;
     }
   };
   int64_t k = tid;
   for (; k + (kUnroll - 1) * NT < sp.nvec; k += kUnroll * NT) {
     uint4 q[kUnroll];
+    uint32_t mb[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) q[u] = load_stream(vp + k + u * NT);
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) consume(q[u], k + u * NT);
+    for (int u = 0; u < kUnroll; ++u) mb[u] = MASK ? mask_bits8(mrow, sp.body_lo + (k + u * NT) * E, nw) : ~0u;
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) consume(q[u], k + u * NT, mb[u]);
   }
   if (k < sp.nvec) {
     uint4 q[kUnroll];
+    uint32_t mb[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u)
       q[u] = k + u * NT < sp.nvec ? load_stream(vp + k + u * NT) : make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u)
-      if (k + u * NT < sp.nvec) consume(q[u], k + u * NT);
+      mb[u] = MASK && k + u * NT < sp.nvec ? mask_bits8(mrow, sp.body_lo + (k + u * NT) * E, nw) : ~0u;
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+      if (k + u * NT < sp.nvec) consume(q[u], k + u * NT, mb[u]);
   }
   int32_t idx = INT32_MAX;
   if (bestk >= 0) {  // lowest index of the thread's maximum inside its winning vector
     float x[E];
     Elem<DT>::unpack(bestq, x);
+    if (MASK) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) x[e] = (bestmb >> e) & 1u ? x[e] : -INFINITY;
+    }
 #pragma unroll
     for (int e = E - 1; e >= 0; --e)
       if (x[e] == best) idx = int32_t(sp.body_lo + bestk * E + e);
@@ -149,18 +173,21 @@ __device__ __forceinline__ void single_mz(float x, float coef, float& m2, float&
   else if (m2 == INFINITY) z2 = __builtin_nanf("");
 }
 
-// Sampling partial of row[lo, hi): (m, z) with m in log2 units, reduced over the workgroup (thread 0).
-template <typename DT>
+// Sampling partial of row[lo, hi): (m, z) with m in log2 units, reduced over the workgroup (thread 0). MASK as
+// for chunk_argmax.
+template <typename DT, bool MASK>
 __device__ __forceinline__ void chunk_lse(const DT* __restrict__ row, int64_t lo, int64_t hi, float coef, Part& out,
-                                          float* red_f, float* red_g) {
+                                          float* red_f, float* red_g, const uint32_t* mrow, int64_t nw) {
   constexpr int E = Elem<DT>::kPerVec;
   const int tid = threadIdx.x;
   const Split sp = split_chunk(row, lo, hi);
   const uint4* __restrict__ vp = reinterpret_cast<const uint4*>(row + sp.body_lo);
   const bool has_h = tid < sp.head;
   const bool has_t = tid < hi - sp.body_hi;
-  const float vh = has_h ? Elem<DT>::load(row, lo + tid) : 0.f;
-  const float vt = has_t ? Elem<DT>::load(row, sp.body_hi + tid) : 0.f;
+  float vh = has_h ? Elem<DT>::load(row, lo + tid) : 0.f;
+  float vt = has_t ? Elem<DT>::load(row, sp.body_hi + tid) : 0.f;
+  if (MASK && has_h && !mask_allows(mrow, lo + tid)) vh = -INFINITY;
+  if (MASK && has_t && !mask_allows(mrow, sp.body_hi + tid)) vt = -INFINITY;
 
   float m = -INFINITY, z = 0.f;
   // Online update with kUnroll vectors: one rescale of z per trip.
@@ -175,25 +202,42 @@ __device__ __forceinline__ void chunk_lse(const DT* __restrict__ row, int64_t lo
 #pragma unroll
     for (int e = 0; e < kUnroll * E; ++e) z += exp2_fast(fmaf(x[e], coef, nm));
   };
+  auto apply_mask = [&](float* xv, uint32_t mb) {
+    if (MASK) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) xv[e] = (mb >> e) & 1u ? xv[e] : -INFINITY;
+    }
+  };
   int64_t k = tid;
   for (; k + (kUnroll - 1) * NT < sp.nvec; k += kUnroll * NT) {
     uint4 q[kUnroll];
+    uint32_t mb[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) q[u] = load_stream(vp + k + u * NT);
-    float x[kUnroll * E];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) Elem<DT>::unpack(q[u], x + u * E);
-    consume(x);
-  }
-  if (k < sp.nvec) {
-    uint4 q[kUnroll];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u)
-      q[u] = k + u * NT < sp.nvec ? load_stream(vp + k + u * NT) : make_uint4(0u, 0u, 0u, 0u);
+    for (int u = 0; u < kUnroll; ++u) mb[u] = MASK ? mask_bits8(mrow, sp.body_lo + (k + u * NT) * E, nw) : ~0u;
     float x[kUnroll * E];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       Elem<DT>::unpack(q[u], x + u * E);
+      apply_mask(x + u * E, mb[u]);
+    }
+    consume(x);
+  }
+  if (k < sp.nvec) {
+    uint4 q[kUnroll];
+    uint32_t mb[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+      q[u] = k + u * NT < sp.nvec ? load_stream(vp + k + u * NT) : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+      mb[u] = MASK && k + u * NT < sp.nvec ? mask_bits8(mrow, sp.body_lo + (k + u * NT) * E, nw) : ~0u;
+    float x[kUnroll * E];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      Elem<DT>::unpack(q[u], x + u * E);
+      apply_mask(x + u * E, mb[u]);
       if (!(k + u * NT < sp.nvec)) {   // past the chunk: contributes nothing
 #pragma unroll
         for (int e = 0; e < E; ++e) x[u * E + e] = -INFINITY;
@@ -236,7 +280,7 @@ __device__ __forceinline__ void chunk_lse(const DT* __restrict__ row, int64_t lo
 // ---------------------------------------------------------------------------------------------------
 // The logits stream.
 // ---------------------------------------------------------------------------------------------------
-template <typename DT, bool SAMPLING, bool TREE>
+template <typename DT, bool SAMPLING, bool TREE, bool MASK>
 __global__ __launch_bounds__(NT) void k_stats(VerifyParams p) {
   __shared__ float red_f[kW];
   __shared__ float red_g[kW];
@@ -272,6 +316,8 @@ __global__ __launch_bounds__(NT) void k_stats(VerifyParams p) {
   const int64_t hi = lo + p.chunk < p.V ? lo + p.chunk : p.V;
   const int64_t row = part == 0 ? off0 + slot : off0 - b + slot;
   const DT* base = static_cast<const DT*>(part == 0 ? p.target : p.draft) + row * p.V;
+  // The vocab mask applies to target rows only.
+  const uint32_t* mrow = MASK && part == 0 ? p.mask + row * p.mask_words : nullptr;
 
   // Chain sampling: row `slot` (target or draft) judges d_{slot+1}. The chunk holding that token reads the
   // logit there while the row streams (one thread), so the request scan needs no gathers of its own.
@@ -282,6 +328,7 @@ __global__ __launch_bounds__(NT) void k_stats(VerifyParams p) {
     const int32_t d = p.draft_tokens[off0 - b + slot];
     if (d >= lo && d < hi) {
       gv = Elem<DT>::load(base, d);
+      if (MASK && mrow && !mask_allows(mrow, d)) gv = -INFINITY;
       gf = kPartGathered;
     }
   }
@@ -306,8 +353,13 @@ __global__ __launch_bounds__(NT) void k_stats(VerifyParams p) {
     qf = (__ballot(f & kPartBadCandId) ? kPartBadCandId : 0u) | (__ballot(f & kPartBadCandQ) ? kPartBadCandQ : 0u);
   }
 
-  if (SAMPLING) chunk_lse<DT>(base, lo, hi, p.coef, s_part, red_f, red_g);
-  else chunk_argmax<DT>(base, lo, hi, s_part, red_f, red_i, red_u);
+  if (MASK && mrow) {
+    if (SAMPLING) chunk_lse<DT, true>(base, lo, hi, p.coef, s_part, red_f, red_g, mrow, p.mask_words);
+    else chunk_argmax<DT, true>(base, lo, hi, s_part, red_f, red_i, red_u, mrow, p.mask_words);
+  } else {
+    if (SAMPLING) chunk_lse<DT, false>(base, lo, hi, p.coef, s_part, red_f, red_g, nullptr, 0);
+    else chunk_argmax<DT, false>(base, lo, hi, s_part, red_f, red_i, red_u, nullptr, 0);
+  }
 
   if (SAMPLING) {
     if (threadIdx.x == NT - 1) {
@@ -355,12 +407,20 @@ hipError_t launch_stats_t(int mode, const VerifyParams& p, hipStream_t stream, h
   if (blocks <= 0) return hipSuccess;
   const bool sampling = mode != SPEC_MODE_GREEDY;
   const dim3 grid{unsigned(blocks)}, block{unsigned(NT)};
-  if (p.tree) {
-    if (sampling) return launch_kernel(k_stats<DT, true, true>, grid, block, 0, stream, ev0, ev1, p);
-    return launch_kernel(k_stats<DT, false, true>, grid, block, 0, stream, ev0, ev1, p);
+  if (p.mask) {
+    if (p.tree) {
+      if (sampling) return launch_kernel(k_stats<DT, true, true, true>, grid, block, 0, stream, ev0, ev1, p);
+      return launch_kernel(k_stats<DT, false, true, true>, grid, block, 0, stream, ev0, ev1, p);
+    }
+    if (sampling) return launch_kernel(k_stats<DT, true, false, true>, grid, block, 0, stream, ev0, ev1, p);
+    return launch_kernel(k_stats<DT, false, false, true>, grid, block, 0, stream, ev0, ev1, p);
   }
-  if (sampling) return launch_kernel(k_stats<DT, true, false>, grid, block, 0, stream, ev0, ev1, p);
-  return launch_kernel(k_stats<DT, false, false>, grid, block, 0, stream, ev0, ev1, p);
+  if (p.tree) {
+    if (sampling) return launch_kernel(k_stats<DT, true, true, false>, grid, block, 0, stream, ev0, ev1, p);
+    return launch_kernel(k_stats<DT, false, true, false>, grid, block, 0, stream, ev0, ev1, p);
+  }
+  if (sampling) return launch_kernel(k_stats<DT, true, false, false>, grid, block, 0, stream, ev0, ev1, p);
+  return launch_kernel(k_stats<DT, false, false, false>, grid, block, 0, stream, ev0, ev1, p);
 }
 
 }  // namespace

@@ -457,6 +457,56 @@ def tree_round_inputs(seed: int = 8000, batch: int = 32, steps: int = 8, topk: i
                            np.array(dst, np.int32), r2t, n_slots)
 
 
+def block_sample(seed: int = 7000, batch: int = 32, block: int = 16, vocab: int = QWEN_VOCAB,
+                 temperature: float = 1.0, parallel: bool = True) -> ChainWorkload:
+    """DFlash-shaped sampling verify for sample-then-match: B 32, block 16 (anchor + 15 drafts), V 151,936,
+    bf16 target rows 3 N(0,1) with one token raised by U(14, 20) (its probability at T = 1 then spans about
+    0.1 .. 0.97, a peaked next-token distribution); the draft proposes that token with probability 0.8 and a
+    uniform token otherwise. Uniforms U[0,1) float32 per row (u_accept for rows 0..14, u_final for row 15)."""
+    kids = np.random.SeedSequence(seed).spawn(batch + 1)
+    m = block - 1
+    offsets = (np.arange(batch + 1) * block).astype(np.int32)
+    T = batch * block
+    target = np.empty((T, vocab), np.uint16)
+    tokens = np.empty(batch * m, np.int32)
+    u_acc = np.empty(batch * m, np.float32)
+    u_fin = np.empty(batch, np.float32)
+
+    def one(b):
+        s_logit, s_tok, s_unif = [np.random.Generator(np.random.PCG64(s)) for s in kids[b + 1].spawn(3)]
+        x = s_logit.standard_normal((block, vocab), dtype=np.float32) * np.float32(3.0)
+        top = s_logit.integers(0, vocab, block)
+        x[np.arange(block), top] += s_logit.uniform(14.0, 20.0, block).astype(np.float32)
+        target[b * block:(b + 1) * block] = bf16_bits(x)
+        pick = s_tok.random(m) < 0.8
+        tokens[b * m:(b + 1) * m] = np.where(pick, top[:m], s_tok.integers(0, vocab, m))
+        u_acc[b * m:(b + 1) * m] = s_unif.random(m, dtype=np.float32)
+        u_fin[b] = s_unif.random(dtype=np.float32)
+
+    _pool_map(one, range(batch), parallel)
+    return ChainWorkload("block_sample", vocab, batch, offsets, target, None, tokens, u_acc, u_fin, temperature,
+                         ("sample_match",), block, meta={"seed": seed})
+
+
+def vocab_masks(seed: int, rows: int, vocab: int, allowed: float, keep=None) -> np.ndarray:
+    """Grammar-like vocab masks: uint32 [rows, ceil(vocab/32)], token v of row i allowed iff bit v % 32 of word
+    v // 32 is set. Each token is allowed with probability `allowed`; keep[i] (an int or a list of ints, -1
+    ignored) lists tokens forced allowed in row i (a grammar usually admits what the model predicts)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    W = (vocab + 31) // 32
+    out = np.empty((rows, W), np.uint32)
+    for i in range(rows):
+        bits = rng.random(W * 32, dtype=np.float32) < np.float32(allowed)
+        bits[vocab:] = False
+        if keep is not None:
+            for k in np.atleast_1d(keep[i]):
+                if 0 <= int(k) < vocab:
+                    bits[int(k)] = True
+        # little bit order: bit j of byte k is token 8k + j, so little-endian word w holds tokens 32w .. 32w+31
+        out[i] = np.packbits(bits, bitorder="little").view("<u4")
+    return out
+
+
 # Full-size workloads (name -> builder); each builder's defaults are the full shapes.
 FULL = {
     "tiny_chain": tiny_chain,
@@ -465,4 +515,5 @@ FULL = {
     "tree": tree,
     "ragged": ragged,
     "chain_sparse": chain_sparse,
+    "block_sample": block_sample,
 }

@@ -44,7 +44,7 @@ extern "C" {
 typedef struct ihipStream_t* hipStream_t;
 typedef struct ihipEvent_t* hipEvent_t;
 
-#define SPEC_ABI_VERSION 5
+#define SPEC_ABI_VERSION 6
 
 /* Host-visible return codes. */
 typedef enum spec_status {
@@ -81,12 +81,28 @@ typedef enum spec_dtype { SPEC_DTYPE_F32 = 0, SPEC_DTYPE_BF16 = 1 } spec_dtype;
  *                outside the candidates remain reachable ([EAGLE→DFlash2] §6.5, sampling verify with the
  *                selector's q; greedy rows carry a one-hot q, i.e. K = 1 with probability 1). A repeated id
  *                adds its masses. The temperature divides the target logits only.
+ *   SAMPLE_MATCH chain only: sample-then-match. Every target row j draws its own token t_j from p_j =
+ *                softmax(logits / temperature) by inverse CDF (row j < m with u_accept of d_{j+1}, row m with
+ *                u_final); d_{j+1} is accepted while it equals t_j, and the first mismatch (or row m) emits t_j.
+ *                Every emitted token is a draw from its row's p. [DFlash] decode loop step 4 (compare each
+ *                draft token with a sample of the posterior, longest matching prefix, first mismatch replaced
+ *                by the posterior sample); [EAGLE→DFlash2] §1.2 (independent target sampling then prefix
+ *                matching is a different implementation from p/q rejection). accept_prob reports p_j(d_{j+1})
+ *                at the compared positions; residual_mass is -1 (no residual).
+ *
+ * Vocab (grammar) mask, every mode, optional: `vocab_mask` holds ceil(vocab/32) 32-bit words per target
+ * row; token v of a row is allowed iff bit (v % 32) of word v / 32 is 1. A masked logit counts as -inf
+ * whatever its value (before temperature, softmax and argmax); draft rows are not masked.
+ * [EAGLE→DFlash2] §5.6.6 (the grammar mask is applied after the target forward, before acceptance) and
+ * §8.4 (sampling reads the distribution after the mask). A row that leaves no token with a finite logit
+ * sets SPEC_ST_NONFINITE in every mode.
  */
 typedef enum spec_mode {
   SPEC_MODE_GREEDY = 0,
   SPEC_MODE_REJECTION = 1,
   SPEC_MODE_TARGET_ONLY = 2,
   SPEC_MODE_REJECTION_SPARSE = 3,
+  SPEC_MODE_SAMPLE_MATCH = 4,
 } spec_mode;
 
 typedef enum spec_kind {
@@ -127,7 +143,7 @@ typedef enum spec_kind {
                                             given tables; the entry (or the request's range) is skipped     */
 
 /*
- * Chain verify (GREEDY, REJECTION or REJECTION_SPARSE).
+ * Chain verify (GREEDY, REJECTION, REJECTION_SPARSE or SAMPLE_MATCH).
  *
  * Request b owns target rows [off[b], off[b+1]) (the ragged packing of [EAGLE→DFlash2] §5.6.5: verify
  * lens [4,2,6] -> offsets [0,4,6,12]); m_b = off[b+1] - off[b] - 1 >= 0 drafts. Draft-side arrays are
@@ -170,7 +186,8 @@ typedef struct spec_chain_args {
   int32_t max_verify_len;        /* upper bound on m_b + 1, 1..1024; a longer request is
                                     reported as SPEC_ST_BAD_OFFSETS                        */
   int32_t dtype;                 /* spec_dtype                                             */
-  int32_t mode;                  /* SPEC_MODE_GREEDY, _REJECTION or _REJECTION_SPARSE       */
+  int32_t mode;                  /* SPEC_MODE_GREEDY, _REJECTION, _REJECTION_SPARSE or
+                                    _SAMPLE_MATCH                                            */
   float temperature;             /* sampling modes: finite, > 0; logits are divided by it    */
   int32_t n_profile_events;
   /* REJECTION_SPARSE only (else NULL / 0): candidate k of draft row i sits at [i * n_cand + k]     */
@@ -178,6 +195,8 @@ typedef struct spec_chain_args {
   const float* cand_q;           /* [total_rows - batch, n_cand] their probabilities        */
   int32_t n_cand;                /* K, 1..1024                                             */
   int32_t reserved;
+  const uint32_t* vocab_mask;    /* optional [total_rows, ceil(vocab/32)] allowed-token bits of
+                                    the target rows (see "Vocab (grammar) mask"); NULL: none   */
 } spec_chain_args;
 
 /*
@@ -216,6 +235,8 @@ typedef struct spec_tree_args {
   float threshold_single;    /* TARGET_ONLY: must be 1.0 (else SPEC_EUNSUPPORTED) */
   float threshold_acc;       /* TARGET_ONLY: must be 1.0 (else SPEC_EUNSUPPORTED) */
   int32_t n_profile_events;
+  const uint32_t* vocab_mask; /* optional [batch*n_nodes, ceil(vocab/32)] allowed-token bits of
+                                 every node row; NULL: none                      */
 } spec_tree_args;
 
 /*

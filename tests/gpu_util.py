@@ -38,9 +38,16 @@ def np_out(o: dict) -> dict:
     return r
 
 
-def run_chain(w, mode, *, target=None, draft=None, ws=None, **kw):
+def dev_mask(mask):
+    """uint32 vocab mask words -> the int32 device tensor the binding takes (same bits)."""
+    return None if mask is None else dev(np.ascontiguousarray(mask, np.uint32).view(np.int32))
+
+
+def run_chain(w, mode, *, target=None, draft=None, ws=None, mask=None, **kw):
     t = dev_logits(w.target) if target is None else target
-    args = dict(max_verify_len=w.max_verify_len, workspace_tensor=ws)
+    args = dict(max_verify_len=w.max_verify_len, workspace_tensor=ws, vocab_mask=dev_mask(mask))
+    if mode == "sample_match":
+        args.update(u_accept=dev(w.u_accept), u_final=dev(w.u_final), temperature=w.temperature)
     if mode == "rejection":
         d = dev_logits(w.draft) if draft is None else draft
         args.update(draft_logits=d, u_accept=dev(w.u_accept), u_final=dev(w.u_final), temperature=w.temperature)
@@ -52,9 +59,9 @@ def run_chain(w, mode, *, target=None, draft=None, ws=None, **kw):
     return np_out(o)
 
 
-def run_tree(w, mode, *, target=None, ws=None, **kw):
+def run_tree(w, mode, *, target=None, ws=None, mask=None, **kw):
     t = dev_logits(w.target) if target is None else target
-    args = dict(workspace_tensor=ws)
+    args = dict(workspace_tensor=ws, vocab_mask=dev_mask(mask))
     if mode == "target_only":
         args.update(u_accept=dev(w.u_accept), u_final=dev(w.u_final), temperature=w.temperature)
     args.update(kw)
@@ -62,8 +69,10 @@ def run_tree(w, mode, *, target=None, ws=None, **kw):
     return np_out(o)
 
 
-def oracle_chain(w, mode, requests=None):
-    kw = dict(max_verify_len=w.max_verify_len, requests=requests)
+def oracle_chain(w, mode, requests=None, mask=None):
+    kw = dict(max_verify_len=w.max_verify_len, requests=requests, vocab_mask=mask)
+    if mode == "sample_match":
+        kw.update(u_accept=w.u_accept, u_final=w.u_final, temperature=w.temperature)
     if mode == "rejection":
         kw.update(draft=w.draft, u_accept=w.u_accept, u_final=w.u_final, temperature=w.temperature)
     elif mode == "rejection_sparse":
@@ -72,19 +81,22 @@ def oracle_chain(w, mode, requests=None):
     return oracle.verify_chain(w.target, w.offsets, w.draft_tokens, mode, **kw)
 
 
-def oracle_tree(w, mode, requests=None):
-    kw = dict(requests=requests)
+def oracle_tree(w, mode, requests=None, mask=None):
+    kw = dict(requests=requests, vocab_mask=mask)
     if mode == "target_only":
         kw.update(u_accept=w.u_accept, u_final=w.u_final, temperature=w.temperature)
     return oracle.verify_tree(w.target, w.parents, w.tokens, w.n_nodes, mode, **kw)
 
 
-def check_exempt(n_requests: int, exempt: int, identical: int, name: str):
+def check_exempt(n_requests: int, exempt: int, identical: int, name: str, any_share: bool = False):
     """Flagged draws are counted, not compared; as a sanity bound most of them still agree (the device's
-    CDF error is about 1e-6, the flag band 1e-5) and they stay a minority of the requests."""
+    CDF error is about 1e-6, the flag band 1e-5) and they stay a minority of the requests. `any_share`: a
+    mode that draws from every row (sample-then-match) meets the 1e-5 band on nearly every draw that lands
+    in a flat tail of a large vocabulary, so only the agreement bound applies."""
     print(f"{name}: {exempt}/{n_requests} requests exempt (oracle NEAR_*), {identical} of them identical",
           flush=True)
-    assert exempt <= max(2, n_requests // 2)
+    if not any_share:
+        assert exempt <= max(2, n_requests // 2)
     assert identical >= exempt // 2
 
 
@@ -132,7 +144,7 @@ def compare_chain(w, mode, o, g, requests=None):
     off = w.offsets
     ex, same = compare(o, g, lambda b: int(off[b]), lambda b: int(off[b + 1]), lambda b: int(off[b]) - b,
                        lambda b: int(off[b + 1]) - b - 1, reqs, mode != "greedy")
-    check_exempt(len(reqs), ex, same, f"{w.name}/{mode}")
+    check_exempt(len(reqs), ex, same, f"{w.name}/{mode}", any_share=mode == "sample_match")
     return ex
 
 

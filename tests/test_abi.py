@@ -32,8 +32,8 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_struct_sizes():
     lib = dva._lib()        # raises on ABI or struct-size mismatch
-    assert dva.abi_version() == 5
-    assert lib.spec_args_size(0) == ctypes.sizeof(dva.ChainArgs) == 192
+    assert dva.abi_version() == 6
+    assert lib.spec_args_size(0) == ctypes.sizeof(dva.ChainArgs) == 200
     assert lib.spec_args_size(1) == ctypes.sizeof(dva.TreeArgs)
     assert lib.spec_args_size(2) == ctypes.sizeof(dva.CommitArgs)
 
@@ -46,6 +46,7 @@ def test_status_strings_and_kernel_counts():
     assert dva.kernel_count("chain", "greedy") == 2
     assert dva.kernel_count("chain", "rejection") == 2
     assert dva.kernel_count("chain", "rejection_sparse") == 2
+    assert dva.kernel_count("chain", "sample_match") == 2
     assert dva.kernel_count("tree", "target_only") == 2
     assert dva.kernel_count("commit", "greedy") == 1
 
@@ -102,6 +103,12 @@ def test_chain_host_checks():
     assert _call_chain(_chain(**sp, n_cand=1025)) == 1
     assert _call_chain(_chain(**dict(sp, cand_q=None), n_cand=4)) == 1
     assert _call_chain(_chain(**sp, n_cand=4)) == 4                           # args fine, no workspace
+    sm = dict(full, mode=4, u_accept=fake, u_final=fake)                       # sample-then-match
+    assert _call_chain(_chain(**sm, temperature=0.0)) == 1
+    assert _call_chain(_chain(**dict(sm, u_accept=None))) == 1
+    assert _call_chain(_chain(**sm)) == 4                                     # args fine, no workspace
+    assert _call_chain(_chain(**sm, vocab_mask=fake)) == 4                    # a mask changes no check
+    assert dva.workspace_bytes("chain", "sample_match", 10, 100, 2, 5) > 0
 
 
 def test_tree_and_commit_host_checks():
@@ -111,6 +118,8 @@ def test_tree_and_commit_host_checks():
     assert lib.spec_verify_tree(ctypes.byref(a), None) == 3                   # rejection on a tree
     a.mode = 3
     assert lib.spec_verify_tree(ctypes.byref(a), None) == 3                   # sparse rejection on a tree
+    a.mode = 4
+    assert lib.spec_verify_tree(ctypes.byref(a), None) == 3                   # sample-then-match on a tree
     a.mode = 2
     a.threshold_single, a.threshold_acc = 0.9, 1.0
     assert lib.spec_verify_tree(ctypes.byref(a), None) == 3                   # thresholds other than 1.0
