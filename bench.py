@@ -13,7 +13,8 @@ roofline: the dominant kernel (k_stats, the logits stream) timed with HIP events
 stop timestamps on the launch stream (hipExtLaunchKernel), against its algorithmic bytes (every target and draft row read once). cpu_baseline: the fp64 CPU
 oracle timed on this host on the same inputs.
 
-    python bench.py [--steps K] [--warmup W] [--workload chain_rejection|block_greedy|tree|ragged|chain_sparse]
+    python bench.py [--steps K] [--warmup W]
+                    [--workload chain_rejection|block_greedy|tree|ragged|chain_sparse|block_sample|chain_rejection_masked]
                     [--no-extra] [--no-cpu-baseline] [--copy-calibration]
 """
 from __future__ import annotations
@@ -68,16 +69,40 @@ def _dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
-def build_sets(name: str):
-    """Seeded input sets (seed 1000*k + i) until the live footprint exceeds 2x the Infinity Cache."""
+def _grammar_mask(w):
+    """A grammar-like vocab mask for a chain workload: 5 % of the tokens allowed per target row, plus the
+    row's argmax and the draft token it judges (a grammar admits what the model predicts)."""
+    import numpy as np
+
     from draft_verification_acceptance_amd import workloads as W
+    keep = []
+    for b in range(w.batch):
+        lo, hi = int(w.offsets[b]), int(w.offsets[b + 1])
+        for j in range(hi - lo):
+            ks = [int(np.argmax(W.bf16_to_f32(w.target[lo + j])))]
+            if j < hi - lo - 1:
+                ks.append(int(w.draft_tokens[lo - b + j]))
+            keep.append(ks)
+    return W.vocab_masks(int(w.meta.get("seed", 0)) + 17, w.total_rows, w.vocab, 0.05, keep)
+
+
+def build_sets(name: str):
+    """Seeded input sets (seed 1000*k + i) until the live footprint exceeds 2x the Infinity Cache.
+    chain_rejection_masked: the chain_rejection sets with a grammar-like vocab mask per target row."""
+    from draft_verification_acceptance_amd import workloads as W
+    masked = name == "chain_rejection_masked"
+    gen = "chain_rejection" if masked else name
     base = {"tiny_chain": 1000, "chain_rejection": 2000, "block_greedy": 3000, "tree": 4000, "ragged": 5000,
-            "chain_sparse": 6000}[name]
+            "chain_sparse": 6000, "block_sample": 7000}[gen]
     sets = []
     total = 0
     i = 0
     while total <= 2 * MALL_BYTES or len(sets) < 2:
-        w = W.FULL[name](seed=base + i)
+        w = W.FULL[gen](seed=base + i)
+        if masked:
+            w.name = name
+            w.meta["seed"] = base + i
+            w.meta["vocab_mask"] = _grammar_mask(w)
         mode = w.modes[-1]
         sets.append(w)
         total += w.algorithmic_bytes(mode)
@@ -101,6 +126,11 @@ class ChainStep:
         elif mode == "rejection_sparse":
             kw.update(cand_ids=_dev(w.cand_ids), cand_q=_dev(w.cand_q), u_accept=_dev(w.u_accept),
                       u_final=_dev(w.u_final), temperature=w.temperature)
+        elif mode == "sample_match":
+            kw.update(u_accept=_dev(w.u_accept), u_final=_dev(w.u_final), temperature=w.temperature)
+        mask = w.meta.get("vocab_mask")
+        if mask is not None:
+            kw.update(vocab_mask=_dev(mask.view("<i4")))
         self.verify = dva.prepare_verify_chain(t, offs, _dev(w.draft_tokens), mode, **kw)
         o = self.verify.outputs
         self.commit = dva.prepare_commit_indices(offs, o["accept_len"], o["accept_index"],
@@ -108,7 +138,7 @@ class ChainStep:
                                                  max_verify_len=w.max_verify_len)
         self.positions = w.total_rows
         self.draft_positions = w.total_rows - w.batch
-        self.bytes = w.algorithmic_bytes(mode)
+        self.bytes = w.algorithmic_bytes(mode) + (mask.nbytes if mask is not None else 0)
         torch.cuda.synchronize()
 
 
@@ -375,8 +405,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=["chain_rejection", "block_greedy", "tree",
-                                                                       "ragged", "chain_sparse"])
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
+                    choices=["chain_rejection", "block_greedy", "tree", "ragged", "chain_sparse", "block_sample",
+                             "chain_rejection_masked"])
     ap.add_argument("--mode", default=None)
     ap.add_argument("--no-extra", action="store_true", help="skip the other full-size workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -398,7 +429,7 @@ def main():
     extra = {}
     if not args.no_extra:
         for name, mode in (("block_greedy", None), ("ragged", None), ("tree", "greedy"), ("tree", "target_only"),
-                           ("chain_sparse", None)):
+                           ("chain_sparse", None), ("block_sample", None), ("chain_rejection_masked", "rejection")):
             if name == args.workload and (mode or "") == (args.mode or ""):
                 continue
             r = run_workload(name, mode, max(50, args.steps // 2), args.warmup)

@@ -187,6 +187,12 @@ spec_status spec_verify_chain(const spec_chain_args* a, hipStream_t stream) {
   p.coef = sampling ? float(kLog2e / double(a->temperature)) : 0.f;
   p.mask = a->vocab_mask;
   p.mask_words = (a->vocab + 31) / 32;
+  // Piece partials need 16-byte aligned rows: the layout asks for them when vocab % 8 == 0, the base
+  // pointer must be aligned too (else the draw narrows whole chunks).
+  const bool aligned = (reinterpret_cast<uintptr_t>(a->target_logits) & 15) == 0;
+  p.piece = lo.n_piece > 0 && aligned ? reinterpret_cast<float2*>(static_cast<char*>(a->workspace) + lo.off_piece)
+                                      : nullptr;
+  p.n_piece = lo.n_piece;
   return launch_pair(a->dtype, a->mode, p, a->profile_events, a->n_profile_events, stream);
 }
 

@@ -96,14 +96,19 @@ __device__ __forceinline__ void complete_memory_ops() {
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
-// Vocab mask rows: bit (v % 32) of word v / 32 is 1 iff token v is allowed. mask_bits8 returns the bits
-// of tokens [v, v + 8) (bit i = token v + i) for v < V; the words past the row are not read.
+// Vocab mask rows: bit (v % 32) of word v / 32 is 1 iff token v is allowed. mask_bits8 returns the bits of
+// tokens [v, v + 8) (bit i = token v + i) for any v < V with two word loads and no branch (a load under a
+// branch would cost the stream a wait for every load in flight); mask_bits8_aligned is the one-load form
+// for v % 8 == 0 (and, for the 4 bits of an fp32 run, v % 4 == 0), where the bits lie in one word.
 __device__ __forceinline__ uint32_t mask_bits8(const uint32_t* mrow, int64_t v, int64_t nwords) {
   const int64_t w = v >> 5;
-  const uint32_t sh = uint32_t(v & 31);
-  uint32_t bits = mrow[w] >> sh;
-  if (sh > 24 && w + 1 < nwords) bits |= mrow[w + 1] << (32u - sh);
-  return bits;
+  const uint32_t lo = mrow[w];
+  const uint32_t hi = mrow[w + 1 < nwords ? w + 1 : w];
+  return uint32_t(((uint64_t(hi) << 32) | lo) >> (v & 31));
+}
+
+__device__ __forceinline__ uint32_t mask_bits8_aligned(const uint32_t* mrow, int64_t v) {
+  return mrow[v >> 5] >> uint32_t(v & 31);
 }
 
 __device__ __forceinline__ bool mask_allows(const uint32_t* mrow, int64_t v) { return (mrow[v >> 5] >> (v & 31)) & 1u; }

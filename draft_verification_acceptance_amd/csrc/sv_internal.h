@@ -43,6 +43,9 @@ namespace sv {
 #ifndef SV_STATS_MIN_CHUNK
 #define SV_STATS_MIN_CHUNK 8192      // fewest tokens per chunk
 #endif
+#ifndef SV_MATCH_CHUNK
+#define SV_MATCH_CHUNK 8192          // sample-then-match: tokens per stream chunk at most (the draw narrows
+#endif                               // its row from the chunk partials, so their size bounds its reads)
 #ifndef SV_STATS_UNROLL
 #define SV_STATS_UNROLL 4            // 16-byte loads in flight per thread per loop trip
 #endif
@@ -64,6 +67,11 @@ constexpr int kWave = 64;            // gfx950 wavefront size
 // round); the launch shape keeps row slots x parts x chunks within it.
 constexpr int kMaxStagedParts = 1024;
 constexpr int kSeg = 512;            // tokens per draw segment (one wave: 8 tokens per lane)
+// Sample-then-match on 16-byte aligned rows: the stream stores the (m, z) of every piece of a row, a piece
+// being what one wave reads in one trip (SV_STATS_UNROLL runs per lane: 2048 tokens in bf16, 1024 in fp32).
+// Chunks are then whole multiples of kPieceChunk tokens (4 waves x 2048).
+constexpr int kPieceMin = 1024;      // smallest piece (fp32): sizes the workspace
+constexpr int64_t kPieceChunk = 8192;
 constexpr int kMaxLen = 1024;        // max verify rows per request (chain) / nodes per tree
 constexpr int kMaxCand = 1024;       // max candidates per draft row (sparse q)
 constexpr int64_t kMaxVocab = int64_t(1) << 22;
@@ -104,7 +112,8 @@ struct Layout {
   int32_t S2 = 1;        // vocab chunks per request in k_draw
   int32_t spc = 1;       // segments per k_draw chunk
   int32_t n_seg = 0;     // segments per row
-  size_t off_cnt2 = 0, off_part = 0, off_seg = 0;
+  int32_t n_piece = 0;   // sample-then-match: piece slots per row (0: no piece partials)
+  size_t off_cnt2 = 0, off_part = 0, off_seg = 0, off_piece = 0;
   size_t bytes = 0;
 };
 
@@ -119,14 +128,24 @@ inline Layout make_layout(int kind, int mode, int64_t total_rows, int64_t vocab,
   // SV_STATS_MIN_CHUNK tokens per chunk and all of a request's partials fitting the scan's LDS.
   const int64_t wgs = sampling ? SV_STATS_WGS : SV_STATS_WGS_GREEDY;
   int64_t s = slots > 0 ? (wgs + slots - 1) / slots : 1;
-  int64_t max_s = vocab / SV_STATS_MIN_CHUNK;
+  const int64_t min_chunk = (mode == SPEC_MODE_SAMPLE_MATCH && SV_MATCH_CHUNK < SV_STATS_MIN_CHUNK)
+                                ? int64_t(SV_MATCH_CHUNK) : int64_t(SV_STATS_MIN_CHUNK);
+  int64_t max_s = vocab / min_chunk;
   const int64_t lds_s = kMaxStagedParts / (int64_t(L) * lo.P);
   if (max_s > lds_s) max_s = lds_s;
   if (max_s < 1) max_s = 1;
+  // Sample-then-match: rows whose length is a multiple of 16 bytes (vocab % 8 == 0) get piece partials from
+  // the stream; other rows fall back to fine chunks, which bound what the draw reads.
+  const bool pieces = mode == SPEC_MODE_SAMPLE_MATCH && kind == SPEC_KIND_CHAIN && vocab % 8 == 0;
+  if (mode == SPEC_MODE_SAMPLE_MATCH && !pieces) {
+    const int64_t fine = (vocab + SV_MATCH_CHUNK - 1) / SV_MATCH_CHUNK;
+    if (s < fine) s = fine;
+  }
   if (s > max_s) s = max_s;
   if (s < 1) s = 1;
   int64_t chunk = (vocab + s - 1) / s;
   chunk = (chunk + 63) / 64 * 64;
+  if (pieces) chunk = (chunk + kPieceChunk - 1) / kPieceChunk * kPieceChunk;
   lo.chunk = chunk;
   lo.S = int32_t((vocab + chunk - 1) / chunk);
   lo.n_seg = int32_t((vocab + kSeg - 1) / kSeg);
@@ -143,6 +162,8 @@ inline Layout make_layout(int kind, int mode, int64_t total_rows, int64_t vocab,
   lo.off_cnt2 = o; o = up(o + (sampling ? kCounterStride * size_t(batch) : 0));
   lo.off_part = o; o = up(o + sizeof(Part) * size_t(slots) * size_t(lo.S));
   lo.off_seg = o;  o = up(o + (sampling ? sizeof(float2) * size_t(batch) * size_t(lo.n_seg) : 0));
+  lo.n_piece = pieces ? int32_t((vocab + kPieceMin - 1) / kPieceMin) : 0;
+  lo.off_piece = o; o = up(o + sizeof(float2) * size_t(batch) * size_t(L) * size_t(lo.n_piece));
   lo.bytes = o;
   (void)total_rows;
   return lo;
@@ -180,6 +201,8 @@ struct VerifyParams {
   int32_t tree;               // 1: tree verify (rows node-major, B * L of them)
   const uint32_t* mask;       // vocab mask of the target rows, [rows, mask_words], or NULL
   int64_t mask_words;         // ceil(V / 32)
+  float2* piece;              // sample-then-match: (m, z) per piece of each target row slot, or NULL
+  int32_t n_piece;            // piece slots per row slot
 };
 
 struct CommitParams {

@@ -5,11 +5,12 @@
 // independent target sampling then prefix matching is a different implementation from p/q rejection).
 //
 // One workgroup of 1024 threads per request, one wave per row, 16 rows at a time in row order; the request
-// stops after the first group of rows that holds a mismatch. A draw does not read the whole row: the
-// stream's partials give every vocab chunk's mass z_c 2^(m_c - m), so the chunk holding u * Z is known at
-// once; the wave then narrows that chunk down (each lane sums a contiguous range of it in float64, a wave
-// scan picks the lane whose range holds the target, and so on until a lane holds at most 8 tokens). Only
-// that chunk of the row is read (about 16 KB at a 152k vocab); the narrower levels hit the cache.
+// stops after the first group of rows that holds a mismatch. A draw does not read the whole row: the stream
+// stored the (m, z) of every piece of the row (2048 tokens in bf16) or, for rows that are not 16-byte
+// aligned, of its chunks, so the unit holding u * Z is known from those masses z_i 2^(m_i - m); the wave
+// then narrows that unit down (each lane sums a contiguous range of it in float64, a wave scan picks the
+// lane whose range holds the target, and so on until a lane holds at most 8 tokens). Only that unit of the
+// row is read (4 KB per row for a bf16 piece); the narrower levels hit the cache.
 #include "sv_scan.h"
 
 namespace sv {
@@ -18,6 +19,7 @@ namespace {
 
 constexpr int kMatchThreads = 1024;
 constexpr int kMatchWaves = kMatchThreads / kWave;
+constexpr int kSumUnrollStream = SV_STATS_UNROLL;   // runs per lane in one trip of the stream: a piece
 // 8-token runs in flight per lane while a range is summed (32 VGPRs of raw words for either type)
 template <typename DT>
 constexpr int sum_unroll() {
@@ -164,18 +166,42 @@ __device__ int wave_draw(const DT* row, int a, int n, double t, float coef, floa
   return a;
 }
 
+// Masses of the units a row's CDF is first split into, in row order: the stream's pieces (when it stored
+// them) or its chunks. unit_mass(i) = z_i 2^(m_i - m) for the row max m, as a float64.
+struct RowUnits {
+  const Part* chunks;     // the row's S chunk partials
+  const float2* pieces;   // or its piece partials (NULL: chunks)
+  int n;                  // units in the row
+  int64_t width;          // tokens per unit
+  __device__ __forceinline__ double mass(int i, float m) const {
+    float mi, zi;
+    if (pieces) {
+      const float2 v = pieces[i];
+      mi = v.x;
+      zi = v.y;
+    } else {
+      const Part pt = load_part(chunks + i, true);
+      mi = pt.a;
+      zi = pt.b;
+    }
+    return zi > 0.f ? double(zi) * exp2(double(mi) - double(m)) : 0.0;
+  }
+};
+
 template <typename DT>
 __global__ __launch_bounds__(kMatchThreads) void k_match(VerifyParams p) {
   __shared__ int32_t s_d[kMaxLen];     // d_{j+1} per row j < m
   __shared__ int32_t s_t[kMaxLen];     // the sample t_j of row j
   __shared__ float s_u[kMaxLen];       // sanitized uniform of row j
-  __shared__ float s_m[kMaxLen];       // merged row max (log2 units)
-  __shared__ float s_z[kMaxLen];       // merged row normaliser
+  __shared__ float s_m[kMaxLen];       // row max (log2 units)
+  __shared__ float s_z[kMaxLen];       // row normaliser, float (accept_prob, status)
   __shared__ float s_g[kMaxLen];       // row j's logit at d_{j+1} (gathered while streaming)
+  __shared__ double s_Z[kMaxLen];      // row normaliser over its units, float64 (the draw)
   __shared__ uint8_t s_near[kMaxLen];
   __shared__ uint32_t s_flags;
   __shared__ int s_r, s_stop;
 
+  constexpr int PW = kSumUnrollStream * kWave * Elem<DT>::kPerVec;   // tokens per stream piece
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -190,79 +216,100 @@ __global__ __launch_bounds__(kMatchThreads) void k_match(VerifyParams p) {
   const int64_t dr0 = off0 - b;
   const int S = p.S;
   const Part* gp = p.part + size_t(b) * p.L * S;   // P = 1: target rows only
-
-  // Load round: per row its draft token, uniform and merged partials.
   if (tid == 0) {
     s_flags = 0;
     s_r = m;
     s_stop = 0;
   }
-  __syncthreads();
+  auto units = [&](int j) -> RowUnits {
+    RowUnits u;
+    u.chunks = gp + size_t(j) * S;
+    u.pieces = p.piece ? p.piece + (size_t(b) * p.L + j) * p.n_piece : nullptr;
+    u.n = p.piece ? int((p.V + PW - 1) / PW) : S;
+    u.width = p.piece ? int64_t(PW) : p.chunk;
+    return u;
+  };
+
+  // Phase 1, every row (one wave per row): its chunk partials merged lane-parallel (status, row max,
+  // normaliser, the gathered logit), its unit masses totalled in float64; its draft token and uniform.
   uint32_t fl = 0;
-  for (int j = tid; j < len; j += kMatchThreads) {
-    const int32_t d = j < m ? p.draft_tokens[dr0 + j] : -1;
-    const float u_raw = j < m ? p.u_accept[dr0 + j] : p.u_final[b];
-    const RowStats r = merge_sampling(ReqParts{nullptr, gp, true}, j * S, S);
-    if (j < m && !(d >= 0 && int64_t(d) < p.V)) fl |= SPEC_ST_BAD_TOKEN;
-    bool ubad = false;
-    s_u[j] = sanitize_u(u_raw, ubad);
-    if (ubad) fl |= SPEC_ST_BAD_UNIFORM;
-    if (z_bad(r.z)) fl |= SPEC_ST_NONFINITE;
-    s_d[j] = d;
-    s_m[j] = r.m;
-    s_z[j] = r.z;
-    s_g[j] = r.g;
+  for (int j = wv; j < len; j += kMatchWaves) {
+    float mj = -INFINITY, zj = 0.f, gj = 0.f;
+    bool gathered = false;
+    for (int c0 = 0; c0 < S; c0 += kWave) {
+      const int c = c0 + lane;
+      Part pt{};
+      pt.a = -INFINITY;
+      if (c < S) pt = load_part(gp + size_t(j) * S + c, true);
+      float cm = pt.a, cz = c < S ? pt.b : 0.f;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) merge_mz(cm, cz, __shfl_xor(cm, o), __shfl_xor(cz, o));
+      merge_mz(mj, zj, cm, cz);
+      const uint64_t gm = __ballot(c < S && (pt.flags & kPartGathered));
+      if (gm) {
+        gj = __shfl(pt.g, __ffsll((unsigned long long)gm) - 1);
+        gathered = true;
+      }
+    }
+    const RowUnits ru = units(j);
+    double Z = 0.0;
+    for (int i0 = 0; i0 < ru.n; i0 += kWave) Z += wave_sum(i0 + lane < ru.n ? ru.mass(i0 + lane, mj) : 0.0);
+    if (lane == 0) {
+      const int32_t d = j < m ? p.draft_tokens[dr0 + j] : -1;
+      const float u_raw = j < m ? p.u_accept[dr0 + j] : p.u_final[b];
+      uint32_t f = 0;
+      if (j < m && !(d >= 0 && int64_t(d) < p.V)) f |= SPEC_ST_BAD_TOKEN;
+      bool ubad = false;
+      s_u[j] = sanitize_u(u_raw, ubad);
+      if (ubad) f |= SPEC_ST_BAD_UNIFORM;
+      if (z_bad(zj)) f |= SPEC_ST_NONFINITE;
+      s_d[j] = d;
+      s_m[j] = mj;
+      s_z[j] = zj;
+      s_g[j] = gathered ? gj : 0.f;
+      s_Z[j] = Z;
+      fl |= f;
+    }
   }
   if (fl) atomicOr(&s_flags, fl);
   __syncthreads();
 
+  // Phase 2: the samples, 16 rows at a time in row order, until a group holds a mismatch.
   for (int j0 = 0; j0 < len; j0 += kMatchWaves) {
     const int j = j0 + wv;
     if (j < len) {
-      // Chunk masses z_c 2^(m_c - m) in float64 (lane c), their total and the chunk holding u * Z.
       const float M = s_m[j];
-      const Part* rp = gp + size_t(j) * S;
-      double Z = 0.0;
-      for (int c0 = 0; c0 < S; c0 += kWave) {
-        const int c = c0 + lane;
-        double mass = 0.0;
-        if (c < S) {
-          const Part pt = load_part(rp + c, true);
-          if (pt.b > 0.f) mass = double(pt.b) * exp2(double(pt.a) - double(M));
-        }
-        Z += wave_sum(mass);
-      }
+      const double Z = s_Z[j];
       const double T = double(s_u[j]) * Z;
-      int csel = -1, clast = -1;
+      const RowUnits ru = units(j);
+      // the unit holding T (the first with positive mass whose cumulative mass passes T; rounding past the
+      // end: the last with positive mass)
+      int usel = -1, ulast = -1;
       double cum0 = 0.0, cum_last = 0.0, carry = 0.0;
-      for (int c0 = 0; c0 < S && csel < 0; c0 += kWave) {
-        const int c = c0 + lane;
-        double mass = 0.0;
-        if (c < S) {
-          const Part pt = load_part(rp + c, true);
-          if (pt.b > 0.f) mass = double(pt.b) * exp2(double(pt.a) - double(M));
-        }
+      for (int i0 = 0; i0 < ru.n && usel < 0; i0 += kWave) {
+        const int i = i0 + lane;
+        const double mass = i < ru.n ? ru.mass(i, M) : 0.0;
         const double incl = carry + wave_inclusive_sum(mass);
         const uint64_t hit = __ballot(mass > 0.0 && T < incl);
         if (hit) {
           const int f = __ffsll((unsigned long long)hit) - 1;
-          csel = c0 + f;
+          usel = i0 + f;
           cum0 = __shfl(incl - mass, f);
         }
         const uint64_t pos = __ballot(mass > 0.0);
         if (pos) {
           const int f = 63 - __clzll((long long)pos);
-          clast = c0 + f;
+          ulast = i0 + f;
           cum_last = __shfl(incl - mass, f);
         }
         carry = __shfl(incl, kWave - 1);
       }
-      if (csel < 0) {   // rounding left u * Z past every chunk (or nothing has mass)
-        csel = clast < 0 ? 0 : clast;
-        cum0 = clast < 0 ? 0.0 : cum_last;
+      if (usel < 0) {   // rounding left u * Z past every unit (or nothing has mass)
+        usel = ulast < 0 ? 0 : ulast;
+        cum0 = ulast < 0 ? 0.0 : cum_last;
       }
-      const int a = int(int64_t(csel) * p.chunk);
-      const int n = int(min(p.V, int64_t(csel + 1) * p.chunk)) - a;
+      const int a = int(int64_t(usel) * ru.width);
+      const int n = int(min(p.V, int64_t(usel + 1) * ru.width)) - a;
       const DT* row = static_cast<const DT*>(p.target) + (off0 + j) * p.V;
       const uint32_t* mrow = p.mask ? p.mask + (off0 + j) * p.mask_words : nullptr;
       double cum1, w_tok;

@@ -44,10 +44,16 @@ __device__ __forceinline__ Split split_chunk(const DT* row, int64_t lo, int64_t 
 // unaligned head and tail elements (rows whose byte offset is not a multiple of 16) are loaded before the
 // stream and folded in after it.
 
-// Greedy partial of row[lo, hi) reduced over the workgroup (result valid in thread 0). MASK: the row's vocab
-// mask `mrow` (nw words) turns disallowed logits into -inf as they are unpacked (one 4-byte mask load per
-// 16-byte logits load, issued with it).
-template <typename DT, bool MASK>
+// Greedy partial of row[lo, hi) reduced over the workgroup (result valid in thread 0). MASK (0: none) applies
+// the row's vocab mask `mrow` (nw words): disallowed logits become -inf as they are unpacked. 1: the chunk's
+// 16-byte runs start at token multiples of the run length, so a run's bits lie in one word (one 4-byte
+// load per 16-byte load, issued with it); 2: any alignment (two word loads).
+template <int MASK>
+__device__ __forceinline__ uint32_t run_mask(const uint32_t* mrow, int64_t v, int64_t nw) {
+  return MASK == 1 ? mask_bits8_aligned(mrow, v) : MASK == 2 ? mask_bits8(mrow, v, nw) : ~0u;
+}
+
+template <typename DT, int MASK>
 __device__ __forceinline__ void chunk_argmax(const DT* __restrict__ row, int64_t lo, int64_t hi, Part& out,
                                              float* red_f, int* red_i, uint32_t* red_u, const uint32_t* mrow,
                                              int64_t nw) {
@@ -95,7 +101,7 @@ __device__ __forceinline__ void chunk_argmax(const DT* __restrict__ row, int64_t
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) q[u] = load_stream(vp + k + u * NT);
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) mb[u] = MASK ? mask_bits8(mrow, sp.body_lo + (k + u * NT) * E, nw) : ~0u;
+    for (int u = 0; u < kUnroll; ++u) mb[u] = run_mask<MASK>(mrow, sp.body_lo + (k + u * NT) * E, nw);
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) consume(q[u], k + u * NT, mb[u]);
   }
@@ -107,7 +113,7 @@ __device__ __forceinline__ void chunk_argmax(const DT* __restrict__ row, int64_t
       q[u] = k + u * NT < sp.nvec ? load_stream(vp + k + u * NT) : make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u)
-      mb[u] = MASK && k + u * NT < sp.nvec ? mask_bits8(mrow, sp.body_lo + (k + u * NT) * E, nw) : ~0u;
+      mb[u] = k + u * NT < sp.nvec ? run_mask<MASK>(mrow, sp.body_lo + (k + u * NT) * E, nw) : ~0u;
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u)
       if (k + u * NT < sp.nvec) consume(q[u], k + u * NT, mb[u]);
@@ -175,7 +181,7 @@ __device__ __forceinline__ void single_mz(float x, float coef, float& m2, float&
 
 // Sampling partial of row[lo, hi): (m, z) with m in log2 units, reduced over the workgroup (thread 0). MASK as
 // for chunk_argmax.
-template <typename DT, bool MASK>
+template <typename DT, int MASK>
 __device__ __forceinline__ void chunk_lse(const DT* __restrict__ row, int64_t lo, int64_t hi, float coef, Part& out,
                                           float* red_f, float* red_g, const uint32_t* mrow, int64_t nw) {
   constexpr int E = Elem<DT>::kPerVec;
@@ -215,7 +221,7 @@ __device__ __forceinline__ void chunk_lse(const DT* __restrict__ row, int64_t lo
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) q[u] = load_stream(vp + k + u * NT);
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) mb[u] = MASK ? mask_bits8(mrow, sp.body_lo + (k + u * NT) * E, nw) : ~0u;
+    for (int u = 0; u < kUnroll; ++u) mb[u] = run_mask<MASK>(mrow, sp.body_lo + (k + u * NT) * E, nw);
     float x[kUnroll * E];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
@@ -232,7 +238,7 @@ __device__ __forceinline__ void chunk_lse(const DT* __restrict__ row, int64_t lo
       q[u] = k + u * NT < sp.nvec ? load_stream(vp + k + u * NT) : make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u)
-      mb[u] = MASK && k + u * NT < sp.nvec ? mask_bits8(mrow, sp.body_lo + (k + u * NT) * E, nw) : ~0u;
+      mb[u] = k + u * NT < sp.nvec ? run_mask<MASK>(mrow, sp.body_lo + (k + u * NT) * E, nw) : ~0u;
     float x[kUnroll * E];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
@@ -277,10 +283,122 @@ __device__ __forceinline__ void chunk_lse(const DT* __restrict__ row, int64_t lo
   }
 }
 
+// Maximum and sum over the 64 lanes of a wave, the result in every lane: a butterfly inside each 16-lane
+// row (DPP quad permutes [1,0,3,2] and [2,3,0,1], then the half-row and row mirrors), then the four row
+// results read out. Every lane must be active.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row_lanes(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));
+  v = fmaxf(v, dpp_f<0x4E>(v));
+  v = fmaxf(v, dpp_f<0x141>(v));
+  v = fmaxf(v, dpp_f<0x140>(v));
+  return fmaxf(fmaxf(row_lanes(v, 0), row_lanes(v, 16)), fmaxf(row_lanes(v, 32), row_lanes(v, 48)));
+}
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v += dpp_f<0xB1>(v);
+  v += dpp_f<0x4E>(v);
+  v += dpp_f<0x141>(v);
+  v += dpp_f<0x140>(v);
+  return (row_lanes(v, 0) + row_lanes(v, 16)) + (row_lanes(v, 32) + row_lanes(v, 48));
+}
+
+// Sampling partial of row[lo, hi) that also stores the (m, z) of every piece (sample-then-match). The row is
+// 16-byte aligned and lo a multiple of kPieceChunk: wave w streams the contiguous quarter of the chunk that
+// starts at lo + w R (R a whole number of pieces), and each of its trips reads one piece (kUnroll runs per
+// lane, 64 lanes side by side, the next trip's loads issued before this one is reduced): the piece max m
+// over the wave first, then z = sum exp2(x * coef - m), stored at prow[piece]. The chunk's (m, z) merges the
+// pieces.
+template <typename DT, int MASK>
+__device__ __forceinline__ void chunk_lse_pieces(const DT* __restrict__ row, int64_t lo, int64_t hi, float coef,
+                                                 Part& out, float* red_f, float* red_g, const uint32_t* mrow,
+                                                 int64_t nw, float2* prow) {
+  constexpr int E = Elem<DT>::kPerVec;
+  constexpr int PW = kUnroll * kWave * E;   // tokens per piece
+  const int lane = lane_id();
+  const int w = threadIdx.x / kWave;
+  const int64_t R = (hi - lo + int64_t(kW) * PW - 1) / (int64_t(kW) * PW) * PW;
+  const int64_t wlo = lo + w * R;
+  const int64_t whi = wlo + R < hi ? wlo + R : hi;
+  const uint4* __restrict__ vp = reinterpret_cast<const uint4*>(row);
+  // A trip wholly inside the wave's range needs no predicates (and, without a mask, no selects).
+  auto load_trip = [&](int64_t p0, bool whole, uint4* q, uint32_t* mb) {
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t v = p0 + int64_t(u * kWave + lane) * E;
+      q[u] = whole || v < whi ? load_stream(vp + v / E) : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t v = p0 + int64_t(u * kWave + lane) * E;
+      mb[u] = whole || v < whi ? run_mask<MASK>(mrow, v, nw) : 0u;   // past the chunk: nothing
+    }
+  };
+  auto piece = [&](const uint4* q, const uint32_t* mb, bool whole, float& pm, float& pz) {
+    float x[kUnroll * E];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      Elem<DT>::unpack(q[u], x + u * E);
+      if (MASK || !whole) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) x[u * E + e] = (mb[u] >> e) & 1u ? x[u * E + e] : -INFINITY;
+      }
+    }
+    float vm = x[0];
+#pragma unroll
+    for (int e = 1; e < kUnroll * E; ++e) vm = fmaxf(vm, x[e]);
+    pm = wave_max_dpp(vm * coef);
+    const float nm = pm == -INFINITY ? 0.f : -pm;
+    float lz = 0.f;
+#pragma unroll
+    for (int e = 0; e < kUnroll * E; ++e) lz += exp2_fast(fmaf(x[e], coef, nm));
+    pz = wave_sum_dpp(lz);
+  };
+  float m = -INFINITY, z = 0.f;
+  uint4 q[kUnroll];
+  uint32_t mb[kUnroll];
+  if (wlo < whi) load_trip(wlo, wlo + PW <= whi, q, mb);
+  for (int64_t p0 = wlo; p0 < whi; p0 += PW) {
+    const bool whole = p0 + PW <= whi;
+    uint4 qn[kUnroll];
+    uint32_t mbn[kUnroll];
+    if (p0 + PW < whi) load_trip(p0 + PW, p0 + 2 * PW <= whi, qn, mbn);
+    float pm, pz;
+    if (whole) piece(q, mb, true, pm, pz);
+    else piece(q, mb, false, pm, pz);
+    if (lane == 0) prow[p0 / PW] = make_float2(pm, pz);
+    merge_mz(m, z, pm, pz);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      q[u] = qn[u];
+      mb[u] = mbn[u];
+    }
+  }
+  if (lane == 0) {
+    red_f[w] = m;
+    red_g[w] = z;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float M = red_f[0], Z = red_g[0];
+    for (int i = 1; i < kW; ++i) merge_mz(M, Z, red_f[i], red_g[i]);
+    out.a = M;
+    out.b = Z;
+    out.idx = 0;
+    out.flags = 0;
+  }
+}
+
 // ---------------------------------------------------------------------------------------------------
 // The logits stream.
 // ---------------------------------------------------------------------------------------------------
-template <typename DT, bool SAMPLING, bool TREE, bool MASK>
+// PIECES: sample-then-match with piece partials (chain sampling only).
+template <typename DT, bool SAMPLING, bool TREE, bool MASK, bool PIECES>
 __global__ __launch_bounds__(NT) void k_stats(VerifyParams p) {
   __shared__ float red_f[kW];
   __shared__ float red_g[kW];
@@ -353,12 +471,25 @@ __global__ __launch_bounds__(NT) void k_stats(VerifyParams p) {
     qf = (__ballot(f & kPartBadCandId) ? kPartBadCandId : 0u) | (__ballot(f & kPartBadCandQ) ? kPartBadCandQ : 0u);
   }
 
-  if (MASK && mrow) {
-    if (SAMPLING) chunk_lse<DT, true>(base, lo, hi, p.coef, s_part, red_f, red_g, mrow, p.mask_words);
-    else chunk_argmax<DT, true>(base, lo, hi, s_part, red_f, red_i, red_u, mrow, p.mask_words);
+  // A 16-byte aligned row start (and chunk starts at multiples of 64 tokens) keeps every run's mask bits in
+  // one word.
+  const bool runs_aligned = (reinterpret_cast<uintptr_t>(base) & 15) == 0 && (lo & 63) == 0;
+  // Sample-then-match with piece partials (aligned target rows; chunks are whole multiples of kPieceChunk).
+  float2* prow = PIECES && part == 0 && runs_aligned && lo % kPieceChunk == 0
+                     ? p.piece + (size_t(b) * p.L + slot) * p.n_piece
+                     : nullptr;
+  if (PIECES && prow) {
+    if (MASK && mrow) chunk_lse_pieces<DT, 1>(base, lo, hi, p.coef, s_part, red_f, red_g, mrow, p.mask_words, prow);
+    else chunk_lse_pieces<DT, 0>(base, lo, hi, p.coef, s_part, red_f, red_g, nullptr, 0, prow);
+  } else if (MASK && mrow && runs_aligned) {
+    if (SAMPLING) chunk_lse<DT, 1>(base, lo, hi, p.coef, s_part, red_f, red_g, mrow, p.mask_words);
+    else chunk_argmax<DT, 1>(base, lo, hi, s_part, red_f, red_i, red_u, mrow, p.mask_words);
+  } else if (MASK && mrow) {
+    if (SAMPLING) chunk_lse<DT, 2>(base, lo, hi, p.coef, s_part, red_f, red_g, mrow, p.mask_words);
+    else chunk_argmax<DT, 2>(base, lo, hi, s_part, red_f, red_i, red_u, mrow, p.mask_words);
   } else {
-    if (SAMPLING) chunk_lse<DT, false>(base, lo, hi, p.coef, s_part, red_f, red_g, nullptr, 0);
-    else chunk_argmax<DT, false>(base, lo, hi, s_part, red_f, red_i, red_u, nullptr, 0);
+    if (SAMPLING) chunk_lse<DT, 0>(base, lo, hi, p.coef, s_part, red_f, red_g, nullptr, 0);
+    else chunk_argmax<DT, 0>(base, lo, hi, s_part, red_f, red_i, red_u, nullptr, 0);
   }
 
   if (SAMPLING) {
@@ -407,20 +538,24 @@ hipError_t launch_stats_t(int mode, const VerifyParams& p, hipStream_t stream, h
   if (blocks <= 0) return hipSuccess;
   const bool sampling = mode != SPEC_MODE_GREEDY;
   const dim3 grid{unsigned(blocks)}, block{unsigned(NT)};
+  if (sampling && !p.tree && mode == SPEC_MODE_SAMPLE_MATCH && p.piece) {
+    if (p.mask) return launch_kernel(k_stats<DT, true, false, true, true>, grid, block, 0, stream, ev0, ev1, p);
+    return launch_kernel(k_stats<DT, true, false, false, true>, grid, block, 0, stream, ev0, ev1, p);
+  }
   if (p.mask) {
     if (p.tree) {
-      if (sampling) return launch_kernel(k_stats<DT, true, true, true>, grid, block, 0, stream, ev0, ev1, p);
-      return launch_kernel(k_stats<DT, false, true, true>, grid, block, 0, stream, ev0, ev1, p);
+      if (sampling) return launch_kernel(k_stats<DT, true, true, true, false>, grid, block, 0, stream, ev0, ev1, p);
+      return launch_kernel(k_stats<DT, false, true, true, false>, grid, block, 0, stream, ev0, ev1, p);
     }
-    if (sampling) return launch_kernel(k_stats<DT, true, false, true>, grid, block, 0, stream, ev0, ev1, p);
-    return launch_kernel(k_stats<DT, false, false, true>, grid, block, 0, stream, ev0, ev1, p);
+    if (sampling) return launch_kernel(k_stats<DT, true, false, true, false>, grid, block, 0, stream, ev0, ev1, p);
+    return launch_kernel(k_stats<DT, false, false, true, false>, grid, block, 0, stream, ev0, ev1, p);
   }
   if (p.tree) {
-    if (sampling) return launch_kernel(k_stats<DT, true, true, false>, grid, block, 0, stream, ev0, ev1, p);
-    return launch_kernel(k_stats<DT, false, true, false>, grid, block, 0, stream, ev0, ev1, p);
+    if (sampling) return launch_kernel(k_stats<DT, true, true, false, false>, grid, block, 0, stream, ev0, ev1, p);
+    return launch_kernel(k_stats<DT, false, true, false, false>, grid, block, 0, stream, ev0, ev1, p);
   }
-  if (sampling) return launch_kernel(k_stats<DT, true, false, false>, grid, block, 0, stream, ev0, ev1, p);
-  return launch_kernel(k_stats<DT, false, false, false>, grid, block, 0, stream, ev0, ev1, p);
+  if (sampling) return launch_kernel(k_stats<DT, true, false, false, false>, grid, block, 0, stream, ev0, ev1, p);
+  return launch_kernel(k_stats<DT, false, false, false, false>, grid, block, 0, stream, ev0, ev1, p);
 }
 
 }  // namespace
