@@ -10,8 +10,10 @@ cache, serves the stream.
 
 Prints ONE JSON line. value = verified positions per second (target rows judged, sum_b (m_b + 1)).
 roofline: the dominant kernel (k_stats, the logits stream) timed with HIP events that take its own start and
-stop timestamps on the launch stream (hipExtLaunchKernel), against its algorithmic bytes (every target and draft row read once). cpu_baseline: the fp64 CPU
-oracle timed on this host on the same inputs.
+stop timestamps on the launch stream (hipExtLaunchKernel), against its algorithmic bytes (every target and
+draft row read once); read_floor: a plain read of the same byte count (spec_read_probe) timed the same way,
+the rate HBM actually delivers at this size. cpu_baseline: the fp64 CPU oracle timed on this host on the
+same inputs.
 
     python bench.py [--steps K] [--warmup W]
                     [--workload chain_rejection|block_greedy|tree|ragged|chain_sparse|block_sample|chain_rejection_masked]
@@ -387,6 +389,28 @@ def load_traffic(name: str):
     return float(vals["k_stats_hbm_bytes_per_launch"])
 
 
+def read_floor(nbytes: int, reps: int = 20) -> dict:
+    """This GPU's achievable HBM read rate at the stream's size: spec_read_probe (a plain read, 16-byte loads)
+    over nbytes, alternating between two buffers of that size as the timed step alternates its input sets (so
+    the 256 MB cache serves neither), each launch timed by events on its own dispatch like the verify
+    kernels."""
+    import torch
+    import draft_verification_acceptance_amd as dva
+    n = nbytes // 16 * 16
+    bufs = [torch.full((n,), i + 1, dtype=torch.uint8, device="cuda") for i in range(2)]
+    sink = torch.zeros(dva.READ_SINK_WORDS, dtype=torch.int32, device="cuda")
+    for i in range(4):
+        dva.read_probe(bufs[i % 2], sink)
+    evs = [dva.HipEvents(2) for _ in range(reps)]
+    for i in range(reps):
+        dva.read_probe(bufs[i % 2], sink, events=evs[i])
+    torch.cuda.synchronize()
+    ms = sum(e.elapsed_ms(0, 1) for e in evs) / reps
+    del bufs
+    torch.cuda.empty_cache()
+    return {"kernel": "k_read_fold", "bytes": n, "avg_launch_ms": ms, "gbs": n / (ms * 1e-3) / 1e9, "launches": reps}
+
+
 def copy_calibration():
     """A plain copy of known size, for scaling rocprofv3's FETCH_SIZE / WRITE_SIZE counters."""
     import torch
@@ -444,6 +468,7 @@ def main():
     stats_ms = main_res["kernel_ms"]["k_stats"]["mean"]
     achieved = main_res["stats_kernel_gbs"]
     traffic = load_traffic(main_res["workload"])
+    floor = read_floor(int(main_res["algorithmic_bytes_per_step"]))
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(main_res["workload"])
@@ -472,7 +497,8 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "k_stats", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "algorithmic_bytes_per_launch": main_res["algorithmic_bytes_per_step"],
-                     "avg_launch_ms": stats_ms},
+                     "avg_launch_ms": stats_ms,
+                     "read_floor": dict(floor, frac=achieved / floor["gbs"])},
         "kernel_ms": main_res["kernel_ms"],
         "mean_accept_len": main_res["mean_accept_len"],
         "status_faults": main_res["status_faults"],

@@ -17,7 +17,7 @@ import os
 import torch
 
 __all__ = [
-    "SpecError", "verify_chain", "verify_tree", "commit_indices", "workspace", "workspace_bytes",
+    "SpecError", "verify_chain", "verify_tree", "commit_indices", "workspace", "workspace_bytes", "read_probe",
     "workspace_init", "kernel_count", "status_string", "abi_version", "library_path", "HipEvents",
     "MODES", "ST", "PreparedCall", "prepare_verify_chain", "prepare_verify_tree", "prepare_commit_indices",
     "plan_layout", "prepare_plan_layout", "plan_budget", "cap_trim", "prepare_cap_trim", "kv_move",
@@ -143,6 +143,8 @@ def _lib():
     lib.spec_workspace_bytes.restype = _sz
     lib.spec_workspace_init.argtypes = [_vp, _sz, _vp]
     lib.spec_workspace_init.restype = ctypes.c_int
+    lib.spec_read_probe.argtypes = [_vp, _sz, _vp, _vp, _vp]
+    lib.spec_read_probe.restype = ctypes.c_int
     lib.spec_kernel_count.argtypes = [_i32, _i32]
     lib.spec_kernel_count.restype = _i32
     lib.spec_status_string.argtypes = [ctypes.c_int]
@@ -192,6 +194,21 @@ def _stream(device) -> int:
 
 def workspace_init(ws: torch.Tensor):
     _check(_lib().spec_workspace_init(ws.data_ptr(), ws.numel() * ws.element_size(), _stream(ws.device)))
+
+
+READ_SINK_WORDS = 8192   # SPEC_READ_SINK_WORDS
+
+
+def read_probe(src: torch.Tensor, sink: torch.Tensor, nbytes: int | None = None, events: "HipEvents | None" = None):
+    """spec_read_probe: a plain read of the first `nbytes` (default: all) bytes of `src` on the current stream.
+    `sink`: an int32 device tensor of READ_SINK_WORDS words the caller zeroes; the XOR of its words is the XOR
+    of every 32-bit word read. `events` (2 of them) take the kernel's start and stop timestamps."""
+    n = src.numel() * src.element_size() if nbytes is None else int(nbytes)
+    if (sink.dtype != torch.int32 or sink.device != src.device or sink.numel() < READ_SINK_WORDS
+            or n > src.numel() * src.element_size()):
+        raise SpecError("read_probe: sink must be READ_SINK_WORDS int32 words on src's device, nbytes within src")
+    _check(_lib().spec_read_probe(src.data_ptr(), n, sink.data_ptr(), events.pointer() if events else None,
+                                  _stream(src.device)))
 
 
 def workspace(kind: str, mode: str, total_rows: int, vocab: int, batch: int, max_verify_len: int,

@@ -12,7 +12,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libspecverify.so")
-SOURCES = ["sv_api.hip", "sv_stats.hip", "sv_draw.hip", "sv_commit.hip", "sv_plan.hip", "sv_tree.hip", "sv_match.hip"]
+SOURCES = ["sv_api.hip", "sv_stats.hip", "sv_draw.hip", "sv_commit.hip", "sv_plan.hip", "sv_tree.hip", "sv_match.hip", "sv_probe.hip"]
 
 # Packed fp32 VALU ops are kept out of the generated code (-packed-fp32-ops).
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",

@@ -136,6 +136,14 @@ spec_status spec_workspace_init(void* workspace, size_t bytes, hipStream_t strea
   return launch_fill_zero(workspace, bytes, stream) == hipSuccess ? SPEC_OK : SPEC_ELAUNCH;
 }
 
+spec_status spec_read_probe(const void* src, size_t bytes, uint32_t* sink, hipEvent_t* events, hipStream_t stream) {
+  if (bytes == 0) return SPEC_OK;
+  if (!src || !sink || (reinterpret_cast<uintptr_t>(src) & 15) || (bytes & 15)) return SPEC_EINVAL;
+  const hipError_t e = launch_read_fold(src, bytes, sink, stream, events ? events[0] : nullptr,
+                                        events ? events[1] : nullptr);
+  return e == hipSuccess ? SPEC_OK : SPEC_ELAUNCH;
+}
+
 spec_status spec_verify_chain(const spec_chain_args* a, hipStream_t stream) {
   if (!a) return SPEC_EINVAL;
   if (a->dtype != SPEC_DTYPE_F32 && a->dtype != SPEC_DTYPE_BF16) return SPEC_EDTYPE;

@@ -117,6 +117,31 @@ __device__ __forceinline__ uint64_t lanes_below(int lane) {
   return lane == 0 ? 0ull : (~0ull >> (64 - lane));
 }
 
+// Maximum and sum over the 64 lanes of a wave, the result in every lane: a butterfly inside each 16-lane
+// row (DPP quad permutes [1,0,3,2] and [2,3,0,1], then the half-row and row mirrors), then the four row
+// results read out. Every lane must be active.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row_lanes(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));
+  v = fmaxf(v, dpp_f<0x4E>(v));
+  v = fmaxf(v, dpp_f<0x141>(v));
+  v = fmaxf(v, dpp_f<0x140>(v));
+  return fmaxf(fmaxf(row_lanes(v, 0), row_lanes(v, 16)), fmaxf(row_lanes(v, 32), row_lanes(v, 48)));
+}
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v += dpp_f<0xB1>(v);
+  v += dpp_f<0x4E>(v);
+  v += dpp_f<0x141>(v);
+  v += dpp_f<0x140>(v);
+  return (row_lanes(v, 0) + row_lanes(v, 16)) + (row_lanes(v, 32) + row_lanes(v, 48));
+}
+
 template <typename T>
 __device__ __forceinline__ T wave_sum(T v) {
 #pragma unroll

@@ -255,8 +255,8 @@ __global__ __launch_bounds__(kThreads) void k_draw(VerifyParams p) {
       float sw = 0.f, sp = 0.f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) { sw += w[j]; sp += pv[j]; }
-      sw = wave_sum(sw);
-      sp = wave_sum(sp);
+      sw = wave_sum_dpp(sw);   // the wave is whole here: s is the same in all of its lanes
+      sp = wave_sum_dpp(sp);
       if (lane == 0) store_seg(p.seg + int64_t(b) * p.n_seg + s, sw, sp);
     }
   }

@@ -231,6 +231,7 @@ __device__ DrawPlan scan_chain_rejection(const VerifyParams& p, int b, int64_t o
   uint8_t* s_acc = reinterpret_cast<uint8_t*>(s_d + L);   // bit0 accepted, bit1 near, bit2 q == 0
   const Part* gp = p.part + size_t(b) * L * PS;
   if (tid == 0) s_flags = 0;
+  const float uf_raw = p.u_final[b];   // one address for the workgroup, in flight with the load round
   chain_load_round(p, gp, len * PS, stage, true, dr0, m, s_d, s_u);
   const ReqParts rp{stage, gp, true};
   uint32_t fl = 0;
@@ -294,7 +295,7 @@ __device__ DrawPlan scan_chain_rejection(const VerifyParams& p, int b, int64_t o
   }
   if (tid == 0) {
     bool ubad = false;
-    s_uf = sanitize_u(p.u_final[b], ubad);
+    s_uf = sanitize_u(uf_raw, ubad);
     if (ubad) fl |= SPEC_ST_BAD_UNIFORM;
   }
   if (fl) atomicOr(&s_flags, fl);
@@ -350,6 +351,7 @@ __device__ DrawPlan scan_tree(const VerifyParams& p, int b, char* smem, Part* st
   int32_t* s_seen = s_list + N;                           // distinct tokens tried at the current node
   const Part* gp = p.part + size_t(b) * N * p.S;
   if (tid == 0) { s_flags = 0; s_nseen = 0; }
+  const float uf_raw = SAMPLING ? p.u_final[b] : 0.f;   // in flight with the load round
   // Load round: partials (when staged), parents, tokens and uniforms.
   {
     const int np = N * p.S;
@@ -532,7 +534,7 @@ __device__ DrawPlan scan_tree(const VerifyParams& p, int b, char* smem, Part* st
   d.seen = s_seen;
   if (SAMPLING) {
     bool ubad = false;
-    d.u = sanitize_u(p.u_final[b], ubad);
+    d.u = sanitize_u(uf_raw, ubad);
     if (ubad) d.status |= SPEC_ST_BAD_UNIFORM;
   }
   return d;

@@ -449,6 +449,17 @@ size_t spec_workspace_bytes(int32_t kind, int32_t mode, int64_t total_rows, int6
    Returns SPEC_EINVAL for a NULL workspace with bytes > 0, SPEC_ELAUNCH if the launch fails. */
 spec_status spec_workspace_init(void* workspace, size_t bytes, hipStream_t stream);
 
+/* A plain read of `bytes` of device memory at `src` (16-byte loads, every byte once, as the logits stream
+   reads its rows), on `stream`: the reference for the stream's rate, this GPU's achievable HBM read rate at
+   the same size, measured beside the verify kernels. Each of its workgroups (at most SPEC_READ_SINK_WORDS)
+   stores the XOR of the 32-bit words it read into its own word of `sink` (device memory, SPEC_READ_SINK_WORDS
+   uint32 words, zeroed by the caller): the XOR of all sink words is the XOR of every word read. events:
+   NULL, or a HOST array of 2 events that take the kernel's own start and stop timestamps (as profile_events
+   do for a verify call). src 16-byte aligned and bytes a multiple of 16, else SPEC_EINVAL (bytes = 0:
+   nothing to do); SPEC_ELAUNCH if the launch fails. Not part of a verify call. */
+#define SPEC_READ_SINK_WORDS 8192
+spec_status spec_read_probe(const void* src, size_t bytes, uint32_t* sink, hipEvent_t* events, hipStream_t stream);
+
 /* Number of kernels a call of this kind/mode launches (events: kernels + 1). Pure host function. */
 int32_t spec_kernel_count(int32_t kind, int32_t mode);
 

@@ -185,3 +185,13 @@ def test_plan_budget_host_argument_checks():
     with pytest.raises(dva.SpecError):
         dva.plan_budget(c, [1.0, 2.0], [5.0, 4.0], survival_eps=-0.5)
     assert dva.plan_budget(np.zeros((0, 3), np.float32), [1.0], [5.0]) == (0, [0.0])
+
+
+def test_read_probe_host_checks():
+    lib = dva._lib()
+    fake = 1 << 40                                                            # never dereferenced
+    assert lib.spec_read_probe(fake, 0, fake, None, None) == 0                # nothing to read
+    assert lib.spec_read_probe(None, 64, fake, None, None) == 1
+    assert lib.spec_read_probe(fake, 64, None, None, None) == 1
+    assert lib.spec_read_probe(fake + 4, 64, fake, None, None) == 1           # src not 16-byte aligned
+    assert lib.spec_read_probe(fake, 60, fake, None, None) == 1               # not whole 16-byte words

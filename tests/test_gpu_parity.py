@@ -189,6 +189,14 @@ def test_vocab_sizes(V):
             compare_chain(ww, mode, o, g)
 
 
+def test_draw_over_1024_segments():
+    """A vocab of more than 1024 draw segments of 512 tokens (more than one per thread of the final
+    workgroup's prefix): peaked rows, so that the draws are not all within the CDF tolerance."""
+    w = W.chain_rejection(seed=2003, batch=6, m=3, vocab=600_001, parallel=False)
+    _say("chain_rejection V=600001")
+    compare_chain(w, "rejection", oracle_chain(w, "rejection"), run_chain(w, "rejection"))
+
+
 @pytest.mark.parametrize("T", [0.05, 0.7, 5.0])
 def test_temperatures(T):
     w = W.chain_rejection(seed=2100, batch=16, m=5, vocab=3001, parallel=False)
