@@ -37,6 +37,9 @@ namespace sv {
 #ifndef SV_STATS_WGS
 #define SV_STATS_WGS 512             // streaming workgroups aimed for per call, sampling modes (rows are
 #endif                               // split into chunks)
+#ifndef SV_MATCH_WGS
+#define SV_MATCH_WGS 1024            // the same, sample-then-match (each wave reduces every piece it reads
+#endif                               // across the wave: more waves keep enough loads in flight)
 #ifndef SV_STATS_WGS_GREEDY
 #define SV_STATS_WGS_GREEDY 1024     // the same, greedy (less work per token: more loads in flight needed)
 #endif
@@ -124,9 +127,10 @@ inline Layout make_layout(int kind, int mode, int64_t total_rows, int64_t vocab,
   lo.L = L;
   lo.P = (kind == SPEC_KIND_CHAIN && mode == SPEC_MODE_REJECTION) ? 2 : 1;
   const int64_t slots = int64_t(batch) * L * lo.P;
-  // Rows are split into S chunks so that about SV_STATS_WGS(_GREEDY) workgroups stream, with at least
-  // SV_STATS_MIN_CHUNK tokens per chunk and all of a request's partials fitting the scan's LDS.
-  const int64_t wgs = sampling ? SV_STATS_WGS : SV_STATS_WGS_GREEDY;
+  // Rows are split into S chunks so that about SV_STATS_WGS (SV_MATCH_WGS, SV_STATS_WGS_GREEDY) workgroups
+  // stream, with at least SV_STATS_MIN_CHUNK tokens per chunk and all of a request's partials fitting the
+  // scan's LDS.
+  const int64_t wgs = mode == SPEC_MODE_SAMPLE_MATCH ? SV_MATCH_WGS : sampling ? SV_STATS_WGS : SV_STATS_WGS_GREEDY;
   int64_t s = slots > 0 ? (wgs + slots - 1) / slots : 1;
   const int64_t min_chunk = (mode == SPEC_MODE_SAMPLE_MATCH && SV_MATCH_CHUNK < SV_STATS_MIN_CHUNK)
                                 ? int64_t(SV_MATCH_CHUNK) : int64_t(SV_STATS_MIN_CHUNK);

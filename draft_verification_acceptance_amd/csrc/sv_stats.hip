@@ -301,17 +301,21 @@ __device__ __forceinline__ void chunk_lse_pieces(const DT* __restrict__ row, int
   const int64_t wlo = lo + w * R;
   const int64_t whi = wlo + R < hi ? wlo + R : hi;
   const uint4* __restrict__ vp = reinterpret_cast<const uint4*>(row);
-  // A trip wholly inside the wave's range needs no predicates (and, without a mask, no selects).
-  auto load_trip = [&](int64_t p0, bool whole, uint4* q, uint32_t* mb) {
+  // Every lane loads (past the wave's range it reloads the range's last run and discards it): a load under a
+  // branch would make the wait for this trip's data also wait for the next trip's, which the loop issues
+  // before reducing this one.
+  auto load_trip = [&](int64_t p0, uint4* q, uint32_t* mb) {
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int64_t v = p0 + int64_t(u * kWave + lane) * E;
-      q[u] = whole || v < whi ? load_stream(vp + v / E) : make_uint4(0u, 0u, 0u, 0u);
+      const uint4 x = load_stream(vp + (v < whi ? v : whi - E) / E);
+      q[u] = v < whi ? x : make_uint4(0u, 0u, 0u, 0u);
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int64_t v = p0 + int64_t(u * kWave + lane) * E;
-      mb[u] = whole || v < whi ? run_mask<MASK>(mrow, v, nw) : 0u;   // past the chunk: nothing
+      const uint32_t x = run_mask<MASK>(mrow, v < whi ? v : whi - E, nw);
+      mb[u] = v < whi ? x : 0u;   // past the chunk: nothing
     }
   };
   auto piece = [&](const uint4* q, const uint32_t* mb, bool whole, float& pm, float& pz) {
@@ -337,15 +341,16 @@ __device__ __forceinline__ void chunk_lse_pieces(const DT* __restrict__ row, int
   float m = -INFINITY, z = 0.f;
   uint4 q[kUnroll];
   uint32_t mb[kUnroll];
-  if (wlo < whi) load_trip(wlo, wlo + PW <= whi, q, mb);
-  for (int64_t p0 = wlo; p0 < whi; p0 += PW) {
-    const bool whole = p0 + PW <= whi;
+  if (wlo < whi) load_trip(wlo, q, mb);
+  int64_t p0 = wlo;
+  // Every piece but the wave's last is whole and has a successor, whose loads go out first.
+  for (; p0 + PW < whi; p0 += PW) {
     uint4 qn[kUnroll];
     uint32_t mbn[kUnroll];
-    if (p0 + PW < whi) load_trip(p0 + PW, p0 + 2 * PW <= whi, qn, mbn);
+    load_trip(p0 + PW, qn, mbn);
+    __builtin_amdgcn_sched_barrier(0);   // keep the successor's loads ahead of this piece's reduction
     float pm, pz;
-    if (whole) piece(q, mb, true, pm, pz);
-    else piece(q, mb, false, pm, pz);
+    piece(q, mb, true, pm, pz);
     if (lane == 0) prow[p0 / PW] = make_float2(pm, pz);
     merge_mz(m, z, pm, pz);
 #pragma unroll
@@ -353,6 +358,13 @@ __device__ __forceinline__ void chunk_lse_pieces(const DT* __restrict__ row, int
       q[u] = qn[u];
       mb[u] = mbn[u];
     }
+  }
+  if (p0 < whi) {
+    float pm, pz;
+    if (p0 + PW <= whi) piece(q, mb, true, pm, pz);
+    else piece(q, mb, false, pm, pz);
+    if (lane == 0) prow[p0 / PW] = make_float2(pm, pz);
+    merge_mz(m, z, pm, pz);
   }
   if (lane == 0) {
     red_f[w] = m;
