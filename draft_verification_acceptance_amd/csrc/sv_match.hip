@@ -9,8 +9,9 @@
 // stored the (m, z) of every piece of the row (2048 tokens in bf16) or, for rows that are not 16-byte
 // aligned, of its chunks, so the unit holding u * Z is known from those masses z_i 2^(m_i - m); the wave
 // then narrows that unit down (each lane sums a contiguous range of it in float64, a wave scan picks the
-// lane whose range holds the target, and so on until a lane holds at most 8 tokens). Only that unit of the
-// row is read (4 KB per row for a bf16 piece); the narrower levels hit the cache.
+// lane whose range holds the target, and so on until a lane holds at most 8 tokens; a unit of at most 2048
+// tokens, a bf16 piece, is decided in one round: each lane holds its 32 tokens and the picked lane walks
+// them). Only that unit of the row is read (4 KB per row for a bf16 piece).
 #include "sv_scan.h"
 
 namespace sv {
@@ -20,10 +21,11 @@ namespace {
 constexpr int kMatchThreads = 1024;
 constexpr int kMatchWaves = kMatchThreads / kWave;
 constexpr int kSumUnrollStream = SV_STATS_UNROLL;   // runs per lane in one trip of the stream: a piece
-// 8-token runs in flight per lane while a range is summed (32 VGPRs of raw words for either type)
+// 8-token runs in flight per lane while a range is summed (16 VGPRs of raw words for either type; the
+// multi-level draw serves units wider than a piece, which only rows without piece partials have)
 template <typename DT>
 constexpr int sum_unroll() {
-  return sizeof(DT) == 2 ? 6 : 4;
+  return sizeof(DT) == 2 ? 4 : 2;
 }
 
 // Raw bits of the logits of tokens [e, e + 8) of a row (bf16: one 16-byte word, fp32: two), -inf from `end`
@@ -166,6 +168,83 @@ __device__ int wave_draw(const DT* row, int a, int n, double t, float coef, floa
   return a;
 }
 
+// wave_draw for a unit of at most kWave * 32 tokens (a stream piece) in one round of loads: every lane holds
+// its whole range (at most 4 runs of 8) in registers; a wave scan of the lane sums picks the lane, whose
+// words are then read out (readlane) so that lane l weighs its l-th token, and a second wave scan picks the
+// token. Same contract as wave_draw.
+template <typename DT>
+__device__ int wave_draw_small(const DT* row, int a, int n, double t, float coef, float m, const uint32_t* mrow,
+                               int64_t mw, double& cum, double& w_tok) {
+  constexpr int kRuns = 4;
+  constexpr int kWords = sizeof(DT) == 2 ? 4 : 8;   // 32-bit words per 8-token run
+  constexpr int kTokPerWord = 4 / int(sizeof(DT));
+  const int lane = lane_id();
+  int per = (n + kWave - 1) / kWave;
+  if (per > 8) per = (per + 7) / 8 * 8;   // 8-token runs stay 16-byte aligned
+  const int la = a + min(n, lane * per);
+  const int lb = a + min(n, (lane + 1) * per);
+  Raw8 r[kRuns];
+#pragma unroll
+  for (int k = 0; k < kRuns; ++k) {
+    r[k].a = make_uint4(0u, 0u, 0u, 0u);
+    r[k].b = r[k].a;
+    if (la + 8 * k < lb) load_raw8<DT>(row, la + 8 * k, lb, r[k]);
+  }
+  double s = 0.0;
+#pragma unroll
+  for (int k = 0; k < kRuns; ++k) {
+    if (la + 8 * k < lb) {
+      float w[8];
+      weights8<DT>(r[k], la + 8 * k, coef, m, mrow, mw, w);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) s += double(w[j]);
+    }
+  }
+  double incl = wave_inclusive_sum(s);
+  uint64_t hit = __ballot(s > 0.0 && t < incl);
+  int f;
+  if (hit) {
+    f = __ffsll((unsigned long long)hit) - 1;
+  } else {
+    const uint64_t pos = __ballot(s > 0.0);
+    f = pos ? 63 - __clzll((long long)pos) : 0;
+  }
+  const double ex_f = __shfl(incl - s, f);
+  t -= ex_f;
+  // Second level: lane l weighs token la_f + l of lane f's range (its word read out of lane f's registers).
+  const int la_f = __shfl(la, f);
+  const int nt = __shfl(lb, f) - la_f;   // at most 32
+  const int widx = lane / kTokPerWord;
+  uint32_t word = 0u;
+#pragma unroll
+  for (int k = 0; k < kRuns; ++k) {
+    const uint32_t rw[8] = {r[k].a.x, r[k].a.y, r[k].a.z, r[k].a.w, r[k].b.x, r[k].b.y, r[k].b.z, r[k].b.w};
+#pragma unroll
+    for (int q = 0; q < kWords; ++q) {
+      const uint32_t v = uint32_t(__builtin_amdgcn_readlane(int(rw[q]), f));
+      if (widx == k * kWords + q) word = v;
+    }
+  }
+  float x;
+  if (sizeof(DT) == 2) x = __uint_as_float((lane & 1) ? (word & 0xFFFF0000u) : (word << 16));
+  else x = __uint_as_float(word);
+  const int tok_l = la_f + lane;
+  const bool allowed = lane < nt && (mrow == nullptr || mask_allows(mrow, tok_l));
+  const double w1 = allowed ? double(exp2_fast(fmaf(x, coef, -m))) : 0.0;
+  incl = wave_inclusive_sum(w1);
+  hit = __ballot(w1 > 0.0 && t < incl);
+  int g;
+  if (hit) {
+    g = __ffsll((unsigned long long)hit) - 1;
+  } else {   // rounding left t past the range: its last token with positive weight
+    const uint64_t pos = __ballot(w1 > 0.0);
+    g = pos ? 63 - __clzll((long long)pos) : 0;
+  }
+  cum = ex_f + __shfl(incl - w1, g);
+  w_tok = __shfl(w1, g);
+  return la_f + g;
+}
+
 // Masses of the units a row's CDF is first split into, in row order: the stream's pieces (when it stored
 // them) or its chunks. unit_mass(i) = z_i 2^(m_i - m) for the row max m, as a float64.
 struct RowUnits {
@@ -188,15 +267,21 @@ struct RowUnits {
   }
 };
 
+// unit_mass of a unit whose (m_i, z_i) is already loaded.
+__device__ __forceinline__ double unit_mass(float2 mz, float m) {
+  return mz.y > 0.f ? double(mz.y) * exp2(double(mz.x) - double(m)) : 0.0;
+}
+
+// Unit masses each lane keeps in registers (units lane + 64 k): rows of up to 128 units never reload them.
+constexpr int kUnitRegs = 4;
+
 template <typename DT>
 __global__ __launch_bounds__(kMatchThreads) void k_match(VerifyParams p) {
   __shared__ int32_t s_d[kMaxLen];     // d_{j+1} per row j < m
   __shared__ int32_t s_t[kMaxLen];     // the sample t_j of row j
-  __shared__ float s_u[kMaxLen];       // sanitized uniform of row j
   __shared__ float s_m[kMaxLen];       // row max (log2 units)
   __shared__ float s_z[kMaxLen];       // row normaliser, float (accept_prob, status)
   __shared__ float s_g[kMaxLen];       // row j's logit at d_{j+1} (gathered while streaming)
-  __shared__ double s_Z[kMaxLen];      // row normaliser over its units, float64 (the draw)
   __shared__ uint8_t s_near[kMaxLen];
   __shared__ uint32_t s_flags;
   __shared__ int s_r, s_stop;
@@ -230,104 +315,127 @@ __global__ __launch_bounds__(kMatchThreads) void k_match(VerifyParams p) {
     return u;
   };
 
-  // Phase 1, every row (one wave per row): its chunk partials merged lane-parallel (status, row max,
-  // normaliser, the gathered logit), its unit masses totalled in float64; its draft token and uniform.
+  // Rows in groups of 16 in row order, one wave per row. Each wave loads what its row needs in one round
+  // (its chunk partials, the raw (m, z) of its units, its draft token and uniforms), merges the partials
+  // (status, row max, normaliser, the gathered logit), totals its unit masses in float64 and, until a group
+  // has held a mismatch, draws its sample: the unit holding u * Z from the masses in registers, then the
+  // token inside that unit. Later groups still merge their partials (their status bits count).
   uint32_t fl = 0;
-  for (int j = wv; j < len; j += kMatchWaves) {
-    float mj = -INFINITY, zj = 0.f, gj = 0.f;
-    bool gathered = false;
-    for (int c0 = 0; c0 < S; c0 += kWave) {
-      const int c = c0 + lane;
-      Part pt{};
-      pt.a = -INFINITY;
-      if (c < S) pt = load_part(gp + size_t(j) * S + c, true);
-      float cm = pt.a, cz = c < S ? pt.b : 0.f;
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) merge_mz(cm, cz, __shfl_xor(cm, o), __shfl_xor(cz, o));
-      merge_mz(mj, zj, cm, cz);
-      const uint64_t gm = __ballot(c < S && (pt.flags & kPartGathered));
-      if (gm) {
-        gj = __shfl(pt.g, __ffsll((unsigned long long)gm) - 1);
-        gathered = true;
-      }
-    }
-    const RowUnits ru = units(j);
-    double Z = 0.0;
-    for (int i0 = 0; i0 < ru.n; i0 += kWave) Z += wave_sum(i0 + lane < ru.n ? ru.mass(i0 + lane, mj) : 0.0);
-    if (lane == 0) {
-      const int32_t d = j < m ? p.draft_tokens[dr0 + j] : -1;
-      const float u_raw = j < m ? p.u_accept[dr0 + j] : p.u_final[b];
-      uint32_t f = 0;
-      if (j < m && !(d >= 0 && int64_t(d) < p.V)) f |= SPEC_ST_BAD_TOKEN;
-      bool ubad = false;
-      s_u[j] = sanitize_u(u_raw, ubad);
-      if (ubad) f |= SPEC_ST_BAD_UNIFORM;
-      if (z_bad(zj)) f |= SPEC_ST_NONFINITE;
-      s_d[j] = d;
-      s_m[j] = mj;
-      s_z[j] = zj;
-      s_g[j] = gathered ? gj : 0.f;
-      s_Z[j] = Z;
-      fl |= f;
-    }
-  }
-  if (fl) atomicOr(&s_flags, fl);
-  __syncthreads();
-
-  // Phase 2: the samples, 16 rows at a time in row order, until a group holds a mismatch.
+  bool stopped = false;
   for (int j0 = 0; j0 < len; j0 += kMatchWaves) {
     const int j = j0 + wv;
     if (j < len) {
-      const float M = s_m[j];
-      const double Z = s_Z[j];
-      const double T = double(s_u[j]) * Z;
       const RowUnits ru = units(j);
-      // the unit holding T (the first with positive mass whose cumulative mass passes T; rounding past the
-      // end: the last with positive mass)
-      int usel = -1, ulast = -1;
-      double cum0 = 0.0, cum_last = 0.0, carry = 0.0;
-      for (int i0 = 0; i0 < ru.n && usel < 0; i0 += kWave) {
-        const int i = i0 + lane;
-        const double mass = i < ru.n ? ru.mass(i, M) : 0.0;
-        const double incl = carry + wave_inclusive_sum(mass);
-        const uint64_t hit = __ballot(mass > 0.0 && T < incl);
-        if (hit) {
-          const int f = __ffsll((unsigned long long)hit) - 1;
-          usel = i0 + f;
-          cum0 = __shfl(incl - mass, f);
+      const Part* rowp = gp + size_t(j) * S;
+      const bool regs = ru.pieces ? ru.n <= kWave * kUnitRegs : S <= kWave;
+      // ---- one round of loads; every lane loads (clamped indices), what is out of range is discarded
+      const Part pt0 = load_part(rowp + min(lane, S - 1), true);
+      float2 ur[kUnitRegs];
+#pragma unroll
+      for (int k = 0; k < kUnitRegs; ++k)
+        ur[k] = ru.pieces ? ru.pieces[min(lane + kWave * k, ru.n - 1)] : make_float2(pt0.a, pt0.b);
+      const int jd = m > 0 ? min(j, m - 1) : 0;
+      const int32_t d_ld = m > 0 ? p.draft_tokens[dr0 + jd] : -1;
+      const float ua_ld = m > 0 ? p.u_accept[dr0 + jd] : 0.f;
+      const float uf_ld = p.u_final[b];
+      // ---- the chunk partials, merged lane-parallel
+      float mj = -INFINITY, zj = 0.f, gj = 0.f;
+      bool gathered = false;
+      for (int c0 = 0; c0 < S; c0 += kWave) {
+        const int c = c0 + lane;
+        const Part pt = c0 == 0 ? pt0 : load_part(rowp + min(c, S - 1), true);
+        float cm = c < S ? pt.a : -INFINITY, cz = c < S ? pt.b : 0.f;
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) merge_mz(cm, cz, __shfl_xor(cm, o), __shfl_xor(cz, o));
+        merge_mz(mj, zj, cm, cz);
+        const uint64_t gm = __ballot(c < S && (pt.flags & kPartGathered));
+        if (gm) {
+          gj = __shfl(pt.g, __ffsll((unsigned long long)gm) - 1);
+          gathered = true;
         }
-        const uint64_t pos = __ballot(mass > 0.0);
-        if (pos) {
-          const int f = 63 - __clzll((long long)pos);
-          ulast = i0 + f;
-          cum_last = __shfl(incl - mass, f);
+      }
+      // ---- unit masses (float64) and their total Z
+      double ms[kUnitRegs];
+      double Z = 0.0;
+      if (regs) {
+#pragma unroll
+        for (int k = 0; k < kUnitRegs; ++k) {
+          ms[k] = lane + kWave * k < ru.n ? unit_mass(ur[k], mj) : 0.0;
+          if (kWave * k < ru.n) Z += wave_sum(ms[k]);
         }
-        carry = __shfl(incl, kWave - 1);
+      } else {
+        for (int i0 = 0; i0 < ru.n; i0 += kWave) Z += wave_sum(i0 + lane < ru.n ? ru.mass(i0 + lane, mj) : 0.0);
       }
-      if (usel < 0) {   // rounding left u * Z past every unit (or nothing has mass)
-        usel = ulast < 0 ? 0 : ulast;
-        cum0 = ulast < 0 ? 0.0 : cum_last;
-      }
-      const int a = int(int64_t(usel) * ru.width);
-      const int n = int(min(p.V, int64_t(usel + 1) * ru.width)) - a;
-      const DT* row = static_cast<const DT*>(p.target) + (off0 + j) * p.V;
-      const uint32_t* mrow = p.mask ? p.mask + (off0 + j) * p.mask_words : nullptr;
-      double cum1, w_tok;
-      const int tok = wave_draw<DT>(row, a, n, T - cum0, p.coef, M, mrow, p.mask_words, cum1, w_tok);
+      const int32_t d = j < m ? d_ld : -1;
+      bool ubad = false;
+      const float u = sanitize_u(j < m ? ua_ld : uf_ld, ubad);
       if (lane == 0) {
-        // Too close to call: u within 1e-5 of a step of the normalised CDF.
-        const double u = double(s_u[j]);
-        const double lo = (cum0 + cum1) / Z;
-        const double gap = fmin(u - lo, lo + w_tok / Z - u);
-        s_t[j] = tok;
-        s_near[j] = !(gap >= double(kNear));
+        uint32_t f = 0;
+        if (j < m && !(d >= 0 && int64_t(d) < p.V)) f |= SPEC_ST_BAD_TOKEN;
+        if (ubad) f |= SPEC_ST_BAD_UNIFORM;
+        if (z_bad(zj)) f |= SPEC_ST_NONFINITE;
+        s_d[j] = d;
+        s_m[j] = mj;
+        s_z[j] = zj;
+        s_g[j] = gathered ? gj : 0.f;
+        fl |= f;
+      }
+      if (!stopped) {
+        const double T = double(u) * Z;
+        // the unit holding T (the first with positive mass whose cumulative mass passes T; rounding past the
+        // end: the last with positive mass)
+        int usel = -1, ulast = -1;
+        double cum0 = 0.0, cum_last = 0.0, carry = 0.0;
+        auto scan_block = [&](int i0, double mass) {
+          const double incl = carry + wave_inclusive_sum(mass);
+          const uint64_t hit = __ballot(mass > 0.0 && T < incl);
+          if (hit) {
+            const int f = __ffsll((unsigned long long)hit) - 1;
+            usel = i0 + f;
+            cum0 = __shfl(incl - mass, f);
+          }
+          const uint64_t pos = __ballot(mass > 0.0);
+          if (pos) {
+            const int f = 63 - __clzll((long long)pos);
+            ulast = i0 + f;
+            cum_last = __shfl(incl - mass, f);
+          }
+          carry = __shfl(incl, kWave - 1);
+        };
+        if (regs) {
+#pragma unroll
+          for (int k = 0; k < kUnitRegs; ++k)
+            if (usel < 0 && kWave * k < ru.n) scan_block(kWave * k, ms[k]);
+        } else {
+          for (int i0 = 0; i0 < ru.n && usel < 0; i0 += kWave)
+            scan_block(i0, i0 + lane < ru.n ? ru.mass(i0 + lane, mj) : 0.0);
+        }
+        if (usel < 0) {   // rounding left u * Z past every unit (or nothing has mass)
+          usel = ulast < 0 ? 0 : ulast;
+          cum0 = ulast < 0 ? 0.0 : cum_last;
+        }
+        const int a = int(int64_t(usel) * ru.width);
+        const int n = int(min(p.V, int64_t(usel + 1) * ru.width)) - a;
+        const DT* row = static_cast<const DT*>(p.target) + (off0 + j) * p.V;
+        const uint32_t* mrow = p.mask ? p.mask + (off0 + j) * p.mask_words : nullptr;
+        double cum1, w_tok;
+        const int tok = n <= kWave * 32
+                            ? wave_draw_small<DT>(row, a, n, T - cum0, p.coef, mj, mrow, p.mask_words, cum1, w_tok)
+                            : wave_draw<DT>(row, a, n, T - cum0, p.coef, mj, mrow, p.mask_words, cum1, w_tok);
+        if (lane == 0) {
+          // Too close to call: u within 1e-5 of a step of the normalised CDF.
+          const double lo = (cum0 + cum1) / Z;
+          const double gap = fmin(double(u) - lo, lo + w_tok / Z - double(u));
+          s_t[j] = tok;
+          s_near[j] = !(gap >= double(kNear));
+        }
       }
     }
     __syncthreads();
-    if (tid == 0) {
+    if (!stopped && tid == 0) {
       for (int jj = j0; jj < min(len, j0 + kMatchWaves); ++jj) {
-        const int32_t d = s_d[jj];
-        if (jj == m || !(d >= 0 && int64_t(d) < p.V && d == s_t[jj])) {
+        const int32_t dd = s_d[jj];
+        if (jj == m || !(dd >= 0 && int64_t(dd) < p.V && dd == s_t[jj])) {
           s_r = jj;
           s_stop = 1;
           break;
@@ -335,9 +443,9 @@ __global__ __launch_bounds__(kMatchThreads) void k_match(VerifyParams p) {
       }
     }
     __syncthreads();
-    if (s_stop) break;
+    stopped = s_stop != 0;
   }
-
+  if (fl) atomicOr(&s_flags, fl);
   const int r = s_r;
   const int32_t bonus = s_t[r];
   uint32_t near = 0;
