@@ -142,6 +142,40 @@ __device__ __forceinline__ float wave_sum_dpp(float v) {
   return (row_lanes(v, 0) + row_lanes(v, 16)) + (row_lanes(v, 32) + row_lanes(v, 48));
 }
 
+// The same for float64 (each DPP move takes one 32-bit half), and an inclusive prefix sum: a Hillis-Steele
+// scan inside each 16-lane row (DPP row shifts by 1, 2, 4, 8; lanes shifted in from outside the row read 0),
+// then the totals of the rows before added in. Every lane must be active.
+template <int CTRL, bool ZERO_OUTSIDE>
+__device__ __forceinline__ double dpp_d(double v) {
+  const unsigned long long b = (unsigned long long)__double_as_longlong(v);
+  const int lo = __builtin_amdgcn_update_dpp(0, int(uint32_t(b)), CTRL, 0xF, 0xF, ZERO_OUTSIDE);
+  const int hi = __builtin_amdgcn_update_dpp(0, int(uint32_t(b >> 32)), CTRL, 0xF, 0xF, ZERO_OUTSIDE);
+  return __longlong_as_double((long long)((unsigned long long)uint32_t(hi) << 32 | uint32_t(lo)));
+}
+__device__ __forceinline__ double row_lanes_d(double v, int l) {
+  const unsigned long long b = (unsigned long long)__double_as_longlong(v);
+  const uint32_t lo = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(b)), l));
+  const uint32_t hi = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(b >> 32)), l));
+  return __longlong_as_double((long long)((unsigned long long)hi << 32 | lo));
+}
+__device__ __forceinline__ double wave_sum_dpp(double v) {
+  v += dpp_d<0xB1, false>(v);
+  v += dpp_d<0x4E, false>(v);
+  v += dpp_d<0x141, false>(v);
+  v += dpp_d<0x140, false>(v);
+  return (row_lanes_d(v, 0) + row_lanes_d(v, 16)) + (row_lanes_d(v, 32) + row_lanes_d(v, 48));
+}
+__device__ __forceinline__ double wave_inclusive_sum_dpp(double v) {
+  v += dpp_d<0x111, true>(v);
+  v += dpp_d<0x112, true>(v);
+  v += dpp_d<0x114, true>(v);
+  v += dpp_d<0x118, true>(v);
+  const double r0 = row_lanes_d(v, 15), r1 = row_lanes_d(v, 31), r2 = row_lanes_d(v, 47);
+  const int row = int(threadIdx.x & (kWave - 1)) >> 4;
+  const double before = row == 0 ? 0.0 : row == 1 ? r0 : row == 2 ? r0 + r1 : (r0 + r1) + r2;
+  return v + before;
+}
+
 template <typename T>
 __device__ __forceinline__ T wave_sum(T v) {
 #pragma unroll

@@ -123,7 +123,7 @@ __device__ int wave_draw(const DT* row, int a, int n, double t, float coef, floa
     } else {
       s = range_sum<DT>(row, la, lb, coef, m, mrow, mw);
     }
-    const double incl = wave_inclusive_sum(s);
+    const double incl = wave_inclusive_sum_dpp(s);
     const double excl = incl - s;
     const uint64_t hit = __ballot(s > 0.0 && t < incl);
     int f;
@@ -133,7 +133,7 @@ __device__ int wave_draw(const DT* row, int a, int n, double t, float coef, floa
       const uint64_t pos = __ballot(s > 0.0);
       f = pos ? 63 - __clzll((long long)pos) : 0;
     }
-    const double ex_f = __shfl(excl, f);
+    const double ex_f = row_lanes_d(excl, f);
     t -= ex_f;
     cum += ex_f;
     if (per <= 8) {
@@ -157,13 +157,13 @@ __device__ int wave_draw(const DT* row, int a, int n, double t, float coef, floa
         if (first >= 0) { pick = first; before = b_first; wp = w_first; }
         else if (last >= 0) { pick = last; before = b_last; wp = w_last; }
       }
-      const int tok = __shfl(la + pick, f);
-      cum += __shfl(before, f);
-      w_tok = __shfl(wp, f);
+      const int tok = __builtin_amdgcn_readlane(la + pick, f);
+      cum += row_lanes_d(before, f);
+      w_tok = row_lanes_d(wp, f);
       return tok;
     }
-    a = __shfl(la, f);
-    n = __shfl(lb, f) - a;
+    a = __builtin_amdgcn_readlane(la, f);
+    n = __builtin_amdgcn_readlane(lb, f) - a;
   }
   return a;
 }
@@ -190,17 +190,18 @@ __device__ int wave_draw_small(const DT* row, int a, int n, double t, float coef
     r[k].b = r[k].a;
     if (la + 8 * k < lb) load_raw8<DT>(row, la + 8 * k, lb, r[k]);
   }
+  // Lane sums: each run of 8 weights added in fp32 (relative error below 1e-6, far inside the 1e-5 band a
+  // draw is flagged in), the runs in float64.
   double s = 0.0;
 #pragma unroll
   for (int k = 0; k < kRuns; ++k) {
     if (la + 8 * k < lb) {
       float w[8];
       weights8<DT>(r[k], la + 8 * k, coef, m, mrow, mw, w);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) s += double(w[j]);
+      s += double(((w[0] + w[1]) + (w[2] + w[3])) + ((w[4] + w[5]) + (w[6] + w[7])));
     }
   }
-  double incl = wave_inclusive_sum(s);
+  double incl = wave_inclusive_sum_dpp(s);
   uint64_t hit = __ballot(s > 0.0 && t < incl);
   int f;
   if (hit) {
@@ -209,11 +210,11 @@ __device__ int wave_draw_small(const DT* row, int a, int n, double t, float coef
     const uint64_t pos = __ballot(s > 0.0);
     f = pos ? 63 - __clzll((long long)pos) : 0;
   }
-  const double ex_f = __shfl(incl - s, f);
+  const double ex_f = row_lanes_d(incl - s, f);
   t -= ex_f;
   // Second level: lane l weighs token la_f + l of lane f's range (its word read out of lane f's registers).
-  const int la_f = __shfl(la, f);
-  const int nt = __shfl(lb, f) - la_f;   // at most 32
+  const int la_f = __builtin_amdgcn_readlane(la, f);
+  const int nt = __builtin_amdgcn_readlane(lb, f) - la_f;   // at most 32
   const int widx = lane / kTokPerWord;
   uint32_t word = 0u;
 #pragma unroll
@@ -231,7 +232,7 @@ __device__ int wave_draw_small(const DT* row, int a, int n, double t, float coef
   const int tok_l = la_f + lane;
   const bool allowed = lane < nt && (mrow == nullptr || mask_allows(mrow, tok_l));
   const double w1 = allowed ? double(exp2_fast(fmaf(x, coef, -m))) : 0.0;
-  incl = wave_inclusive_sum(w1);
+  incl = wave_inclusive_sum_dpp(w1);
   hit = __ballot(w1 > 0.0 && t < incl);
   int g;
   if (hit) {
@@ -240,8 +241,8 @@ __device__ int wave_draw_small(const DT* row, int a, int n, double t, float coef
     const uint64_t pos = __ballot(w1 > 0.0);
     g = pos ? 63 - __clzll((long long)pos) : 0;
   }
-  cum = ex_f + __shfl(incl - w1, g);
-  w_tok = __shfl(w1, g);
+  cum = ex_f + row_lanes_d(incl - w1, g);
+  w_tok = row_lanes_d(w1, g);
   return la_f + g;
 }
 
@@ -263,13 +264,14 @@ struct RowUnits {
       mi = pt.a;
       zi = pt.b;
     }
-    return zi > 0.f ? double(zi) * exp2(double(mi) - double(m)) : 0.0;
+    return zi > 0.f ? double(zi) * double(exp2_fast(mi - m)) : 0.0;
   }
 };
 
-// unit_mass of a unit whose (m_i, z_i) is already loaded.
+// unit_mass of a unit whose (m_i, z_i) is already loaded. 2^(m_i - m) in fp32 (m_i <= m: a factor in
+// (0, 1], as accurate as the fp32 z_i it scales).
 __device__ __forceinline__ double unit_mass(float2 mz, float m) {
-  return mz.y > 0.f ? double(mz.y) * exp2(double(mz.x) - double(m)) : 0.0;
+  return mz.y > 0.f ? double(mz.y) * double(exp2_fast(mz.x - m)) : 0.0;
 }
 
 // Unit masses each lane keeps in registers (units lane + 64 k): rows of up to 128 units never reload them.
@@ -345,12 +347,19 @@ __global__ __launch_bounds__(kMatchThreads) void k_match(VerifyParams p) {
         const int c = c0 + lane;
         const Part pt = c0 == 0 ? pt0 : load_part(rowp + min(c, S - 1), true);
         float cm = c < S ? pt.a : -INFINITY, cz = c < S ? pt.b : 0.f;
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) merge_mz(cm, cz, __shfl_xor(cm, o), __shfl_xor(cz, o));
-        merge_mz(mj, zj, cm, cz);
+        // butterfly inside each 16-lane row (DPP), then the four row results
+        merge_mz(cm, cz, dpp_f<0xB1>(cm), dpp_f<0xB1>(cz));
+        merge_mz(cm, cz, dpp_f<0x4E>(cm), dpp_f<0x4E>(cz));
+        merge_mz(cm, cz, dpp_f<0x141>(cm), dpp_f<0x141>(cz));
+        merge_mz(cm, cz, dpp_f<0x140>(cm), dpp_f<0x140>(cz));
+        float rm = row_lanes(cm, 0), rz = row_lanes(cz, 0);
+        merge_mz(rm, rz, row_lanes(cm, 16), row_lanes(cz, 16));
+        merge_mz(rm, rz, row_lanes(cm, 32), row_lanes(cz, 32));
+        merge_mz(rm, rz, row_lanes(cm, 48), row_lanes(cz, 48));
+        merge_mz(mj, zj, rm, rz);
         const uint64_t gm = __ballot(c < S && (pt.flags & kPartGathered));
         if (gm) {
-          gj = __shfl(pt.g, __ffsll((unsigned long long)gm) - 1);
+          gj = row_lanes(pt.g, __ffsll((unsigned long long)gm) - 1);
           gathered = true;
         }
       }
@@ -361,10 +370,10 @@ __global__ __launch_bounds__(kMatchThreads) void k_match(VerifyParams p) {
 #pragma unroll
         for (int k = 0; k < kUnitRegs; ++k) {
           ms[k] = lane + kWave * k < ru.n ? unit_mass(ur[k], mj) : 0.0;
-          if (kWave * k < ru.n) Z += wave_sum(ms[k]);
+          if (kWave * k < ru.n) Z += wave_sum_dpp(ms[k]);
         }
       } else {
-        for (int i0 = 0; i0 < ru.n; i0 += kWave) Z += wave_sum(i0 + lane < ru.n ? ru.mass(i0 + lane, mj) : 0.0);
+        for (int i0 = 0; i0 < ru.n; i0 += kWave) Z += wave_sum_dpp(i0 + lane < ru.n ? ru.mass(i0 + lane, mj) : 0.0);
       }
       const int32_t d = j < m ? d_ld : -1;
       bool ubad = false;
@@ -387,20 +396,20 @@ __global__ __launch_bounds__(kMatchThreads) void k_match(VerifyParams p) {
         int usel = -1, ulast = -1;
         double cum0 = 0.0, cum_last = 0.0, carry = 0.0;
         auto scan_block = [&](int i0, double mass) {
-          const double incl = carry + wave_inclusive_sum(mass);
+          const double incl = carry + wave_inclusive_sum_dpp(mass);
           const uint64_t hit = __ballot(mass > 0.0 && T < incl);
           if (hit) {
             const int f = __ffsll((unsigned long long)hit) - 1;
             usel = i0 + f;
-            cum0 = __shfl(incl - mass, f);
+            cum0 = row_lanes_d(incl - mass, f);
           }
           const uint64_t pos = __ballot(mass > 0.0);
           if (pos) {
             const int f = 63 - __clzll((long long)pos);
             ulast = i0 + f;
-            cum_last = __shfl(incl - mass, f);
+            cum_last = row_lanes_d(incl - mass, f);
           }
-          carry = __shfl(incl, kWave - 1);
+          carry = row_lanes_d(incl, kWave - 1);
         };
         if (regs) {
 #pragma unroll
