@@ -13,7 +13,8 @@ roofline: the dominant kernel (k_stats, the logits stream) timed with HIP events
 stop timestamps on the launch stream (hipExtLaunchKernel), against its algorithmic bytes (every target and
 draft row read once); read_floor: a plain read of the same byte count (spec_read_probe) timed the same way,
 the rate HBM actually delivers at this size. cpu_baseline: the fp64 CPU oracle timed on this host on the
-same inputs.
+same inputs, one thread; cpu_baseline_parallel: the same oracle with the requests split over one forked
+process per core of this process's CPU share (at most 16), run before the GPU is touched.
 
     python bench.py [--steps K] [--warmup W]
                     [--workload chain_rejection|block_greedy|tree|ragged|chain_sparse|block_sample|chain_rejection_masked]
@@ -371,6 +372,72 @@ def cpu_baseline(name: str, budget_s: float = 12.0) -> dict:
                       f"{w.total_rows} verify rows, fp64 numpy, one thread) incl. commit; {dt:.1f} s"}
 
 
+_PAR = {}   # the workload the forked oracle workers split (set before the pool forks)
+
+
+def _oracle_requests(args):
+    """One worker of the row-parallel oracle run: full passes over requests [b0, b1) of the chain workload in
+    _PAR until the time budget, verify + commit as in cpu_baseline."""
+    import numpy as np
+
+    import oracle
+    from draft_verification_acceptance_amd import workloads as W
+    b0, b1, budget_s = args
+    w, mode = _PAR["w"], _PAR["mode"]
+    off = w.offsets
+    r0, r1 = int(off[b0]), int(off[b1])
+    d0, d1 = r0 - b0, r1 - b1
+    offs = (off[b0:b1 + 1] - r0).astype(np.int32)
+    sl = lambda a, lo, hi: None if a is None else a[lo:hi]
+    slots = W.verify_slots_for(r1 - r0)
+    seq = W.seq_lens_for(b1 - b0)
+    rows = passes = 0
+    t0 = time.perf_counter()
+    while True:
+        o = oracle.verify_chain(w.target[r0:r1], offs, w.draft_tokens[d0:d1], mode, draft=sl(w.draft, d0, d1),
+                                u_accept=w.u_accept[d0:d1], u_final=w.u_final[b0:b1], temperature=w.temperature,
+                                max_verify_len=w.max_verify_len, cand_ids=sl(w.cand_ids, d0, d1),
+                                cand_q=sl(w.cand_q, d0, d1))
+        oracle.commit_indices(offs, o["accept_len"], o["accept_index"], slots, seq, w.max_verify_len)
+        passes += 1
+        rows += r1 - r0
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    return rows, time.perf_counter() - t0
+
+
+def cpu_baseline_parallel(name: str, budget_s: float = 8.0) -> dict | None:
+    """The same oracle, row-parallel: the requests of the chain workload split over forked worker processes,
+    one per core of this process's CPU share (at most 16), each repeating full passes over its requests. Call
+    it before this process touches the GPU (the workers are forks of it)."""
+    import multiprocessing as mp
+
+    from draft_verification_acceptance_amd import workloads as W
+    if name == "tree":
+        return None
+    w = W.FULL[name](seed={"chain_rejection": 2000, "block_greedy": 3000, "ragged": 5000, "chain_sparse": 6000,
+                           "block_sample": 7000, "chain_rejection_masked": 2000}.get(name, 2000))
+    if name == "chain_rejection_masked" or name == "block_sample":
+        return None
+    n = max(1, min(16, len(os.sched_getaffinity(0)), w.batch))
+    _PAR["w"], _PAR["mode"] = w, w.modes[-1]
+    cuts = [round(i * w.batch / n) for i in range(n + 1)]
+    with mp.get_context("fork").Pool(n) as pool:
+        res = pool.map(_oracle_requests, [(cuts[i], cuts[i + 1], budget_s) for i in range(n)])
+    _PAR.clear()
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
+    rate = sum(r / t for r, t in res)
+    return {"value": rate, "unit": "positions/s", "cores": n, "kind": "oracle", "cpu": model,
+            "sample": f"{n} forked workers, requests split evenly over them, each repeating full passes over its "
+                      f"requests (fp64 numpy, one thread each) incl. commit for ~{budget_s:.0f} s; value = sum of "
+                      f"the workers' rates"}
+
+
 def load_traffic(name: str):
     """HBM bytes per k_stats launch from the committed rocprofv3 counter summary (profiles/), if the counters
     were taken on the current kernel sources; None otherwise."""
@@ -447,6 +514,8 @@ def main():
         copy_calibration()
         return
 
+    # The row-parallel oracle forks its workers, so it runs before anything in this process touches the GPU.
+    cpu_par = None if args.no_cpu_baseline else cpu_baseline_parallel(args.workload)
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     main_res = run_workload(args.workload, args.mode, args.steps, args.warmup)
@@ -503,6 +572,7 @@ def main():
         "mean_accept_len": main_res["mean_accept_len"],
         "status_faults": main_res["status_faults"],
         "cpu_baseline": cpu,
+        "cpu_baseline_parallel": cpu_par,
         "other_workloads": extra,
         "kernel_source_hash": kernel_source_hash(),
     }

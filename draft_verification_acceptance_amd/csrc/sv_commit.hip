@@ -70,21 +70,27 @@ __global__ __launch_bounds__(kCommitThreads) void k_commit(spec_commit_args a) {
       }
     }
     const int b = t0 + tid;
+    // the request's words, loaded with the rows (its accept length too, used only if its offsets pass)
+    const int bc = min(b, B - 1);
+    const int32_t off0_ld = a.row_offsets[bc];
+    const int32_t off1_ld = a.row_offsets[bc + 1];
+    const int32_t seq_ld = a.seq_lens[bc];
+    const int32_t r_ld = a.accept_len[bc];
     int32_t off0 = 0, len = 0, r = 0, seq = 0;
     uint32_t st = 0;
     if (b < B) {
-      off0 = a.row_offsets[b];
-      const int32_t off1 = a.row_offsets[b + 1];
+      off0 = off0_ld;
+      const int32_t off1 = off1_ld;
       len = off1 - off0;
       bool ok = off0 >= b && off1 > off0 && off1 <= T - B + b + 1 && len <= L;
       if (b == 0 && off0 != 0) ok = false;
       if (b == B - 1 && off1 != T) ok = false;
-      seq = a.seq_lens[b];
+      seq = seq_ld;
       if (!ok) {
         st = SPEC_ST_BAD_OFFSETS;
         len = 0;
       } else {
-        r = a.accept_len[b];
+        r = r_ld;
         if (r < 0 || r >= len) {
           st |= SPEC_ST_BAD_ACCEPT;
           r = r < 0 ? 0 : len - 1;
