@@ -239,8 +239,8 @@ __device__ __forceinline__ T wave_inclusive_sum(T v) {
 __device__ __forceinline__ void block_scan_d(double v, double* red, double& excl, double& incl, double& total) {
   const int lane = lane_id();
   const int w = threadIdx.x / kWave;
-  const double inc = wave_inclusive_sum(v);
-  const double prev = __shfl_up(inc, 1);
+  const double inc = wave_inclusive_sum_dpp(v);
+  const double prev = dpp_d<0x138, true>(inc);   // wave_shr:1, lane i reads lane i - 1's value exactly
   __syncthreads();
   if (lane == kWave - 1) red[w] = inc;
   __syncthreads();

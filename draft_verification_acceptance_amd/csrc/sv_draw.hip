@@ -336,7 +336,7 @@ __global__ __launch_bounds__(kThreads) void k_draw(VerifyParams p) {
       run += double(use_p ? pv[j] : w[j]);
       inc[j] = run;
     }
-    const double lane_incl = wave_inclusive_sum(run);
+    const double lane_incl = wave_inclusive_sum_dpp(run);
     const double base = sel_excl + (lane_incl - run);
     int hit = -1, lastpos = -1;
 #pragma unroll
@@ -350,25 +350,25 @@ __global__ __launch_bounds__(kThreads) void k_draw(VerifyParams p) {
     double c_lo, c_hi;
     if (hmask) {
       const int f = __ffsll((unsigned long long)hmask) - 1;
-      const int j = __shfl(hit, f);
+      const int j = __builtin_amdgcn_readlane(hit, f);
       double hi = 0.0, wj = 0.0;
 #pragma unroll
       for (int k = 0; k < 8; ++k)
         if (k == j) { hi = base + inc[k]; wj = double(use_p ? pv[k] : w[k]); }
-      c_hi = __shfl(hi, f);
-      c_lo = __shfl(hi - wj, f);
+      c_hi = row_lanes_d(hi, f);
+      c_lo = row_lanes_d(hi - wj, f);
       x = g_lo + 8 * f + j;
     } else {
       // rounding left u * Z past the segment: its last token with positive weight
       const uint64_t pmask = __ballot(lastpos >= 0);
       const int l = pmask ? 63 - __clzll((long long)pmask) : 0;
-      const int j = __shfl(lastpos, l);
+      const int j = __builtin_amdgcn_readlane(lastpos, l);
       double hi = 0.0, wj = 0.0;
 #pragma unroll
       for (int k = 0; k < 8; ++k)
         if (k == j) { hi = base + inc[k]; wj = double(use_p ? pv[k] : w[k]); }
-      c_hi = __shfl(hi, l);
-      c_lo = __shfl(hi - wj, l);
+      c_hi = row_lanes_d(hi, l);
+      c_lo = row_lanes_d(hi - wj, l);
       x = g_lo + 8 * l + (j < 0 ? 0 : j);
     }
     if (lane == 0) {
