@@ -89,6 +89,17 @@ def test_sample_match_vocab_sizes(V):
         compare_chain(ww, "sample_match", oracle_chain(ww, "sample_match"), run_chain(ww, "sample_match"))
 
 
+@pytest.mark.parametrize("V", [600_008, 600_001])
+def test_sample_match_many_units(V):
+    """Rows with more units than the draw keeps in registers: 600008 (bf16 pieces of 2048 tokens: 293 of them;
+    fp32 pieces of 1024: 586) and 600001 (not 16-byte aligned: 73 stream chunks, more than one per lane)."""
+    w = W.block_sample(seed=95, batch=6, block=3, vocab=V, temperature=0.6, parallel=False)
+    for bf16 in (True, False):
+        _say("sample_match many units", V, "bf16" if bf16 else "fp32")
+        ww = w if bf16 else _chain_from(w, W.bf16_to_f32(w.target), None)
+        compare_chain(ww, "sample_match", oracle_chain(ww, "sample_match"), run_chain(ww, "sample_match"))
+
+
 def _long_workload(seed, B, L, V, breaks):
     """Requests of L rows whose rows are all but certain (one token raised by 60): the draft copies that token
     except at the positions in `breaks[b]` (None: never), so the accepted prefix crosses the kernel's groups
