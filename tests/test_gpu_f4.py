@@ -79,7 +79,7 @@ def test_sample_match_ragged_small_vocab():
     compare_chain(w, "sample_match", oracle_chain(w, "sample_match"), run_chain(w, "sample_match"))
 
 
-@pytest.mark.parametrize("V", [1, 7, 8195, 151937])
+@pytest.mark.parametrize("V", [1, 7, 4096, 8195, 151936, 151937])   # multiples of 8: piece partials
 def test_sample_match_vocab_sizes(V):
     # peaked rows (block_sample): most draws land on a wide CDF step, so few are too close to call
     w = W.block_sample(seed=91 + V, batch=12, block=4, vocab=V, parallel=False)
