@@ -250,7 +250,10 @@ typedef struct spec_tree_args {
  *   evict_offsets[b], evict_slots  optional: the request's verify rows NOT listed in its accept_index, in
  *                                  ascending row order (their KV must stop being visible, §8.2)
  * row_offsets has the chain meaning (trees: [0, N, 2N, ...]). capacity (length of src_slots / dst_pos /
- * evict_slots) must be >= total_rows. Invalid accept_len / accept_index set SPEC_ST_BAD_ACCEPT.
+ * evict_slots) must be >= total_rows. Invalid accept_len / accept_index set SPEC_ST_BAD_ACCEPT: an
+ * accept_len outside [0, rows) is clamped into it; an accept_index entry outside the request's rows commits
+ * src_slots = -1; an entry naming a row a second time commits that row's slot again; the request evicts
+ * exactly the rows no entry names (so its evict count is rows - distinct named rows).
  */
 typedef struct spec_commit_args {
   const int32_t* row_offsets;  /* [batch+1]                    */

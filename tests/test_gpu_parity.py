@@ -425,6 +425,40 @@ def test_commit_parity_chain_and_tree():
     assert g2["status"][0] & oracle.ST_BAD_ACCEPT and g2["status"][1] & oracle.ST_BAD_ACCEPT
 
 
+@pytest.mark.parametrize("seed", [31, 32])
+def test_commit_random_accept_index(seed):
+    """Seeded commit inputs that mix the form the verify kernels write (accept_index = the request's first r + 1
+    rows) with scrambled ones: other rows of the request, rows listed twice, rows of other requests, -1, and
+    accept lengths out of range. Every output equals the oracle's."""
+    rng = np.random.default_rng(seed)
+    B = 300
+    lens = rng.integers(1, 17, B)
+    offs = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(offs[-1])
+    acc = np.full(T, -1, np.int32)
+    alen = np.zeros(B, np.int32)
+    for b in range(B):
+        o0, n = int(offs[b]), int(lens[b])
+        r = int(rng.integers(0, n))
+        kind = rng.integers(0, 6)
+        if kind == 0:                       # accept length out of range (clamped and reported)
+            alen[b] = int(rng.choice([-1, n, n + 3]))
+            acc[o0:o0 + n] = np.arange(o0, o0 + n)
+            continue
+        alen[b] = r
+        if kind <= 2:                       # the verify kernels' form
+            acc[o0:o0 + r + 1] = np.arange(o0, o0 + r + 1)
+        elif kind == 3:                     # a permutation of the request's rows
+            acc[o0:o0 + r + 1] = o0 + rng.permutation(n)[: r + 1]
+        elif kind == 4:                     # duplicates
+            acc[o0:o0 + r + 1] = o0 + rng.integers(0, max(1, r), r + 1)
+        else:                               # rows outside the request, or -1
+            acc[o0:o0 + r + 1] = rng.choice([-1, 0, T - 1, o0 + n], r + 1)
+    print("commit random", seed, flush=True)
+    _commit_check(offs, alen, acc, rng.integers(0, 1 << 40, T).astype(np.int64),
+                  rng.integers(0, 4096, B).astype(np.int32), 16)
+
+
 def test_inconsistent_offsets_are_reported_and_stay_in_bounds():
     # Offsets that describe no valid packing; every request checks its own bounds (draft rows inside
     # [0, T - B)), reports BAD_OFFSETS, and the kernels touch nothing outside the given buffers.
