@@ -118,6 +118,24 @@ def test_commit_worked_example_defgh():
     assert [g["verify_input"][int(s) - 100] for s in c["evict_slots"]] == g["temporary_kv"]
 
 
+def test_commit_invalid_accept_index_by_hand():
+    """Invalid accept_index forms, worked by hand: two requests of 5 rows (rows 0-4 and 5-9, slots 100 + row).
+    Request 0 (r = 3) lists rows 2, 2, 4, 7: row 2 twice (committed twice), row 7 outside it (committed as -1);
+    the rows it names are {2, 4}, so it evicts rows 0, 1, 3. Request 1 (accept_len 9, clamped to 4) lists its
+    rows 5..9 in order: all committed, nothing evicted. Both are flagged BAD_ACCEPT."""
+    offs = np.array([0, 5, 10])
+    acc = np.array([2, 2, 4, 7, -1, 5, 6, 7, 8, 9])
+    slots = np.arange(100, 110, dtype=np.int64)
+    c = oracle.commit_indices(offs, np.array([3, 9]), acc, slots, np.array([40, 60]), 5)
+    assert list(c["commit_offsets"]) == [0, 4, 9]
+    assert list(c["src_slots"]) == [102, 102, 104, -1, 105, 106, 107, 108, 109]
+    assert list(c["dst_pos"]) == [40, 41, 42, 43, 60, 61, 62, 63, 64]
+    assert list(c["new_seq_lens"]) == [44, 65]
+    assert list(c["evict_offsets"]) == [0, 3, 3]
+    assert list(c["evict_slots"]) == [100, 101, 103]
+    assert all(int(st) & oracle.ST_BAD_ACCEPT for st in c["status"])
+
+
 def test_verify_len_cutoff_example():
     g = golden("verify_len_cutoff.json")
     V = 32
