@@ -285,6 +285,58 @@ def test_status_bits_nan_bad_token_bad_uniform_bad_offsets():
     assert g["status"][2] & oracle.ST_BAD_OFFSETS
 
 
+@pytest.mark.parametrize("seed", [41, 42, 43])
+def test_random_faults_match_the_oracle(seed):
+    """Seeded fault injection over ragged requests: NaN, +inf and -inf logits (a few, or a whole row), draft
+    tokens outside [0, V), uniforms that are NaN, negative or >= 1; greedy, rejection and sample-then-match.
+    Every request's status and outputs equal the oracle's (a NONFINITE request: its flag)."""
+    rng = np.random.default_rng(seed)
+    V, B = 257, 24
+    lens = rng.integers(1, 7, B)
+    offs = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(offs[-1])
+    tl = rng.normal(0, 2, (T, V)).astype(np.float32)
+    dl = rng.normal(0, 2, (T - B, V)).astype(np.float32)
+    toks = rng.integers(0, V, T - B).astype(np.int32)
+    for b in range(B):                           # half the drafts agree with the target's argmax
+        o0, n = int(offs[b]), int(lens[b])
+        for j in range(n - 1):
+            if rng.random() < 0.5:
+                toks[o0 - b + j] = int(np.argmax(tl[o0 + j]))
+    ua = rng.random(T - B).astype(np.float32)
+    uf = rng.random(B).astype(np.float32)
+    for b in range(B):
+        o0, n = int(offs[b]), int(lens[b])
+        d0 = o0 - b
+        kind = int(rng.integers(0, 14))
+        row = o0 + int(rng.integers(0, n))
+        if kind == 5:
+            tl[row, rng.integers(0, V)] = np.nan
+        elif kind == 6 and n > 1:
+            dl[d0 + int(rng.integers(0, n - 1)), rng.integers(0, V)] = np.nan
+        elif kind == 7:
+            tl[row, rng.integers(0, V)] = np.inf
+        elif kind == 8:
+            tl[row, :] = -np.inf
+        elif kind == 9 and n > 1:
+            toks[d0 + int(rng.integers(0, n - 1))] = int(rng.choice([-1, V, V + 7]))
+        elif kind == 10 and n > 1:
+            ua[d0 + int(rng.integers(0, n - 1))] = rng.choice([np.nan, 1.0, -0.25, 3.0])
+        elif kind == 11:
+            uf[b] = rng.choice([np.nan, 1.0, -0.5])
+        elif kind == 12:
+            tl[row, rng.integers(0, V, 20)] = -np.inf
+        elif kind == 13 and n > 1:
+            dl[d0 + int(rng.integers(0, n - 1)), :] = -np.inf
+    w = W.ChainWorkload("faults", V, B, offs, tl, dl, toks, ua, uf, 0.9, ("greedy", "rejection", "sample_match"),
+                        6)
+    for mode in ("greedy", "rejection", "sample_match"):
+        _say("random faults", seed, mode)
+        g = run_chain(w, mode)
+        o = oracle_chain(w, mode)
+        compare_chain(w, mode, o, g)
+
+
 def test_tree_edge_cases():
     rng = np.random.default_rng(13)
     V = 50
