@@ -369,6 +369,51 @@ def test_tree_edge_cases():
                 assert g["status"][3] & oracle.ST_BAD_PARENT
 
 
+@pytest.mark.parametrize("seed", [51, 52])
+def test_random_tree_faults_match_the_oracle(seed):
+    """Seeded fault injection on trees of 12 nodes: NaN, +inf and -inf logits (a few, or a whole row), node
+    tokens outside [0, V), parents that do not precede their node, uniforms that are NaN or outside [0, 1);
+    greedy and target-only against the oracle."""
+    rng = np.random.default_rng(seed)
+    V, B, N = 97, 20, 12
+    target = rng.normal(0, 2, (B * N, V)).astype(np.float32)
+    parents = np.zeros(B * N, np.int32)
+    tokens = np.zeros(B * N, np.int32)
+    for b in range(B):
+        parents[b * N] = -1
+        for i in range(1, N):
+            p = int(rng.integers(0, i))
+            parents[b * N + i] = p
+            row = target[b * N + p]
+            tokens[b * N + i] = int(np.argmax(row)) if rng.random() < 0.5 else int(rng.integers(V))
+    ua = rng.random(B * N).astype(np.float32)
+    uf = rng.random(B).astype(np.float32)
+    for b in range(B):
+        kind = int(rng.integers(0, 12))
+        node = b * N + int(rng.integers(0, N))
+        child = b * N + int(rng.integers(1, N))
+        if kind == 4:
+            target[node, rng.integers(0, V)] = np.nan
+        elif kind == 5:
+            target[node, rng.integers(0, V)] = np.inf
+        elif kind == 6:
+            target[node, :] = -np.inf
+        elif kind == 7:
+            tokens[child] = int(rng.choice([-3, V, V + 1]))
+        elif kind == 8:
+            parents[child] = int(rng.integers(child - b * N, N + 2))   # not before the node (or past N)
+        elif kind == 9:
+            ua[child] = rng.choice([np.nan, 1.0, -0.5])
+        elif kind == 10:
+            uf[b] = rng.choice([np.nan, 2.0])
+        elif kind == 11:
+            target[node, rng.integers(0, V, 10)] = -np.inf
+    tw = W.TreeWorkload("tree faults", V, B, N, target, parents, tokens, ua, uf, 0.8)
+    for mode in ("greedy", "target_only"):
+        _say("random tree faults", seed, mode)
+        compare_tree(tw, mode, oracle_tree(tw, mode), run_tree(tw, mode))
+
+
 def test_chain_shaped_tree_matches_chain_on_gpu():
     w = W.block_greedy(seed=3003, batch=16, vocab=5003, parallel=False)
     N = 16
