@@ -108,6 +108,38 @@ def test_chain_sparse_fp32_and_ragged():
     compare_chain(w, "rejection_sparse", o, g)
 
 
+@pytest.mark.parametrize("seed", [61, 62])
+def test_chain_sparse_random_corrupt_candidates(seed):
+    """Seeded corruption of sparse candidate lists (ragged fp32 chains): ids outside [0, V), duplicated ids
+    (the drafted token's among them), masses that are negative, NaN, infinite or sum past 1, a row whose
+    entries are all invalid, and drafted tokens that are no candidate. Device = oracle for every request."""
+    rng = np.random.default_rng(seed)
+    w = W.chain_sparse(seed=6100 + seed, vocab=997, K=8, temperature=0.8, greedy_frac=0.3, batch=24, bf16=False,
+                       ragged=True, parallel=False)
+    ids, q = w.cand_ids.copy(), w.cand_q.copy()
+    D, K = ids.shape
+    for i in range(D):
+        kind = int(rng.integers(0, 10))
+        c = int(rng.integers(0, K))
+        if kind == 0:
+            ids[i, c] = int(rng.choice([-1, w.vocab, w.vocab + 50]))
+        elif kind == 1:
+            ids[i, c] = ids[i, (c + 1) % K]
+        elif kind == 2:
+            q[i, c] = rng.choice([-0.25, np.nan, np.inf, -np.inf])
+        elif kind == 3:
+            q[i] *= 3.0                                  # masses past 1
+        elif kind == 4:
+            ids[i, :] = -5                               # nothing valid
+        elif kind == 5:
+            w.draft_tokens[i] = int(np.setdiff1d(np.arange(w.vocab), ids[i])[0])
+        elif kind == 6:
+            ids[i, c] = w.draft_tokens[i]                # the drafted token listed (again)
+    w.cand_ids, w.cand_q = ids, q
+    _say("chain_sparse corrupt candidates", seed)
+    compare_chain(w, "rejection_sparse", oracle_chain(w, "rejection_sparse"), run_chain(w, "rejection_sparse"))
+
+
 # Full sizes, the benchmark's launch configuration; the oracle checks a sample of requests.
 def test_full_chain_sparse():
     w = W.chain_sparse()
