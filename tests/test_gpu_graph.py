@@ -16,11 +16,18 @@ pytestmark = pytest.mark.gpu
 SENTINEL = 0x5A5A5A5A
 
 
-def _chain_calls(w, mode):
+def _chain_calls(w, mode, mask=None):
     kw = dict(max_verify_len=w.max_verify_len)
     if mode == "rejection":
         kw.update(draft_logits=dev_logits(w.draft), u_accept=dev(w.u_accept), u_final=dev(w.u_final),
                   temperature=w.temperature)
+    elif mode == "rejection_sparse":
+        kw.update(cand_ids=dev(w.cand_ids, torch.int32), cand_q=dev(w.cand_q), u_accept=dev(w.u_accept),
+                  u_final=dev(w.u_final), temperature=w.temperature)
+    elif mode == "sample_match":
+        kw.update(u_accept=dev(w.u_accept), u_final=dev(w.u_final), temperature=w.temperature)
+    if mask is not None:
+        kw.update(vocab_mask=dev(np.ascontiguousarray(mask, np.uint32).view(np.int32)))
     offs = dev(w.offsets, torch.int32)
     v = dva.prepare_verify_chain(dev_logits(w.target), offs, dev(w.draft_tokens, torch.int32), mode, **kw)
     o = v.outputs
@@ -55,7 +62,8 @@ def _poison(v, c):
             t.fill_(SENTINEL)
 
 
-@pytest.mark.parametrize("case", ["chain_rejection", "block_greedy", "tree_target_only", "ragged"])
+@pytest.mark.parametrize("case", ["chain_rejection", "block_greedy", "tree_target_only", "ragged", "block_sample",
+                                  "chain_sparse", "chain_masked"])
 def test_graph_replays_match_eager(case):
     print("graph replay", case, flush=True)
     if case == "chain_rejection":
@@ -64,8 +72,16 @@ def test_graph_replays_match_eager(case):
         v, c = _chain_calls(W.block_greedy(seed=3011, vocab=20011, parallel=False), "greedy")
     elif case == "tree_target_only":
         v, c = _tree_calls(W.tree(seed=4011, vocab=12007, parallel=False), "target_only")
-    else:
+    elif case == "ragged":
         v, c = _chain_calls(W.ragged(seed=5011, batch=96, vocab=4099, parallel=False), "rejection")
+    elif case == "block_sample":
+        v, c = _chain_calls(W.block_sample(seed=7011, vocab=20008, parallel=False), "sample_match")
+    elif case == "chain_sparse":
+        v, c = _chain_calls(W.chain_sparse(seed=6011, vocab=20011, parallel=False), "rejection_sparse")
+    else:
+        w = W.chain_rejection(seed=2013, vocab=20011, parallel=False)
+        keep = [int(np.argmax(w.target[i])) for i in range(w.total_rows)]
+        v, c = _chain_calls(w, "rejection", W.vocab_masks(13, w.total_rows, w.vocab, 0.3, keep))
     # other eager work on other buffers between replays: a different workload through the same library
     ov, oc = _chain_calls(W.chain_rejection(seed=2012, vocab=3001, parallel=False), "rejection")
 
