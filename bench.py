@@ -13,8 +13,9 @@ roofline: the dominant kernel (k_stats, the logits stream) timed with HIP events
 stop timestamps on the launch stream (hipExtLaunchKernel), against its algorithmic bytes (every target and
 draft row read once); read_floor: a plain read of the same byte count (spec_read_probe) timed the same way,
 the rate HBM actually delivers at this size. cpu_baseline: the fp64 CPU oracle timed on this host on the
-same inputs, one thread; cpu_baseline_parallel: the same oracle with the requests split over one forked
-process per core of this process's CPU share (at most 16), run before the GPU is touched.
+same inputs, one thread pinned to one core; cpu_baseline_parallel: the same oracle with the requests split over
+one forked process per core of this process's CPU share (at most 16, each pinned), both run before the GPU is
+touched.
 
     python bench.py [--steps K] [--warmup W]
                     [--workload chain_rejection|block_greedy|tree|ragged|chain_sparse|block_sample|chain_rejection_masked]
@@ -338,7 +339,8 @@ def run_tree_round(steps: int) -> dict:
 
 
 def cpu_baseline(name: str, budget_s: float = 12.0) -> dict:
-    """The fp64 oracle on this host's cores, on the canonical input set of the timed workload."""
+    """The fp64 oracle in this process, one thread, on the canonical input set of the timed workload (used for
+    the tree workload; chains get the pinned runs of cpu_baselines)."""
     import numpy as np
 
     import oracle
@@ -376,13 +378,14 @@ _PAR = {}   # the workload the forked oracle workers split (set before the pool 
 
 
 def _oracle_requests(args):
-    """One worker of the row-parallel oracle run: full passes over requests [b0, b1) of the chain workload in
-    _PAR until the time budget, verify + commit as in cpu_baseline."""
+    """One worker of the oracle runs: pinned to one CPU, full passes over requests [b0, b1) of the chain
+    workload in _PAR until the time budget (at most max_passes), verify + commit."""
     import numpy as np
 
     import oracle
     from draft_verification_acceptance_amd import workloads as W
-    b0, b1, budget_s = args
+    b0, b1, budget_s, cpu, max_passes = args
+    os.sched_setaffinity(0, {cpu})
     w, mode = _PAR["w"], _PAR["mode"]
     off = w.offsets
     r0, r1 = int(off[b0]), int(off[b1])
@@ -401,29 +404,35 @@ def _oracle_requests(args):
         oracle.commit_indices(offs, o["accept_len"], o["accept_index"], slots, seq, w.max_verify_len)
         passes += 1
         rows += r1 - r0
-        if time.perf_counter() - t0 >= budget_s:
+        if time.perf_counter() - t0 >= budget_s or passes >= max_passes:
             break
-    return rows, time.perf_counter() - t0
+    return rows, time.perf_counter() - t0, passes
 
 
-def cpu_baseline_parallel(name: str, budget_s: float = 8.0) -> dict | None:
-    """The same oracle, row-parallel: the requests of the chain workload split over forked worker processes,
-    one per core of this process's CPU share (at most 16), each repeating full passes over its requests. Call
-    it before this process touches the GPU (the workers are forks of it)."""
+def cpu_baselines(name: str, budget_single: float = 8.0, budget_par: float = 8.0):
+    """The fp64 oracle on this host, on the canonical input set of the timed workload (a chain workload):
+    (single, parallel). single: one forked worker pinned to one core, repeated full passes over all
+    requests (verify + commit). parallel: the requests split evenly over one forked worker per core of this
+    process's CPU share (at most 16), each pinned to its own core and repeating full passes over its
+    requests; value = the sum of the workers' rates. Call it before this process touches the GPU (the
+    workers are forks of it)."""
     import multiprocessing as mp
 
     from draft_verification_acceptance_amd import workloads as W
-    if name == "tree":
-        return None
-    w = W.FULL[name](seed={"chain_rejection": 2000, "block_greedy": 3000, "ragged": 5000, "chain_sparse": 6000,
-                           "block_sample": 7000, "chain_rejection_masked": 2000}.get(name, 2000))
-    if name == "chain_rejection_masked" or name == "block_sample":
-        return None
-    n = max(1, min(16, len(os.sched_getaffinity(0)), w.batch))
+    seeds = {"chain_rejection": 2000, "block_greedy": 3000, "ragged": 5000, "chain_sparse": 6000}
+    if name not in seeds:
+        return None, None
+    w = W.FULL[name](seed=seeds[name])
+    cpus = sorted(os.sched_getaffinity(0))
+    n = max(1, min(16, len(cpus), w.batch))
     _PAR["w"], _PAR["mode"] = w, w.modes[-1]
+    ctx = mp.get_context("fork")
+    with ctx.Pool(1) as pool:
+        # the last CPU of the share: CPU 0 also serves the system, which halved the rate there
+        rows, dt, passes = pool.map(_oracle_requests, [(0, w.batch, budget_single, cpus[-1], 20)])[0]
     cuts = [round(i * w.batch / n) for i in range(n + 1)]
-    with mp.get_context("fork").Pool(n) as pool:
-        res = pool.map(_oracle_requests, [(cuts[i], cuts[i + 1], budget_s) for i in range(n)])
+    with ctx.Pool(n) as pool:
+        res = pool.map(_oracle_requests, [(cuts[i], cuts[i + 1], budget_par, cpus[i], 1 << 30) for i in range(n)])
     _PAR.clear()
     model = ""
     try:
@@ -431,11 +440,16 @@ def cpu_baseline_parallel(name: str, budget_s: float = 8.0) -> dict | None:
             model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
     except OSError:
         pass
-    rate = sum(r / t for r, t in res)
-    return {"value": rate, "unit": "positions/s", "cores": n, "kind": "oracle", "cpu": model,
-            "sample": f"{n} forked workers, requests split evenly over them, each repeating full passes over its "
-                      f"requests (fp64 numpy, one thread each) incl. commit for ~{budget_s:.0f} s; value = sum of "
-                      f"the workers' rates"}
+    single = {"value": rows / dt, "unit": "positions/s", "cores": 1, "kind": "oracle", "cpu": model,
+              "sample": f"{passes} full pass(es) over one input set of the timed workload ({w.batch} requests, "
+                        f"{w.total_rows} verify rows, fp64 numpy, one thread pinned to one core) incl. commit; "
+                        f"{dt:.1f} s"}
+    par = {"value": sum(r / t for r, t, _ in res), "unit": "positions/s", "cores": n, "kind": "oracle",
+           "cpu": model,
+           "sample": f"{n} forked workers pinned to one core each, requests split evenly over them, each "
+                     f"repeating full passes over its requests (fp64 numpy, one thread each) incl. commit for "
+                     f"~{budget_par:.0f} s; value = sum of the workers' rates"}
+    return single, par
 
 
 def load_traffic(name: str):
@@ -514,8 +528,8 @@ def main():
         copy_calibration()
         return
 
-    # The row-parallel oracle forks its workers, so it runs before anything in this process touches the GPU.
-    cpu_par = None if args.no_cpu_baseline else cpu_baseline_parallel(args.workload)
+    # The oracle runs fork their workers, so they go before anything in this process touches the GPU.
+    cpu, cpu_par = (None, None) if args.no_cpu_baseline else cpu_baselines(args.workload)
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     main_res = run_workload(args.workload, args.mode, args.steps, args.warmup)
@@ -536,11 +550,10 @@ def main():
         extra["tree_round"] = run_tree_round(max(50, args.steps // 2))
     stats_ms = main_res["kernel_ms"]["k_stats"]["mean"]
     achieved = main_res["stats_kernel_gbs"]
+    if cpu is None and not args.no_cpu_baseline and args.workload == "tree":
+        cpu = cpu_baseline("tree")
     traffic = load_traffic(main_res["workload"])
     floor = read_floor(int(main_res["algorithmic_bytes_per_step"]))
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(main_res["workload"])
     line = {
         "metric": METRIC,
         "value": main_res["positions_per_s"],
