@@ -229,6 +229,42 @@ def test_draw_over_1024_segments():
     compare_chain(w, "rejection", oracle_chain(w, "rejection"), run_chain(w, "rejection"))
 
 
+def test_maximum_vocab():
+    """V = 2^22, the largest vocab the library accepts (8192 draw segments, 2048 sample-then-match pieces per
+    row): rows of zeros with a few raised tokens (so that draws land on wide CDF steps), fp32 and bf16, chain
+    greedy / rejection / sample-then-match and a 3-node tree, against the oracle."""
+    rng = np.random.default_rng(22)
+    V = 1 << 22
+    offs = np.array([0, 3, 5], np.int32)
+    T, B = 5, 2
+    spikes = rng.integers(0, V, (T, 3))
+    tl = np.zeros((T, V), np.float32)
+    dl = np.zeros((T - B, V), np.float32)
+    for i in range(T):
+        tl[i, spikes[i]] = [21.0, 20.0, 19.0]
+    for i in range(T - B):
+        row = i + int(np.searchsorted(offs - np.arange(B + 1), i, "right")) - 1   # draft row j of b: target row j of b
+        dl[i, spikes[row]] = [19.0, 21.0, 20.0]
+    toks = np.array([spikes[0, 0], spikes[1, 1], spikes[3, 0]], np.int32)
+    for bf16 in (False, True):
+        t_ = W.bf16_bits(tl) if bf16 else tl
+        d_ = W.bf16_bits(dl) if bf16 else dl
+        w = W.ChainWorkload("maxvocab", V, B, offs, t_, d_, toks, rng.random(T - B).astype(np.float32),
+                            rng.random(B).astype(np.float32), 1.0, ("greedy", "rejection", "sample_match"), 3)
+        for mode in ("greedy", "rejection", "sample_match"):
+            _say("maximum vocab", mode, "bf16" if bf16 else "fp32")
+            compare_chain(w, mode, oracle_chain(w, mode), run_chain(w, mode))
+    tt = np.zeros((3, V), np.float32)
+    for i in range(3):
+        tt[i, spikes[i]] = [21.0, 20.0, 19.0]
+    tw = W.TreeWorkload("maxvocab tree", V, 1, 3, tt, np.array([-1, 0, 0], np.int32),
+                        np.array([0, spikes[0, 1], spikes[0, 0]], np.int32), rng.random(3).astype(np.float32),
+                        rng.random(1).astype(np.float32), 1.0)
+    for mode in ("greedy", "target_only"):
+        _say("maximum vocab tree", mode)
+        compare_tree(tw, mode, oracle_tree(tw, mode), run_tree(tw, mode))
+
+
 @pytest.mark.parametrize("T", [0.05, 0.7, 5.0])
 def test_temperatures(T):
     w = W.chain_rejection(seed=2100, batch=16, m=5, vocab=3001, parallel=False)
