@@ -229,6 +229,28 @@ def test_draw_over_1024_segments():
     compare_chain(w, "rejection", oracle_chain(w, "rejection"), run_chain(w, "rejection"))
 
 
+def test_long_rejection_request_reads_partials_unstaged():
+    """A rejection request of 700 rows has 1400 row partials, more than the scan stages in LDS (1024): it reads
+    them from the workspace instead. With draft = target every draft is accepted (alpha = 1, r = m = 699); with
+    a noisy draft the first rejection falls somewhere. Both against the oracle, next to short requests."""
+    rng = np.random.default_rng(70)
+    V = 509
+    lens = np.array([700, 1, 40])
+    offs = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T, B = int(offs[-1]), 3
+    tl = rng.normal(0, 2, (T, V)).astype(np.float32)
+    same = np.concatenate([tl[offs[b]:offs[b + 1] - 1] for b in range(B)])   # draft row j = target row j
+    for noisy in (False, True):
+        dl = same + (rng.normal(0, 1.0, same.shape).astype(np.float32) if noisy else 0.0)
+        toks = np.array([int(np.argmax(r)) for r in dl], np.int32)
+        w = _chain_from(tl, dl, offs, toks, rng.random(T - B), rng.random(B), 1.0, 700)
+        _say("long rejection request, noisy draft" if noisy else "long rejection request, draft = target")
+        g = run_chain(w, "rejection")
+        compare_chain(w, "rejection", oracle_chain(w, "rejection"), g)
+        if not noisy:
+            assert int(g["accept_len"][0]) == 699
+
+
 def test_maximum_vocab():
     """V = 2^22, the largest vocab the library accepts (8192 draw segments, 2048 sample-then-match pieces per
     row): rows of zeros with a few raised tokens (so that draws land on wide CDF steps), fp32 and bf16, chain
