@@ -176,6 +176,18 @@ __device__ __forceinline__ double wave_inclusive_sum_dpp(double v) {
   return v + before;
 }
 
+// The same inclusive prefix sum for int.
+__device__ __forceinline__ int wave_inclusive_sum_dpp(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);
+  const int r0 = __builtin_amdgcn_readlane(v, 15), r1 = __builtin_amdgcn_readlane(v, 31),
+            r2 = __builtin_amdgcn_readlane(v, 47);
+  const int row = int(threadIdx.x & (kWave - 1)) >> 4;
+  return v + (row == 0 ? 0 : row == 1 ? r0 : row == 2 ? r0 + r1 : (r0 + r1) + r2);
+}
+
 template <typename T>
 __device__ __forceinline__ T wave_sum(T v) {
 #pragma unroll

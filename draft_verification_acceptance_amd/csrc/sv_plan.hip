@@ -26,6 +26,9 @@ namespace {
 constexpr int kPlanThreads = 1024;
 constexpr int kPlanWaves = kPlanThreads / kWave;
 constexpr int kPlanCache = 15360;   // survival values kept in LDS (60 KB; else recomputed each pass)
+constexpr int kPlanPer = kPlanCache / kPlanThreads;   // cached entries per thread
+constexpr int kPlanBatch = 16;   // confidences of one request read from LDS per round
+static_assert(kPlanCache % kPlanThreads == 0, "whole entries per thread");
 
 struct PlanParams {
   spec_plan_args a;
@@ -76,7 +79,7 @@ __device__ __forceinline__ void hist_add(unsigned int* h, bool valid, unsigned i
   const uint64_t vm = __ballot(valid);
   if (!vm) return;
   const int leader = __ffsll((unsigned long long)vm) - 1;
-  const unsigned int b0 = __shfl(bin, leader);
+  const unsigned int b0 = unsigned(__builtin_amdgcn_readlane(int(bin), leader));
   const bool same = valid && bin == b0;
   const uint64_t sm = __ballot(same);
   if (lane_id() == leader) atomicAdd(&h[b0], unsigned(__popcll(sm)));
@@ -94,7 +97,7 @@ __device__ __forceinline__ void find_digit(const unsigned int* h, int k, int& di
     c[i] = h[lane * 4 + i];
     c4 += int(c[i]);
   }
-  const int before0 = wave_inclusive_sum(c4) - c4;
+  const int before0 = wave_inclusive_sum_dpp(c4) - c4;
   int found = -1, kn = 0, cn = 0, before = before0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -107,11 +110,13 @@ __device__ __forceinline__ void find_digit(const unsigned int* h, int k, int& di
   }
   const uint64_t m = __ballot(found >= 0);
   const int src = __ffsll((unsigned long long)m) - 1;
-  digit = __shfl(found, src);
-  k_in_bin = __shfl(kn, src);
-  bin_n = __shfl(cn, src);
+  digit = __builtin_amdgcn_readlane(found, src);
+  k_in_bin = __builtin_amdgcn_readlane(kn, src);
+  bin_n = __builtin_amdgcn_readlane(cn, src);
 }
 
+// PER: the entries per thread the cached top-K keeps in registers (at least ceil(R*W / kPlanThreads)).
+template <int PER>
 __global__ __launch_bounds__(kPlanThreads) void k_plan(PlanParams pp) {
   const spec_plan_args& a = pp.a;
   extern __shared__ __align__(16) float s_surv[];   // [R*W] when it fits kPlanCache
@@ -150,36 +155,48 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(PlanParams pp) {
   }
   for (int i = tid; i < 3 * 256; i += kPlanThreads) (&s_hist[0][0])[i] = 0u;
   __syncthreads();
-  // Confidence flags; in top-K mode the cached values become the survival products (in place).
+  // Confidence flags; in top-K mode the cached values become the survival products (in place), and the
+  // selectable ones (survival >= eps) are counted on the way. A request's cached row is read kPlanBatch values
+  // per LDS round (indices clamped into the row, so the reads need no branch).
+  long long cnt = 0;
   bool dummy = false;
   for (int r = r_lo; r < r_hi; ++r) {
-    float s = 1.f;
     bool bad = false;
-    for (int j = 0; j < W; ++j) {
-      const float c = sanitize_conf(cached ? s_surv[r * W + j] : a.confidence[int64_t(r) * W + j], bad);
-      s = s * c;
-      if (in_place) s_surv[r * W + j] = s;
+    if (cached) {
+      float s = 1.f;
+      for (int j0 = 0; j0 < W; j0 += kPlanBatch) {
+        float c[kPlanBatch];
+#pragma unroll
+        for (int t = 0; t < kPlanBatch; ++t) c[t] = s_surv[r * W + min(j0 + t, W - 1)];
+#pragma unroll
+        for (int t = 0; t < kPlanBatch; ++t) {
+          if (j0 + t >= W) break;
+          s = s * sanitize_conf(c[t], bad);
+          if (in_place) {
+            s_surv[r * W + j0 + t] = s;
+            cnt += s >= eps;
+          }
+        }
+      }
+    } else {
+      for (int j = 0; j < W; ++j) sanitize_conf(a.confidence[int64_t(r) * W + j], bad);
     }
     if (a.status) a.status[r] = bad ? SPEC_ST_BAD_CONF : 0u;
   }
   __syncthreads();
 
-  // Survival of entry (r, j) while walking request r in position order: the cached product (top-K mode),
-  // or the running product `run` of the sanitized confidences in global memory.
-#define SV_PLAN_SURV(r, j, run)                                                                             \
-  (in_place ? s_surv[(r) * W + (j)]                                                                        \
-            : (run = run * sanitize_conf(a.confidence[int64_t(r) * W + (j)], dummy)))
+  // Survival of entry (r, j) while walking request r in position order (batches too large for LDS): the
+  // running product `run` of the sanitized confidences in global memory.
+#define SV_PLAN_SURV(r, j, run) (run = run * sanitize_conf(a.confidence[int64_t(r) * W + (j)], dummy))
 
   // Top-K: the budget-th smallest key T among the selectable entries: a radix select with 8-bit digits,
   // most significant first, one barrier per digit (three histogram buffers rotate: the one a pass fills,
-  // the one it clears for the next pass, and the one the slowest wave may still be reading).
+  // the one it clears for the next pass, and the one the slowest wave may still be reading). Cached, each
+  // thread keeps the keys of its entries tid + v * kPlanThreads in registers for every pass.
   unsigned long long T = 0;
   bool any = false;
   if (topk) {
-    long long cnt = 0;
-    if (cached) {
-      for (int e = tid; e < n; e += kPlanThreads) cnt += s_surv[e] >= eps;
-    } else {
+    if (!cached) {
       for (int r = r_lo; r < r_hi; ++r) {
         float run = 1.f;
         for (int j = 0; j < W; ++j) cnt += SV_PLAN_SURV(r, j, run) >= eps;
@@ -189,8 +206,29 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(PlanParams pp) {
     plan_block_excl(cnt, s_red, total);
     const int K = int(min((long long)a.budget, total));
     any = K > 0;
-    const int step_r = W > 0 ? kPlanThreads / W : 0, step_j = W > 0 ? kPlanThreads % W : 0;
-    if (any) {
+    if (any) {   // uniform; then n > 0 and W > 0
+      const int nv = (n + kPlanThreads - 1) / kPlanThreads;   // at most PER when cached
+      unsigned long long key[PER];   // 0: not selectable (every selectable key is nonzero)
+      if (cached) {
+        // entry e = r * W + j; (r, j) advance by (kPlanThreads / W, kPlanThreads % W) per entry, no division
+        const int step_r = kPlanThreads / W, step_j = kPlanThreads % W;
+        int r = tid / W, j = tid % W;
+#pragma unroll
+        for (int v = 0; v < PER; ++v) {
+          key[v] = 0ull;
+          const int e = v * kPlanThreads + tid;
+          if (v < nv && e < n) {
+            const float sv = s_surv[e];
+            if (sv >= eps) key[v] = plan_key(sv, j, r);
+          }
+          r += step_r;
+          j += step_j;
+          if (j >= W) {
+            j -= W;
+            ++r;
+          }
+        }
+      }
       unsigned long long prefix = 0ull, mask = 0ull;
       int k = K;
       for (int pass = 0; pass < 8; ++pass) {
@@ -199,28 +237,11 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(PlanParams pp) {
         unsigned int* Z = s_hist[(pass + 1) % 3];
         for (int i = tid; i < 256; i += kPlanThreads) Z[i] = 0u;
         if (cached) {
-          // entry e = r * W + j; (r, j) advance by (step_r, step_j) per trip, without a division
-          int r = tid / W, j = tid % W;
-          for (int e0 = 0; e0 < n; e0 += kPlanThreads) {   // uniform trip count: whole waves call hist_add
-            const int e = e0 + tid;
-            bool v = false;
-            unsigned int bin = 0u;
-            if (e < n) {
-              const float sv = s_surv[e];
-              if (sv >= eps) {
-                const unsigned long long key = plan_key(sv, j, r);
-                if ((key & mask) == prefix) {
-                  v = true;
-                  bin = unsigned((key >> shift) & 255u);
-                }
-              }
-            }
-            hist_add(H, v, bin);
-            r += step_r;
-            j += step_j;
-            if (j >= W) {
-              j -= W;
-              ++r;
+#pragma unroll
+          for (int v = 0; v < PER; ++v) {
+            if (v < nv) {   // uniform: whole waves call hist_add
+              const bool ok = key[v] != 0ull && (key[v] & mask) == prefix;
+              hist_add(H, ok, unsigned((key[v] >> shift) & 255u));
             }
           }
         } else {
@@ -231,9 +252,9 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(PlanParams pp) {
             for (int j = 0; j < W; ++j) {
               const float sv = SV_PLAN_SURV(r, j, run);
               if (!(sv >= eps)) continue;
-              const unsigned long long key = plan_key(sv, j, r);
-              if ((key & mask) != prefix) continue;
-              const unsigned int bin = unsigned((key >> shift) & 255u);
+              const unsigned long long key2 = plan_key(sv, j, r);
+              if ((key2 & mask) != prefix) continue;
+              const unsigned int bin = unsigned((key2 >> shift) & 255u);
               if (bin != run_bin) {
                 if (run_n) atomicAdd(&H[run_bin], run_n);
                 run_bin = bin;
@@ -265,18 +286,40 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(PlanParams pp) {
     int sel = 0;
     if (a.mode == SPEC_PLAN_THRESHOLD) {   // the first position whose own confidence is below the threshold
       sel = W;
-      for (int j = 0; j < W; ++j)
-        if (sanitize_conf(cached ? s_surv[r * W + j] : a.confidence[int64_t(r) * W + j], dummy) < a.threshold) {
-          sel = j;
-          break;
+      if (cached) {
+        for (int j0 = 0; j0 < W && sel == W; j0 += kPlanBatch) {
+          float c[kPlanBatch];
+#pragma unroll
+          for (int t = 0; t < kPlanBatch; ++t) c[t] = s_surv[r * W + min(j0 + t, W - 1)];
+#pragma unroll
+          for (int t = kPlanBatch - 1; t >= 0; --t)   // the lowest position below the threshold wins
+            if (j0 + t < W && sanitize_conf(c[t], dummy) < a.threshold) sel = j0 + t;
         }
+      } else {
+        for (int j = 0; j < W; ++j)
+          if (sanitize_conf(a.confidence[int64_t(r) * W + j], dummy) < a.threshold) {
+            sel = j;
+            break;
+          }
+      }
     } else if (!topk) {
       sel = W;
     } else if (any) {
-      float run = 1.f;
-      for (int j = 0; j < W; ++j) {
-        const float sv = SV_PLAN_SURV(r, j, run);
-        if (sv >= eps && plan_key(sv, j, r) <= T) ++sel;
+      if (cached) {
+        for (int j0 = 0; j0 < W; j0 += kPlanBatch) {
+          float c[kPlanBatch];
+#pragma unroll
+          for (int t = 0; t < kPlanBatch; ++t) c[t] = s_surv[r * W + min(j0 + t, W - 1)];
+#pragma unroll
+          for (int t = 0; t < kPlanBatch; ++t)
+            if (j0 + t < W && c[t] >= eps && plan_key(c[t], j0 + t, r) <= T) ++sel;
+        }
+      } else {
+        float run = 1.f;
+        for (int j = 0; j < W; ++j) {
+          const float sv = SV_PLAN_SURV(r, j, run);
+          if (sv >= eps && plan_key(sv, j, r) <= T) ++sel;
+        }
       }
     }
     const int vl = min(max(1 + sel, a.min_verify_len), a.max_verify_len);
@@ -339,8 +382,17 @@ double sps_at(double M, const double* xs, const double* ys, int n) {
 }  // namespace
 
 hipError_t launch_plan(const spec_plan_args& a, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
-  const size_t smem = int64_t(a.batch) * a.width <= kPlanCache ? size_t(a.batch) * a.width * sizeof(float) : 0;
-  return launch_kernel(k_plan, dim3(1), dim3(kPlanThreads), smem, stream, ev0, ev1, PlanParams{a});
+  const int64_t n = int64_t(a.batch) * a.width;
+  const size_t smem = n <= kPlanCache ? size_t(n) * sizeof(float) : 0;
+  // the smallest register set that holds a thread's cached entries (uncached batches keep none)
+  const int64_t nv = n <= kPlanCache ? (n + kPlanThreads - 1) / kPlanThreads : 1;
+  const PlanParams pp{a};
+  const dim3 g(1), blk(kPlanThreads);
+  if (nv <= 1) return launch_kernel(k_plan<1>, g, blk, smem, stream, ev0, ev1, pp);
+  if (nv <= 2) return launch_kernel(k_plan<2>, g, blk, smem, stream, ev0, ev1, pp);
+  if (nv <= 4) return launch_kernel(k_plan<4>, g, blk, smem, stream, ev0, ev1, pp);
+  if (nv <= 8) return launch_kernel(k_plan<8>, g, blk, smem, stream, ev0, ev1, pp);
+  return launch_kernel(k_plan<kPlanPer>, g, blk, smem, stream, ev0, ev1, pp);
 }
 
 hipError_t launch_cap_trim(const spec_cap_trim_args& a, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {

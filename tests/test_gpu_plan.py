@@ -43,7 +43,9 @@ def test_plan_worked_example():
 
 @pytest.mark.parametrize("R,Wd,kind,seed", [(2, 3, "beta", 1), (64, 7, "beta", 2), (512, 15, "beta", 3),
                                              (512, 15, "ties", 4), (37, 5, "ties", 5), (1500, 15, "beta", 6),
-                                             (4000, 8, "ties", 7), (1, 1, "beta", 8), (1024, 1, "ties", 9)])
+                                             (4000, 8, "ties", 7), (1, 1, "beta", 8), (1024, 1, "ties", 9),
+                                             (150, 10, "beta", 10), (1000, 15, "beta", 12), (1000, 15, "ties", 13),
+                                             (1024, 15, "beta", 14), (1025, 15, "beta", 15)])
 def test_plan_topk_matches_oracle(R, Wd, kind, seed):
     rng = np.random.default_rng(seed)
     if kind == "beta":
