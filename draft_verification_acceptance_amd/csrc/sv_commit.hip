@@ -109,12 +109,7 @@ __global__ __launch_bounds__(kCommitThreads) void k_commit(spec_commit_args a) {
       }
     }
     const uint64_t mine = (uint64_t(uint32_t(len)) << 32) | uint32_t(len > 0 ? r + 1 : 0);
-    uint64_t inc = mine;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      const uint64_t n = __shfl_up(inc, o);
-      if (lane >= o) inc += n;
-    }
+    const uint64_t inc = wave_inclusive_sum_dpp(mine);
     if (lane == kWave - 1) red[wv] = inc;
     t_len[tid] = len;
     t_r[tid] = r;

@@ -188,6 +188,28 @@ __device__ __forceinline__ int wave_inclusive_sum_dpp(int v) {
   return v + (row == 0 ? 0 : row == 1 ? r0 : row == 2 ? r0 + r1 : (r0 + r1) + r2);
 }
 
+// And for uint64 (each DPP move takes one 32-bit half; the sums are exact modulo 2^64).
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  const int lo = __builtin_amdgcn_update_dpp(0, int(uint32_t(v)), CTRL, 0xF, 0xF, true);
+  const int hi = __builtin_amdgcn_update_dpp(0, int(uint32_t(v >> 32)), CTRL, 0xF, 0xF, true);
+  return (uint64_t(uint32_t(hi)) << 32) | uint32_t(lo);
+}
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
+  const uint32_t lo = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(v)), l));
+  const uint32_t hi = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(v >> 32)), l));
+  return (uint64_t(hi) << 32) | lo;
+}
+__device__ __forceinline__ uint64_t wave_inclusive_sum_dpp(uint64_t v) {
+  v += dpp_u64<0x111>(v);
+  v += dpp_u64<0x112>(v);
+  v += dpp_u64<0x114>(v);
+  v += dpp_u64<0x118>(v);
+  const uint64_t r0 = readlane_u64(v, 15), r1 = readlane_u64(v, 31), r2 = readlane_u64(v, 47);
+  const int row = int(threadIdx.x & (kWave - 1)) >> 4;
+  return v + (row == 0 ? 0ull : row == 1 ? r0 : row == 2 ? r0 + r1 : (r0 + r1) + r2);
+}
+
 template <typename T>
 __device__ __forceinline__ T wave_sum(T v) {
 #pragma unroll
