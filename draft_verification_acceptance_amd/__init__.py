@@ -135,9 +135,11 @@ def _lib():
     for f in (lib.spec_verify_chain, lib.spec_verify_tree, lib.spec_commit_indices, lib.spec_plan_layout,
               lib.spec_cap_trim, lib.spec_kv_move, lib.spec_tree_build):
         f.restype = ctypes.c_int
-    _dp = ctypes.POINTER(ctypes.c_double)
-    lib.spec_plan_budget.argtypes = [ctypes.POINTER(ctypes.c_float), _i32, _i32, _dp, _dp, _i32, _f32,
-                                     ctypes.POINTER(_i32), _dp, ctypes.POINTER(_i32)]
+    import numpy as np
+    _f32a = np.ctypeslib.ndpointer(dtype=np.float32, flags="C_CONTIGUOUS")
+    _f64a = np.ctypeslib.ndpointer(dtype=np.float64, flags="C_CONTIGUOUS")
+    lib.spec_plan_budget.argtypes = [_f32a, _i32, _i32, _f64a, _f64a, _i32, _f32, ctypes.POINTER(_i32), _f64a,
+                                     ctypes.POINTER(_i32)]
     lib.spec_plan_budget.restype = ctypes.c_int
     lib.spec_workspace_bytes.argtypes = [_i32, _i32, _i64, _i64, _i32, _i32]
     lib.spec_workspace_bytes.restype = _sz
@@ -513,9 +515,10 @@ def commit_indices(row_offsets: torch.Tensor, accept_len: torch.Tensor, accept_i
 # ----------------------------------------------------------------------------------------------------
 # verify-length planner and accept cutoff
 # ----------------------------------------------------------------------------------------------------
-def plan_budget(confidence_hist, sps_rows, sps, *, survival_eps: float = 0.0) -> tuple[int, list]:
+def plan_budget(confidence_hist, sps_rows, sps, *, survival_eps: float = 0.0):
     """spec_plan_budget (host function): the verify budget K* from lagged confidences [batch, width] (a host
-    array: numpy or CPU tensor, float32) and an SPS table. Returns (K*, predicted throughput for K = 0..n)."""
+    array: numpy or CPU tensor, float32) and an SPS table. Returns (K*, predicted throughput for K = 0..n as a
+    float64 numpy array)."""
     import numpy as np
     c = np.ascontiguousarray(confidence_hist.cpu().numpy() if isinstance(confidence_hist, torch.Tensor)
                              else confidence_hist, dtype=np.float32)
@@ -528,11 +531,9 @@ def plan_budget(confidence_hist, sps_rows, sps, *, survival_eps: float = 0.0) ->
         raise ValueError("sps_rows and sps must be 1-D of equal length")
     theta = np.zeros(R * W + 1, np.float64)
     k, n = _i32(), _i32()
-    _dp = ctypes.POINTER(ctypes.c_double)
-    _check(_lib().spec_plan_budget(c.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), R, W, xs.ctypes.data_as(_dp),
-                                   ys.ctypes.data_as(_dp), len(xs), float(survival_eps), ctypes.byref(k),
-                                   theta.ctypes.data_as(_dp), ctypes.byref(n)))
-    return int(k.value), theta[:n.value + 1].tolist()
+    _check(_lib().spec_plan_budget(c, R, W, xs, ys, len(xs), float(survival_eps), ctypes.byref(k), theta,
+                                   ctypes.byref(n)))
+    return int(k.value), theta[:n.value + 1]
 
 
 def prepare_plan_layout(confidence: torch.Tensor, *, mode: str = "topk", budget: int = -1, threshold: float = 0.5,

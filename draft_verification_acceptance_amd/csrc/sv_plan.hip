@@ -13,8 +13,8 @@
 // 8-bit digits finds the budget-th smallest key T in 8 passes over the entries; the selected entries are the
 // keys <= T. The survival products are float32 in position order, so every decision is a function of
 // the inputs alone.
-#include <algorithm>
-#include <functional>
+#include <string.h>
+
 #include <vector>
 
 #include "sv_device.h"
@@ -368,15 +368,40 @@ __global__ void k_cap_trim(spec_cap_trim_args a) {
   }
 }
 
-// Steps per second at M target rows: linear between the table points, the nearest end value outside.
-double sps_at(double M, const double* xs, const double* ys, int n) {
+// Steps per second at M target rows: linear between the table points, the nearest end value outside. `i` is
+// the table segment of the previous call, M never smaller (the search only moves forward); slope[i] =
+// (ys[i + 1] - ys[i]) / (xs[i + 1] - xs[i]).
+double sps_at(double M, const double* xs, const double* ys, const double* slope, int n, int& i) {
 #pragma clang fp contract(off)
   if (M <= xs[0]) return ys[0];
   if (M >= xs[n - 1]) return ys[n - 1];
-  int i = 0;
   while (!(xs[i] <= M && M < xs[i + 1])) ++i;
-  const double slope = (ys[i + 1] - ys[i]) / (xs[i + 1] - xs[i]);
-  return slope * (M - xs[i]) + ys[i];
+  return slope[i] * (M - xs[i]) + ys[i];
+}
+
+// Non-negative floats in descending order: their bit patterns order like their values, so an LSD radix sort
+// (8-bit digits, ascending) of the complemented patterns does it; a digit that is the same for every value is
+// skipped. Equal values are interchangeable, so any correct sort leaves the same sequence.
+void sort_desc_nonneg(std::vector<float>& a) {
+  const size_t n = a.size();
+  std::vector<uint32_t> k(n), t(n);
+  for (size_t i = 0; i < n; ++i) {
+    uint32_t b;
+    memcpy(&b, &a[i], 4);
+    k[i] = ~b;
+  }
+  for (int sh = 0; sh < 32; sh += 8) {
+    size_t cnt[257] = {0};
+    for (size_t i = 0; i < n; ++i) ++cnt[((k[i] >> sh) & 255u) + 1];
+    if (n && cnt[((k[0] >> sh) & 255u) + 1] == n) continue;
+    for (int d = 0; d < 256; ++d) cnt[d + 1] += cnt[d];
+    for (size_t i = 0; i < n; ++i) t[cnt[(k[i] >> sh) & 255u]++] = k[i];
+    k.swap(t);
+  }
+  for (size_t i = 0; i < n; ++i) {
+    const uint32_t b = ~k[i];
+    memcpy(&a[i], &b, 4);
+  }
 }
 
 }  // namespace
@@ -413,14 +438,17 @@ spec_status plan_budget_host(const float* conf, int32_t R, int32_t W, const doub
       if (s >= eps) a.push_back(s);
     }
   }
-  std::sort(a.begin(), a.end(), std::greater<float>());
+  sort_desc_nonneg(a);   // the survival products are >= 0 (sanitized confidences)
+  std::vector<double> slope(size_t(n_sps), 0.0);
+  for (int32_t i = 0; i + 1 < n_sps; ++i) slope[i] = (sps[i + 1] - sps[i]) / (sps_rows[i + 1] - sps_rows[i]);
+  int seg = 0;
   double N = double(R);
-  double best = N * sps_at(double(R), sps_rows, sps, n_sps);
+  double best = N * sps_at(double(R), sps_rows, sps, slope.data(), n_sps, seg);
   int32_t k_best = 0;
   if (theta) theta[0] = best;
   for (size_t k = 1; k <= a.size(); ++k) {
     N += double(a[k - 1]);
-    const double th = N * sps_at(double(R) + double(k), sps_rows, sps, n_sps);
+    const double th = N * sps_at(double(R) + double(k), sps_rows, sps, slope.data(), n_sps, seg);
     if (theta) theta[k] = th;
     if (th > best) {
       best = th;

@@ -184,7 +184,8 @@ def test_plan_budget_host_argument_checks():
         dva.plan_budget(c, [1.0, 2.0], [5.0, float("nan")])
     with pytest.raises(dva.SpecError):
         dva.plan_budget(c, [1.0, 2.0], [5.0, 4.0], survival_eps=-0.5)
-    assert dva.plan_budget(np.zeros((0, 3), np.float32), [1.0], [5.0]) == (0, [0.0])
+    K0, th0 = dva.plan_budget(np.zeros((0, 3), np.float32), [1.0], [5.0])
+    assert K0 == 0 and th0.dtype == np.float64 and list(th0) == [0.0]
 
 
 def test_read_probe_host_checks():

@@ -50,3 +50,15 @@ def test_host_budget_matches_oracle(seed):
     Ko, tho = op.plan_budget(conf, rows, sps, eps)
     assert K == Ko
     assert np.array_equal(np.asarray(theta), tho)
+
+
+def test_host_budget_at_the_ragged_shape():
+    """The planner workload's shape (512 requests x 15 drafts): every digit of the descending sort is in use."""
+    from draft_verification_acceptance_amd import workloads as W
+    w = W.planner_inputs()
+    for eps, quant in ((0.0, False), (0.05, False), (0.0, True)):
+        conf = np.round(w.conf_hist * 8) / 8 if quant else w.conf_hist     # quant: thousands of exact ties
+        K, theta = dva.plan_budget(conf.astype(np.float32), w.sps_rows, w.sps, survival_eps=eps)
+        Ko, tho = op.plan_budget(conf.astype(np.float32), w.sps_rows, w.sps, eps)
+        assert K == Ko
+        assert np.array_equal(theta, tho)
