@@ -45,7 +45,8 @@ def test_plan_worked_example():
                                              (512, 15, "ties", 4), (37, 5, "ties", 5), (1500, 15, "beta", 6),
                                              (4000, 8, "ties", 7), (1, 1, "beta", 8), (1024, 1, "ties", 9),
                                              (150, 10, "beta", 10), (1000, 15, "beta", 12), (1000, 15, "ties", 13),
-                                             (1024, 15, "beta", 14), (1025, 15, "beta", 15)])
+                                             (1024, 15, "beta", 14), (1025, 15, "beta", 15),
+                                             (960, 16, "beta", 18), (2457, 15, "ties", 17), (2458, 15, "beta", 16)])
 def test_plan_topk_matches_oracle(R, Wd, kind, seed):
     rng = np.random.default_rng(seed)
     if kind == "beta":
@@ -53,7 +54,7 @@ def test_plan_topk_matches_oracle(R, Wd, kind, seed):
     else:   # few distinct values: many exact ties in the ranking
         conf = rng.choice(np.array([1.0, 0.9, 0.5, 0.5, 0.25], np.float32), (R, Wd))
     n = R * Wd
-    print("plan topk", R, Wd, kind, f"cached={n <= 14336}", flush=True)
+    print("plan topk", R, Wd, kind, f"cached={n <= 15360}", flush=True)
     for budget in sorted({0, 1, n // 3, n // 2, n - 1, n, n + 5}):
         for eps in (0.0, 0.3):
             g = _plan(conf, budget=budget, survival_eps=eps)
