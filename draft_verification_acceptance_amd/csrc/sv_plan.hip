@@ -116,10 +116,13 @@ __device__ __forceinline__ void find_digit(const unsigned int* h, int k, int& di
 }
 
 // PER: the entries per thread the cached top-K keeps in registers (at least ceil(R*W / kPlanThreads)).
-template <int PER>
+// PAD: the width is even and the LDS rows are padded to the odd stride W + 1.
+template <int PER, bool PAD>
 __global__ __launch_bounds__(kPlanThreads) void k_plan(PlanParams pp) {
   const spec_plan_args& a = pp.a;
-  extern __shared__ __align__(16) float s_surv[];   // [R*W] when it fits kPlanCache
+  // [R][Wp] when R*W fits kPlanCache (at most 2 * kPlanCache floats): even rows padded to the odd stride W + 1,
+  // so that threads walking consecutive requests read different LDS banks
+  extern __shared__ __align__(16) float s_surv[];
   __shared__ unsigned int s_hist[3][256];
   __shared__ long long s_red[kPlanWaves];
 
@@ -130,6 +133,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(PlanParams pp) {
   const int per = (R + kPlanThreads - 1) / kPlanThreads;
   const int r_lo = min(R, tid * per);
   const int r_hi = min(R, r_lo + per);
+  const int Wp = PAD ? W + 1 : W;
   const bool cached = n <= kPlanCache;
   const bool topk = a.mode == SPEC_PLAN_TOPK && a.budget >= 0;
   const bool in_place = cached && a.mode == SPEC_PLAN_TOPK;
@@ -137,8 +141,12 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(PlanParams pp) {
 
   // The confidences go to LDS when they fit, with coalesced loads issued 8 per thread at a time (a
   // thread walking its own request's row load by load would wait a memory round trip per position).
-  if (cached) {
+  if (cached && n > 0) {
     constexpr int U = 8;
+    // entry i = r * W + j goes to r * Wp + j; (r, j) advance by (kPlanThreads / W, kPlanThreads % W) per
+    // kPlanThreads entries, no division
+    const int step_r = kPlanThreads / W, step_j = kPlanThreads % W;
+    int r = tid / W, j = tid % W;
     for (int base = 0; base < n; base += kPlanThreads * U) {
       float v[U];
 #pragma unroll
@@ -146,10 +154,24 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(PlanParams pp) {
         const int i = base + u * kPlanThreads + tid;
         v[u] = i < n ? a.confidence[i] : 0.f;
       }
+      if (!PAD) {   // odd rows are stored unpadded
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int i = base + u * kPlanThreads + tid;
+          if (i < n) s_surv[i] = v[u];
+        }
+        continue;
+      }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int i = base + u * kPlanThreads + tid;
-        if (i < n) s_surv[i] = v[u];
+        if (i < n) s_surv[r * Wp + j] = v[u];
+        r += step_r;
+        j += step_j;
+        if (j >= W) {
+          j -= W;
+          ++r;
+        }
       }
     }
   }
@@ -167,13 +189,13 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(PlanParams pp) {
       for (int j0 = 0; j0 < W; j0 += kPlanBatch) {
         float c[kPlanBatch];
 #pragma unroll
-        for (int t = 0; t < kPlanBatch; ++t) c[t] = s_surv[r * W + min(j0 + t, W - 1)];
+        for (int t = 0; t < kPlanBatch; ++t) c[t] = s_surv[r * Wp + min(j0 + t, W - 1)];
 #pragma unroll
         for (int t = 0; t < kPlanBatch; ++t) {
           if (j0 + t >= W) break;
           s = s * sanitize_conf(c[t], bad);
           if (in_place) {
-            s_surv[r * W + j0 + t] = s;
+            s_surv[r * Wp + j0 + t] = s;
             cnt += s >= eps;
           }
         }
@@ -210,24 +232,29 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(PlanParams pp) {
       const int nv = (n + kPlanThreads - 1) / kPlanThreads;   // at most PER when cached
       unsigned long long key[PER];   // 0: not selectable (every selectable key is nonzero)
       if (cached) {
-        // entry e = r * W + j; (r, j) advance by (kPlanThreads / W, kPlanThreads % W) per entry, no division
+        // entry e = r * W + j (at r * Wp + j in LDS); (r, j) advance as in the load above. Unpadded rows are
+        // read at e (one base address and immediate offsets), padded ones at r * Wp + j.
         const int step_r = kPlanThreads / W, step_j = kPlanThreads % W;
-        int r = tid / W, j = tid % W;
+        const auto build = [&](auto at) {
+          int r = tid / W, j = tid % W;
 #pragma unroll
-        for (int v = 0; v < PER; ++v) {
-          key[v] = 0ull;
-          const int e = v * kPlanThreads + tid;
-          if (v < nv && e < n) {
-            const float sv = s_surv[e];
-            if (sv >= eps) key[v] = plan_key(sv, j, r);
+          for (int v = 0; v < PER; ++v) {
+            key[v] = 0ull;
+            const int e = v * kPlanThreads + tid;
+            if (v < nv && e < n) {
+              const float sv = s_surv[at(e, r, j)];
+              if (sv >= eps) key[v] = plan_key(sv, j, r);
+            }
+            r += step_r;
+            j += step_j;
+            if (j >= W) {
+              j -= W;
+              ++r;
+            }
           }
-          r += step_r;
-          j += step_j;
-          if (j >= W) {
-            j -= W;
-            ++r;
-          }
-        }
+        };
+        if (!PAD) build([](int e, int, int) { return e; });
+        else build([Wp](int, int r, int j) { return r * Wp + j; });
       }
       unsigned long long prefix = 0ull, mask = 0ull;
       int k = K;
@@ -290,7 +317,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(PlanParams pp) {
         for (int j0 = 0; j0 < W && sel == W; j0 += kPlanBatch) {
           float c[kPlanBatch];
 #pragma unroll
-          for (int t = 0; t < kPlanBatch; ++t) c[t] = s_surv[r * W + min(j0 + t, W - 1)];
+          for (int t = 0; t < kPlanBatch; ++t) c[t] = s_surv[r * Wp + min(j0 + t, W - 1)];
 #pragma unroll
           for (int t = kPlanBatch - 1; t >= 0; --t)   // the lowest position below the threshold wins
             if (j0 + t < W && sanitize_conf(c[t], dummy) < a.threshold) sel = j0 + t;
@@ -309,7 +336,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(PlanParams pp) {
         for (int j0 = 0; j0 < W; j0 += kPlanBatch) {
           float c[kPlanBatch];
 #pragma unroll
-          for (int t = 0; t < kPlanBatch; ++t) c[t] = s_surv[r * W + min(j0 + t, W - 1)];
+          for (int t = 0; t < kPlanBatch; ++t) c[t] = s_surv[r * Wp + min(j0 + t, W - 1)];
 #pragma unroll
           for (int t = 0; t < kPlanBatch; ++t)
             if (j0 + t < W && c[t] >= eps && plan_key(c[t], j0 + t, r) <= T) ++sel;
@@ -408,16 +435,25 @@ void sort_desc_nonneg(std::vector<float>& a) {
 
 hipError_t launch_plan(const spec_plan_args& a, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
   const int64_t n = int64_t(a.batch) * a.width;
-  const size_t smem = n <= kPlanCache ? size_t(n) * sizeof(float) : 0;
+  const bool cached = n <= kPlanCache;
+  // even rows padded to the odd stride W + 1: at most 2 * kPlanCache floats (120 KB of gfx950's 160 KB)
+  const size_t smem = cached && n > 0 ? size_t(a.batch) * size_t(a.width | 1) * sizeof(float) : 0;
   // the smallest register set that holds a thread's cached entries (uncached batches keep none)
-  const int64_t nv = n <= kPlanCache ? (n + kPlanThreads - 1) / kPlanThreads : 1;
+  const int64_t nv = cached ? (n + kPlanThreads - 1) / kPlanThreads : 1;
   const PlanParams pp{a};
   const dim3 g(1), blk(kPlanThreads);
-  if (nv <= 1) return launch_kernel(k_plan<1>, g, blk, smem, stream, ev0, ev1, pp);
-  if (nv <= 2) return launch_kernel(k_plan<2>, g, blk, smem, stream, ev0, ev1, pp);
-  if (nv <= 4) return launch_kernel(k_plan<4>, g, blk, smem, stream, ev0, ev1, pp);
-  if (nv <= 8) return launch_kernel(k_plan<8>, g, blk, smem, stream, ev0, ev1, pp);
-  return launch_kernel(k_plan<kPlanPer>, g, blk, smem, stream, ev0, ev1, pp);
+  if (a.width % 2 == 0) {
+    if (nv <= 1) return launch_kernel(k_plan<1, true>, g, blk, smem, stream, ev0, ev1, pp);
+    if (nv <= 2) return launch_kernel(k_plan<2, true>, g, blk, smem, stream, ev0, ev1, pp);
+    if (nv <= 4) return launch_kernel(k_plan<4, true>, g, blk, smem, stream, ev0, ev1, pp);
+    if (nv <= 8) return launch_kernel(k_plan<8, true>, g, blk, smem, stream, ev0, ev1, pp);
+    return launch_kernel(k_plan<kPlanPer, true>, g, blk, smem, stream, ev0, ev1, pp);
+  }
+  if (nv <= 1) return launch_kernel(k_plan<1, false>, g, blk, smem, stream, ev0, ev1, pp);
+  if (nv <= 2) return launch_kernel(k_plan<2, false>, g, blk, smem, stream, ev0, ev1, pp);
+  if (nv <= 4) return launch_kernel(k_plan<4, false>, g, blk, smem, stream, ev0, ev1, pp);
+  if (nv <= 8) return launch_kernel(k_plan<8, false>, g, blk, smem, stream, ev0, ev1, pp);
+  return launch_kernel(k_plan<kPlanPer, false>, g, blk, smem, stream, ev0, ev1, pp);
 }
 
 hipError_t launch_cap_trim(const spec_cap_trim_args& a, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {

@@ -86,6 +86,9 @@ def test_plan_bad_confidences_and_degenerate_shapes():
     # no drafts proposed: every request verifies its anchor only
     z = _plan(np.zeros((5, 0), np.float32), budget=3)
     assert list(z["verify_lens"]) == [1] * 5 and list(z["offsets"]) == [0, 1, 2, 3, 4, 5]
+    # many requests, no drafts: nothing to cache
+    z2 = _plan(np.zeros((40000, 0), np.float32), budget=3)
+    assert (z2["verify_lens"] == 1).all() and int(z2["offsets"][-1]) == 40000
     # no requests
     e = _plan(np.zeros((0, 4), np.float32), budget=3)
     assert list(e["offsets"]) == [0]
