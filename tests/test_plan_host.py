@@ -62,3 +62,23 @@ def test_host_budget_at_the_ragged_shape():
         Ko, tho = op.plan_budget(conf.astype(np.float32), w.sps_rows, w.sps, eps)
         assert K == Ko
         assert np.array_equal(theta, tho)
+
+
+@pytest.mark.parametrize("case", ["zeros", "ones", "single", "all_below_eps", "nan_rows", "powers_of_two"])
+def test_host_budget_degenerate_inputs(case):
+    """Inputs whose sorted survival list is degenerate: every value equal, one value, none selectable, NaNs
+    sanitised to 0, and values that differ only in their exponent (a single digit of the descending sort)."""
+    rng = np.random.default_rng(7)
+    conf = {"zeros": np.zeros((9, 4), np.float32),
+            "ones": np.ones((9, 4), np.float32),
+            "single": np.array([[0.7]], np.float32),
+            "all_below_eps": np.full((6, 5), 0.2, np.float32),
+            "nan_rows": np.where(rng.random((8, 6)) < 0.5, np.nan, 0.9).astype(np.float32),
+            "powers_of_two": np.float32(2.0) ** -rng.integers(0, 6, (12, 7)).astype(np.float32)}[case]
+    rows = np.array([1.0, 20.0, 60.0, 200.0])
+    sps = np.array([120.0, 100.0, 70.0, 30.0])
+    for eps in (0.0, 0.3):
+        K, theta = dva.plan_budget(conf, rows, sps, survival_eps=eps)
+        Ko, tho = op.plan_budget(conf, rows, sps, eps)
+        assert K == Ko
+        assert np.array_equal(theta, tho)
