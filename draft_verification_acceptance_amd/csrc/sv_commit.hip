@@ -138,7 +138,11 @@ __global__ __launch_bounds__(kCommitThreads) void k_commit(spec_commit_args a) {
     // ---- the request's entries: the usual form (its first r + 1 rows in order) or any other ----
     const CommitTile tw0{w0, n_st, s_ai, s_vs, a.accept_index, a.verify_slots};
     const int64_t lo_r = int64_t(off0) - w0;
-    const bool inwin = len > 0 && lo_r >= 0 && lo_r + len <= n_st;   // all of the request's rows staged
+    // All of the request's rows are staged AND sit at their packed place in the tile (the rows of the requests
+    // before it in this tile come first). Packed places of different requests never overlap, so such requests
+    // can share the bitmap s_accb. A request whose own offsets pass but overlap another's (inconsistent
+    // offsets elsewhere in the batch) takes the per-request loops instead.
+    const bool inwin = len > 0 && lo_r >= 0 && lo_r + len <= n_st && lo_r == int64_t(incl >> 32) - len;
     bool ident = inwin;
     if (ident) {
       // The form the verify kernels write: the bits of rows lo_r .. lo_r + r in s_idw all set. Every entry

@@ -666,3 +666,54 @@ def test_inconsistent_offsets_are_reported_and_stay_in_bounds():
         gc = _commit_check(np.array(offs, np.int32), np.zeros(B, np.int32), np.arange(T, dtype=np.int32),
                            np.arange(T, dtype=np.int64), np.zeros(B, np.int32), 16)
         assert np.any(gc["status"] & oracle.ST_BAD_OFFSETS)
+
+
+def _overlapping_commit_case(rng):
+    """Offsets where one interior offset jumps past the next: that request fails its checks, and the requests
+    on either side of it both pass while their rows overlap. accept_index holds permutations of each passing
+    request's rows (later requests overwrite the entries they share), so entries name rows twice, rows of the
+    neighbour, or rows in scrambled order. Returns None when the case would need more than T output entries."""
+    B = int(rng.integers(3, 9))
+    lens = rng.integers(1, 7, B)
+    offs = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    T = int(offs[-1])
+    k = int(rng.integers(1, B - 1))
+    offs[k] = min(int(offs[k + 1]) + int(rng.integers(1, 4)), T - B + k)
+    if not offs[k] > offs[k + 1]:
+        return None
+    ok = [oracle.verify._chain_offsets_ok(offs, b, T, B, 16) for b in range(B)]
+    if not (ok[k - 1] and ok[k + 1]):
+        return None
+    acc = rng.integers(-1, T, T).astype(np.int32)
+    alen = np.zeros(B, np.int32)
+    for b in range(B):
+        if not ok[b]:
+            continue
+        lo, hi = int(offs[b]), int(offs[b + 1])
+        r = int(rng.integers(0, hi - lo))
+        alen[b] = r
+        acc[lo:lo + r + 1] = lo + rng.permutation(hi - lo)[: r + 1]
+    slots = rng.integers(0, 1 << 40, T).astype(np.int64)
+    seq = rng.integers(0, 4096, B).astype(np.int32)
+    o = oracle.commit_indices(offs, alen, acc, slots, seq, 16)
+    if o["commit_offsets"][-1] > T or o["evict_offsets"][-1] > T:
+        return None
+    return offs.astype(np.int32), alen, acc, slots, seq
+
+
+def test_commit_overlapping_passing_requests():
+    """Two requests whose own offsets pass but whose rows overlap (the request between them is bad), with
+    permuted accept_index entries: each is committed and evicted exactly as the oracle does (no spurious
+    BAD_ACCEPT from the other's entries)."""
+    # the hand case: offsets [0, 4, 2, 6], requests 0 and 2 share rows 2-3
+    _commit_check(np.array([0, 4, 2, 6], np.int32), np.array([3, 0, 1], np.int32),
+                  np.array([1, 0, 3, 2, 5, 4], np.int32), np.arange(10, 16, dtype=np.int64),
+                  np.array([7, 0, 9], np.int32), 16)
+    rng = np.random.default_rng(41)
+    done = 0
+    while done < 40:
+        c = _overlapping_commit_case(rng)
+        if c is None:
+            continue
+        _commit_check(*c, 16)
+        done += 1
