@@ -27,7 +27,7 @@ __all__ = [
 _PKG = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_PKG, "libspecverify.so")
 
-ABI_VERSION = 6
+ABI_VERSION = 7
 MODES = {"greedy": 0, "rejection": 1, "target_only": 2, "rejection_sparse": 3, "sample_match": 4}
 KIND_CHAIN, KIND_TREE, KIND_COMMIT, KIND_PLAN, KIND_CAP_TRIM, KIND_KV_MOVE, KIND_TREE_BUILD = 0, 1, 2, 3, 4, 5, 6
 PLAN_MODES = {"topk": 0, "threshold": 1}
@@ -126,13 +126,14 @@ def _lib():
         raise RuntimeError(f"{library_path} is not built; run `python -m draft_verification_acceptance_amd.build`")
     lib = ctypes.CDLL(library_path)
     lib.spec_verify_chain.argtypes = [ctypes.POINTER(ChainArgs), _vp]
+    lib.spec_verify_chain_noalloc.argtypes = [ctypes.POINTER(ChainArgs), _vp]
     lib.spec_verify_tree.argtypes = [ctypes.POINTER(TreeArgs), _vp]
     lib.spec_commit_indices.argtypes = [ctypes.POINTER(CommitArgs), _vp]
     lib.spec_plan_layout.argtypes = [ctypes.POINTER(PlanArgs), _vp]
     lib.spec_cap_trim.argtypes = [ctypes.POINTER(CapTrimArgs), _vp]
     lib.spec_kv_move.argtypes = [ctypes.POINTER(KvMoveArgs), _vp]
     lib.spec_tree_build.argtypes = [ctypes.POINTER(TreeBuildArgs), _vp]
-    for f in (lib.spec_verify_chain, lib.spec_verify_tree, lib.spec_commit_indices, lib.spec_plan_layout,
+    for f in (lib.spec_verify_chain, lib.spec_verify_chain_noalloc, lib.spec_verify_tree, lib.spec_commit_indices, lib.spec_plan_layout,
               lib.spec_cap_trim, lib.spec_kv_move, lib.spec_tree_build):
         f.restype = ctypes.c_int
     import numpy as np
@@ -199,6 +200,7 @@ def workspace_init(ws: torch.Tensor):
 
 
 READ_SINK_WORDS = 8192   # SPEC_READ_SINK_WORDS
+NOALLOC_SCRATCH_BYTES = 4 << 20   # SPEC_NOALLOC_SCRATCH_BYTES
 
 
 def read_probe(src: torch.Tensor, sink: torch.Tensor, nbytes: int | None = None, events: "HipEvents | None" = None):
@@ -326,8 +328,10 @@ def prepare_verify_chain(target_logits: torch.Tensor, target_offsets: torch.Tens
                          temperature: float = 1.0, max_verify_len: int | None = None, workspace_tensor=None,
                          out: dict | None = None, accept_prob: bool = True, residual_mass: bool = True,
                          cand_ids: torch.Tensor | None = None, cand_q: torch.Tensor | None = None,
-                         vocab_mask: torch.Tensor | None = None) -> PreparedCall:
-    """Checks and marshals the arguments of spec_verify_chain once (see verify_chain)."""
+                         vocab_mask: torch.Tensor | None = None, noalloc: bool = False) -> PreparedCall:
+    """Checks and marshals the arguments of spec_verify_chain once (see verify_chain). noalloc: call
+    spec_verify_chain_noalloc instead (the library's static per-GPU scratch serves as the workspace; no
+    workspace tensor is made or passed)."""
     lib = _lib()
     dev = target_logits.device
     if target_logits.dim() != 2:
@@ -359,7 +363,10 @@ def prepare_verify_chain(target_logits: torch.Tensor, target_offsets: torch.Tens
     if mode != "greedy":
         _req(u_accept, "u_accept", torch.float32, D, dev)
         _req(u_final, "u_final", torch.float32, B, dev)
-    if workspace_tensor is None:
+    if noalloc:
+        if workspace_tensor is not None:
+            raise ValueError("noalloc calls take no workspace tensor")
+    elif workspace_tensor is None:
         workspace_tensor = workspace("chain", mode, T, V, B, max_verify_len, dev)
     o = _outputs(out, dev, B, T, D, accept_prob, residual_mass)
     a = ChainArgs()
@@ -374,8 +381,8 @@ def prepare_verify_chain(target_logits: torch.Tensor, target_offsets: torch.Tens
     a.status = o["status"].data_ptr()
     a.accept_prob = _ptr(o.get("accept_prob")) if accept_prob else None
     a.residual_mass = _ptr(o.get("residual_mass")) if residual_mass else None
-    a.workspace = workspace_tensor.data_ptr()
-    a.workspace_bytes = workspace_tensor.numel()
+    a.workspace = None if noalloc else workspace_tensor.data_ptr()
+    a.workspace_bytes = 0 if noalloc else workspace_tensor.numel()
     a.total_rows, a.vocab, a.batch = T, V, B
     a.max_verify_len = int(max_verify_len)
     a.dtype = DTYPES[target_logits.dtype]
@@ -387,7 +394,7 @@ def prepare_verify_chain(target_logits: torch.Tensor, target_offsets: torch.Tens
     a.vocab_mask = _ptr(vocab_mask)
     keep = [target_logits, target_offsets, draft_tokens, draft_logits, u_accept, u_final, cand_ids, cand_q,
             vocab_mask, workspace_tensor]
-    return PreparedCall(lib.spec_verify_chain, a, o, keep, dev)
+    return PreparedCall(lib.spec_verify_chain_noalloc if noalloc else lib.spec_verify_chain, a, o, keep, dev)
 
 
 def verify_chain(target_logits: torch.Tensor, target_offsets: torch.Tensor, draft_tokens: torch.Tensor,
@@ -398,7 +405,8 @@ def verify_chain(target_logits: torch.Tensor, target_offsets: torch.Tensor, draf
     uniforms and logits packed with m_b entries per request from off[b]-b; max_verify_len bounds m_b + 1.
     Keywords: draft_logits (rejection), cand_ids / cand_q ([T_rows - B, K] int32 / float32, rejection_sparse),
     u_accept, u_final, temperature, max_verify_len, workspace_tensor, out, accept_prob, residual_mass,
-    vocab_mask (int32 [T_rows, ceil(V/32)] allowed-token bits of the target rows, bit v % 32 of word v // 32).
+    vocab_mask (int32 [T_rows, ceil(V/32)] allowed-token bits of the target rows, bit v % 32 of word v // 32),
+    noalloc (spec_verify_chain_noalloc: no workspace; calls needing more than NOALLOC_SCRATCH_BYTES raise).
     Modes: greedy, rejection, rejection_sparse, sample_match. Returns the output tensors (accept_len, bonus,
     out_tokens, accept_index, status, accept_prob, residual_mass)."""
     return prepare_verify_chain(target_logits, target_offsets, draft_tokens, mode, **kw).run(events)

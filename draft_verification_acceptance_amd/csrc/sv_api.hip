@@ -2,10 +2,16 @@
 // Nothing here allocates, synchronises or reads device memory.
 #include <math.h>
 
+#include <mutex>
 
 #include "sv_internal.h"
 
 using namespace sv;
+
+// The workspace of spec_verify_chain_noalloc: one copy per GPU, held until the process ends. Host code never
+// passes this name to a kernel (on the host it is only a stand-in for the symbol); it looks up the array's
+// device address once per GPU and uses that address.
+static __device__ __align__(256) char scratch[SPEC_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -70,6 +76,34 @@ spec_status launch_pair(int dtype, int mode, VerifyParams& p, hipEvent_t* ev, in
   return e == hipSuccess ? SPEC_OK : SPEC_ELAUNCH;
 }
 
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];   // device address of `scratch` on each GPU, once looked up
+
+// Device address of `scratch` on the GPU that runs `stream`, looked up (with that GPU current) on the
+// first call for that GPU.
+spec_status scratch_for(hipStream_t stream, void** out) {
+  int dev = -1, cur = -1;
+  if (hipStreamGetDevice(stream, &dev) != hipSuccess || hipGetDevice(&cur) != hipSuccess) return SPEC_ELAUNCH;
+  if (dev < 0 || dev >= kMaxDevices) return SPEC_EINVAL;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return SPEC_ELAUNCH;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur && hipSetDevice(cur) != hipSuccess) return SPEC_ELAUNCH;
+    if (e != hipSuccess || p == nullptr) return SPEC_ELAUNCH;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return SPEC_OK;
+}
+
+// spec_verify_chain with the workspace given explicitly; `noalloc`: it is the static scratch (a call too large
+// for it is SPEC_ESCRATCH, looked up only once the arguments have passed their checks).
+spec_status verify_chain_impl(const spec_chain_args* a, void* ws, size_t ws_bytes, bool noalloc,
+                              hipStream_t stream);
+
 }  // namespace
 
 extern "C" {
@@ -97,6 +131,9 @@ const char* spec_status_string(spec_status s) {
     case SPEC_EUNSUPPORTED: return "SPEC_EUNSUPPORTED: mode / kind / threshold combination not implemented";
     case SPEC_EWORKSPACE: return "SPEC_EWORKSPACE: workspace missing or too small";
     case SPEC_ELAUNCH: return "SPEC_ELAUNCH: kernel launch or event record failed";
+    case SPEC_ESCRATCH:
+      return "SPEC_ESCRATCH: the call needs a larger workspace than the static scratch of "
+             "spec_verify_chain_noalloc (SPEC_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown spec_status";
   }
 }
@@ -146,6 +183,20 @@ spec_status spec_read_probe(const void* src, size_t bytes, uint32_t* sink, hipEv
 
 spec_status spec_verify_chain(const spec_chain_args* a, hipStream_t stream) {
   if (!a) return SPEC_EINVAL;
+  return verify_chain_impl(a, a->workspace, a->workspace_bytes, false, stream);
+}
+
+spec_status spec_verify_chain_noalloc(const spec_chain_args* a, hipStream_t stream) {
+  if (!a) return SPEC_EINVAL;
+  return verify_chain_impl(a, nullptr, SPEC_NOALLOC_SCRATCH_BYTES, true, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+spec_status verify_chain_impl(const spec_chain_args* a, void* ws, size_t ws_bytes, bool noalloc,
+                              hipStream_t stream) {
   if (a->dtype != SPEC_DTYPE_F32 && a->dtype != SPEC_DTYPE_BF16) return SPEC_EDTYPE;
   if (a->mode == SPEC_MODE_TARGET_ONLY) return SPEC_EUNSUPPORTED;
   if (a->mode != SPEC_MODE_GREEDY && a->mode != SPEC_MODE_REJECTION && a->mode != SPEC_MODE_REJECTION_SPARSE &&
@@ -174,7 +225,12 @@ spec_status spec_verify_chain(const spec_chain_args* a, hipStream_t stream) {
   if (sparse && D > 0 && (!a->cand_ids || !a->cand_q)) return SPEC_EINVAL;
   const Layout lo = make_layout(SPEC_KIND_CHAIN, a->mode, a->total_rows, a->vocab, a->batch, a->max_verify_len);
   if (!grid_fits(lo, a->batch)) return SPEC_EINVAL;
-  if (!a->workspace || a->workspace_bytes < lo.bytes) return SPEC_EWORKSPACE;
+  if (noalloc) {
+    if (lo.bytes > ws_bytes) return SPEC_ESCRATCH;
+    const spec_status st = scratch_for(stream, &ws);
+    if (st != SPEC_OK) return st;
+  }
+  if (!ws || ws_bytes < lo.bytes) return SPEC_EWORKSPACE;
 
   VerifyParams p{};
   p.target = a->target_logits;
@@ -187,7 +243,7 @@ spec_status spec_verify_chain(const spec_chain_args* a, hipStream_t stream) {
   p.u_accept = a->u_accept;
   p.u_final = a->u_final;
   fill_outputs(p, a);
-  carve(p, lo, a->workspace);
+  carve(p, lo, ws);
   p.V = a->vocab;
   p.total_rows = a->total_rows;
   p.B = a->batch;
@@ -198,11 +254,14 @@ spec_status spec_verify_chain(const spec_chain_args* a, hipStream_t stream) {
   // Piece partials need 16-byte aligned rows: the layout asks for them when vocab % 8 == 0, the base
   // pointer must be aligned too (else the draw narrows whole chunks).
   const bool aligned = (reinterpret_cast<uintptr_t>(a->target_logits) & 15) == 0;
-  p.piece = lo.n_piece > 0 && aligned ? reinterpret_cast<float2*>(static_cast<char*>(a->workspace) + lo.off_piece)
-                                      : nullptr;
+  p.piece = lo.n_piece > 0 && aligned ? reinterpret_cast<float2*>(static_cast<char*>(ws) + lo.off_piece) : nullptr;
   p.n_piece = lo.n_piece;
   return launch_pair(a->dtype, a->mode, p, a->profile_events, a->n_profile_events, stream);
 }
+
+}  // namespace
+
+extern "C" {
 
 spec_status spec_verify_tree(const spec_tree_args* a, hipStream_t stream) {
   if (!a) return SPEC_EINVAL;

@@ -44,7 +44,7 @@ extern "C" {
 typedef struct ihipStream_t* hipStream_t;
 typedef struct ihipEvent_t* hipEvent_t;
 
-#define SPEC_ABI_VERSION 6
+#define SPEC_ABI_VERSION 7
 
 /* Host-visible return codes. */
 typedef enum spec_status {
@@ -54,6 +54,7 @@ typedef enum spec_status {
   SPEC_EUNSUPPORTED = 3,  /* valid request this library does not implement (mode/kind pair, thresholds) */
   SPEC_EWORKSPACE = 4,    /* workspace NULL or smaller than spec_workspace_bytes()                        */
   SPEC_ELAUNCH = 5,       /* a kernel launch or event record returned an error                           */
+  SPEC_ESCRATCH = 6,      /* spec_verify_chain_noalloc: the call needs more than SPEC_NOALLOC_SCRATCH_BYTES */
 } spec_status;
 
 typedef enum spec_dtype { SPEC_DTYPE_F32 = 0, SPEC_DTYPE_BF16 = 1 } spec_dtype;
@@ -440,6 +441,19 @@ typedef struct spec_tree_build_args {
 spec_status spec_tree_build(const spec_tree_build_args* args, hipStream_t stream);
 
 spec_status spec_verify_chain(const spec_chain_args* args, hipStream_t stream);
+
+/* spec_verify_chain for callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): the same kernels and results, with the workspace taken
+ * from a static device array of SPEC_NOALLOC_SCRATCH_BYTES bytes inside the library instead of
+ * args->workspace (workspace / workspace_bytes are ignored and may be NULL / 0). The caller still passes
+ * every input and output. The array exists once per GPU and stays until the process ends; its address is
+ * looked up on the first call on each GPU (the GPU of `stream`). Nothing in it has to start at zero (each
+ * call resets what it counts with), but every call on one GPU shares it: calls that overlap on one GPU
+ * (other streams, other threads) race. A call whose spec_workspace_bytes exceeds the array returns
+ * SPEC_ESCRATCH and launches nothing. No allocation or free of any kind is made. */
+#define SPEC_NOALLOC_SCRATCH_BYTES ((size_t)4 << 20)
+spec_status spec_verify_chain_noalloc(const spec_chain_args* args, hipStream_t stream);
+
 spec_status spec_verify_tree(const spec_tree_args* args, hipStream_t stream);
 spec_status spec_commit_indices(const spec_commit_args* args, hipStream_t stream);
 

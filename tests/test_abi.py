@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_struct_sizes():
     lib = dva._lib()        # raises on ABI or struct-size mismatch
-    assert dva.abi_version() == 6
+    assert dva.abi_version() == 7
     assert lib.spec_args_size(0) == ctypes.sizeof(dva.ChainArgs) == 200
     assert lib.spec_args_size(1) == ctypes.sizeof(dva.TreeArgs)
     assert lib.spec_args_size(2) == ctypes.sizeof(dva.CommitArgs)
@@ -40,7 +40,7 @@ def test_abi_version_and_struct_sizes():
 
 def test_status_strings_and_kernel_counts():
     for code, word in [(0, "SPEC_OK"), (1, "EINVAL"), (2, "EDTYPE"), (3, "EUNSUPPORTED"), (4, "EWORKSPACE"),
-                       (5, "ELAUNCH")]:
+                       (5, "ELAUNCH"), (6, "ESCRATCH")]:
         assert word in dva.status_string(code)
     assert "unknown" in dva.status_string(99)
     assert dva.kernel_count("chain", "greedy") == 2
@@ -109,6 +109,31 @@ def test_chain_host_checks():
     assert _call_chain(_chain(**sm)) == 4                                     # args fine, no workspace
     assert _call_chain(_chain(**sm, vocab_mask=fake)) == 4                    # a mask changes no check
     assert dva.workspace_bytes("chain", "sample_match", 10, 100, 2, 5) > 0
+
+
+def test_noalloc_host_checks():
+    """spec_verify_chain_noalloc checks the same arguments, ignores the workspace fields, and refuses a call whose
+    workspace would not fit its static scratch with SPEC_ESCRATCH before touching any GPU."""
+    lib = dva._lib()
+    call = lambda a: lib.spec_verify_chain_noalloc(ctypes.byref(a), None)  # noqa: E731
+    assert lib.spec_verify_chain_noalloc(None, None) == 1
+    assert call(_chain(dtype=7)) == 2
+    assert call(_chain(mode=2)) == 3
+    assert call(_chain()) == 1                                                # null pointers
+    assert call(_chain(batch=0, total_rows=0)) == 0
+    fake = 1 << 40
+    full = dict(target_logits=fake, target_offsets=fake, draft_tokens=fake, accept_len=fake, bonus=fake,
+                out_tokens=fake, accept_index=fake, status=fake, mode=1, draft_logits=fake, u_accept=fake,
+                u_final=fake)
+    # 8192 requests x 16 rows at V 151936: more than SPEC_NOALLOC_SCRATCH_BYTES of workspace
+    big = dict(total_rows=8192 * 16, vocab=151936, batch=8192, max_verify_len=16)
+    need = dva.workspace_bytes("chain", "rejection", big["total_rows"], big["vocab"], big["batch"], 16)
+    assert need > dva.NOALLOC_SCRATCH_BYTES
+    assert call(_chain(**full, **big)) == 6                                   # ESCRATCH
+    assert call(_chain(**full, **big, workspace=fake, workspace_bytes=1 << 40)) == 6   # workspace ignored
+    # the chain rejection workload (B 64, m 7, V 151936) and the ragged one (B 512, up to 16 rows) fit
+    assert dva.workspace_bytes("chain", "rejection", 512, 151936, 64, 8) <= dva.NOALLOC_SCRATCH_BYTES
+    assert dva.workspace_bytes("chain", "rejection", 8192, 151936, 512, 16) <= dva.NOALLOC_SCRATCH_BYTES
 
 
 def test_tree_and_commit_host_checks():
