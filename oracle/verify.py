@@ -155,12 +155,24 @@ def draw(w: np.ndarray, u: float) -> tuple[int, float, float]:
     return k, gap, Z
 
 
+def near_cdf_band(gap: float) -> bool:
+    """The draw's u lies within 1e-5 of a step of the normalised CDF: too close to call, flagged and counted
+    (the band the verify step's contract fixes for residual-CDF gaps)."""
+    return gap < NEAR
+
+
+def near_cdf_mass(gap: float, Z: float) -> bool:
+    """READING (an accommodation of fp32 arithmetic, not a rule of the pages): the draw's margin measured in
+    probability mass, gap * Z, is below 1e-6. A verifier that forms p and q in fp32 knows each probability to
+    about 1e-7 relative, so the steps of the normalised residual CDF of a residual with small total mass Z
+    are known only to about 1e-6 / Z. This widens the 1e-5 band only where Z < 0.1, i.e. for rejections
+    between nearly equal p and q; on the seeded workloads it adds no exemption (tested)."""
+    return gap * Z < NEAR_MASS
+
+
 def near_cdf(gap: float, Z: float) -> bool:
-    """A draw is too close to call when u lies within 1e-5 of a step of the normalised CDF, or when that
-    margin in probability mass, gap * Z, is below 1e-6: probabilities computed in fp32 carry errors of that
-    size, so for a residual of small total mass Z the normalised steps are only known to about 1e-6 / Z.
-    READING: the pages fix no precision; this widens the 1e-5 band only where Z < 0.1."""
-    return gap < NEAR or gap * Z < NEAR_MASS
+    """A final draw too close to call: near_cdf_band or near_cdf_mass."""
+    return near_cdf_band(gap) or near_cdf_mass(gap, Z)
 
 
 def sample_then_match(ps: list, toks: list, tok_ok: list, us: list) -> tuple[int, int, list, int | None]:
@@ -179,7 +191,7 @@ def sample_then_match(ps: list, toks: list, tok_ok: list, us: list) -> tuple[int
     near = None
     for j in range(m + 1):
         t, gap, Z = draw(ps[j], us[j])
-        if near_cdf(gap, Z) and near is None:
+        if near_cdf_band(gap) and near is None:   # p_j itself: Z = 1, the mass clause adds nothing
             near = j
         if j < m:
             alphas.append(ps[j][toks[j]] if tok_ok[j] else 0.0)
@@ -199,6 +211,7 @@ def _sentinel_outputs(n_rows: int, n_draft: int, batch: int) -> dict:
         "accept_prob": np.full(n_draft, np.nan),
         "residual_mass": np.full(batch, np.nan),
         "flag_pos": np.full(batch, -2, np.int64),
+        "near_mass_only": np.zeros(batch, bool),
         "evaluated": np.zeros(batch, bool),
     }
 
@@ -222,8 +235,11 @@ def verify_chain(target: np.ndarray, offsets: np.ndarray, draft_tokens: np.ndarr
     vocab_mask [T_rows, ceil(V/32)] (optional) masks the target rows (mask_row); draft rows are not masked.
     `requests` limits the work to some requests (the others keep sentinel values: -2 / NaN).
 
-    Returns accept_len, bonus, out_tokens, accept_index, status, accept_prob, residual_mass and flag_pos
-    (oracle only: number of leading emitted tokens fixed before the first NEAR_* decision; r+1 if none).
+    Returns accept_len, bonus, out_tokens, accept_index, status, accept_prob, residual_mass, and (oracle
+    only) flag_pos = the position of the first decision too close to call (NEAR_ALPHA at the test of d_j:
+    j-1; NEAR_CDF at the final draw: r; a sample-then-match sample at row j: j), i.e. the number of leading
+    emitted tokens that no such decision can change; r+1 if none. near_mass_only: the request's only flag is
+    a final draw caught by near_cdf_mass alone.
     """
     assert mode in ("greedy", "rejection", "rejection_sparse", "sample_match")
     T, V = target.shape
@@ -344,6 +360,7 @@ def _chain_request(out, b, target, offsets, draft_tokens, mode, draft, u_accept,
             w = ps[r]
         x, gap, resid = draw(w, uf)
         if near_cdf(gap, resid):
+            out["near_mass_only"][b] = flag_pos is None and not near_cdf_band(gap)
             st |= ST_NEAR_CDF
             flag_pos = r if flag_pos is None else flag_pos
 
@@ -464,6 +481,7 @@ def _tree_request(out, b, target, parents, tokens, N, mode, u_accept, u_final, t
             w = p
         x, gap, resid = draw(w, uf)
         if near_cdf(gap, resid):
+            out["near_mass_only"][b] = flag_pos is None and not near_cdf_band(gap)
             st |= ST_NEAR_CDF
             flag_pos = len(path) - 1 if flag_pos is None else flag_pos
 

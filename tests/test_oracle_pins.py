@@ -849,6 +849,101 @@ def test_sparse_duplicate_and_invalid_candidates():
 
 
 # ----------------------------------------------------------------------------------------------------
+# the "too close to call" bands and flag_pos, placed by hand
+# ----------------------------------------------------------------------------------------------------
+# Decisions within 1e-5 of their threshold are flagged and counted instead of compared: |u - alpha| < 1e-5
+# for an accept test, a CDF gap < 1e-5 for a draw. Each case below puts u 0.9e-5 or 1.1e-5 from a threshold
+# whose value is known in closed form (probabilities 1/4, 1/2, 2/3 ... from logits ln p), so a band of the
+# wrong width, a flag on an unexamined test or a flag_pos one position off fails. flag_pos = the position of
+# the first flagged decision (the test of d_j: j - 1; the final draw: r; a sample at row j: j), r + 1 if none.
+LN = lambda *p: [float(np.log(x)) for x in p]  # noqa: E731
+
+
+def _flag_cases():
+    """(name, oracle call, expected (status NEAR bits, flag_pos, accept_len, first emitted tokens))."""
+    A, C = oracle.ST_NEAR_ALPHA, oracle.ST_NEAR_CDF
+    cases = []
+    # final draw of a lone anchor row, p = [1/4, 1/4, 1/2]: CDF steps at 1/4 and 1/2
+    for u, near, tok in ((0.5 - 0.9e-5, True, 1), (0.5 - 1.1e-5, False, 1), (0.5 + 0.9e-5, True, 2),
+                         (0.5 + 1.1e-5, False, 2), (0.25 - 0.9e-5, True, 0), (0.25 + 1.1e-5, False, 1),
+                         (0.75, False, 2)):
+        cases.append((f"anchor draw u={u}", lambda u=u: chain_call([LN(.25, .25, .5)], None, [], [], u, 1.0),
+                      (C if near else 0, 0 if near else 1, 0, (tok,))))
+    # residual draw: p = [.4, .3, .3], q = [.2, .1, .7], d1 = 2 rejected (alpha 3/7, u .9); w = [.2, .2, 0],
+    # Z = .4, normalised step at 1/2 (gap * Z stays above 1e-6: only the 1e-5 band decides)
+    for u, near, tok in ((0.5 - 0.9e-5, True, 0), (0.5 - 1.1e-5, False, 0), (0.5 + 0.9e-5, True, 1),
+                         (0.5 + 1.1e-5, False, 1)):
+        cases.append((f"residual draw u={u}", lambda u=u: chain_call([LN(.4, .3, .3), LN(.5, .25, .25)],
+                                                                     [LN(.2, .1, .7)], [2], [0.9], u, 1.0),
+                      (C if near else 0, 0 if near else 1, 0, (tok,))))
+    # accept test: p = [1/2, 1/2], q = [3/4, 1/4], d1 = 0: alpha = 2/3; row 1 p = [1/2, 1/2], u_final 1/4
+    a23 = 2.0 / 3.0
+    for du, near, r in ((-0.9e-5, True, 1), (0.9e-5, True, 0), (-1.1e-5, False, 1), (1.1e-5, False, 0)):
+        tok = (0, 0) if r == 1 else (1,)           # rejected: residual [0, 1/4] -> token 1
+        cases.append((f"accept test du={du}", lambda du=du: chain_call([LN(.5, .5), LN(.5, .5)], [LN(.75, .25)], [0],
+                                                                       [a23 + du], 0.25, 1.0),
+                      (A if near else 0, 0 if near else r + 1, r, tok)))
+    # the third test of a chain is the near one: d = [1, 1, 0] (alpha 1, 1, 2/3) -> flag_pos 2
+    rows, drows = [LN(.5, .5)] * 4, [LN(.75, .25)] * 3
+    cases.append(("third test near", lambda: chain_call(rows, drows, [1, 1, 0], [0.3, 0.3, a23 - 0.5e-5], 0.25, 1.0),
+                  (A, 2, 3, (1, 1, 0, 0))))
+    cases.append(("third test clear", lambda: chain_call(rows, drows, [1, 1, 0], [0.3, 0.3, a23 - 2e-5], 0.25, 1.0),
+                  (0, 4, 3, (1, 1, 0, 0))))
+    # tests after the first rejection are never examined, so never flagged
+    cases.append(("unexamined", lambda: chain_call(rows, drows, [0, 0, 0], [0.9, a23 + 1e-7, a23 - 1e-7], 0.5, 1.0),
+                  (0, 1, 0, (1,))))
+    # the mass clause: p = [.2, .3, .5], q = [.195, .295, .51], d1 = 2 rejected (alpha .98, u .99); w = [.005,
+    # .005, 0], Z = .01, normalised step at 1/2: 5e-5 from it is outside the 1e-5 band but gap * Z = 5e-7 < 1e-6
+    for u, near in ((0.5 - 5e-5, True), (0.5 - 2e-4, False), (0.5 + 5e-5, True), (0.5 + 2e-4, False)):
+        cases.append((f"mass clause u={u}", lambda u=u: chain_call([LN(.2, .3, .5), LN(.3, .3, .4)], [LN(.195, .295, .51)],
+                                                                   [2], [0.99], u, 1.0),
+                      (C if near else 0, 0 if near else 1, 0, (0 if u < 0.5 else 1,))))
+    # tree target-only: root p = [1/4, 1/4, 1/2], children tokens 0 (node 1) and 1 (node 2); node 2 has child
+    # token 2 (node 3), node 2's row p = [1/4, 1/4, 1/2]: cumulative masses 1/4, 1/2 at the root, 1/2 at node 2
+    rows_t = np.array([LN(.25, .25, .5)] * 4, np.float32)
+    par, toks = np.array([-1, 0, 0, 2]), np.array([0, 0, 1, 2])
+
+    def tree(u0, u2, uf):
+        ua = np.array([u0, 0.5, u2, 0.5])
+        return oracle.verify_tree(rows_t, par, toks, 4, "target_only", u_accept=ua, u_final=np.array([uf]))
+    cases.append(("tree root near", lambda: tree(0.25 + 0.9e-5, 0.3, 0.9), (A, 0, 2, (1, 2, 2))))
+    cases.append(("tree root clear", lambda: tree(0.25 + 1.1e-5, 0.3, 0.9), (0, 3, 2, (1, 2, 2))))
+    cases.append(("tree depth-1 near", lambda: tree(0.3, 0.5 - 0.9e-5, 0.9), (A, 1, 2, (1, 2, 2))))
+    cases.append(("tree depth-1 clear", lambda: tree(0.3, 0.5 - 1.1e-5, 0.9), (0, 3, 2, (1, 2, 2))))
+    # sample-then-match: p = [1/4, 1/4, 1/2] on every row, drafts [1, 1]: row 1's sample u .5 - 0.9e-5 (token 1,
+    # matches d2) is near -> flag_pos 1; all matched, row 2 samples token 2
+    rows_s = [LN(.25, .25, .5)] * 3
+    for u1, near in ((0.5 - 0.9e-5, True), (0.5 - 1.1e-5, False)):
+        cases.append((f"sample-then-match u={u1}",
+                      lambda u1=u1: chain_call(rows_s, None, [1, 1], [0.3, u1], 0.9, 1.0, mode="sample_match"),
+                      (C if near else 0, 1 if near else 3, 2, (1, 1, 2))))
+    return cases
+
+
+def flag_pin_failures():
+    fails = []
+    for name, call, (bits, fpos, r, toks) in _flag_cases():
+        o = call()
+        got = (int(o["status"][0]) & (oracle.ST_NEAR_ALPHA | oracle.ST_NEAR_CDF), int(o["flag_pos"][0]),
+               int(o["accept_len"][0]), emitted(o))
+        if got != (bits, fpos, r, toks):
+            fails.append((name, got, (bits, fpos, r, toks)))
+    return fails
+
+
+def test_flag_bands_and_flag_pos_by_hand():
+    assert flag_pin_failures() == []
+
+
+def test_mass_clause_is_marked():
+    """near_mass_only marks exactly the requests whose only flag is the mass clause."""
+    o = chain_call([LN(.2, .3, .5), LN(.3, .3, .4)], [LN(.195, .295, .51)], [2], [0.99], 0.5 - 5e-5, 1.0)
+    assert o["near_mass_only"][0] and abs(o["residual_mass"][0] - 0.01) < 1e-6
+    o = chain_call([LN(.4, .3, .3), LN(.5, .25, .25)], [LN(.2, .1, .7)], [2], [0.9], 0.5 - 0.9e-5, 1.0)
+    assert not o["near_mass_only"][0] and o["status"][0] & oracle.ST_NEAR_CDF
+
+
+# ----------------------------------------------------------------------------------------------------
 # planted mistakes: each plausible bug in the oracle must fail one of the pins above
 # ----------------------------------------------------------------------------------------------------
 def test_pins_catch_swapped_residual(monkeypatch):
@@ -932,3 +1027,37 @@ def test_p_zero_is_never_accepted():
     s = np.zeros((1, V), np.float32)
     o = chain_call(t, s, [3], [0.0], 0.5, 1.0)
     assert int(o["accept_len"][0]) == 0 and o["accept_prob"][0] == 0.0
+
+
+def test_pins_catch_flag_band_ten_times_too_wide(monkeypatch):
+    monkeypatch.setattr(ov, "NEAR", 1e-4)
+    assert any(n.startswith(("anchor", "residual", "accept", "tree", "sample")) for n, _, _ in flag_pin_failures())
+
+
+def test_pins_catch_flag_band_ten_times_too_narrow(monkeypatch):
+    monkeypatch.setattr(ov, "NEAR", 1e-6)
+    assert len(flag_pin_failures()) >= 5
+
+
+def test_pins_catch_mass_clause_dropped_or_widened(monkeypatch):
+    monkeypatch.setattr(ov, "near_cdf_mass", lambda gap, Z: False)
+    assert any(n.startswith("mass clause") for n, _, _ in flag_pin_failures())
+    monkeypatch.setattr(ov, "near_cdf_mass", lambda gap, Z: gap * Z < 1e-5)
+    assert any(n.startswith("mass clause") for n, _, _ in flag_pin_failures())
+
+
+@pytest.mark.parametrize("shift", [1, -1])
+def test_pins_catch_flag_pos_off_by_one(monkeypatch, shift):
+    """flag_pos one position late or early (on flagged requests) fails the hand-placed cases."""
+    def shifted(fn):
+        def call(*a, **k):
+            o = fn(*a, **k)
+            near = (o["status"] & (oracle.ST_NEAR_ALPHA | oracle.ST_NEAR_CDF)) != 0
+            o["flag_pos"] = np.where(near, o["flag_pos"] + shift, o["flag_pos"])
+            return o
+        return call
+    monkeypatch.setattr(oracle, "verify_chain", shifted(ov.verify_chain))
+    monkeypatch.setattr(oracle, "verify_tree", shifted(ov.verify_tree))
+    fails = {n.split(" u=")[0].split(" du=")[0] for n, _, _ in flag_pin_failures()}
+    assert {"anchor draw", "residual draw", "accept test", "third test near", "tree root near",
+            "tree depth-1 near", "sample-then-match"} <= fails
