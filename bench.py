@@ -2,9 +2,10 @@
 """Throughput of the speculative-decoding verify -> accept -> commit hot path on one MI355X.
 
 One step = one verify round of the timed workload (K steps captured into a HIP graph and timed as one replay;
-then K eager steps from Python for reference, and K more with per-kernel HIP events): spec_verify_chain (every target and draft logit row
-streamed once, accept scan, residual / bonus draw, outputs) followed by spec_commit_indices (KV commit
-compaction), both through the C ABI. Inputs are synthetic, seeded and resident in HBM before timing; a
+then K eager steps from Python for reference, and K more with per-kernel HIP events): spec_verify_chain (every
+target and draft logit row streamed once, accept scan, residual / bonus draw, outputs) with the KV commit
+compaction fused into the same call (--commit separate: spec_commit_indices as its own launch), through the
+C ABI. Inputs are synthetic, seeded and resident in HBM before timing; a
 rotation of input sets keeps the live footprint above twice the 256 MB Infinity Cache so HBM, not the
 cache, serves the stream.
 
@@ -103,6 +104,7 @@ def build_sets(name: str):
     i = 0
     while total <= 2 * MALL_BYTES or len(sets) < 2:
         w = W.FULL[gen](seed=base + i)
+        w.meta["seed"] = base + i
         if masked:
             w.name = name
             w.meta["seed"] = base + i
@@ -115,7 +117,7 @@ def build_sets(name: str):
 
 
 class ChainStep:
-    def __init__(self, w, mode):
+    def __init__(self, w, mode, fused=True):
         import torch
 
         import draft_verification_acceptance_amd as dva
@@ -135,11 +137,16 @@ class ChainStep:
         mask = w.meta.get("vocab_mask")
         if mask is not None:
             kw.update(vocab_mask=_dev(mask.view("<i4")))
-        self.verify = dva.prepare_verify_chain(t, offs, _dev(w.draft_tokens), mode, **kw)
-        o = self.verify.outputs
-        self.commit = dva.prepare_commit_indices(offs, o["accept_len"], o["accept_index"],
-                                                 _dev(W.verify_slots_for(w.total_rows)), _dev(W.seq_lens_for(w.batch)),
-                                                 max_verify_len=w.max_verify_len)
+        slots, seq = _dev(W.verify_slots_for(w.total_rows)), _dev(W.seq_lens_for(w.batch))
+        if fused:   # the KV commit inside the verify call
+            self.verify = dva.prepare_verify_chain(t, offs, _dev(w.draft_tokens), mode, verify_slots=slots,
+                                                   seq_lens=seq, **kw)
+            self.commit = None
+        else:
+            self.verify = dva.prepare_verify_chain(t, offs, _dev(w.draft_tokens), mode, **kw)
+            o = self.verify.outputs
+            self.commit = dva.prepare_commit_indices(offs, o["accept_len"], o["accept_index"], slots, seq,
+                                                     max_verify_len=w.max_verify_len)
         self.positions = w.total_rows
         self.draft_positions = w.total_rows - w.batch
         self.bytes = w.algorithmic_bytes(mode) + (mask.nbytes if mask is not None else 0)
@@ -147,7 +154,7 @@ class ChainStep:
 
 
 class TreeStep:
-    def __init__(self, w, mode):
+    def __init__(self, w, mode, fused=True):
         import numpy as np
         import torch
 
@@ -157,20 +164,24 @@ class TreeStep:
         kw = {}
         if mode == "target_only":
             kw = dict(u_accept=_dev(w.u_accept), u_final=_dev(w.u_final), temperature=w.temperature)
+        slots, seq = _dev(W.verify_slots_for(w.total_rows)), _dev(W.seq_lens_for(w.batch))
+        if fused:
+            kw.update(verify_slots=slots, seq_lens=seq)
         self.verify = dva.prepare_verify_tree(_dev_logits(w.target), _dev(w.parents), _dev(w.tokens), w.n_nodes, mode,
                                               **kw)
-        o = self.verify.outputs
-        offs = _dev((np.arange(w.batch + 1) * w.n_nodes).astype(np.int32))
-        self.commit = dva.prepare_commit_indices(offs, o["accept_len"], o["accept_index"],
-                                                 _dev(W.verify_slots_for(w.total_rows)), _dev(W.seq_lens_for(w.batch)),
-                                                 max_verify_len=w.n_nodes)
+        self.commit = None
+        if not fused:
+            o = self.verify.outputs
+            offs = _dev((np.arange(w.batch + 1) * w.n_nodes).astype(np.int32))
+            self.commit = dva.prepare_commit_indices(offs, o["accept_len"], o["accept_index"], slots, seq,
+                                                     max_verify_len=w.n_nodes)
         self.positions = w.total_rows
         self.draft_positions = w.total_rows - w.batch
         self.bytes = w.algorithmic_bytes(mode)
         torch.cuda.synchronize()
 
 
-def run_workload(name: str, mode: str | None, steps: int, warmup: int) -> dict:
+def run_workload(name: str, mode: str | None, steps: int, warmup: int, fused: bool = True) -> dict:
     import numpy as np
     import torch
 
@@ -179,16 +190,19 @@ def run_workload(name: str, mode: str | None, steps: int, warmup: int) -> dict:
     sets = build_sets(name)
     mode = mode or sets[0].modes[-1]
     kind = "tree" if name == "tree" else "chain"
-    st = [(TreeStep if kind == "tree" else ChainStep)(w, mode) for w in sets]
+    st = [(TreeStep if kind == "tree" else ChainStep)(w, mode, fused) for w in sets]
+
+    def step(s, ev_v=None, ev_c=None):
+        s.verify.run(ev_v)
+        if s.commit is not None:
+            s.commit.run(ev_c)
     _log(f"[bench] {name}/{mode}: {len(sets)} input sets, {sum(s.bytes for s in st) / 1e6:.0f} MB live, "
          f"setup {time.time() - t0:.1f}s")
     nk = dva.kernel_count(kind, mode)
     ev_v = [dva.HipEvents(2 * nk) for _ in range(steps)]   # start / stop of each kernel
     ev_c = [dva.HipEvents(2) for _ in range(steps)]
     for i in range(warmup):
-        s = st[i % len(st)]
-        s.verify.run()
-        s.commit.run()
+        step(st[i % len(st)])
     torch.cuda.synchronize()
     # The K timed steps are captured once into a HIP graph (the library launches only kernels on the
     # caller's stream: no allocation, memset or synchronisation) and replayed with one host launch, so the
@@ -196,9 +210,7 @@ def run_workload(name: str, mode: str | None, steps: int, warmup: int) -> dict:
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         for i in range(steps):
-            s = st[i % len(st)]
-            s.verify.run()
-            s.commit.run()
+            step(st[i % len(st)])
     graph.replay()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
@@ -208,29 +220,33 @@ def run_workload(name: str, mode: str | None, steps: int, warmup: int) -> dict:
     # The same steps issued eagerly from Python (host launch path included), for reference.
     t2 = time.perf_counter()
     for i in range(steps):
-        s = st[i % len(st)]
-        s.verify.run()
-        s.commit.run()
+        step(st[i % len(st)])
     torch.cuda.synchronize()
     wall_eager = time.perf_counter() - t2
     del graph
     # Same steps again with HIP events taking each kernel's start / stop timestamps (per-kernel durations).
     for i in range(steps):
-        s = st[i % len(st)]
-        s.verify.run(ev_v[i])
-        s.commit.run(ev_c[i])
+        step(st[i % len(st)], ev_v[i], ev_c[i])
     torch.cuda.synchronize()
     k_stats = np.array([e.elapsed_ms(0, 1) for e in ev_v])
     k_draw = np.array([e.elapsed_ms(2, 3) for e in ev_v]) if nk > 1 else np.zeros(steps)
-    k_commit = np.array([e.elapsed_ms(0, 1) for e in ev_c])
+    k_commit = np.array([e.elapsed_ms(0, 1) for e in ev_c]) if not fused else None
     verify_ms = k_stats + k_draw
     positions = np.mean([st[i % len(st)].positions for i in range(steps)])
     draft_positions = np.mean([st[i % len(st)].draft_positions for i in range(steps)])
     nbytes = np.mean([st[i % len(st)].bytes for i in range(steps)])
-    # Sanity of the last results (no data faults in these synthetic inputs).
+    # Sanity of the last results (no data faults in these synthetic inputs), and the device's own count of
+    # decisions too close to call on the canonical input set (set 0, re-run eagerly).
     stat = st[(steps - 1) % len(st)].verify.outputs["status"].cpu().numpy().view(np.uint32)
     bad = int(np.count_nonzero(stat & ~np.uint32(dva.ST.NEAR_ALPHA | dva.ST.NEAR_CDF)))
     acc = st[(steps - 1) % len(st)].verify.outputs["accept_len"].float().mean().item()
+    step(st[0])
+    torch.cuda.synchronize()
+    st0 = st[0].verify.outputs["status"].cpu().numpy().view(np.uint32)
+    near = {"requests": int(st0.size), "near_alpha": int(np.count_nonzero(st0 & np.uint32(dva.ST.NEAR_ALPHA))),
+            "near_cdf": int(np.count_nonzero(st0 & np.uint32(dva.ST.NEAR_CDF))),
+            "flagged": int(np.count_nonzero(st0 & np.uint32(dva.ST.NEAR_ALPHA | dva.ST.NEAR_CDF))),
+            "input_set_seed": int(sets[0].meta["seed"])}
     ms_step = wall * 1e3 / steps
     stats_ms = float(np.mean(k_stats))
     return {
@@ -244,8 +260,11 @@ def run_workload(name: str, mode: str | None, steps: int, warmup: int) -> dict:
         "step_hbm_fraction": nbytes / (ms_step * 1e-3) / (HBM_PEAK_GBS * 1e9),
         "kernel_ms": {"k_stats": {"mean": stats_ms, "p10": float(np.percentile(k_stats, 10)),
                                   "p50": float(np.median(k_stats)), "p90": float(np.percentile(k_stats, 90))},
-                      "k_draw": float(np.mean(k_draw)), "k_commit": float(np.mean(k_commit)),
+                      "k_draw": float(np.mean(k_draw)),
+                      "k_commit": float(np.mean(k_commit)) if k_commit is not None else "fused into k_draw / k_scan",
                       "verify_kernels_p50": float(np.median(verify_ms))},
+        "commit": "fused" if fused else "separate launch",
+        "device_flags": near,
         "stats_kernel_gbs": nbytes / (stats_ms * 1e-3) / 1e9,
         "mean_accept_len": acc,
         "status_faults": bad,
@@ -517,6 +536,8 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the other full-size workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--commit", choices=["fused", "separate"], default="fused",
+                    help="the KV commit inside the verify call (default) or as its own spec_commit_indices launch")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -532,19 +553,20 @@ def main():
     cpu, cpu_par = (None, None) if args.no_cpu_baseline else cpu_baselines(args.workload)
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
-    main_res = run_workload(args.workload, args.mode, args.steps, args.warmup)
+    fused = args.commit == "fused"
+    main_res = run_workload(args.workload, args.mode, args.steps, args.warmup, fused)
     extra = {}
     if not args.no_extra:
         for name, mode in (("block_greedy", None), ("ragged", None), ("tree", "greedy"), ("tree", "target_only"),
                            ("chain_sparse", None), ("block_sample", None), ("chain_rejection_masked", "rejection")):
             if name == args.workload and (mode or "") == (args.mode or ""):
                 continue
-            r = run_workload(name, mode, max(50, args.steps // 2), args.warmup)
+            r = run_workload(name, mode, max(50, args.steps // 2), args.warmup, fused)
             extra[f"{name}/{r['mode']}"] = {k: r[k] for k in ("verify_positions_per_step", "ms_per_step",
                                                               "ms_per_step_eager",
                                                               "positions_per_s", "step_hbm_fraction",
                                                               "stats_kernel_gbs", "kernel_ms", "mean_accept_len",
-                                                              "status_faults")}
+                                                              "status_faults", "device_flags", "commit")}
             torch.cuda.empty_cache()
         extra["planner"] = run_planner(max(50, args.steps // 2))
         extra["tree_round"] = run_tree_round(max(50, args.steps // 2))
@@ -582,6 +604,8 @@ def main():
                      "avg_launch_ms": stats_ms,
                      "read_floor": dict(floor, frac=achieved / floor["gbs"])},
         "kernel_ms": main_res["kernel_ms"],
+        "commit": main_res["commit"],
+        "device_flags": main_res["device_flags"],
         "mean_accept_len": main_res["mean_accept_len"],
         "status_faults": main_res["status_faults"],
         "cpu_baseline": cpu,

@@ -27,7 +27,7 @@ __all__ = [
 _PKG = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_PKG, "libspecverify.so")
 
-ABI_VERSION = 7
+ABI_VERSION = 8
 MODES = {"greedy": 0, "rejection": 1, "target_only": 2, "rejection_sparse": 3, "sample_match": 4}
 KIND_CHAIN, KIND_TREE, KIND_COMMIT, KIND_PLAN, KIND_CAP_TRIM, KIND_KV_MOVE, KIND_TREE_BUILD = 0, 1, 2, 3, 4, 5, 6
 PLAN_MODES = {"topk": 0, "threshold": 1}
@@ -67,7 +67,7 @@ class ChainArgs(ctypes.Structure):
                 ("workspace", _vp), ("workspace_bytes", _sz), ("profile_events", _vp), ("total_rows", _i64),
                 ("vocab", _i64), ("batch", _i32), ("max_verify_len", _i32), ("dtype", _i32), ("mode", _i32),
                 ("temperature", _f32), ("n_profile_events", _i32), ("cand_ids", _vp), ("cand_q", _vp),
-                ("n_cand", _i32), ("reserved", _i32), ("vocab_mask", _vp)]
+                ("n_cand", _i32), ("reserved", _i32), ("vocab_mask", _vp), ("commit", _vp)]
 
 
 class TreeArgs(ctypes.Structure):
@@ -76,7 +76,7 @@ class TreeArgs(ctypes.Structure):
                 ("accept_prob", _vp), ("residual_mass", _vp), ("workspace", _vp), ("workspace_bytes", _sz),
                 ("profile_events", _vp), ("vocab", _i64), ("batch", _i32), ("n_nodes", _i32), ("dtype", _i32),
                 ("mode", _i32), ("temperature", _f32), ("threshold_single", _f32), ("threshold_acc", _f32),
-                ("n_profile_events", _i32), ("vocab_mask", _vp)]
+                ("n_profile_events", _i32), ("vocab_mask", _vp), ("commit", _vp)]
 
 
 class CommitArgs(ctypes.Structure):
@@ -322,16 +322,51 @@ class PreparedCall:
         return self.outputs
 
 
+def _fused_commit(verify_slots, seq_lens, B: int, T: int, dev, evict: bool, o: dict, keep: list):
+    """The CommitArgs of a fused commit (verify_slots int64 [T], seq_lens int32 [B]); its outputs are added to
+    the verify outputs `o` as commit_offsets, src_slots, dst_pos, new_seq_lens, commit_status and (evict)
+    evict_offsets, evict_slots. Returns the address of the struct, kept alive through `keep`."""
+    _req(verify_slots, "verify_slots", torch.int64, T, dev)
+    _req(seq_lens, "seq_lens", torch.int32, B, dev)
+
+    def get(name, n, dtype):
+        t = o.get(name)
+        if t is None:
+            t = torch.empty(n, dtype=dtype, device=dev)
+            o[name] = t
+        return _req(t, name, dtype, n, dev)
+    get("commit_offsets", B + 1, torch.int32)
+    get("src_slots", T, torch.int64)
+    get("dst_pos", T, torch.int32)
+    get("new_seq_lens", B, torch.int32)
+    get("commit_status", B, torch.int32)
+    if evict:
+        get("evict_offsets", B + 1, torch.int32)
+        get("evict_slots", T, torch.int64)
+    c = CommitArgs()
+    c.verify_slots, c.seq_lens = _ptr(verify_slots), _ptr(seq_lens)
+    c.commit_offsets, c.src_slots, c.dst_pos = _ptr(o["commit_offsets"]), _ptr(o["src_slots"]), _ptr(o["dst_pos"])
+    c.new_seq_lens, c.status = _ptr(o["new_seq_lens"]), _ptr(o["commit_status"])
+    c.evict_slots = _ptr(o.get("evict_slots")) if evict else None
+    c.evict_offsets = _ptr(o.get("evict_offsets")) if evict else None
+    c.total_rows, c.capacity, c.batch = T, T, B
+    keep += [verify_slots, seq_lens, c]
+    return ctypes.addressof(c)
+
+
 def prepare_verify_chain(target_logits: torch.Tensor, target_offsets: torch.Tensor, draft_tokens: torch.Tensor,
                          mode: str = "greedy", *, draft_logits: torch.Tensor | None = None,
                          u_accept: torch.Tensor | None = None, u_final: torch.Tensor | None = None,
                          temperature: float = 1.0, max_verify_len: int | None = None, workspace_tensor=None,
                          out: dict | None = None, accept_prob: bool = True, residual_mass: bool = True,
                          cand_ids: torch.Tensor | None = None, cand_q: torch.Tensor | None = None,
-                         vocab_mask: torch.Tensor | None = None, noalloc: bool = False) -> PreparedCall:
+                         vocab_mask: torch.Tensor | None = None, noalloc: bool = False,
+                         verify_slots: torch.Tensor | None = None, seq_lens: torch.Tensor | None = None,
+                         commit_evict: bool = True) -> PreparedCall:
     """Checks and marshals the arguments of spec_verify_chain once (see verify_chain). noalloc: call
     spec_verify_chain_noalloc instead (the library's static per-GPU scratch serves as the workspace; no
-    workspace tensor is made or passed)."""
+    workspace tensor is made or passed). verify_slots / seq_lens: fuse the round's KV commit into the call
+    (its outputs join the verify outputs, see _fused_commit)."""
     lib = _lib()
     dev = target_logits.device
     if target_logits.dim() != 2:
@@ -394,6 +429,8 @@ def prepare_verify_chain(target_logits: torch.Tensor, target_offsets: torch.Tens
     a.vocab_mask = _ptr(vocab_mask)
     keep = [target_logits, target_offsets, draft_tokens, draft_logits, u_accept, u_final, cand_ids, cand_q,
             vocab_mask, workspace_tensor]
+    if verify_slots is not None or seq_lens is not None:
+        a.commit = _fused_commit(verify_slots, seq_lens, B, T, dev, commit_evict, o, keep)
     return PreparedCall(lib.spec_verify_chain_noalloc if noalloc else lib.spec_verify_chain, a, o, keep, dev)
 
 
@@ -406,7 +443,10 @@ def verify_chain(target_logits: torch.Tensor, target_offsets: torch.Tensor, draf
     Keywords: draft_logits (rejection), cand_ids / cand_q ([T_rows - B, K] int32 / float32, rejection_sparse),
     u_accept, u_final, temperature, max_verify_len, workspace_tensor, out, accept_prob, residual_mass,
     vocab_mask (int32 [T_rows, ceil(V/32)] allowed-token bits of the target rows, bit v % 32 of word v // 32),
-    noalloc (spec_verify_chain_noalloc: no workspace; calls needing more than NOALLOC_SCRATCH_BYTES raise).
+    noalloc (spec_verify_chain_noalloc: no workspace; calls needing more than NOALLOC_SCRATCH_BYTES raise),
+    verify_slots (int64 [T_rows]) and seq_lens (int32 [B]) to fuse the KV commit of the round into the call
+    (outputs commit_offsets, src_slots, dst_pos, new_seq_lens, commit_status, evict_offsets, evict_slots as
+    commit_indices gives them; commit_evict=False drops the evict lists).
     Modes: greedy, rejection, rejection_sparse, sample_match. Returns the output tensors (accept_len, bonus,
     out_tokens, accept_index, status, accept_prob, residual_mass)."""
     return prepare_verify_chain(target_logits, target_offsets, draft_tokens, mode, **kw).run(events)
@@ -416,8 +456,10 @@ def prepare_verify_tree(target_logits: torch.Tensor, parents: torch.Tensor, toke
                         mode: str = "greedy", *, u_accept=None, u_final=None, temperature: float = 1.0,
                         threshold_single: float = 1.0, threshold_acc: float = 1.0, workspace_tensor=None,
                         out: dict | None = None, accept_prob: bool = True, residual_mass: bool = True,
-                        vocab_mask: torch.Tensor | None = None) -> PreparedCall:
-    """Checks and marshals the arguments of spec_verify_tree once (see verify_tree)."""
+                        vocab_mask: torch.Tensor | None = None, verify_slots: torch.Tensor | None = None,
+                        seq_lens: torch.Tensor | None = None, commit_evict: bool = True) -> PreparedCall:
+    """Checks and marshals the arguments of spec_verify_tree once (see verify_tree; verify_slots / seq_lens:
+    fused KV commit as for prepare_verify_chain)."""
     lib = _lib()
     dev = target_logits.device
     if target_logits.dim() != 2 or target_logits.dtype not in DTYPES:
@@ -457,6 +499,8 @@ def prepare_verify_tree(target_logits: torch.Tensor, parents: torch.Tensor, toke
     a.threshold_single, a.threshold_acc = float(threshold_single), float(threshold_acc)
     a.vocab_mask = _ptr(vocab_mask)
     keep = [target_logits, parents, tokens, u_accept, u_final, vocab_mask, workspace_tensor]
+    if verify_slots is not None or seq_lens is not None:
+        a.commit = _fused_commit(verify_slots, seq_lens, B, rows, dev, commit_evict, o, keep)
     return PreparedCall(lib.spec_verify_tree, a, o, keep, dev)
 
 

@@ -20,7 +20,7 @@ constexpr double kLog2e = 1.4426950408889634;
 // The logits stream launches B x L x P x S workgroups and the draw B x S2: both within one grid dimension.
 bool grid_fits(const Layout& lo, int32_t batch) {
   const int64_t stream_wgs = int64_t(batch) * lo.L * lo.P * lo.S;
-  const int64_t draw_wgs = int64_t(batch) * lo.S2;
+  const int64_t draw_wgs = int64_t(batch) * (lo.S2 + 1);   // + the scan-only workgroup of a fused commit
   return stream_wgs <= INT32_MAX && draw_wgs <= INT32_MAX;
 }
 
@@ -62,6 +62,33 @@ void carve(VerifyParams& p, const Layout& lo, void* ws) {
   p.S2 = lo.S2;
   p.spc = lo.spc;
   p.n_seg = lo.n_seg;
+}
+
+// The fused commit's arguments (NULL: none), checked as spec_commit_indices checks its own; its counter and
+// published accept results live in the workspace. Call after carve() and once p.B is set.
+spec_status fill_commit(VerifyParams& p, const spec_commit_args* c, int64_t total_rows, const Layout& lo, void* ws) {
+  p.cm_on = 0;
+  if (!c) return SPEC_OK;
+  if (!c->verify_slots || !c->seq_lens || !c->commit_offsets || !c->src_slots || !c->dst_pos || !c->new_seq_lens ||
+      !c->status)
+    return SPEC_EINVAL;
+  if ((c->evict_slots == nullptr) != (c->evict_offsets == nullptr)) return SPEC_EINVAL;
+  if (c->capacity < total_rows) return SPEC_EINVAL;
+  char* w = static_cast<char*>(ws) + lo.off_cm;
+  p.cm_on = 1;
+  p.ccnt = reinterpret_cast<unsigned long long*>(w);
+  p.pub_r = reinterpret_cast<int32_t*>(w + kCounterStride);
+  p.pub_path = p.tree ? p.pub_r + p.B : nullptr;
+  p.verify_slots = c->verify_slots;
+  p.seq_lens = c->seq_lens;
+  p.commit_offsets = c->commit_offsets;
+  p.src_slots = c->src_slots;
+  p.dst_pos = c->dst_pos;
+  p.new_seq_lens = c->new_seq_lens;
+  p.cstatus = c->status;
+  p.evict_slots = c->evict_slots;
+  p.evict_offsets = c->evict_offsets;
+  return SPEC_OK;
 }
 
 // The two kernels of a verify call: the logits stream, then the greedy scans, the sample-then-match
@@ -256,6 +283,8 @@ spec_status verify_chain_impl(const spec_chain_args* a, void* ws, size_t ws_byte
   const bool aligned = (reinterpret_cast<uintptr_t>(a->target_logits) & 15) == 0;
   p.piece = lo.n_piece > 0 && aligned ? reinterpret_cast<float2*>(static_cast<char*>(ws) + lo.off_piece) : nullptr;
   p.n_piece = lo.n_piece;
+  const spec_status cs = fill_commit(p, a->commit, a->total_rows, lo, ws);
+  if (cs != SPEC_OK) return cs;
   return launch_pair(a->dtype, a->mode, p, a->profile_events, a->n_profile_events, stream);
 }
 
@@ -306,6 +335,8 @@ spec_status spec_verify_tree(const spec_tree_args* a, hipStream_t stream) {
   p.coef = tgt ? float(kLog2e / double(a->temperature)) : 0.f;
   p.mask = a->vocab_mask;
   p.mask_words = (a->vocab + 31) / 32;
+  const spec_status cs = fill_commit(p, a->commit, rows, lo, a->workspace);
+  if (cs != SPEC_OK) return cs;
   return launch_pair(a->dtype, a->mode, p, a->profile_events, a->n_profile_events, stream);
 }
 

@@ -16,8 +16,9 @@
 // Layout of the work: k_draw workgroup (b, c) covers a contiguous range of 512-token segments of request
 // b's row; each wave reduces whole segments (8 consecutive tokens per lane, 16-byte loads) and stores
 // (sum w, sum p) per segment. The request's last workgroup takes a float64 prefix over the
-// segments, then rescans the single segment holding u * Z in float64, token by token.
-#include "sv_scan.h"
+// segments, then rescans the single segment holding u * Z in float64, token by token. With a fused KV
+// commit each request has one more workgroup that only scans and counts the request for the commit.
+#include "sv_fused.h"
 
 namespace sv {
 
@@ -183,27 +184,39 @@ __global__ __launch_bounds__(kThreads) void k_draw(VerifyParams p) {
   __shared__ int s_sel;
   __shared__ double s_sel_excl;
 
-  const int b = blockIdx.x / p.S2;
-  const int c = blockIdx.x % p.S2;
+  // Workgroups per request: S2 that draw (chunk c covers segments [c * spc, (c + 1) * spc)) and, with a fused
+  // commit, one more in front that only runs the scan, writes its outputs and takes part in the commit. The
+  // commit's last arrival does the batch's commit while the memory system is busy with the draws (each of its
+  // loads then waits long): in a workgroup without draw work that delays no draw.
+  const int lead = p.cm_on ? 1 : 0;
+  const int b = blockIdx.x / (p.S2 + lead);
+  const int cw = blockIdx.x % (p.S2 + lead);
+  const bool scan_only = lead && cw == 0;
+  const int c = cw - lead;
+  const bool writes = lead ? scan_only : c == 0;   // the workgroup that writes the scan's outputs
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wv = tid / kWave;
 
-  // The request's scan (every workgroup of the request computes the same plan; chunk 0 writes the outputs
-  // it determines).
+  // The request's scan (every workgroup of the request computes the same plan).
   const int nst = staged_parts(p.L, p.P, p.S);
   Part* stage = nst ? reinterpret_cast<Part*>(smem) : nullptr;
   char* rows = smem + size_t(nst) * sizeof(Part);
   DrawPlan d;
   if (TREE) {
-    d = scan_tree<DT, true>(p, b, rows, stage, c == 0);
+    d = scan_tree<DT, true>(p, b, rows, stage, writes);
   } else {
     int64_t off0, len;
     if (!chain_request(p, b, off0, len)) {
-      if (c == 0 && tid == 0) write_bad_offsets(p, b);
+      if (writes && tid == 0) write_bad_offsets(p, b);
+      if (scan_only && commit_arrive<kThreads>(p, b, -1, nullptr)) fused_commit<kThreads, TREE>(p);
       return;   // no draw for b: all of b's workgroups agree
     }
-    d = scan_chain_rejection<SPARSE>(p, b, off0, int(len), rows, stage, c == 0);
+    d = scan_chain_rejection<SPARSE>(p, b, off0, int(len), rows, stage, writes);
+  }
+  if (scan_only) {
+    if (commit_arrive<kThreads>(p, b, d.r, d.path)) fused_commit<kThreads, TREE>(p);
+    return;
   }
 
   RowCtx r;
@@ -229,15 +242,31 @@ __global__ __launch_bounds__(kThreads) void k_draw(VerifyParams p) {
   const int n_adj = sparse ? p.K : d.n_seen;
   const int n_seen = collect_adjust(adj_ids, adj_a, n_adj, e_lo, e_hi, s_seen, s_seen_a, s_wcnt);
 
-  // Lane l of a wave owns tokens [s*512 + 8l, s*512 + 8l + 8) of segment s. A trip covers kTrip segments
-  // per wave with all of their loads issued before any is used.
+  // Lane l of a wave owns tokens [s*512 + 8l, s*512 + 8l + 8) of segment s; wave w takes segments
+  // s_begin + w, s_begin + w + kW, ... A trip covers kTrip segments per wave with all of their loads issued
+  // before any is used.
   constexpr int kW = kThreads / kWave;
   constexpr int kTrip = SV_DRAW_TRIP;
-  for (int s0 = s_begin + wv; s0 < s_end; s0 += kTrip * kW) {
+  constexpr int kStep = kTrip * kW;
+  const int64_t seg_base = int64_t(b) * p.n_seg;
+  auto reduce_seg = [&](const Raw8& at, const Raw8& aq, int s) {
+    const int64_t e = int64_t(s) * kSeg + 8 * lane;
+    float x[8], y[8], w[8], pv[8];
+    unpack_raw8<DT>(at, x);
+    if (r.xq) unpack_raw8<DT>(aq, y);
+    weights8(r, e, p.V, x, y, s_seen, s_seen_a, n_seen, w, pv);
+    float sw = 0.f, sp = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) { sw += w[j]; sp += pv[j]; }
+    sw = wave_sum_dpp(sw);   // the wave is whole here: s is the same in all of its lanes
+    sp = wave_sum_dpp(sp);
+    if (lane == 0) store_seg(p.seg + seg_base + s, sw, sp);
+  };
+  for (int t0 = s_begin + wv; t0 < s_end; t0 += kStep) {
     Raw8 rt[kTrip], rq[kTrip];
 #pragma unroll
     for (int u = 0; u < kTrip; ++u) {
-      const int s = s0 + u * kW;
+      const int s = t0 + u * kW;
       if (s < s_end) {
         load_raw8<DT>(r.xt, int64_t(s) * kSeg + 8 * lane, p.V, r.vec, rt[u]);
         if (r.xq) load_raw8<DT>(r.xq, int64_t(s) * kSeg + 8 * lane, p.V, r.vec, rq[u]);
@@ -245,19 +274,9 @@ __global__ __launch_bounds__(kThreads) void k_draw(VerifyParams p) {
     }
 #pragma unroll
     for (int u = 0; u < kTrip; ++u) {
-      const int s = s0 + u * kW;
+      const int s = t0 + u * kW;
       if (s >= s_end) break;
-      const int64_t e = int64_t(s) * kSeg + 8 * lane;
-      float x[8], y[8], w[8], pv[8];
-      unpack_raw8<DT>(rt[u], x);
-      if (r.xq) unpack_raw8<DT>(rq[u], y);
-      weights8(r, e, p.V, x, y, s_seen, s_seen_a, n_seen, w, pv);
-      float sw = 0.f, sp = 0.f;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) { sw += w[j]; sp += pv[j]; }
-      sw = wave_sum_dpp(sw);   // the wave is whole here: s is the same in all of its lanes
-      sp = wave_sum_dpp(sp);
-      if (lane == 0) store_seg(p.seg + int64_t(b) * p.n_seg + s, sw, sp);
+      reduce_seg(rt[u], rq[u], s);
     }
   }
 
@@ -388,7 +407,7 @@ __global__ __launch_bounds__(kThreads) void k_draw(VerifyParams p) {
 
 template <typename DT>
 hipError_t launch_draw_t(int mode, const VerifyParams& p, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
-  const int64_t blocks = int64_t(p.B) * p.S2;
+  const int64_t blocks = int64_t(p.B) * (p.S2 + (p.cm_on ? 1 : 0));
   if (blocks <= 0) return hipSuccess;
   const size_t smem = scan_smem_bytes(p.tree != 0, true, p.L, p.P, p.S);
   const dim3 grid{unsigned(blocks)}, block{unsigned(kThreads)};

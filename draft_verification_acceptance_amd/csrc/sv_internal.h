@@ -20,6 +20,9 @@
 //             of the request locates the inverse-CDF step (fp64 prefix over segments, then inside one
 //             segment) and writes the token and the status.
 //   k_commit  one workgroup: exclusive scan of accept_len + 1 and the slot gathers of the KV commit.
+//   A fused commit (a verify call given commit arguments) runs the same commit inside k_scan / k_draw /
+//   k_match: every request's accept scan publishes its result and counts itself; the workgroup that counts
+//   last writes the commit lists for the whole batch (no extra launch).
 #pragma once
 
 #include <hip/hip_ext.h>
@@ -117,6 +120,7 @@ struct Layout {
   int32_t n_seg = 0;     // segments per row
   int32_t n_piece = 0;   // sample-then-match: piece slots per row (0: no piece partials)
   size_t off_cnt2 = 0, off_part = 0, off_seg = 0, off_piece = 0;
+  size_t off_cm = 0;     // fused commit: counter, then the published accept lengths and tree paths
   size_t bytes = 0;
 };
 
@@ -168,6 +172,9 @@ inline Layout make_layout(int kind, int mode, int64_t total_rows, int64_t vocab,
   lo.off_seg = o;  o = up(o + (sampling ? sizeof(float2) * size_t(batch) * size_t(lo.n_seg) : 0));
   lo.n_piece = pieces ? int32_t((vocab + kPieceMin - 1) / kPieceMin) : 0;
   lo.off_piece = o; o = up(o + sizeof(float2) * size_t(batch) * size_t(L) * size_t(lo.n_piece));
+  // fused commit: one counter line, an accept length per request and (trees) the accepted path of each
+  lo.off_cm = o; o = up(o + kCounterStride + sizeof(int32_t) * size_t(batch) *
+                                                (1 + (kind == SPEC_KIND_TREE ? size_t(L) : 0)));
   lo.bytes = o;
   (void)total_rows;
   return lo;
@@ -207,6 +214,22 @@ struct VerifyParams {
   int64_t mask_words;         // ceil(V / 32)
   float2* piece;              // sample-then-match: (m, z) per piece of each target row slot, or NULL
   int32_t n_piece;            // piece slots per row slot
+  // Fused KV commit (cm_on): each request's accept scan publishes its accept length (trees: and its path)
+  // in pub_r / pub_path and counts itself on ccnt (reset by the logits stream); the workgroup that counts
+  // last writes the commit outputs for the whole batch.
+  int32_t cm_on;
+  unsigned long long* ccnt;
+  int32_t* pub_r;             // [B]
+  int32_t* pub_path;          // trees: [B, L] node indices of the accepted path
+  const int64_t* verify_slots;
+  const int32_t* seq_lens;
+  int32_t* commit_offsets;
+  int64_t* src_slots;
+  int32_t* dst_pos;
+  int32_t* new_seq_lens;
+  uint32_t* cstatus;
+  int64_t* evict_slots;       // optional
+  int32_t* evict_offsets;     // optional
 };
 
 struct CommitParams {

@@ -12,7 +12,7 @@
 // lane whose range holds the target, and so on until a lane holds at most 8 tokens; a unit of at most 2048
 // tokens, a bf16 piece, is decided in one round: each lane holds its 32 tokens and the picked lane walks
 // them). Only that unit of the row is read (4 KB per row for a bf16 piece).
-#include "sv_scan.h"
+#include "sv_fused.h"
 
 namespace sv {
 
@@ -296,6 +296,7 @@ __global__ __launch_bounds__(kMatchThreads) void k_match(VerifyParams p) {
   int64_t off0, len64;
   if (!chain_request(p, b, off0, len64)) {
     if (tid == 0) write_bad_offsets(p, b);
+    if (p.cm_on && commit_arrive<kMatchThreads>(p, b, -1, nullptr)) fused_commit<kMatchThreads, false>(p);
     return;
   }
   const int len = int(len64);
@@ -478,6 +479,7 @@ __global__ __launch_bounds__(kMatchThreads) void k_match(VerifyParams p) {
     p.status[b] = s_flags;
     if (p.residual_mass) p.residual_mass[b] = -1.f;
   }
+  if (p.cm_on && commit_arrive<kMatchThreads>(p, b, r, nullptr)) fused_commit<kMatchThreads, false>(p);
 }
 
 }  // namespace

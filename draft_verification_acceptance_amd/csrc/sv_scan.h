@@ -102,14 +102,18 @@ __device__ __forceinline__ bool z_bad(float z) { return !(z > 0.f && z < INFINIT
 // Request b of a chain batch: [off0, off0 + len) is usable iff its offsets pass the request's own checks
 // (non-empty, at most L rows, and the bounds every valid batch meets that keep its draft rows inside
 // [0, total_rows - B): off[b] >= b, off[b+1] <= total_rows - B + b + 1; off[0] = 0, off[B] = total_rows).
+__device__ __forceinline__ bool chain_offsets_ok(const VerifyParams& p, int b, int64_t off0, int64_t off1) {
+  bool ok = off0 >= b && off1 > off0 && off1 <= p.total_rows - p.B + b + 1 && off1 - off0 <= p.L;
+  if (b == 0 && off0 != 0) ok = false;
+  if (b == p.B - 1 && off1 != p.total_rows) ok = false;
+  return ok;
+}
+
 __device__ __forceinline__ bool chain_request(const VerifyParams& p, int b, int64_t& off0, int64_t& len) {
   off0 = p.offsets[b];
   const int64_t off1 = p.offsets[b + 1];
   len = off1 - off0;
-  bool ok = off0 >= b && off1 > off0 && off1 <= p.total_rows - p.B + b + 1 && len <= p.L;
-  if (b == 0 && off0 != 0) ok = false;
-  if (b == p.B - 1 && off1 != p.total_rows) ok = false;
-  return ok;
+  return chain_offsets_ok(p, b, off0, off1);
 }
 
 // Outputs indexed by request for a request whose offsets fail their checks.
@@ -131,6 +135,8 @@ struct DrawPlan {
   uint32_t status;      // request status bits of the scan
   int32_t n_seen;       // tree target-only: tokens excluded from the draw (listed in `seen`, LDS)
   const int32_t* seen;
+  int32_t r;            // accepted drafts
+  const int32_t* path;  // tree: the accepted path's node indices, root first (LDS); chain: NULL
 };
 
 // Load round of a chain scan: the request's n partials (when staged) and its n_tok draft tokens and
@@ -162,7 +168,7 @@ __device__ __forceinline__ void chain_load_round(const VerifyParams& p, const Pa
 // ---------------------------------------------------------------------------------------------------
 // Chain greedy: writes every output of request b.
 // ---------------------------------------------------------------------------------------------------
-__device__ void scan_chain_greedy(const VerifyParams& p, int b, int64_t off0, int len, char* smem, Part* stage) {
+__device__ int scan_chain_greedy(const VerifyParams& p, int b, int64_t off0, int len, char* smem, Part* stage) {
   __shared__ int s_red[kThreads / kWave];
   __shared__ uint32_t s_flags;
   const int tid = threadIdx.x;
@@ -204,6 +210,7 @@ __device__ void scan_chain_greedy(const VerifyParams& p, int b, int64_t off0, in
     p.status[b] = s_flags;
     if (p.residual_mass) p.residual_mass[b] = -1.f;
   }
+  return r;
 }
 
 // ---------------------------------------------------------------------------------------------------
@@ -321,6 +328,8 @@ __device__ DrawPlan scan_chain_rejection(const VerifyParams& p, int b, int64_t o
   d.status = s_flags;
   d.n_seen = 0;
   d.seen = nullptr;
+  d.r = r;
+  d.path = nullptr;
   return d;
 }
 
@@ -532,6 +541,8 @@ __device__ DrawPlan scan_tree(const VerifyParams& p, int b, char* smem, Part* st
   d.status = s_flags;
   d.n_seen = SAMPLING ? s_nseen : 0;
   d.seen = s_seen;
+  d.r = r;
+  d.path = s_path;
   if (SAMPLING) {
     bool ubad = false;
     d.u = sanitize_u(uf_raw, ubad);

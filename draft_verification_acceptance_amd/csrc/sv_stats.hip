@@ -11,7 +11,7 @@
 //             row's candidates.
 // A vocab mask ([EAGLE→DFlash2] §5.6.6, §8.4: applied to the target logits after the forward, before
 // acceptance) turns the disallowed logits of a target row into -inf as they stream.
-#include "sv_scan.h"
+#include "sv_fused.h"
 
 namespace sv {
 
@@ -395,6 +395,8 @@ __global__ __launch_bounds__(NT) void k_stats(VerifyParams p) {
   __shared__ float s_g;
   __shared__ uint32_t s_gf;
 
+  // The fused commit of this call counts its requests from 0.
+  if (p.cm_on && blockIdx.x == 0 && threadIdx.x == 0) store_agent(p.ccnt, 0ull);
   // Workgroup ids go round-robin over the XCDs. A request's (slot, part, chunk) order is rotated by its
   // index, so that the slots short requests leave empty do not always fall on the same XCDs.
   const int per_req = p.L * p.P * p.S;
@@ -507,16 +509,22 @@ __global__ __launch_bounds__(kThreads) void k_scan(VerifyParams p) {
   const int nst = staged_parts(p.L, p.P, p.S);
   Part* stage = nst ? reinterpret_cast<Part*>(smem) : nullptr;
   char* rows = smem + size_t(nst) * sizeof(Part);
-  if (p.tree) {
-    scan_tree<DT, false>(p, b, rows, stage, true);
-    return;
-  }
+  int r = -1;
+  const int32_t* path = nullptr;
   int64_t off0, len;
-  if (!chain_request(p, b, off0, len)) {
+  if (p.tree) {
+    const DrawPlan d = scan_tree<DT, false>(p, b, rows, stage, true);
+    r = d.r;
+    path = d.path;
+  } else if (!chain_request(p, b, off0, len)) {
     if (threadIdx.x == 0) write_bad_offsets(p, b);
-    return;
+  } else {
+    r = scan_chain_greedy(p, b, off0, int(len), rows, stage);
   }
-  scan_chain_greedy(p, b, off0, int(len), rows, stage);
+  if (p.cm_on && commit_arrive<kThreads>(p, b, r, path)) {
+    if (p.tree) fused_commit<kThreads, true>(p);
+    else fused_commit<kThreads, false>(p);
+  }
 }
 
 template <typename DT>

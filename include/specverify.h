@@ -44,7 +44,7 @@ extern "C" {
 typedef struct ihipStream_t* hipStream_t;
 typedef struct ihipEvent_t* hipEvent_t;
 
-#define SPEC_ABI_VERSION 7
+#define SPEC_ABI_VERSION 8
 
 /* Host-visible return codes. */
 typedef enum spec_status {
@@ -161,6 +161,23 @@ typedef enum spec_kind {
  *   accept_prob[off[b]-b+j]   opt.: alpha_{j+1} where tested (sampling modes), else -1
  *   residual_mass[b]          opt.: sum of the final draw's weights (sampling modes), -1 in GREEDY
  */
+typedef struct spec_commit_args spec_commit_args;
+
+/*
+ * Fused KV commit (optional, chain and tree verify): `commit` (a HOST pointer, NULL = none) asks the verify call
+ * to also produce this round's KV commit lists in the same launches ([EAGLE→DFlash2] §5.6: the accept step
+ * returns the accept lengths, bonus tokens and commit lengths together; §5.6.6 commit_lens = correct_len + 1).
+ * The outputs are exactly those spec_commit_indices would give for row_offsets = target_offsets (chain) or
+ * [0, N, 2N, ..] (tree), accept_len / accept_index = this call's outputs, total_rows, batch and
+ * max_verify_len = this call's (tree: n_nodes). From *commit only verify_slots, seq_lens, the outputs
+ * (commit_offsets, src_slots, dst_pos, new_seq_lens, status and the optional evict_slots / evict_offsets) and
+ * capacity (>= total_rows) are used; its row_offsets, accept_len, accept_index, total_rows, batch,
+ * max_verify_len and profile events are ignored. The commit runs in the call's second kernel, in the
+ * workgroup that finishes its request's accept scan last, so it adds no launch and no kernel to
+ * spec_kernel_count. A NULL verify_slots / seq_lens / output, or capacity < total_rows, is SPEC_EINVAL. When
+ * requests report SPEC_ST_BAD_OFFSETS (the batch's verify outputs are then unspecified) every request whose own
+ * offsets pass still commits its first accept_len + 1 rows; batch 0 launches nothing (commit_offsets untouched).
+ */
 typedef struct spec_chain_args {
   const void* target_logits;     /* [total_rows, vocab]                                   */
   const int32_t* target_offsets; /* [batch+1], off[0] = 0, off[batch] = total_rows           */
@@ -198,6 +215,7 @@ typedef struct spec_chain_args {
   int32_t reserved;
   const uint32_t* vocab_mask;    /* optional [total_rows, ceil(vocab/32)] allowed-token bits of
                                     the target rows (see "Vocab (grammar) mask"); NULL: none   */
+  const spec_commit_args* commit; /* optional HOST pointer: fused KV commit (see above)        */
 } spec_chain_args;
 
 /*
@@ -238,6 +256,7 @@ typedef struct spec_tree_args {
   int32_t n_profile_events;
   const uint32_t* vocab_mask; /* optional [batch*n_nodes, ceil(vocab/32)] allowed-token bits of
                                  every node row; NULL: none                      */
+  const spec_commit_args* commit; /* optional HOST pointer: fused KV commit (see spec_chain_args) */
 } spec_tree_args;
 
 /*
@@ -256,7 +275,7 @@ typedef struct spec_tree_args {
  * src_slots = -1; an entry naming a row a second time commits that row's slot again; the request evicts
  * exactly the rows no entry names (so its evict count is rows - distinct named rows).
  */
-typedef struct spec_commit_args {
+struct spec_commit_args {
   const int32_t* row_offsets;  /* [batch+1]                    */
   const int32_t* accept_len;   /* [batch]                      */
   const int32_t* accept_index; /* [total_rows]                 */
@@ -276,7 +295,7 @@ typedef struct spec_commit_args {
   int32_t max_verify_len;      /* upper bound on rows per request, 1..1024 */
   int32_t n_profile_events;
   int32_t reserved;
-} spec_commit_args;
+};
 
 /*
  * Verify-length planner, device side: how many of each request's W proposed drafts this round verifies

@@ -32,8 +32,8 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_struct_sizes():
     lib = dva._lib()        # raises on ABI or struct-size mismatch
-    assert dva.abi_version() == 7
-    assert lib.spec_args_size(0) == ctypes.sizeof(dva.ChainArgs) == 200
+    assert dva.abi_version() == 8
+    assert lib.spec_args_size(0) == ctypes.sizeof(dva.ChainArgs) == 208
     assert lib.spec_args_size(1) == ctypes.sizeof(dva.TreeArgs)
     assert lib.spec_args_size(2) == ctypes.sizeof(dva.CommitArgs)
 
@@ -109,6 +109,30 @@ def test_chain_host_checks():
     assert _call_chain(_chain(**sm)) == 4                                     # args fine, no workspace
     assert _call_chain(_chain(**sm, vocab_mask=fake)) == 4                    # a mask changes no check
     assert dva.workspace_bytes("chain", "sample_match", 10, 100, 2, 5) > 0
+
+
+def test_fused_commit_host_checks():
+    """A verify call given commit arguments checks them as spec_commit_indices does, before any launch."""
+    lib = dva._lib()
+    fake = 1 << 40
+    full = dict(target_logits=fake, target_offsets=fake, draft_tokens=fake, accept_len=fake, bonus=fake,
+                out_tokens=fake, accept_index=fake, status=fake, workspace=fake, workspace_bytes=1 << 30)
+    good = dict(verify_slots=fake, seq_lens=fake, commit_offsets=fake, src_slots=fake, dst_pos=fake,
+                new_seq_lens=fake, status=fake, capacity=10)
+    for bad in (dict(verify_slots=None), dict(seq_lens=None), dict(src_slots=None), dict(status=None),
+                dict(capacity=9), dict(evict_slots=fake)):
+        c = dva.CommitArgs(**dict(good, **bad))
+        a = _chain(**full)
+        a.commit = ctypes.addressof(c)
+        assert lib.spec_verify_chain(ctypes.byref(a), None) == 1, bad
+        t = dva.TreeArgs()
+        t.vocab, t.batch, t.n_nodes, t.dtype, t.mode = 100, 2, 5, 1, 0
+        for k in ("target_logits", "parents", "tokens", "accept_len", "bonus", "out_tokens", "accept_index", "status",
+                  "workspace"):
+            setattr(t, k, fake)
+        t.workspace_bytes = 1 << 30
+        t.commit = ctypes.addressof(c)
+        assert lib.spec_verify_tree(ctypes.byref(t), None) == 1, bad
 
 
 def test_noalloc_host_checks():
