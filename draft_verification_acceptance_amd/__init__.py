@@ -25,7 +25,8 @@ __all__ = [
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-library_path = os.path.join(_PKG, "libspecverify.so")
+# SPECVERIFY_LIBRARY: another build of the same library (the host-sanitizer build of build.py --sanitize)
+library_path = os.environ.get("SPECVERIFY_LIBRARY") or os.path.join(_PKG, "libspecverify.so")
 
 ABI_VERSION = 8
 MODES = {"greedy": 0, "rejection": 1, "target_only": 2, "rejection_sparse": 3, "sample_match": 4}

@@ -150,8 +150,8 @@ size_t spec_args_size(int32_t kind) {
   }
 }
 
-const char* spec_status_string(spec_status s) {
-  switch (s) {
+const char* spec_status_string(int32_t code) {
+  switch (code) {
     case SPEC_OK: return "SPEC_OK";
     case SPEC_EINVAL: return "SPEC_EINVAL: invalid argument (null pointer or size out of range)";
     case SPEC_EDTYPE: return "SPEC_EDTYPE: unsupported logits dtype";

@@ -499,8 +499,9 @@ spec_status spec_read_probe(const void* src, size_t bytes, uint32_t* sink, hipEv
 /* Number of kernels a call of this kind/mode launches (events: kernels + 1). Pure host function. */
 int32_t spec_kernel_count(int32_t kind, int32_t mode);
 
-/* Static string naming a return code. Pure host function. */
-const char* spec_status_string(spec_status s);
+/* Static string naming a return code (any int: codes that are no spec_status get "unknown spec_status").
+   Pure host function. */
+const char* spec_status_string(int32_t code);
 
 /* SPEC_ABI_VERSION the library was built with, and sizeof of the argument structs (ABI checks). */
 int32_t spec_abi_version(void);
