@@ -20,7 +20,7 @@ __all__ = [
     "SpecError", "verify_chain", "verify_tree", "commit_indices", "workspace", "workspace_bytes", "read_probe",
     "workspace_init", "kernel_count", "status_string", "abi_version", "library_path", "HipEvents",
     "MODES", "ST", "PreparedCall", "prepare_verify_chain", "prepare_verify_tree", "prepare_commit_indices",
-    "plan_layout", "prepare_plan_layout", "plan_budget", "cap_trim", "prepare_cap_trim", "kv_move",
+    "plan_layout", "prepare_plan_layout", "plan_budget", "plan_budget_cost", "cap_trim", "prepare_cap_trim", "kv_move",
     "prepare_kv_move", "tree_build", "prepare_tree_build",
 ]
 
@@ -143,6 +143,9 @@ def _lib():
     lib.spec_plan_budget.argtypes = [_f32a, _i32, _i32, _f64a, _f64a, _i32, _f32, ctypes.POINTER(_i32), _f64a,
                                      ctypes.POINTER(_i32)]
     lib.spec_plan_budget.restype = ctypes.c_int
+    lib.spec_plan_budget_cost.argtypes = [_f32a, _i32, _i32, _f64a, _f64a, _i32, _f64a, _f64a, _i32, _f32,
+                                          ctypes.POINTER(_i32), _f64a, ctypes.POINTER(_i32)]
+    lib.spec_plan_budget_cost.restype = ctypes.c_int
     lib.spec_workspace_bytes.argtypes = [_i32, _i32, _i64, _i64, _i32, _i32]
     lib.spec_workspace_bytes.restype = _sz
     lib.spec_workspace_init.argtypes = [_vp, _sz, _vp]
@@ -586,6 +589,25 @@ def plan_budget(confidence_hist, sps_rows, sps, *, survival_eps: float = 0.0):
     k, n = _i32(), _i32()
     _check(_lib().spec_plan_budget(c, R, W, xs, ys, len(xs), float(survival_eps), ctypes.byref(k), theta,
                                    ctypes.byref(n)))
+    return int(k.value), theta[:n.value + 1]
+
+
+def plan_budget_cost(confidence_hist, req_rows, req_cost, tok_rows, tok_cost, *, survival_eps: float = 0.0):
+    """spec_plan_budget_cost (host function): the verify budget K* under an additive step-cost table (per-batch
+    cost at the request count plus per-row cost at the target row count). Returns (K*, N(K) / T for K = 0..n)."""
+    import numpy as np
+    c = np.ascontiguousarray(confidence_hist.cpu().numpy() if isinstance(confidence_hist, torch.Tensor)
+                             else confidence_hist, dtype=np.float32)
+    if c.ndim != 2:
+        raise ValueError("confidence_hist must be [batch, width]")
+    R, W = c.shape
+    tabs = [np.ascontiguousarray(t, dtype=np.float64) for t in (req_rows, req_cost, tok_rows, tok_cost)]
+    if tabs[0].shape != tabs[1].shape or tabs[2].shape != tabs[3].shape or any(t.ndim != 1 for t in tabs):
+        raise ValueError("each cost table is two 1-D arrays of equal length")
+    theta = np.zeros(R * W + 1, np.float64)
+    k, n = _i32(), _i32()
+    _check(_lib().spec_plan_budget_cost(c, R, W, tabs[0], tabs[1], len(tabs[0]), tabs[2], tabs[3], len(tabs[2]),
+                                        float(survival_eps), ctypes.byref(k), theta, ctypes.byref(n)))
     return int(k.value), theta[:n.value + 1]
 
 

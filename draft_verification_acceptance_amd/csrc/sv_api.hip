@@ -388,6 +388,29 @@ spec_status spec_plan_budget(const float* conf, int32_t batch, int32_t width, co
   return plan_budget_host(conf, batch, width, sps_rows, sps, n_sps, survival_eps, budget, theta, n_entries);
 }
 
+spec_status spec_plan_budget_cost(const float* conf, int32_t batch, int32_t width, const double* req_rows,
+                                  const double* req_cost, int32_t n_req, const double* tok_rows,
+                                  const double* tok_cost, int32_t n_tok, float survival_eps, int32_t* budget,
+                                  double* theta, int32_t* n_entries) {
+  if (batch < 0 || width < 0 || n_req < 1 || n_tok < 1 || !req_rows || !req_cost || !tok_rows || !tok_cost ||
+      !budget)
+    return SPEC_EINVAL;
+  if (int64_t(batch) * width > INT32_MAX - 1) return SPEC_EINVAL;
+  if (int64_t(batch) * width > 0 && !conf) return SPEC_EINVAL;
+  if (!(survival_eps >= 0.f)) return SPEC_EINVAL;
+  // rows strictly increasing; per-batch costs >= 0 and per-row costs > 0, so every predicted step time is > 0
+  for (int32_t i = 0; i < n_req; ++i) {
+    if (!isfinite(req_rows[i]) || !isfinite(req_cost[i]) || !(req_cost[i] >= 0.0)) return SPEC_EINVAL;
+    if (i > 0 && !(req_rows[i] > req_rows[i - 1])) return SPEC_EINVAL;
+  }
+  for (int32_t i = 0; i < n_tok; ++i) {
+    if (!isfinite(tok_rows[i]) || !isfinite(tok_cost[i]) || !(tok_cost[i] > 0.0)) return SPEC_EINVAL;
+    if (i > 0 && !(tok_rows[i] > tok_rows[i - 1])) return SPEC_EINVAL;
+  }
+  return plan_budget_cost_host(conf, batch, width, req_rows, req_cost, n_req, tok_rows, tok_cost, n_tok,
+                               survival_eps, budget, theta, n_entries);
+}
+
 spec_status spec_cap_trim(const spec_cap_trim_args* a, hipStream_t stream) {
   if (!a) return SPEC_EINVAL;
   if (a->batch < 0 || a->total_rows < 0 || a->total_rows > INT32_MAX) return SPEC_EINVAL;

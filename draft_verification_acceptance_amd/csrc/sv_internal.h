@@ -266,6 +266,10 @@ hipError_t launch_tree_build(const spec_tree_build_args& a, hipStream_t stream, 
 size_t tree_build_smem(int topk, int n_steps, int n_nodes, bool* q_cached);
 spec_status plan_budget_host(const float* conf, int32_t R, int32_t W, const double* sps_rows, const double* sps,
                              int32_t n_sps, float eps, int32_t* budget, double* theta, int32_t* n_entries);
+spec_status plan_budget_cost_host(const float* conf, int32_t R, int32_t W, const double* req_rows,
+                                  const double* req_cost, int32_t n_req, const double* tok_rows,
+                                  const double* tok_cost, int32_t n_tok, float eps, int32_t* budget, double* theta,
+                                  int32_t* n_entries);
 hipError_t launch_fill_zero(void* ptr, size_t bytes, hipStream_t stream);
 hipError_t launch_read_fold(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream, hipEvent_t ev0,
                             hipEvent_t ev1);

@@ -461,8 +461,11 @@ hipError_t launch_cap_trim(const spec_cap_trim_args& a, hipStream_t stream, hipE
   return launch_kernel(k_cap_trim, dim3(blocks), dim3(256), 0, stream, ev0, ev1, a);
 }
 
-spec_status plan_budget_host(const float* conf, int32_t R, int32_t W, const double* sps_rows, const double* sps,
-                             int32_t n_sps, float eps, int32_t* budget, double* theta, int32_t* n_entries) {
+namespace {
+
+// The sorted survival list of the host budget: the products of the sanitized confidences in position order
+// (float32, as the device takes them), the ones below eps dropped, descending.
+std::vector<float> sorted_survival(const float* conf, int32_t R, int32_t W, float eps) {
 #pragma clang fp contract(off)
   std::vector<float> a;
   a.reserve(size_t(R) * W);
@@ -475,16 +478,36 @@ spec_status plan_budget_host(const float* conf, int32_t R, int32_t W, const doub
     }
   }
   sort_desc_nonneg(a);   // the survival products are >= 0 (sanitized confidences)
-  std::vector<double> slope(size_t(n_sps), 0.0);
-  for (int32_t i = 0; i + 1 < n_sps; ++i) slope[i] = (sps[i + 1] - sps[i]) / (sps_rows[i + 1] - sps_rows[i]);
-  int seg = 0;
+  return a;
+}
+
+// A table read by the planner's rule, with its slopes computed once.
+struct Table {
+  const double* xs;
+  const double* ys;
+  int n;
+  std::vector<double> slope;
+  int seg = 0;   // the segment of the previous read; reads only move forward
+  Table(const double* x, const double* y, int n_) : xs(x), ys(y), n(n_), slope(size_t(n_), 0.0) {
+#pragma clang fp contract(off)
+    for (int i = 0; i + 1 < n; ++i) slope[i] = (ys[i + 1] - ys[i]) / (xs[i + 1] - xs[i]);
+  }
+  double at(double M) { return sps_at(M, xs, ys, slope.data(), n, seg); }
+};
+
+// K* = argmax over 0 <= K <= n of value(N(K), R + K), N(K) = R + a_1 + .. + a_K (float64 prefix sums in the
+// sorted order), the smallest K among equal values.
+template <typename F>
+void budget_search(const std::vector<float>& a, int32_t R, F value, int32_t* budget, double* theta,
+                   int32_t* n_entries) {
+#pragma clang fp contract(off)
   double N = double(R);
-  double best = N * sps_at(double(R), sps_rows, sps, slope.data(), n_sps, seg);
+  double best = value(N, double(R));
   int32_t k_best = 0;
   if (theta) theta[0] = best;
   for (size_t k = 1; k <= a.size(); ++k) {
     N += double(a[k - 1]);
-    const double th = N * sps_at(double(R) + double(k), sps_rows, sps, slope.data(), n_sps, seg);
+    const double th = value(N, double(R) + double(k));
     if (theta) theta[k] = th;
     if (th > best) {
       best = th;
@@ -493,6 +516,32 @@ spec_status plan_budget_host(const float* conf, int32_t R, int32_t W, const doub
   }
   *budget = k_best;
   if (n_entries) *n_entries = int32_t(a.size());
+}
+
+}  // namespace
+
+spec_status plan_budget_host(const float* conf, int32_t R, int32_t W, const double* sps_rows, const double* sps,
+                             int32_t n_sps, float eps, int32_t* budget, double* theta, int32_t* n_entries) {
+  const std::vector<float> a = sorted_survival(conf, R, W, eps);
+  Table t(sps_rows, sps, n_sps);
+  budget_search(a, R, [&](double N, double M) {
+#pragma clang fp contract(off)
+    return N * t.at(M);
+  }, budget, theta, n_entries);
+  return SPEC_OK;
+}
+
+spec_status plan_budget_cost_host(const float* conf, int32_t R, int32_t W, const double* req_rows,
+                                  const double* req_cost, int32_t n_req, const double* tok_rows,
+                                  const double* tok_cost, int32_t n_tok, float eps, int32_t* budget, double* theta,
+                                  int32_t* n_entries) {
+  const std::vector<float> a = sorted_survival(conf, R, W, eps);
+  Table tr(req_rows, req_cost, n_req), tt(tok_rows, tok_cost, n_tok);
+  const double c = tr.at(double(R));
+  budget_search(a, R, [&](double N, double M) {
+#pragma clang fp contract(off)
+    return N / (c + tt.at(M));
+  }, budget, theta, n_entries);
   return SPEC_OK;
 }
 

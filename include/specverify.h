@@ -354,6 +354,22 @@ spec_status spec_plan_budget(const float* confidence_hist, int32_t batch, int32_
                              double* theta, int32_t* n_entries);
 
 /*
+ * The same host budget under an additive cost table ([EAGLE→DFlash2] §5.6.3: with an additive cost table the
+ * objective becomes N(K) / T(R, R + K)): K* = argmax over 0 <= K <= n of (batch + a_1 + .. + a_K) /
+ * (T_req(batch) + T_tok(batch + K)), the smallest K among equal values. The pages name the table without
+ * defining T; here a step's predicted time is the sum of a per-batch term read from (req_rows, req_cost) at
+ * the request count and a per-row term read from (tok_rows, tok_cost) at the target row count, each linear
+ * between its points and the nearest end value outside them (as for SPS). With T_req = 0 and T_tok = 1 / SPS
+ * at every row count it is spec_plan_budget. theta receives N(K) / T for K = 0 .. n (output per unit of the
+ * tables' time). Rows must increase strictly, req_cost >= 0 and tok_cost > 0 (every step time positive),
+ * all finite; else SPEC_EINVAL, as for bad sizes or null pointers. Pure host function.
+ */
+spec_status spec_plan_budget_cost(const float* confidence_hist, int32_t batch, int32_t width,
+                                  const double* req_rows, const double* req_cost, int32_t n_req,
+                                  const double* tok_rows, const double* tok_cost, int32_t n_tok,
+                                  float survival_eps, int32_t* budget, double* theta, int32_t* n_entries);
+
+/*
  * Accept cutoff of a verify run over the full proposal width ([EAGLE→DFlash2] §5.6.6: the accept kernel's
  * cap_trim / commit_lens / block_accept_lens). For request b with rows [row_offsets[b], row_offsets[b+1])
  * of a full-width verify (raw_accept_len, raw_bonus, out_tokens from spec_verify_chain) and the plan's

@@ -24,6 +24,8 @@ READINGS (where the pages leave a step open):
   * K* is the argmax of N(K) * SPS(R + K) over every prefix budget 0 <= K <= n ([EAGLE→DFlash2] §5.6.3
     evaluates all prefix budgets with one cumulative sum); on equal values the smallest K wins;
   * SPS(M) between table points is linear in M, and outside the table it is the nearest end value;
+  * the additive cost table's T(R, M) = T_req(R) + T_tok(M), two tables read by the same rule
+    (budget_from_survival_cost);
   * budget < 0 stands for "no budget" (the relay had nothing): every request verifies all W drafts;
   * threshold truncation compares each position's own confidence c_{r,j}, not the survival, and verifies the
     drafts before the first one below the threshold (all W if none is);
@@ -68,7 +70,8 @@ def survival(conf: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
 
 
 def sps_at(M: float, sps_rows: np.ndarray, sps: np.ndarray) -> float:
-    """Steps per second at M target rows: linear between table points, the end value outside."""
+    """Steps per second at M target rows: linear between table points, the end value outside (the same
+    rule reads the additive cost tables)."""
     xs = [float(x) for x in sps_rows]
     ys = [float(y) for y in sps]
     if M <= xs[0]:
@@ -105,6 +108,37 @@ def plan_budget(conf_hist: np.ndarray, sps_rows, sps, eps: float = 0.0) -> tuple
     """The host budget from lagged confidences (survival taken first)."""
     A, _ = survival(conf_hist)
     return budget_from_survival(A, sps_rows, sps, eps)
+
+
+def budget_from_survival_cost(A_hist: np.ndarray, req_rows, req_cost, tok_rows, tok_cost,
+                              eps: float = 0.0) -> tuple[int, np.ndarray]:
+    """Host budget under an additive cost table ([EAGLE→DFlash2] §5.6.3: with an additive cost table the
+    objective N(K) * SPS(R + K) becomes N(K) / T(R, R + K)). READING: the pages name the table but do not
+    define T; here T(R, M) = T_req(R) + T_tok(M), the predicted time of one step with R requests and M target
+    rows as the sum of a per-batch term and a per-row term, each read from its own table (linear between
+    points, the end value outside, as for SPS). With T_req = 0 and T_tok = 1 / SPS at every integer M this is
+    the SPS objective. Same sort, prefix sums and tie rule as budget_from_survival. Returns (K*, theta)."""
+    A_hist = np.asarray(A_hist, np.float32)
+    R = A_hist.shape[0]
+    a = sorted((float(v) for v in A_hist.ravel() if v >= np.float32(eps)), reverse=True)
+    c = sps_at(R, req_rows, req_cost)
+    theta = np.zeros(len(a) + 1)
+    N = float(R)
+    theta[0] = N / (c + sps_at(R, tok_rows, tok_cost))
+    best, k_best = theta[0], 0
+    for K in range(1, len(a) + 1):
+        N += a[K - 1]
+        theta[K] = N / (c + sps_at(R + K, tok_rows, tok_cost))
+        if theta[K] > best:
+            best, k_best = theta[K], K
+    return k_best, theta
+
+
+def plan_budget_cost(conf_hist: np.ndarray, req_rows, req_cost, tok_rows, tok_cost,
+                     eps: float = 0.0) -> tuple[int, np.ndarray]:
+    """The additive-cost host budget from lagged confidences (survival taken first)."""
+    A, _ = survival(conf_hist)
+    return budget_from_survival_cost(A, req_rows, req_cost, tok_rows, tok_cost, eps)
 
 
 def ragged_offsets(verify_lens) -> np.ndarray:

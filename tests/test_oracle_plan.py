@@ -107,6 +107,60 @@ def test_budget_is_the_best_of_every_length_vector(seed):
     assert abs(_theta(A, list(lay["selected"]), rows, sps) - best) <= 1e-9 * best
 
 
+# ----------------------------------------------------------------------------------------------------
+# the additive cost-table budget: K* = argmax N(K) / T(R, R + K), T(R, M) = T_req(R) + T_tok(M)
+# ----------------------------------------------------------------------------------------------------
+def test_cost_budget_reproduces_the_k_table():
+    """With no per-batch term and T_tok = 1 / SPS at every table point (the table has a point at every M
+    the search visits) the additive objective is the SPS objective: the pages' K table, K* = 4."""
+    g = _golden("dspark_budget_k4.json")
+    tok = 1.0 / np.asarray(g["sps"], np.float64)
+    K, theta = op.budget_from_survival_cost(g["history_survival"], [1.0], [0.0], g["sps_rows"], tok)
+    assert K == g["K_star"]
+    assert np.allclose(theta, g["predicted_tokens_per_s"], atol=1e-5)   # survival in float32, as printed
+    Ks, theta_s = op.budget_from_survival(g["history_survival"], g["sps_rows"], g["sps"])
+    assert Ks == K and np.allclose(theta, theta_s, rtol=1e-14)
+
+
+def _theta_cost(A, lens, R, req_rows, req_cost, tok_rows, tok_cost):
+    N = R + sum(float(A[r, j]) for r in range(A.shape[0]) for j in range(lens[r]))
+    return N / (op.sps_at(R, req_rows, req_cost) + op.sps_at(R + sum(lens), tok_rows, tok_cost))
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_cost_budget_is_the_best_of_every_length_vector(seed):
+    """max over every l in {0..W}^R of N(l) / T(R, M(l)) equals the prefix-budget argmax; the top-K allocation
+    at K* reaches it."""
+    rng = np.random.default_rng(100 + seed)
+    R, W = int(rng.integers(1, 4)), int(rng.integers(1, 4))
+    conf = rng.uniform(0.05, 1.0, (R, W)).astype(np.float32)
+    A, _ = op.survival(conf)
+    req_rows, req_cost = np.array([1.0, 4.0]), np.sort(rng.uniform(0.0, 5e-3, 2))
+    tok_rows = np.arange(R, R * (W + 1) + 1, dtype=np.float64)
+    tok_cost = np.cumsum(rng.uniform(0, 2e-3, len(tok_rows))) + 1e-3     # time grows with the rows
+    best = max(_theta_cost(A, lens, R, req_rows, req_cost, tok_rows, tok_cost)
+               for lens in itertools.product(range(W + 1), repeat=R))
+    K, theta = op.budget_from_survival_cost(A, req_rows, req_cost, tok_rows, tok_cost)
+    assert abs(theta[K] - best) <= 1e-12 * best
+    lay = op.plan_from_survival(A, K)
+    assert abs(_theta_cost(A, list(lay["selected"]), R, req_rows, req_cost, tok_rows, tok_cost) - best) <= 1e-12 * best
+
+
+def test_cost_budget_special_cases():
+    A = np.array([[0.9, 0.6, 0.2], [0.8, 0.5, 0.1]], np.float32)
+    rows = np.array([2.0, 8.0])
+    # a per-row cost that does not grow: every positive-survival draft pays
+    assert op.budget_from_survival_cost(A, [1.0], [1e-3], rows, [1e-3, 1e-3])[0] == 6
+    # a per-row cost that grows steeply: none pays
+    assert op.budget_from_survival_cost(A, [1.0], [0.0], rows, [1e-3, 1.0])[0] == 0
+    # a larger fixed per-batch cost makes extra rows relatively cheaper: K* never falls as it grows, and
+    # with a per-batch cost far above the per-row one every draft pays
+    ks = [op.budget_from_survival_cost(A, [1.0], [c], rows, [1e-3, 3e-3])[0] for c in (0.0, 1e-3, 1e-2, 1e-1, 10.0)]
+    assert ks == sorted(ks) and ks[0] < 6 and ks[-1] == 6
+    # eps drops entries from the sort
+    assert op.budget_from_survival_cost(A, [1.0], [1e-3], rows, [1e-3, 1e-3], eps=0.55)[0] == 3
+
+
 def _pairwise_selected(A, K, eps=0.0):
     """The device kernel's formulation on the pages: rank(e) = number of entries before e (survival greater,
     or equal and position smaller, or equal position and request smaller); e is selected iff rank < K."""
@@ -279,3 +333,30 @@ def test_pins_catch_trim_with_the_wrong_sign(monkeypatch):
 
 def test_plan_status_bits_match_the_library_abi_values():
     assert op.ST_BAD_ACCEPT == oracle.ST_BAD_ACCEPT
+
+
+def test_pins_catch_cost_multiplied_instead_of_divided(monkeypatch):
+    monkeypatch.setattr(op, "budget_from_survival_cost", _bad_cost)
+    with pytest.raises(AssertionError):
+        test_cost_budget_reproduces_the_k_table()
+
+
+def _bad_cost(A_hist, req_rows, req_cost, tok_rows, tok_cost, eps=0.0):
+    """N(K) * T(R, R + K): the cost read as a rate."""
+    A_hist = np.asarray(A_hist, np.float32)
+    R = A_hist.shape[0]
+    a = sorted((float(v) for v in A_hist.ravel() if v >= np.float32(eps)), reverse=True)
+    theta = [R * (op.sps_at(R, req_rows, req_cost) + op.sps_at(R, tok_rows, tok_cost))]
+    N = float(R)
+    for K in range(1, len(a) + 1):
+        N += a[K - 1]
+        theta.append(N * (op.sps_at(R, req_rows, req_cost) + op.sps_at(R + K, tok_rows, tok_cost)))
+    return int(np.argmax(theta)), np.array(theta)
+
+
+def test_pins_catch_cost_without_the_batch_term(monkeypatch):
+    orig = op.budget_from_survival_cost
+    monkeypatch.setattr(op, "budget_from_survival_cost",
+                        lambda A, rr, rc, tr, tc, eps=0.0: orig(A, rr, [0.0] * len(rc), tr, tc, eps))
+    with pytest.raises(AssertionError):
+        test_cost_budget_special_cases()

@@ -82,3 +82,43 @@ def test_host_budget_degenerate_inputs(case):
         Ko, tho = op.plan_budget(conf, rows, sps, eps)
         assert K == Ko
         assert np.array_equal(theta, tho)
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_host_cost_budget_matches_oracle(seed):
+    """spec_plan_budget_cost against oracle.plan.plan_budget_cost: K* and every N(K) / T agree exactly."""
+    rng = np.random.default_rng(50 + seed)
+    R, W = int(rng.integers(1, 64)), int(rng.integers(1, 16))
+    conf = rng.beta(4, 1.5, (R, W)).astype(np.float32)
+    if seed % 4 == 0:
+        conf = np.round(conf * 4) / 4                               # exact ties in the sort
+    n_req, n_tok = int(rng.integers(1, 4)), int(rng.integers(1, 6))
+    req_rows = np.sort(rng.choice(np.arange(1, 80), n_req, replace=False)).astype(np.float64)
+    req_cost = rng.uniform(0.0, 2e-3, n_req) * (seed % 3 != 0)       # some tables with no per-batch term
+    tok_rows = np.sort(rng.choice(np.arange(1, R * (W + 1) + 4), n_tok, replace=False)).astype(np.float64)
+    tok_cost = np.sort(rng.uniform(1e-4, 5e-3, n_tok))
+    eps = float(rng.choice([0.0, 0.05, 0.3]))
+    K, theta = dva.plan_budget_cost(conf, req_rows, req_cost, tok_rows, tok_cost, survival_eps=eps)
+    Ko, tho = op.plan_budget_cost(conf, req_rows, req_cost, tok_rows, tok_cost, eps)
+    assert K == Ko
+    assert np.array_equal(np.asarray(theta), tho)
+
+
+def test_host_cost_budget_k_table_and_checks():
+    with open(os.path.join(GOLDEN, "dspark_budget_k4.json")) as f:
+        g = json.load(f)
+    A = np.asarray(g["history_survival"], np.float32)
+    conf = np.empty_like(A)
+    for r in range(A.shape[0]):
+        prev = np.float32(1.0)
+        for j in range(A.shape[1]):
+            conf[r, j] = np.float32(A[r, j] / prev)
+            prev = np.float32(prev * conf[r, j])
+    K, theta = dva.plan_budget_cost(conf, [1.0], [0.0], g["sps_rows"], 1.0 / np.asarray(g["sps"], np.float64))
+    assert K == g["K_star"] and np.allclose(theta, g["predicted_tokens_per_s"], atol=1e-4)
+    for bad in (dict(tok_cost=[0.0, 1e-3]), dict(req_cost=[-1e-3]), dict(tok_rows=[5.0, 5.0]),
+                dict(tok_cost=[np.inf, 1e-3])):
+        kw = dict(req_rows=[1.0], req_cost=[0.0], tok_rows=[2.0, 8.0], tok_cost=[1e-3, 2e-3])
+        kw.update(bad)
+        with pytest.raises(dva.SpecError):
+            dva.plan_budget_cost(conf, kw["req_rows"], kw["req_cost"], kw["tok_rows"], kw["tok_cost"])
