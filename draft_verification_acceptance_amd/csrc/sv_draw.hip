@@ -188,11 +188,13 @@ __global__ __launch_bounds__(kThreads) void k_draw(VerifyParams p) {
   // commit, one more in front that only runs the scan, writes its outputs and takes part in the commit. The
   // commit's last arrival does the batch's commit while the memory system is busy with the draws (each of its
   // loads then waits long): in a workgroup without draw work that delays no draw.
+  // The scan-only workgroups come first in the grid (b = blockIdx): they start at once, and they leave early,
+  // so draw workgroups that did not fit beside them start soon after.
   const int lead = p.cm_on ? 1 : 0;
-  const int b = blockIdx.x / (p.S2 + lead);
-  const int cw = blockIdx.x % (p.S2 + lead);
-  const bool scan_only = lead && cw == 0;
-  const int c = cw - lead;
+  const bool scan_only = lead && int(blockIdx.x) < p.B;
+  const int dw = int(blockIdx.x) - lead * p.B;   // draw workgroup index
+  const int b = scan_only ? int(blockIdx.x) : dw / p.S2;
+  const int c = scan_only ? -1 : dw % p.S2;
   const bool writes = lead ? scan_only : c == 0;   // the workgroup that writes the scan's outputs
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);

@@ -42,7 +42,7 @@ __device__ bool commit_arrive(const VerifyParams& p, int b, int r, const int32_t
   return s_last_commit != 0;
 }
 
-constexpr int kFcWindow = 2048;     // verify rows whose slots a tile loads up front (with the request words)
+constexpr int kFcWindow = 1024;     // verify rows whose slots a tile loads up front (with the request words)
 
 // The request of the tile that holds flat row i, given the inclusive row prefix `incl` over its nb requests.
 __device__ __forceinline__ int fc_owner(const int32_t* incl, int nb, int i) {
