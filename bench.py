@@ -44,15 +44,18 @@ def _log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-STATS_SOURCES = ("sv_stats.hip", "sv_scan.h", "sv_device.h", "sv_internal.h")   # what k_stats is compiled from
+# What the verify kernels (k_stats and the second kernel with the fused commit) are compiled from, with the
+# build flags: counter summaries taken on other sources are not reused.
+VERIFY_SOURCES = ("csrc/sv_stats.hip", "csrc/sv_draw.hip", "csrc/sv_match.hip", "csrc/sv_scan.h", "csrc/sv_fused.h",
+                  "csrc/sv_device.h", "csrc/sv_internal.h", "csrc/sv_api.hip", "build.py")
 
 
 def kernel_source_hash() -> str:
-    """Hash of the k_stats sources: counter summaries taken on other sources are not reused."""
+    """Hash of the verify kernels' sources and build flags."""
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "draft_verification_acceptance_amd", "csrc")
-    for f in STATS_SOURCES:
-        with open(os.path.join(csrc, f), "rb") as fh:
+    pkg = os.path.join(ROOT, "draft_verification_acceptance_amd")
+    for f in VERIFY_SOURCES:
+        with open(os.path.join(pkg, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
 
@@ -147,10 +150,34 @@ class ChainStep:
             o = self.verify.outputs
             self.commit = dva.prepare_commit_indices(offs, o["accept_len"], o["accept_index"], slots, seq,
                                                      max_verify_len=w.max_verify_len)
+        self.mode = mode
         self.positions = w.total_rows
         self.draft_positions = w.total_rows - w.batch
         self.bytes = w.algorithmic_bytes(mode) + (mask.nbytes if mask is not None else 0)
         torch.cuda.synchronize()
+
+    def draw_bytes(self, accept_len) -> float:
+        """Logit bytes the second kernel reads by design for these results (row partials aside): rejection, the
+        target and draft rows of the rejected slot (one target row when every draft is accepted; sparse q, that
+        row's candidate pairs instead of a draft row); sample-then-match, one 2048-token piece of every row
+        drawn (rows go in groups of 16 up to the group holding the first mismatch); greedy, none."""
+        import numpy as np
+        w = self.w
+        mask = w.meta.get("vocab_mask")
+        row = w.vocab * w.target.itemsize
+        row_t = row + (mask.shape[1] * mask.itemsize if mask is not None else 0)   # with its mask words
+        n_draft = np.diff(w.offsets.astype(np.int64)) - 1
+        a = np.asarray(accept_len, np.int64)
+        rejected = a < n_draft
+        if self.mode == "rejection":
+            return float(w.batch * row_t + np.count_nonzero(rejected) * row)
+        if self.mode == "rejection_sparse":
+            pair = w.cand_ids.shape[1] * (w.cand_ids.itemsize + w.cand_q.itemsize)
+            return float(w.batch * row_t + np.count_nonzero(rejected) * pair)
+        if self.mode == "sample_match":
+            drawn = np.minimum(n_draft + 1, (a // 16 + 1) * 16)
+            return float(np.sum(drawn) * min(row, 2048 * w.target.itemsize))
+        return 0.0
 
 
 class TreeStep:
@@ -175,10 +202,17 @@ class TreeStep:
             offs = _dev((np.arange(w.batch + 1) * w.n_nodes).astype(np.int32))
             self.commit = dva.prepare_commit_indices(offs, o["accept_len"], o["accept_index"], slots, seq,
                                                      max_verify_len=w.n_nodes)
+        self.mode = mode
         self.positions = w.total_rows
         self.draft_positions = w.total_rows - w.batch
         self.bytes = w.algorithmic_bytes(mode)
         torch.cuda.synchronize()
+
+    def draw_bytes(self, accept_len) -> float:
+        """Logit bytes the second kernel reads by design (row partials aside): target_only, the one target row
+        each request draws from (the residual at the node where it stopped, or the bonus row); greedy, none."""
+        w = self.w
+        return float(w.batch * w.vocab * w.target.itemsize) if self.mode == "target_only" else 0.0
 
 
 def run_workload(name: str, mode: str | None, steps: int, warmup: int, fused: bool = True) -> dict:
@@ -240,6 +274,9 @@ def run_workload(name: str, mode: str | None, steps: int, warmup: int, fused: bo
     stat = st[(steps - 1) % len(st)].verify.outputs["status"].cpu().numpy().view(np.uint32)
     bad = int(np.count_nonzero(stat & ~np.uint32(dva.ST.NEAR_ALPHA | dva.ST.NEAR_CDF)))
     acc = st[(steps - 1) % len(st)].verify.outputs["accept_len"].float().mean().item()
+    # Every set's outputs hold its last eager run: the second kernel's by-design logit bytes per step.
+    draw_nbytes = np.mean([st[i % len(st)].draw_bytes(st[i % len(st)].verify.outputs["accept_len"].cpu().numpy())
+                           for i in range(steps)])
     step(st[0])
     torch.cuda.synchronize()
     st0 = st[0].verify.outputs["status"].cpu().numpy().view(np.uint32)
@@ -252,7 +289,8 @@ def run_workload(name: str, mode: str | None, steps: int, warmup: int, fused: bo
     return {
         "workload": name, "mode": mode, "batch": sets[0].batch, "vocab": sets[0].vocab,
         "verify_positions_per_step": float(positions), "draft_positions_per_step": float(draft_positions),
-        "algorithmic_bytes_per_step": float(nbytes), "rotation_sets": len(sets),
+        "algorithmic_bytes_per_step": float(nbytes), "draw_logit_bytes_per_step": float(draw_nbytes),
+        "rotation_sets": len(sets),
         "ms_per_step": ms_step,
         "ms_per_step_eager": wall_eager * 1e3 / steps,
         "positions_per_s": positions / (ms_step * 1e-3),
@@ -471,10 +509,11 @@ def cpu_baselines(name: str, budget_single: float = 8.0, budget_par: float = 8.0
     return single, par
 
 
-def load_traffic(name: str):
-    """HBM bytes per k_stats launch from the committed rocprofv3 counter summary (profiles/), if the counters
-    were taken on the current kernel sources; None otherwise."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{name}.txt")
+def load_traffic(name: str, mode: str):
+    """HBM bytes per launch of the verify kernels for one workload, from its committed rocprofv3 counter summary
+    (profiles/traffic_<workload>_<mode>.txt), if the counters were taken on the current kernel sources; None
+    otherwise."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{name}_{mode}.txt")
     if not os.path.exists(path):
         return None
     vals = {}
@@ -486,7 +525,11 @@ def load_traffic(name: str):
             vals[k.strip()] = v.strip()
     if vals.get("kernel_source_hash") != kernel_source_hash():
         return None
-    return float(vals["k_stats_hbm_bytes_per_launch"])
+    return {"k_stats_hbm_bytes_per_launch": float(vals["k_stats_hbm_bytes_per_launch"]),
+            "k_stats_ratio_to_algorithmic": float(vals["k_stats_ratio_to_algorithmic"]),
+            "second_kernel": vals["second_kernel"],
+            "second_kernel_hbm_bytes_per_launch": float(vals["second_kernel_hbm_bytes_per_launch"]),
+            "source": os.path.relpath(path, ROOT)}
 
 
 def read_floor(nbytes: int, reps: int = 20) -> dict:
@@ -562,11 +605,12 @@ def main():
             if name == args.workload and (mode or "") == (args.mode or ""):
                 continue
             r = run_workload(name, mode, max(50, args.steps // 2), args.warmup, fused)
-            extra[f"{name}/{r['mode']}"] = {k: r[k] for k in ("verify_positions_per_step", "ms_per_step",
-                                                              "ms_per_step_eager",
-                                                              "positions_per_s", "step_hbm_fraction",
-                                                              "stats_kernel_gbs", "kernel_ms", "mean_accept_len",
-                                                              "status_faults", "device_flags", "commit")}
+            e = {k: r[k] for k in ("verify_positions_per_step", "ms_per_step", "ms_per_step_eager",
+                                   "positions_per_s", "step_hbm_fraction", "stats_kernel_gbs", "kernel_ms",
+                                   "algorithmic_bytes_per_step", "draw_logit_bytes_per_step", "mean_accept_len",
+                                   "status_faults", "device_flags", "commit")}
+            e["traffic"] = load_traffic(name, r["mode"])
+            extra[f"{name}/{r['mode']}"] = e
             torch.cuda.empty_cache()
         extra["planner"] = run_planner(max(50, args.steps // 2))
         extra["tree_round"] = run_tree_round(max(50, args.steps // 2))
@@ -574,7 +618,7 @@ def main():
     achieved = main_res["stats_kernel_gbs"]
     if cpu is None and not args.no_cpu_baseline and args.workload == "tree":
         cpu = cpu_baseline("tree")
-    traffic = load_traffic(main_res["workload"])
+    traffic = load_traffic(main_res["workload"], main_res["mode"])
     floor = read_floor(int(main_res["algorithmic_bytes_per_step"]))
     line = {
         "metric": METRIC,
@@ -599,8 +643,11 @@ def main():
         "draft_positions_per_s": main_res["draft_positions_per_s"],
         "step_hbm_fraction": main_res["step_hbm_fraction"],
         "roofline": {"bound": "hbm", "kernel": "k_stats", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic["k_stats_hbm_bytes_per_launch"] if traffic else None,
+                     "traffic_detail": traffic,
                      "algorithmic_bytes_per_launch": main_res["algorithmic_bytes_per_step"],
+                     "draw_logit_bytes_per_launch": main_res["draw_logit_bytes_per_step"],
                      "avg_launch_ms": stats_ms,
                      "read_floor": dict(floor, frac=achieved / floor["gbs"])},
         "kernel_ms": main_res["kernel_ms"],
