@@ -75,9 +75,9 @@ constexpr int kMaxStagedParts = 1024;
 constexpr int kSeg = 512;            // tokens per draw segment (one wave: 8 tokens per lane)
 // Sample-then-match on 16-byte aligned rows: the stream stores the (m, z) of every piece of a row, a piece
 // being what one wave reads in one trip (SV_STATS_UNROLL runs per lane: 2048 tokens in bf16, 1024 in fp32).
-// Chunks are then whole multiples of kPieceChunk tokens (4 waves x 2048).
+// Chunks are then whole multiples of kPieceChunk tokens (a bf16 piece, two fp32 pieces).
 constexpr int kPieceMin = 1024;      // smallest piece (fp32): sizes the workspace
-constexpr int64_t kPieceChunk = 8192;
+constexpr int64_t kPieceChunk = 2048;
 constexpr int kMaxLen = 1024;        // max verify rows per request (chain) / nodes per tree
 constexpr int kMaxCand = 1024;       // max candidates per draft row (sparse q)
 constexpr int64_t kMaxVocab = int64_t(1) << 22;

@@ -284,11 +284,11 @@ __device__ __forceinline__ void chunk_lse(const DT* __restrict__ row, int64_t lo
 }
 
 // Sampling partial of row[lo, hi) that also stores the (m, z) of every piece (sample-then-match). The row is
-// 16-byte aligned and lo a multiple of kPieceChunk: wave w streams the contiguous quarter of the chunk that
-// starts at lo + w R (R a whole number of pieces), and each of its trips reads one piece (kUnroll runs per
-// lane, 64 lanes side by side, the next trip's loads issued before this one is reduced): the piece max m
-// over the wave first, then z = sum exp2(x * coef - m), stored at prow[piece]. The chunk's (m, z) merges the
-// pieces.
+// 16-byte aligned and lo a multiple of kPieceChunk (a whole number of pieces): wave w streams pieces w,
+// w + kW, ... of the chunk (the workgroup's waves side by side), each trip one piece (kUnroll runs per lane,
+// 64 lanes side by side, the next trip's loads issued before this one is reduced): the piece max m over the
+// wave first, then z = sum exp2(x * coef - m), stored at prow[piece]. The chunk's (m, z) merges each wave's
+// pieces in order, then the waves.
 template <typename DT, int MASK>
 __device__ __forceinline__ void chunk_lse_pieces(const DT* __restrict__ row, int64_t lo, int64_t hi, float coef,
                                                  Part& out, float* red_f, float* red_g, const uint32_t* mrow,
@@ -297,9 +297,9 @@ __device__ __forceinline__ void chunk_lse_pieces(const DT* __restrict__ row, int
   constexpr int PW = kUnroll * kWave * E;   // tokens per piece
   const int lane = lane_id();
   const int w = threadIdx.x / kWave;
-  const int64_t R = (hi - lo + int64_t(kW) * PW - 1) / (int64_t(kW) * PW) * PW;
-  const int64_t wlo = lo + w * R;
-  const int64_t whi = wlo + R < hi ? wlo + R : hi;
+  constexpr int64_t kStride = int64_t(kW) * PW;   // wave w takes pieces w, w + kW, ... of the chunk
+  const int64_t wlo = lo + int64_t(w) * PW;
+  const int64_t whi = hi;
   const uint4* __restrict__ vp = reinterpret_cast<const uint4*>(row);
   // Every lane loads (past the wave's range it reloads the range's last run and discards it): a load under a
   // branch would make the wait for this trip's data also wait for the next trip's, which the loop issues
@@ -344,10 +344,10 @@ __device__ __forceinline__ void chunk_lse_pieces(const DT* __restrict__ row, int
   if (wlo < whi) load_trip(wlo, q, mb);
   int64_t p0 = wlo;
   // Every piece but the wave's last is whole and has a successor, whose loads go out first.
-  for (; p0 + PW < whi; p0 += PW) {
+  for (; p0 + kStride < whi; p0 += kStride) {
     uint4 qn[kUnroll];
     uint32_t mbn[kUnroll];
-    load_trip(p0 + PW, qn, mbn);
+    load_trip(p0 + kStride, qn, mbn);
     __builtin_amdgcn_sched_barrier(0);   // keep the successor's loads ahead of this piece's reduction
     float pm, pz;
     piece(q, mb, true, pm, pz);
