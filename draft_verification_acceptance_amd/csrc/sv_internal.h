@@ -60,7 +60,7 @@ namespace sv {
 #define SV_DRAW_THREADS 256          // threads per workgroup of k_draw and k_scan
 #endif
 #ifndef SV_DRAW_TRIP
-#define SV_DRAW_TRIP 4               // draw segments each wave has in flight per trip
+#define SV_DRAW_TRIP 2               // draw segments each wave has in flight per trip
 #endif
 #ifndef SV_DRAW_WGS
 #define SV_DRAW_WGS 1024             // draw workgroups aimed for per call
