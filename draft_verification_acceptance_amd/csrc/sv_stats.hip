@@ -527,6 +527,179 @@ __global__ __launch_bounds__(kThreads) void k_scan(VerifyParams p) {
   }
 }
 
+// ---------------------------------------------------------------------------------------------------
+// Greedy chains of a small batch in one workgroup. Every input that the batch's scans and its commit read
+// (offsets, row partials, draft tokens; with a fused commit also seq_lens and verify_slots) goes into LDS in
+// one load round; a wave per request then runs the scan, and the commit lists follow from LDS, with no
+// hand-off between workgroups. The outputs are those of k_scan and its fused commit.
+// ---------------------------------------------------------------------------------------------------
+constexpr int kOneThreads = 1024;
+constexpr int kOneWaves = kOneThreads / kWave;
+constexpr int kOneMaxB = kOneThreads;   // requests (a thread each in the commit's scan)
+constexpr int kOneMaxParts = 2048;      // B * L * S row partials
+constexpr int kOneMaxRows = 2048;       // verify rows of the batch
+constexpr int kOneMaxLen = kWave;       // rows per request (a lane each)
+constexpr int kOnePer = 2;              // loads per thread and array in the load round
+
+struct GreedyPart {   // the greedy fields of a row partial
+  float a;
+  int32_t idx;
+  uint32_t flags;
+};
+
+template <typename DT>
+__global__ __launch_bounds__(kOneThreads) void k_scan_one(VerifyParams p) {
+  __shared__ GreedyPart s_pt[kOneMaxParts];
+  __shared__ int32_t s_tok[kOneMaxRows];
+  __shared__ int64_t s_vs[kOneMaxRows];
+  __shared__ int32_t s_off[kOneMaxB + 1];
+  __shared__ int32_t s_seq[kOneMaxB];
+  __shared__ int32_t s_r[kOneMaxB];       // accepted drafts of request b, -1: its offsets failed
+  __shared__ uint64_t s_wsum[kOneWaves];
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wv = tid / kWave;
+  const int B = p.B;
+  const int S = p.S;
+  const int64_t T = p.total_rows;
+  const int n_parts = B * p.L * S;   // the part area of request b starts at b * L * S (P = 1)
+
+  // ---- the load round: every load of this thread issued before any is used ----
+  {
+    Part pv[kOnePer];
+    int32_t tv[kOnePer], ov[kOnePer];
+    int64_t vv[kOnePer];
+#pragma unroll
+    for (int k = 0; k < kOnePer; ++k) {
+      const int i = tid + k * kOneThreads;
+      pv[k] = i < n_parts ? load_part(p.part + i, false) : Part{};
+      tv[k] = i < T - B ? p.draft_tokens[i] : 0;
+      vv[k] = p.cm_on && i < T ? p.verify_slots[i] : 0;
+      ov[k] = i <= B ? p.offsets[i] : 0;
+    }
+    const int32_t sq = p.cm_on && tid < B ? p.seq_lens[tid] : 0;
+#pragma unroll
+    for (int k = 0; k < kOnePer; ++k) {
+      const int i = tid + k * kOneThreads;
+      if (i < n_parts) s_pt[i] = GreedyPart{pv[k].a, pv[k].idx, pv[k].flags};
+      if (i < T - B) s_tok[i] = tv[k];
+      if (p.cm_on && i < T) s_vs[i] = vv[k];
+      if (i <= B) s_off[i] = ov[k];
+    }
+    if (tid < B) s_seq[tid] = sq;
+  }
+  __syncthreads();
+
+  // ---- the scans: a wave per request, a lane per row (the rules of scan_chain_greedy) ----
+  for (int b = wv; b < B; b += kOneWaves) {
+    const int64_t o0 = s_off[b], o1 = s_off[b + 1];
+    if (!chain_offsets_ok(p, b, o0, o1)) {
+      if (lane == 0) {
+        write_bad_offsets(p, b);
+        s_r[b] = -1;
+      }
+      continue;
+    }
+    const int len = int(o1 - o0);
+    const int m = len - 1;
+    const int64_t dr0 = o0 - b;
+    const int j = lane;
+    GreedyPart row{-INFINITY, INT32_MAX, 0u};
+    uint32_t f = 0;
+    int32_t d = -1;
+    bool fails = false;
+    if (j < len) {
+      const GreedyPart* rp = s_pt + (size_t(b) * p.L + j) * S;
+      row = rp[0];
+      for (int c = 1; c < S; ++c) {
+        const GreedyPart q = rp[c];
+        if (better(q.a, q.idx, row.a, row.idx)) {
+          row.a = q.a;
+          row.idx = q.idx;
+        }
+        row.flags |= q.flags;
+      }
+      if (row.flags & kPartNaN) f |= SPEC_ST_NONFINITE;
+      if (p.mask && row.a == -INFINITY) f |= SPEC_ST_NONFINITE;   // the mask left no finite logit
+      if (j < m) {   // test of d_{j+1} against row j
+        d = s_tok[dr0 + j];
+        const bool ok = d >= 0 && int64_t(d) < p.V;
+        if (!ok) f |= SPEC_ST_BAD_TOKEN;
+        fails = !ok || d != row.idx;
+      }
+    }
+    const uint64_t fm = __ballot(fails);
+    const int r = fm ? min(__ffsll((unsigned long long)fm) - 1, m) : m;
+    const uint32_t fl = (__ballot(f & SPEC_ST_NONFINITE) ? uint32_t(SPEC_ST_NONFINITE) : 0u) |
+                        (__ballot(f & SPEC_ST_BAD_TOKEN) ? uint32_t(SPEC_ST_BAD_TOKEN) : 0u);
+    const int32_t bonus = __shfl(row.idx, r);
+    if (j < len) {
+      p.out_tokens[o0 + j] = j < r ? d : (j == r ? bonus : -1);
+      p.accept_index[o0 + j] = j <= r ? int32_t(o0 + j) : -1;
+    }
+    if (p.accept_prob && j < m) p.accept_prob[dr0 + j] = -1.f;
+    if (lane == 0) {
+      p.accept_len[b] = r;
+      p.bonus[b] = bonus;
+      p.status[b] = fl;
+      if (p.residual_mass) p.residual_mass[b] = -1.f;
+      s_r[b] = r;
+    }
+  }
+  if (!p.cm_on) return;
+  __syncthreads();
+
+  // ---- the commit lists: per request counts and their exclusive scan, then the rows ----
+  int32_t* s_co = reinterpret_cast<int32_t*>(s_pt);   // the partials are no longer needed
+  int32_t* s_eo = s_co + kOneMaxB;
+  {
+    const int b = tid;
+    const bool has = b < B;
+    const int r = has ? s_r[b] : -1;
+    const bool ok = r >= 0;
+    const uint64_t c = ok ? uint64_t(r) + 1 : 0;
+    const uint64_t e = ok ? uint64_t(s_off[b + 1] - s_off[b]) - c : 0;
+    const uint64_t mine = (c << 32) | e;   // both sums stay below 2^31: no carry between the halves
+    const uint64_t inc = wave_inclusive_sum_dpp(mine);
+    if (lane == kWave - 1) s_wsum[wv] = inc;
+    __syncthreads();
+    uint64_t base = 0;
+    for (int w = 0; w < wv; ++w) base += s_wsum[w];
+    const uint64_t ex = base + inc - mine;
+    if (has) {
+      const int32_t co = int32_t(ex >> 32), eo = int32_t(uint32_t(ex));
+      p.commit_offsets[b] = co;
+      p.new_seq_lens[b] = s_seq[b] + int32_t(c);
+      if (p.evict_offsets) p.evict_offsets[b] = eo;
+      p.cstatus[b] = ok ? 0u : SPEC_ST_BAD_OFFSETS;
+      s_co[b] = co;
+      s_eo[b] = eo;
+      if (b == B - 1) {
+        const uint64_t tot = ex + mine;
+        p.commit_offsets[B] = int32_t(tot >> 32);
+        if (p.evict_offsets) p.evict_offsets[B] = int32_t(uint32_t(tot));
+      }
+    }
+  }
+  __syncthreads();
+  for (int b = wv; b < B; b += kOneWaves) {
+    const int r = s_r[b];
+    if (r < 0) continue;
+    const int64_t o0 = s_off[b];
+    const int len = int(s_off[b + 1] - o0);
+    const int k = lane;
+    if (k < len) {
+      const int64_t v = s_vs[o0 + k];
+      if (k <= r) {
+        p.src_slots[int64_t(s_co[b]) + k] = v;
+        p.dst_pos[int64_t(s_co[b]) + k] = s_seq[b] + k;
+      } else if (p.evict_slots) {
+        p.evict_slots[int64_t(s_eo[b]) + (k - r - 1)] = v;
+      }
+    }
+  }
+}
+
 template <typename DT>
 hipError_t launch_stats_t(int mode, const VerifyParams& p, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
   const int64_t blocks = int64_t(p.B) * p.L * p.P * p.S;
@@ -553,6 +726,12 @@ hipError_t launch_stats_t(int mode, const VerifyParams& p, hipStream_t stream, h
   return launch_kernel(k_stats<DT, false, false, false, false>, grid, block, 0, stream, ev0, ev1, p);
 }
 
+// Whether a greedy batch goes to k_scan_one: a chain batch whose partials, tokens and rows fit its LDS arrays.
+bool scan_one_fits(const VerifyParams& p) {
+  return !p.tree && p.P == 1 && p.B <= kOneMaxB && p.L <= kOneMaxLen &&
+         int64_t(p.B) * p.L * p.S <= kOneMaxParts && p.total_rows <= kOneMaxRows;
+}
+
 }  // namespace
 
 hipError_t launch_stats(int dtype, int mode, const VerifyParams& p, hipStream_t stream, hipEvent_t ev0,
@@ -563,6 +742,11 @@ hipError_t launch_stats(int dtype, int mode, const VerifyParams& p, hipStream_t 
 
 hipError_t launch_scan(int dtype, const VerifyParams& p, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
   if (p.B <= 0) return hipSuccess;
+  if (scan_one_fits(p)) {   // a small greedy chain batch: one workgroup
+    const dim3 grid{1u}, block{unsigned(kOneThreads)};
+    if (dtype == SPEC_DTYPE_BF16) return launch_kernel(k_scan_one<uint16_t>, grid, block, 0, stream, ev0, ev1, p);
+    return launch_kernel(k_scan_one<float>, grid, block, 0, stream, ev0, ev1, p);
+  }
   const size_t smem = scan_smem_bytes(p.tree != 0, false, p.L, p.P, p.S);
   const dim3 grid{unsigned(p.B)}, block{unsigned(kThreads)};
   if (dtype == SPEC_DTYPE_BF16) return launch_kernel(k_scan<uint16_t>, grid, block, smem, stream, ev0, ev1, p);

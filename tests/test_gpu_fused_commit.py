@@ -101,6 +101,25 @@ def test_fused_commit_many_tiles_and_bad_offsets(mode):
     _check(g, offs, w.max_verify_len, slots, seq, accept_index=np.arange(w.total_rows, dtype=np.int32))
 
 
+@pytest.mark.parametrize("mode", ["greedy", "rejection"])
+def test_fused_commit_small_batch_bad_offsets(mode):
+    """40 requests (greedy: the one-workgroup path, which scans and commits the batch from LDS), with the
+    same kinds of failing offsets."""
+    w = W.ragged(seed=5033, batch=40, vocab=64, parallel=False)
+    slots = np.random.default_rng(5).integers(0, 1 << 40, w.total_rows).astype(np.int64)
+    seq = np.random.default_rng(6).integers(0, 4096, w.batch).astype(np.int32)
+    g = np_out(dva.verify_chain(dev_logits(w.target), dev(w.offsets, torch.int32), dev(w.draft_tokens, torch.int32),
+                                mode, verify_slots=dev(slots), seq_lens=dev(seq), **_chain_kw(w, mode)))
+    _check(g, w.offsets, w.max_verify_len, slots, seq)
+    offs = w.offsets.copy()
+    offs[7] = offs[8] + 1            # request 7 fails; 6 and 8 pass with overlapping rows
+    offs[20] = offs[19]              # request 19 empty
+    g = np_out(dva.verify_chain(dev_logits(w.target), dev(offs, torch.int32), dev(w.draft_tokens, torch.int32),
+                                mode, verify_slots=dev(slots), seq_lens=dev(seq), **_chain_kw(w, mode)))
+    assert g["commit_status"][7] & oracle.ST_BAD_OFFSETS and g["commit_status"][19] & oracle.ST_BAD_OFFSETS
+    _check(g, offs, w.max_verify_len, slots, seq, accept_index=np.arange(w.total_rows, dtype=np.int32))
+
+
 def _poison(outs):
     for t in outs.values():
         t.fill_(-12345.0 if t.dtype == torch.float32 else -5)

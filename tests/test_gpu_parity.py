@@ -373,11 +373,13 @@ def test_status_bits_nan_bad_token_bad_uniform_bad_offsets():
     assert g["status"][2] & oracle.ST_BAD_OFFSETS
 
 
-@pytest.mark.parametrize("seed", [41, 42, 43])
-def test_random_faults_match_the_oracle(seed):
+@pytest.mark.parametrize("seed,max_len", [(41, 6), (42, 6), (43, 6), (41, 100)])
+def test_random_faults_match_the_oracle(seed, max_len):
     """Seeded fault injection over ragged requests: NaN, +inf and -inf logits (a few, or a whole row), draft
     tokens outside [0, V), uniforms that are NaN, negative or >= 1; greedy, rejection and sample-then-match.
-    Every request's status and outputs equal the oracle's (a NONFINITE request: its flag)."""
+    Every request's status and outputs equal the oracle's (a NONFINITE request: its flag). max_verify_len 6
+    runs small greedy batches in one workgroup, 100 (more rows per request than a wave has lanes) in one
+    workgroup per request."""
     rng = np.random.default_rng(seed)
     V, B = 257, 24
     lens = rng.integers(1, 7, B)
@@ -417,9 +419,9 @@ def test_random_faults_match_the_oracle(seed):
         elif kind == 13 and n > 1:
             dl[d0 + int(rng.integers(0, n - 1)), :] = -np.inf
     w = W.ChainWorkload("faults", V, B, offs, tl, dl, toks, ua, uf, 0.9, ("greedy", "rejection", "sample_match"),
-                        6)
+                        max_len)
     for mode in ("greedy", "rejection", "sample_match"):
-        _say("random faults", seed, mode)
+        _say("random faults", seed, max_len, mode)
         g = run_chain(w, mode)
         o = oracle_chain(w, mode)
         compare_chain(w, mode, o, g)
