@@ -42,7 +42,8 @@ __device__ bool commit_arrive(const VerifyParams& p, int b, int r, const int32_t
   return s_last_commit != 0;
 }
 
-constexpr int kFcWindow = 1024;     // verify rows whose slots a tile loads up front (with the request words)
+constexpr int kFcWindow = 1024;     // verify rows whose slots a tile loads up front (with the request words):
+                                    // the default, sized for the LDS of kernels whose every workgroup holds it
 
 // The request of the tile that holds flat row i, given the inclusive row prefix `incl` over its nb requests.
 __device__ __forceinline__ int fc_owner(const int32_t* incl, int nb, int i) {
@@ -57,27 +58,27 @@ __device__ __forceinline__ int fc_owner(const int32_t* incl, int nb, int i) {
 
 // The commit lists of the whole batch, written by one workgroup of NT threads (NT a multiple of kFcTile).
 // Requests go in tiles (a thread each). A tile costs one round of loads: its requests' words (offsets, seq_len,
-// published accept length) and the slots of the kFcWindow verify rows that follow the previous tile's rows (for
+// published accept length) and the slots of the WIN verify rows that follow the previous tile's rows (for
 // trees also the published path entries, laid out like the rows), all issued before any is used and parked
 // in LDS. When the tile's requests are packed (each request's rows follow the previous one's, as in every valid
 // batch) those rows are exactly the tile's; otherwise (inconsistent offsets) each row is gathered on its own.
-template <int NT, bool TREE>
+template <int NT, bool TREE, int WIN = kFcWindow>
 __device__ void fused_commit(const VerifyParams& p) {
   constexpr int TW = kFcTile / kWave;   // waves that hold one request each in the tile's scan
-  constexpr int K = kFcWindow / NT;     // window rows loaded per thread
+  constexpr int K = WIN / NT;           // window rows loaded per thread
   __shared__ int32_t f_off0[kFcTile], f_r[kFcTile], f_seq[kFcTile], f_co[kFcTile], f_eo[kFcTile];
   __shared__ int32_t f_rows[kFcTile];    // inclusive prefix of the tile's rows
   __shared__ uint64_t f_wsum[TW];
   __shared__ int f_unpacked;
-  __shared__ int64_t f_vs[kFcWindow];    // verify_slots of the window rows
-  __shared__ int32_t f_node[TREE ? kFcWindow : 1];        // trees: published path entries of the window rows
-  __shared__ uint32_t f_bits[TREE ? kFcWindow / 32 : 1];  // trees: the tile's accepted nodes, by row
+  __shared__ int64_t f_vs[WIN];    // verify_slots of the window rows
+  __shared__ int32_t f_node[TREE ? WIN : 1];        // trees: published path entries of the window rows
+  __shared__ uint32_t f_bits[TREE ? WIN / 32 : 1];  // trees: the tile's accepted nodes, by row
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wv = tid / kWave;
   const int B = p.B;
   const int64_t T = TREE ? int64_t(B) * p.L : p.total_rows;
-  const int tile_n = min(kFcTile, max(1, kFcWindow / p.L));   // a packed tile's rows fit the window
+  const int tile_n = min(kFcTile, max(1, WIN / p.L));   // a packed tile's rows fit the window
   int64_t carry_c = 0, carry_e = 0, row0 = 0;
   for (int t0 = 0; t0 < B; t0 += tile_n) {
     const int nb = min(tile_n, B - t0);
@@ -136,7 +137,7 @@ __device__ void fused_commit(const VerifyParams& p) {
     if (lane == kWave - 1 && wv < TW) f_wsum[wv] = inc;
     if (tid == 0) f_unpacked = 0;
     if (TREE)
-      for (int w = tid; w < kFcWindow / 32; w += NT) f_bits[w] = 0u;
+      for (int w = tid; w < WIN / 32; w += NT) f_bits[w] = 0u;
     __syncthreads();
     uint64_t base = 0;
     for (int w = 0; w < min(wv, TW); ++w) base += f_wsum[w];

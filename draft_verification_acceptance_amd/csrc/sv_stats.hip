@@ -522,7 +522,9 @@ __global__ __launch_bounds__(kThreads) void k_scan(VerifyParams p) {
     r = scan_chain_greedy(p, b, off0, int(len), rows, stage);
   }
   if (p.cm_on && commit_arrive<kThreads>(p, b, r, path)) {
-    if (p.tree) fused_commit<kThreads, true>(p);
+    // k_scan has B workgroups, so the tree commit can hold a wider window (one tile for 32 requests of 64
+    // nodes) without costing the kernel occupancy that matters.
+    if (p.tree) fused_commit<kThreads, true, 2 * kFcWindow>(p);
     else fused_commit<kThreads, false>(p);
   }
 }
