@@ -80,18 +80,8 @@ def _dev(a):
 def _grammar_mask(w):
     """A grammar-like vocab mask for a chain workload: 5 % of the tokens allowed per target row, plus the
     row's argmax and the draft token it judges (a grammar admits what the model predicts)."""
-    import numpy as np
-
     from draft_verification_acceptance_amd import workloads as W
-    keep = []
-    for b in range(w.batch):
-        lo, hi = int(w.offsets[b]), int(w.offsets[b + 1])
-        for j in range(hi - lo):
-            ks = [int(np.argmax(W.bf16_to_f32(w.target[lo + j])))]
-            if j < hi - lo - 1:
-                ks.append(int(w.draft_tokens[lo - b + j]))
-            keep.append(ks)
-    return W.vocab_masks(int(w.meta.get("seed", 0)) + 17, w.total_rows, w.vocab, 0.05, keep)
+    return W.vocab_masks(int(w.meta.get("seed", 0)) + 17, w.total_rows, w.vocab, 0.05, W.chain_keep(w))
 
 
 def build_sets(name: str):

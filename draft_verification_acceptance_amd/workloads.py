@@ -488,6 +488,21 @@ def block_sample(seed: int = 7000, batch: int = 32, block: int = 16, vocab: int 
                          ("sample_match",), block, meta={"seed": seed})
 
 
+def chain_keep(w) -> list:
+    """Per target row of a chain workload, the tokens a grammar-like mask keeps allowed: the row's argmax and
+    the draft token the row judges (a grammar admits what the model predicts, so acceptances still happen)."""
+    keep = []
+    for b in range(w.batch):
+        lo, hi = int(w.offsets[b]), int(w.offsets[b + 1])
+        for j in range(hi - lo):
+            row = w.target[lo + j]
+            ks = [int(np.argmax(bf16_to_f32(row) if row.dtype == np.uint16 else row))]
+            if j < hi - lo - 1:
+                ks.append(int(w.draft_tokens[lo - b + j]))
+            keep.append(ks)
+    return keep
+
+
 def vocab_masks(seed: int, rows: int, vocab: int, allowed: float, keep=None) -> np.ndarray:
     """Grammar-like vocab masks: uint32 [rows, ceil(vocab/32)], token v of row i allowed iff bit v % 32 of word
     v // 32 is set. Each token is allowed with probability `allowed`; keep[i] (an int or a list of ints, -1

@@ -184,15 +184,7 @@ def test_sample_match_chi_square(masked):
 # ----------------------------------------------------------------------------------------------------
 def _chain_keep(w):
     """Per target row: its judged draft token and its argmax stay allowed, so acceptances still happen."""
-    keep = []
-    for b in range(w.batch):
-        lo, hi = int(w.offsets[b]), int(w.offsets[b + 1])
-        for j in range(hi - lo):
-            ks = [int(np.argmax(_f32(w.target[lo + j])))]
-            if j < hi - lo - 1:
-                ks.append(int(w.draft_tokens[lo - b + j]))
-            keep.append(ks)
-    return keep
+    return W.chain_keep(w)
 
 
 def _check_allowed_outputs(g, mask, rows_of):
@@ -249,7 +241,7 @@ def test_mask_full_chain_rejection_and_block_sample():
     _say("mask full chain_rejection")
     g = run_chain(w, "rejection", mask=mask)
     o = oracle_chain(w, "rejection", mask=mask)
-    compare_chain(w, "rejection", o, g)
+    compare_chain(w, "rejection", o, g, expect=FLAGGED[("chain_rejection+mask13", "rejection")])
     assert not np.any(g["status"] & ~np.uint32(oracle.ST_NEAR_ALPHA | oracle.ST_NEAR_CDF))
     rows = [(b, np.arange(int(w.offsets[b]), int(w.offsets[b + 1]))) for b in range(w.batch)]
     _check_allowed_outputs(g, mask, rows)
@@ -257,7 +249,8 @@ def test_mask_full_chain_rejection_and_block_sample():
     smask = W.vocab_masks(14, s.total_rows, s.vocab, 0.05, _chain_keep(s))
     _say("mask full block_sample")
     gs = run_chain(s, "sample_match", mask=smask)
-    compare_chain(s, "sample_match", oracle_chain(s, "sample_match", mask=smask), gs)
+    compare_chain(s, "sample_match", oracle_chain(s, "sample_match", mask=smask), gs,
+                  expect=FLAGGED[("block_sample+mask14", "sample_match")])
     rows = [(b, np.arange(int(s.offsets[b]), int(s.offsets[b + 1]))) for b in range(s.batch)]
     _check_allowed_outputs(gs, smask, rows)
 

@@ -27,12 +27,18 @@ EXPECTED = {
     ("ragged", "rejection"): 20,
     ("chain_sparse", "rejection_sparse"): 11,
     ("block_sample", "sample_match"): 7,
+    # the full-size workloads under a grammar-like mask (5 % of each row allowed, plus its argmax and the token
+    # it judges), mask seeds 13 and 14 (tests/test_gpu_f4.py)
+    ("chain_rejection+mask13", "rejection"): 0,
+    ("block_sample+mask14", "sample_match"): 1,
 }
 
 
 def _run(key):
     name, mode = key
+    name, _, mseed = name.partition("+mask")
     w = W.FULL[name]()
+    mask = W.vocab_masks(int(mseed), w.total_rows, w.vocab, 0.05, W.chain_keep(w)) if mseed else None
     if name == "tree":
         o = oracle.verify_tree(w.target, w.parents, w.tokens, w.n_nodes, mode, u_accept=w.u_accept,
                                u_final=w.u_final, temperature=w.temperature)
@@ -44,6 +50,8 @@ def _run(key):
             kw.update(draft=w.draft)
         if mode == "rejection_sparse":
             kw.update(cand_ids=w.cand_ids, cand_q=w.cand_q)
+        if mask is not None:
+            kw.update(vocab_mask=mask)
         o = oracle.verify_chain(w.target, w.offsets, w.draft_tokens, mode, **kw)
     st = o["status"]
     return key, dict(batch=w.batch, flagged=int(np.count_nonzero(st & (oracle.ST_NEAR_ALPHA | oracle.ST_NEAR_CDF))),
