@@ -53,6 +53,17 @@ __device__ __forceinline__ uint32_t run_mask(const uint32_t* mrow, int64_t v, in
   return MASK == 1 ? mask_bits8_aligned(mrow, v) : MASK == 2 ? mask_bits8(mrow, v, nw) : ~0u;
 }
 
+// x[e] = bit e of mb set ? x[e] : -inf. Two instructions per element: the bit sign-extended into a full word
+// (v_bfe_i32), then -inf's bits inserted where that word is clear (v_bfi_b32).
+template <int N>
+__device__ __forceinline__ void apply_run_mask(float* x, uint32_t mb) {
+#pragma unroll
+  for (int e = 0; e < N; ++e) {
+    const uint32_t keep = uint32_t(int32_t(mb << (31 - e)) >> 31);
+    x[e] = __uint_as_float((keep & __float_as_uint(x[e])) | (~keep & 0xff800000u));
+  }
+}
+
 template <typename DT, int MASK>
 __device__ __forceinline__ void chunk_argmax(const DT* __restrict__ row, int64_t lo, int64_t hi, Part& out,
                                              float* red_f, int* red_i, uint32_t* red_u, const uint32_t* mrow,
@@ -79,8 +90,7 @@ __device__ __forceinline__ void chunk_argmax(const DT* __restrict__ row, int64_t
     float x[E];
     Elem<DT>::unpack(qv, x);
     if (MASK) {
-#pragma unroll
-      for (int e = 0; e < E; ++e) x[e] = (mb >> e) & 1u ? x[e] : -INFINITY;
+      apply_run_mask<E>(x, mb);
     }
     float vm = x[0];
 #pragma unroll
@@ -210,8 +220,7 @@ __device__ __forceinline__ void chunk_lse(const DT* __restrict__ row, int64_t lo
   };
   auto apply_mask = [&](float* xv, uint32_t mb) {
     if (MASK) {
-#pragma unroll
-      for (int e = 0; e < E; ++e) xv[e] = (mb >> e) & 1u ? xv[e] : -INFINITY;
+      apply_run_mask<E>(xv, mb);
     }
   };
   int64_t k = tid;
@@ -324,8 +333,7 @@ __device__ __forceinline__ void chunk_lse_pieces(const DT* __restrict__ row, int
     for (int u = 0; u < kUnroll; ++u) {
       Elem<DT>::unpack(q[u], x + u * E);
       if (MASK || !whole) {
-#pragma unroll
-        for (int e = 0; e < E; ++e) x[u * E + e] = (mb[u] >> e) & 1u ? x[u * E + e] : -INFINITY;
+        apply_run_mask<E>(x + u * E, mb[u]);
       }
     }
     float vm = x[0];
