@@ -61,6 +61,7 @@ void carve(VerifyParams& p, const Layout& lo, void* ws) {
   p.S = lo.S;
   p.S2 = lo.S2;
   p.spc = lo.spc;
+  p.bseg = lo.bseg;
   p.n_seg = lo.n_seg;
 }
 

@@ -13,11 +13,11 @@
 // sum_{t<=v} w_t > u * sum w ([EAGLE→DFlash2] §6.2, inverse-CDF rule); if rounding leaves u past the last
 // step the last positive-weight token is taken. Weights summing to 0 fall back to p (flagged).
 //
-// Layout of the work: k_draw workgroup (b, c) covers a contiguous range of 512-token segments of request
-// b's row; each wave reduces whole segments (8 consecutive tokens per lane, 16-byte loads) and stores
-// (sum w, sum p) per segment. The request's last workgroup takes a float64 prefix over the
-// segments, then rescans the single segment holding u * Z in float64, token by token. With a fused KV
-// commit each request has one more workgroup that only scans and counts the request for the commit.
+// Layout of the work: S2 workgroups per request take batches of 512-token segments of request b's row from
+// the request's counter until none is left; each wave reduces whole segments (8 consecutive tokens per lane,
+// 16-byte loads) and stores (sum w, sum p) per segment. The request's last workgroup takes a float64 prefix
+// over the segments, then rescans the single segment holding u * Z in float64, token by token. With a fused
+// KV commit each request has one more workgroup that only scans and counts the request for the commit.
 #include "sv_fused.h"
 
 namespace sv {
@@ -181,20 +181,23 @@ __global__ __launch_bounds__(kThreads) void k_draw(VerifyParams p) {
   __shared__ double red_d[kThreads / kWave];
   __shared__ int red_i[kThreads / kWave];
   __shared__ int s_last;
+  __shared__ int s_batch;
   __shared__ int s_sel;
   __shared__ double s_sel_excl;
 
-  // Workgroups per request: S2 that draw (chunk c covers segments [c * spc, (c + 1) * spc)) and, with a fused
-  // commit, one more in front that only runs the scan, writes its outputs and takes part in the commit. The
-  // commit's last arrival does the batch's commit while the memory system is busy with the draws (each of its
-  // loads then waits long): in a workgroup without draw work that delays no draw.
-  // The scan-only workgroups come first in the grid (b = blockIdx): they start at once, and they leave early,
-  // so draw workgroups that did not fit beside them start soon after.
+  // Workgroups per request: S2 that draw and, with a fused commit, one more in front that only runs the
+  // scan, writes its outputs and takes part in the commit. The commit's last arrival does the batch's commit
+  // while the memory system is busy with the draws (each of its loads then waits long): in a workgroup without
+  // draw work that delays no draw. The scan-only workgroups come first in the grid (b = blockIdx): they start
+  // at once, and they leave early, so draw workgroups that did not fit beside them start soon after.
+  // Draw workgroup c of request b has index c * B + b: a request's workgroups are spread over the dispatch
+  // order. Waves are served oldest first, so the earlier workgroups stream faster; taking the segments in
+  // batches from a counter lets them take more, and every request ends at about the same time.
   const int lead = p.cm_on ? 1 : 0;
   const bool scan_only = lead && int(blockIdx.x) < p.B;
   const int dw = int(blockIdx.x) - lead * p.B;   // draw workgroup index
-  const int b = scan_only ? int(blockIdx.x) : dw / p.S2;
-  const int c = scan_only ? -1 : dw % p.S2;
+  const int b = scan_only ? int(blockIdx.x) : dw % p.B;
+  const int c = scan_only ? -1 : dw / p.B;
   const bool writes = lead ? scan_only : c == 0;   // the workgroup that writes the scan's outputs
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -233,16 +236,11 @@ __global__ __launch_bounds__(kThreads) void k_draw(VerifyParams p) {
   r.inv_zq = 1.f / d.z_q;
   r.vec = (reinterpret_cast<uintptr_t>(r.xt) & 15) == 0 && (reinterpret_cast<uintptr_t>(r.xq) & 15) == 0;
 
-  const int s_begin = c * p.spc;
-  const int s_end = min(p.n_seg, s_begin + p.spc);
-  const int64_t e_lo = int64_t(s_begin) * kSeg;
-  const int64_t e_hi = int64_t(s_end) * kSeg;
   // The adjustment list: the sparse candidates of the draft row, or the tokens the tree walk tried (LDS).
   const bool sparse = SPARSE && d.row_q >= 0;
   const int32_t* adj_ids = sparse ? p.cand_ids + int64_t(d.row_q) * p.K : d.seen;
   const float* adj_a = sparse ? p.cand_q + int64_t(d.row_q) * p.K : nullptr;
   const int n_adj = sparse ? p.K : d.n_seen;
-  const int n_seen = collect_adjust(adj_ids, adj_a, n_adj, e_lo, e_hi, s_seen, s_seen_a, s_wcnt);
 
   // Lane l of a wave owns tokens [s*512 + 8l, s*512 + 8l + 8) of segment s; wave w takes segments
   // s_begin + w, s_begin + w + kW, ... A trip covers kTrip segments per wave with all of their loads issued
@@ -251,7 +249,7 @@ __global__ __launch_bounds__(kThreads) void k_draw(VerifyParams p) {
   constexpr int kTrip = SV_DRAW_TRIP;
   constexpr int kStep = kTrip * kW;
   const int64_t seg_base = int64_t(b) * p.n_seg;
-  auto reduce_seg = [&](const Raw8& at, const Raw8& aq, int s) {
+  auto reduce_seg = [&](const Raw8& at, const Raw8& aq, int s, int n_seen) {
     const int64_t e = int64_t(s) * kSeg + 8 * lane;
     float x[8], y[8], w[8], pv[8];
     unpack_raw8<DT>(at, x);
@@ -264,22 +262,44 @@ __global__ __launch_bounds__(kThreads) void k_draw(VerifyParams p) {
     sp = wave_sum_dpp(sp);
     if (lane == 0) store_seg(p.seg + seg_base + s, sw, sp);
   };
-  for (int t0 = s_begin + wv; t0 < s_end; t0 += kStep) {
-    Raw8 rt[kTrip], rq[kTrip];
+  // Batches of p.bseg segments (whole trips) from the request's counter, which the logits stream of this call
+  // reset to 0; the next batch is asked for while this one streams. A workgroup stops at the first number past
+  // the last batch: every batch is taken by exactly one workgroup, which stores its segment sums before it
+  // counts itself below.
+  unsigned long long* next_batch = p.cnt2 + size_t(b) * kCounterWords + kBatchWord;
+  const int n_batch = (p.n_seg + p.bseg - 1) / p.bseg;
+  if (tid == 0) s_batch = int(atomicAdd(next_batch, 1ull));
+  __syncthreads();
+  int batch = s_batch;
+  while (batch < n_batch) {
+    const int s_begin = batch * p.bseg;
+    const int s_end = min(p.n_seg, s_begin + p.bseg);
+    const int n_seen = n_adj ? collect_adjust(adj_ids, adj_a, n_adj, int64_t(s_begin) * kSeg,
+                                              int64_t(s_end) * kSeg, s_seen, s_seen_a, s_wcnt)
+                             : 0;
+    int ask = 0;
+    for (int t0 = s_begin + wv; t0 < s_end; t0 += kStep) {
+      Raw8 rt[kTrip], rq[kTrip];
 #pragma unroll
-    for (int u = 0; u < kTrip; ++u) {
-      const int s = t0 + u * kW;
-      if (s < s_end) {
-        load_raw8<DT>(r.xt, int64_t(s) * kSeg + 8 * lane, p.V, r.vec, rt[u]);
-        if (r.xq) load_raw8<DT>(r.xq, int64_t(s) * kSeg + 8 * lane, p.V, r.vec, rq[u]);
+      for (int u = 0; u < kTrip; ++u) {
+        const int s = t0 + u * kW;
+        if (s < s_end) {
+          load_raw8<DT>(r.xt, int64_t(s) * kSeg + 8 * lane, p.V, r.vec, rt[u]);
+          if (r.xq) load_raw8<DT>(r.xq, int64_t(s) * kSeg + 8 * lane, p.V, r.vec, rq[u]);
+        }
+      }
+      if (t0 == s_begin && tid == 0) ask = int(atomicAdd(next_batch, 1ull));   // behind this trip's loads
+#pragma unroll
+      for (int u = 0; u < kTrip; ++u) {
+        const int s = t0 + u * kW;
+        if (s >= s_end) break;
+        reduce_seg(rt[u], rq[u], s, n_seen);
       }
     }
-#pragma unroll
-    for (int u = 0; u < kTrip; ++u) {
-      const int s = t0 + u * kW;
-      if (s >= s_end) break;
-      reduce_seg(rt[u], rq[u], s);
-    }
+    __syncthreads();   // every wave is past this batch's adjustment list and s_batch
+    if (tid == 0) s_batch = ask;
+    __syncthreads();
+    batch = s_batch;
   }
 
   complete_memory_ops();   // every wave's segment sums are stored before the workgroup is counted

@@ -86,6 +86,11 @@ constexpr int64_t kMaxVocab = int64_t(1) << 22;
 // one memory channel while the logits stream saturates HBM.
 constexpr size_t kCounterStride = 256;
 constexpr size_t kCounterWords = kCounterStride / sizeof(unsigned long long);
+constexpr size_t kBatchWord = kCounterWords / 2;   // draw: the request's next segment batch (own 128-byte half)
+#ifndef SV_DRAW_BATCHES
+#define SV_DRAW_BATCHES 4
+#endif
+constexpr int kDrawBatchesPerWg = SV_DRAW_BATCHES;  // draw: segment batches per workgroup aimed for
 constexpr float kNear = 1e-5f;       // |u - alpha| / CDF-gap band reported as NEAR_*
 constexpr float kNearMass = 1e-6f;   // CDF-gap band in probability mass (gap * total weight)
 
@@ -116,7 +121,8 @@ struct Layout {
   int32_t S = 1;         // vocab chunks per row in k_stats
   int64_t chunk = 0;     // tokens per chunk in k_stats
   int32_t S2 = 1;        // vocab chunks per request in k_draw
-  int32_t spc = 1;       // segments per k_draw chunk
+  int32_t spc = 1;       // segments per k_draw workgroup on average
+  int32_t bseg = 1;      // segments per batch that a k_draw workgroup takes at a time
   int32_t n_seg = 0;     // segments per row
   int32_t n_piece = 0;   // sample-then-match: piece slots per row (0: no piece partials)
   size_t off_cnt2 = 0, off_part = 0, off_seg = 0, off_piece = 0;
@@ -165,6 +171,10 @@ inline Layout make_layout(int kind, int mode, int64_t total_rows, int64_t vocab,
   if (s2 < 1) s2 = 1;
   lo.spc = int32_t((lo.n_seg + s2 - 1) / s2);
   lo.S2 = (lo.n_seg + lo.spc - 1) / lo.spc;
+  // Batches of whole trips (every wave SV_DRAW_TRIP segments), about kDrawBatchesPerWg per workgroup.
+  const int64_t trip_segs = int64_t(kThreads / kWave) * SV_DRAW_TRIP;
+  const int64_t trips = (lo.spc + trip_segs * kDrawBatchesPerWg - 1) / (trip_segs * kDrawBatchesPerWg);
+  lo.bseg = int32_t(trip_segs * (trips > 0 ? trips : 1));
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
   size_t o = 0;
   lo.off_cnt2 = o; o = up(o + (sampling ? kCounterStride * size_t(batch) : 0));
@@ -208,6 +218,7 @@ struct VerifyParams {
   int32_t B, L, P, S;
   int32_t K;                  // sparse q: candidates per draft row (0 otherwise)
   int32_t S2, spc, n_seg;     // draw pass: workgroups per request, segments per workgroup, segments per row
+  int32_t bseg;               // draw pass: segments per batch
   float coef;                 // log2(e) / temperature (sampling modes)
   int32_t tree;               // 1: tree verify (rows node-major, B * L of them)
   const uint32_t* mask;       // vocab mask of the target rows, [rows, mask_words], or NULL

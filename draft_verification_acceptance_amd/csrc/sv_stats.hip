@@ -424,8 +424,11 @@ __global__ __launch_bounds__(NT) void k_stats(VerifyParams p) {
   }
   const int rows_here = part == 0 ? int(len) : int(len) - 1;
   if (slot >= rows_here) return;   // slot beyond this request's rows
-  if (SAMPLING && slot == 0 && part == 0 && chunk == 0 && threadIdx.x == 0)
-    store_agent(p.cnt2 + size_t(b) * kCounterWords, 0ull);   // the draw pass of this call counts from 0
+  if (SAMPLING && slot == 0 && part == 0 && chunk == 0 && threadIdx.x == 0) {
+    // the draw pass of this call counts its workgroups and hands out its segment batches from 0
+    store_agent(p.cnt2 + size_t(b) * kCounterWords, 0ull);
+    store_agent(p.cnt2 + size_t(b) * kCounterWords + kBatchWord, 0ull);
+  }
 
   const int64_t lo = int64_t(chunk) * p.chunk;
   const int64_t hi = lo + p.chunk < p.V ? lo + p.chunk : p.V;
