@@ -314,19 +314,39 @@ __global__ __launch_bounds__(kThreads) void k_draw(VerifyParams p) {
   const int R = (p.n_seg + kThreads - 1) / kThreads;
   const int r_lo = min(p.n_seg, tid * R);
   const int r_hi = min(p.n_seg, r_lo + R);
+  // A thread's segment sums are loaded once, all together, and kept in registers (rows of up to
+  // kThreads * kSegRegs segments); longer rows read them again where they are used.
+  constexpr int kSegRegs = 4;
+  const bool regs = R <= kSegRegs;
+  float2 sv[kSegRegs];
+  if (regs) {
+#pragma unroll
+    for (int k = 0; k < kSegRegs; ++k) sv[k] = r_lo + k < r_hi ? seg[r_lo + k] : make_float2(0.f, 0.f);
+  }
+  // f(s, sums of segment s) for the thread's segments in order, until f returns true.
+  auto for_segs = [&](auto&& f) {
+    if (regs) {
+#pragma unroll
+      for (int k = 0; k < kSegRegs; ++k)
+        if (r_lo + k < r_hi && f(r_lo + k, sv[k])) return;
+    } else {
+      for (int s = r_lo; s < r_hi; ++s)
+        if (f(s, seg[s])) return;
+    }
+  };
   uint32_t flags = 0;
   bool use_p = false;
   double excl, incl, Z;
   {
     double loc = 0.0;
-    for (int s = r_lo; s < r_hi; ++s) loc += double(seg[s].x);
+    for_segs([&](int, float2 v) { loc += double(v.x); return false; });
     block_scan_d(loc, red_d, excl, incl, Z);
   }
   if (!(Z > 0.0)) {   // weights summed to zero: draw from p instead
     use_p = true;
     flags |= SPEC_ST_ZERO_RESIDUAL;
     double loc = 0.0;
-    for (int s = r_lo; s < r_hi; ++s) loc += double(seg[s].y);
+    for_segs([&](int, float2 v) { loc += double(v.y); return false; });
     block_scan_d(loc, red_d, excl, incl, Z);
   }
   const double target = double(d.u) * Z;
@@ -336,12 +356,13 @@ __global__ __launch_bounds__(kThreads) void k_draw(VerifyParams p) {
     double acc = excl;
     int sel = -1, last_pos = -1;
     double sel_excl = 0.0, last_excl = 0.0;
-    for (int s = r_lo; s < r_hi; ++s) {
-      const double ws = double(use_p ? seg[s].y : seg[s].x);
+    for_segs([&](int s, float2 v) {
+      const double ws = double(use_p ? v.y : v.x);
       if (ws > 0.0) { last_pos = s; last_excl = acc; }
-      if (target < acc + ws && ws > 0.0) { sel = s; sel_excl = acc; break; }
+      if (target < acc + ws && ws > 0.0) { sel = s; sel_excl = acc; return true; }
       acc += ws;
-    }
+      return false;
+    });
     if (sel < 0) { sel = last_pos; sel_excl = last_excl; }
     if (sel >= 0) { s_sel = sel; s_sel_excl = sel_excl; }
   }
@@ -351,13 +372,18 @@ __global__ __launch_bounds__(kThreads) void k_draw(VerifyParams p) {
   if (sel < 0) {
     // u * Z beyond every range (rounding or a non-finite row): the last segment with positive weight.
     int lastpos = -1;
-    for (int s = r_lo; s < r_hi; ++s)
-      if ((use_p ? seg[s].y : seg[s].x) > 0.f) lastpos = s;
+    for_segs([&](int s, float2 v) {
+      if ((use_p ? v.y : v.x) > 0.f) lastpos = s;
+      return false;
+    });
     lastpos = block_max_i(lastpos, red_i);
     sel = lastpos < 0 ? 0 : lastpos;
     // its start: recompute the prefix below it
     double loc = 0.0;
-    for (int s = r_lo; s < min(r_hi, sel); ++s) loc += double(use_p ? seg[s].y : seg[s].x);
+    for_segs([&](int s, float2 v) {
+      if (s < sel) loc += double(use_p ? v.y : v.x);
+      return false;
+    });
     double e2, i2, t2;
     block_scan_d(loc, red_d, e2, i2, t2);
     sel_excl = t2;
