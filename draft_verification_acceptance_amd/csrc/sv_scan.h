@@ -241,6 +241,100 @@ __device__ DrawPlan scan_chain_rejection(const VerifyParams& p, int b, int64_t o
   const float uf_raw = p.u_final[b];   // one address for the workgroup, in flight with the load round
   chain_load_round(p, gp, len * PS, stage, true, dr0, m, s_d, s_u);
   const ReqParts rp{stage, gp, true};
+  if (len <= kWave) {
+    // A lane per row in wave 0, the same arithmetic as below: the first failure, the flags and the plan's
+    // row values come from ballots and lane reads, and one barrier hands the plan to the other waves.
+    __shared__ DrawPlan s_plan;
+    if (tid < kWave) {
+      const int j = tid;
+      uint32_t f = 0;
+      float a = 0.f;
+      bool acc = false, near = false, zq = false;
+      RowStats t{0.f, 1.f, 0.f, 0.f, 0u}, qr{0.f, 1.f, 0.f, 0.f, 0u};
+      int32_t d = 0;
+      if (j < len) {
+        t = merge_sampling(rp, j * PS, p.S);
+        if (z_bad(t.z)) f |= SPEC_ST_NONFINITE;
+      }
+      if (j < m) {
+        if (!SPARSE) {
+          qr = merge_sampling(rp, j * PS + p.S, p.S);
+          if (z_bad(qr.z)) f |= SPEC_ST_NONFINITE;
+        } else {
+          if (t.flags & kPartBadCandId) f |= SPEC_ST_BAD_TOKEN;
+          if (t.flags & kPartBadCandQ) f |= SPEC_ST_BAD_Q;
+        }
+        d = s_d[j];
+        const bool ok = d >= 0 && int64_t(d) < p.V;
+        if (!ok) f |= SPEC_ST_BAD_TOKEN;
+        bool ubad = false;
+        const float u = sanitize_u(s_u[j], ubad);
+        if (ubad) f |= SPEC_ST_BAD_UNIFORM;
+        if (ok && SPARSE) {
+          const float qd = t.q;
+          if (!(qd > 0.f)) {
+            zq = true;
+            a = t.g > -INFINITY ? 1.f : 0.f;
+          } else {
+            a = fminf(1.f, exp2_fast(fmaf(t.g, p.coef, -t.m)) / (t.z * qd));
+          }
+        } else if (ok) {
+          if (qr.g == -INFINITY) {
+            zq = true;
+            a = t.g > -INFINITY ? 1.f : 0.f;
+          } else {
+            const float et = fmaf(t.g, p.coef, -t.m);
+            const float eq = fmaf(qr.g, p.coef, -qr.m);
+            a = fminf(1.f, exp2_fast(et - eq) * (qr.z / t.z));
+          }
+        }
+        acc = u < a;
+        near = fabsf(u - a) < kNear;
+      }
+      const uint64_t fails = __ballot(j < m && !acc);
+      const int r = fails ? min(__ffsll((unsigned long long)fails) - 1, m) : m;
+      const bool examined = j < m && j <= r;
+      uint32_t fl = 0;
+#pragma unroll
+      for (uint32_t bit = 1; bit <= SPEC_ST_BAD_Q; bit <<= 1)
+        if (__ballot(f & bit)) fl |= bit;
+      if (__ballot(examined && near)) fl |= SPEC_ST_NEAR_ALPHA;
+      if (__ballot(examined && zq)) fl |= SPEC_ST_ZERO_Q;
+      bool ubad = false;
+      const float uf = sanitize_u(uf_raw, ubad);
+      if (ubad) fl |= SPEC_ST_BAD_UNIFORM;
+      if (write_out) {
+        if (p.accept_prob && j < m) p.accept_prob[dr0 + j] = examined ? a : -1.f;
+        // out_tokens[off0 + r] belongs to the draw's last workgroup, possibly on another XCD: no other
+        // workgroup may store to it.
+        if (j < len) {
+          if (j != r) p.out_tokens[off0 + j] = j < r ? d : -1;
+          p.accept_index[off0 + j] = j <= r ? int32_t(off0 + j) : -1;
+        }
+        if (j == 0) p.accept_len[b] = r;
+      }
+      const float mt = __shfl(t.m, r), zt = __shfl(t.z, r), mq = __shfl(qr.m, r), zqr = __shfl(qr.z, r);
+      if (j == 0) {
+        DrawPlan pl;
+        pl.row_t = int32_t(off0 + r);
+        pl.row_q = r < m ? int32_t(dr0 + r) : -1;
+        pl.out_pos = int32_t(off0 + r);
+        pl.m_t = mt;
+        pl.z_t = zt;
+        pl.m_q = r < m && !SPARSE ? mq : 0.f;
+        pl.z_q = r < m && !SPARSE ? zqr : 1.f;
+        pl.u = uf;
+        pl.status = fl;
+        pl.n_seen = 0;
+        pl.seen = nullptr;
+        pl.r = r;
+        pl.path = nullptr;
+        s_plan = pl;
+      }
+    }
+    __syncthreads();
+    return s_plan;
+  }
   uint32_t fl = 0;
   int fail = INT32_MAX;
   for (int j = tid; j < len; j += kThreads) {
