@@ -713,6 +713,178 @@ __global__ __launch_bounds__(kOneThreads) void k_scan_one(VerifyParams p) {
   }
 }
 
+// Greedy trees of a small batch in one workgroup, the same way: partials, parents, tokens (and with a fused
+// commit seq_lens and verify slots) in LDS from one load round, a wave per tree with a lane per node (the walk
+// of scan_tree: from the root, the lowest-index child whose token is its parent's argmax, by ballot), and the
+// commit lists from LDS (accepted nodes in path order, the others evicted in node order).
+template <typename DT>
+__global__ __launch_bounds__(kOneThreads) void k_tree_one(VerifyParams p) {
+  __shared__ GreedyPart s_pt[kOneMaxParts];
+  __shared__ int32_t s_par[kOneMaxRows];
+  __shared__ int32_t s_tok[kOneMaxRows];
+  __shared__ int64_t s_vs[kOneMaxRows];
+  __shared__ int32_t s_seq[kOneMaxB];
+  __shared__ int32_t s_r[kOneMaxB];
+  __shared__ uint64_t s_path[kOneMaxB];   // the accepted nodes of each tree, one bit per node
+  __shared__ uint64_t s_wsum[kOneWaves];
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wv = tid / kWave;
+  const int B = p.B, N = p.L, S = p.S;
+  const int T = B * N;
+  const int n_parts = T * S;
+
+  // ---- the load round: every load of this thread issued before any is used ----
+  {
+    Part pv[kOnePer];
+    int32_t av[kOnePer], tv[kOnePer];
+    int64_t vv[kOnePer];
+#pragma unroll
+    for (int k = 0; k < kOnePer; ++k) {
+      const int i = tid + k * kOneThreads;
+      pv[k] = i < n_parts ? load_part(p.part + i, false) : Part{};
+      av[k] = i < T ? p.parents[i] : 0;
+      tv[k] = i < T ? p.tokens[i] : 0;
+      vv[k] = p.cm_on && i < T ? p.verify_slots[i] : 0;
+    }
+    const int32_t sq = p.cm_on && tid < B ? p.seq_lens[tid] : 0;
+#pragma unroll
+    for (int k = 0; k < kOnePer; ++k) {
+      const int i = tid + k * kOneThreads;
+      if (i < n_parts) s_pt[i] = GreedyPart{pv[k].a, pv[k].idx, pv[k].flags};
+      if (i < T) {
+        s_par[i] = av[k];
+        s_tok[i] = tv[k];
+        if (p.cm_on) s_vs[i] = vv[k];
+      }
+    }
+    if (tid < B) s_seq[tid] = sq;
+  }
+  __syncthreads();
+
+  // ---- the walks: a wave per tree, a lane per node (the rules of scan_tree) ----
+  for (int b = wv; b < B; b += kOneWaves) {
+    const int i = lane;
+    const int64_t base = int64_t(b) * N;
+    uint32_t f = 0;
+    int32_t arg = INT32_MAX, par = -2, tok = -1;
+    if (i < N) {
+      const GreedyPart* rp = s_pt + (size_t(b) * N + i) * S;
+      GreedyPart row = rp[0];
+      for (int c = 1; c < S; ++c) {
+        const GreedyPart q = rp[c];
+        if (better(q.a, q.idx, row.a, row.idx)) {
+          row.a = q.a;
+          row.idx = q.idx;
+        }
+        row.flags |= q.flags;
+      }
+      arg = row.idx;
+      if (row.flags & kPartNaN) f |= SPEC_ST_NONFINITE;
+      if (p.mask && row.a == -INFINITY) f |= SPEC_ST_NONFINITE;   // the mask left no finite logit
+      const int32_t a = s_par[base + i];
+      const int32_t t = s_tok[base + i];
+      if (i == 0) {
+        if (a != -1) f |= SPEC_ST_BAD_PARENT;
+      } else {
+        const bool pok = a >= 0 && a < i;
+        if (!pok) f |= SPEC_ST_BAD_PARENT;
+        const bool tok_ok = t >= 0 && int64_t(t) < p.V;
+        if (!tok_ok) f |= SPEC_ST_BAD_TOKEN;
+        par = pok ? a : -2;
+        tok = tok_ok ? t : -1;
+      }
+    }
+    uint64_t path = 1;   // node 0, the root
+    int cur = 0, r = 0;
+    while (true) {
+      const int32_t want = __shfl(arg, cur);
+      const uint64_t hit = __ballot(i < N && i > cur && par == cur && tok == want);
+      if (!hit) break;
+      cur = __ffsll((unsigned long long)hit) - 1;
+      path |= 1ull << cur;
+      ++r;
+    }
+    uint32_t fl = 0;
+#pragma unroll
+    for (uint32_t bit = 1; bit <= SPEC_ST_BAD_PARENT; bit <<= 1)
+      if (__ballot(f & bit)) fl |= bit;
+    const int32_t bonus = __shfl(arg, cur);
+    // Lane i writes as node i (on the path at position k = the accepted nodes below it, since node indices
+    // grow along the path: accept_index[k] = node i, out_tokens[k - 1] = its token) and as output row i (past
+    // r: -1; at r: the bonus).
+    if (i < N) {
+      if ((path >> i) & 1ull) {
+        const int k = __popcll(path & lanes_below(i));
+        p.accept_index[base + k] = int32_t(base + i);
+        if (k > 0) p.out_tokens[base + k - 1] = tok;
+      }
+      if (i == r) p.out_tokens[base + r] = bonus;
+      if (i > r) {
+        p.out_tokens[base + i] = -1;
+        p.accept_index[base + i] = -1;
+      }
+      if (p.accept_prob) p.accept_prob[base + i] = -1.f;
+    }
+    if (lane == 0) {
+      p.accept_len[b] = r;
+      p.bonus[b] = bonus;
+      p.status[b] = fl;
+      if (p.residual_mass) p.residual_mass[b] = -1.f;
+      s_r[b] = r;
+      s_path[b] = path;
+    }
+  }
+  if (!p.cm_on) return;
+  __syncthreads();
+
+  // ---- the commit lists: per tree counts and their exclusive scan, then the nodes ----
+  int32_t* s_co = reinterpret_cast<int32_t*>(s_pt);   // the partials are no longer needed
+  int32_t* s_eo = s_co + kOneMaxB;
+  {
+    const int b = tid;
+    const bool has = b < B;
+    const uint64_t c = has ? uint64_t(s_r[b]) + 1 : 0;
+    const uint64_t e = has ? uint64_t(N) - c : 0;
+    const uint64_t mine = (c << 32) | e;   // both sums stay below 2^31: no carry between the halves
+    const uint64_t inc = wave_inclusive_sum_dpp(mine);
+    if (lane == kWave - 1) s_wsum[wv] = inc;
+    __syncthreads();
+    uint64_t pre = 0;
+    for (int w = 0; w < wv; ++w) pre += s_wsum[w];
+    const uint64_t ex = pre + inc - mine;
+    if (has) {
+      const int32_t co = int32_t(ex >> 32), eo = int32_t(uint32_t(ex));
+      p.commit_offsets[b] = co;
+      p.new_seq_lens[b] = s_seq[b] + int32_t(c);
+      if (p.evict_offsets) p.evict_offsets[b] = eo;
+      p.cstatus[b] = 0u;
+      s_co[b] = co;
+      s_eo[b] = eo;
+      if (b == B - 1) {
+        const uint64_t tot = ex + mine;
+        p.commit_offsets[B] = int32_t(tot >> 32);
+        if (p.evict_offsets) p.evict_offsets[B] = int32_t(uint32_t(tot));
+      }
+    }
+  }
+  __syncthreads();
+  for (int b = wv; b < B; b += kOneWaves) {
+    const int i = lane;
+    if (i < N) {
+      const uint64_t path = s_path[b];
+      const int below = __popcll(path & lanes_below(i));
+      const int64_t v = s_vs[int64_t(b) * N + i];
+      if ((path >> i) & 1ull) {
+        p.src_slots[int64_t(s_co[b]) + below] = v;
+        p.dst_pos[int64_t(s_co[b]) + below] = s_seq[b] + below;
+      } else if (p.evict_slots) {
+        p.evict_slots[int64_t(s_eo[b]) + (i - below)] = v;
+      }
+    }
+  }
+}
+
 template <typename DT>
 hipError_t launch_stats_t(int mode, const VerifyParams& p, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
   const int64_t blocks = int64_t(p.B) * p.L * p.P * p.S;
@@ -739,10 +911,12 @@ hipError_t launch_stats_t(int mode, const VerifyParams& p, hipStream_t stream, h
   return launch_kernel(k_stats<DT, false, false, false, false>, grid, block, 0, stream, ev0, ev1, p);
 }
 
-// Whether a greedy batch goes to k_scan_one: a chain batch whose partials, tokens and rows fit its LDS arrays.
+// Whether a greedy batch goes to one workgroup (k_scan_one, k_tree_one): its partials, tokens and rows fit the
+// LDS arrays, and a request's rows (a tree's nodes) fit a wave.
 bool scan_one_fits(const VerifyParams& p) {
-  return !p.tree && p.P == 1 && p.B <= kOneMaxB && p.L <= kOneMaxLen &&
-         int64_t(p.B) * p.L * p.S <= kOneMaxParts && p.total_rows <= kOneMaxRows;
+  const int64_t rows = p.tree ? int64_t(p.B) * p.L : p.total_rows;
+  return p.P == 1 && p.B <= kOneMaxB && p.L <= kOneMaxLen && int64_t(p.B) * p.L * p.S <= kOneMaxParts &&
+         rows <= kOneMaxRows;
 }
 
 }  // namespace
@@ -755,8 +929,12 @@ hipError_t launch_stats(int dtype, int mode, const VerifyParams& p, hipStream_t 
 
 hipError_t launch_scan(int dtype, const VerifyParams& p, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
   if (p.B <= 0) return hipSuccess;
-  if (scan_one_fits(p)) {   // a small greedy chain batch: one workgroup
+  if (scan_one_fits(p)) {   // a small greedy batch: one workgroup
     const dim3 grid{1u}, block{unsigned(kOneThreads)};
+    if (p.tree) {
+      if (dtype == SPEC_DTYPE_BF16) return launch_kernel(k_tree_one<uint16_t>, grid, block, 0, stream, ev0, ev1, p);
+      return launch_kernel(k_tree_one<float>, grid, block, 0, stream, ev0, ev1, p);
+    }
     if (dtype == SPEC_DTYPE_BF16) return launch_kernel(k_scan_one<uint16_t>, grid, block, 0, stream, ev0, ev1, p);
     return launch_kernel(k_scan_one<float>, grid, block, 0, stream, ev0, ev1, p);
   }
