@@ -55,6 +55,7 @@ void carve(VerifyParams& p, const Layout& lo, void* ws) {
   p.cnt2 = reinterpret_cast<unsigned long long*>(w + lo.off_cnt2);
   p.part = reinterpret_cast<Part*>(w + lo.off_part);
   p.seg = reinterpret_cast<float2*>(w + lo.off_seg);
+  p.mrow = reinterpret_cast<uint4*>(w + lo.off_mrow);
   p.chunk = lo.chunk;
   p.L = lo.L;
   p.P = lo.P;

@@ -79,6 +79,8 @@ constexpr int kSeg = 512;            // tokens per draw segment (one wave: 8 tok
 constexpr int kPieceMin = 1024;      // smallest piece (fp32): sizes the workspace
 constexpr int64_t kPieceChunk = 2048;
 constexpr int kMaxLen = 1024;        // max verify rows per request (chain) / nodes per tree
+constexpr int kMatchSplitMaxLen = 16;   // sample-then-match: requests of up to this many rows are drawn by
+                                        // several workgroups (four rows each), longer ones by one
 constexpr int kMaxCand = 1024;       // max candidates per draft row (sparse q)
 constexpr int64_t kMaxVocab = int64_t(1) << 22;
 // Per-request completion counters sit 256 bytes apart: a request's workgroups all update its counter at
@@ -127,6 +129,7 @@ struct Layout {
   int32_t n_piece = 0;   // sample-then-match: piece slots per row (0: no piece partials)
   size_t off_cnt2 = 0, off_part = 0, off_seg = 0, off_piece = 0;
   size_t off_cm = 0;     // fused commit: counter, then the published accept lengths and tree paths
+  size_t off_mrow = 0;   // sample-then-match on short requests: each row's published result (16 B)
   size_t bytes = 0;
 };
 
@@ -185,6 +188,9 @@ inline Layout make_layout(int kind, int mode, int64_t total_rows, int64_t vocab,
   // fused commit: one counter line, an accept length per request and (trees) the accepted path of each
   lo.off_cm = o; o = up(o + kCounterStride + sizeof(int32_t) * size_t(batch) *
                                                 (1 + (kind == SPEC_KIND_TREE ? size_t(L) : 0)));
+  lo.off_mrow = o;
+  o = up(o + (mode == SPEC_MODE_SAMPLE_MATCH && kind == SPEC_KIND_CHAIN && L <= kMatchSplitMaxLen
+                  ? 16 * size_t(batch) * size_t(L) : 0));
   lo.bytes = o;
   (void)total_rows;
   return lo;
@@ -224,6 +230,7 @@ struct VerifyParams {
   const uint32_t* mask;       // vocab mask of the target rows, [rows, mask_words], or NULL
   int64_t mask_words;         // ceil(V / 32)
   float2* piece;              // sample-then-match: (m, z) per piece of each target row slot, or NULL
+  uint4* mrow;                // sample-then-match on short requests: published row results [B, L]
   int32_t n_piece;            // piece slots per row slot
   // Fused KV commit (cm_on): each request's accept scan publishes its accept length (trees: and its path)
   // in pub_r / pub_path and counts itself on ccnt (reset by the logits stream); the workgroup that counts

@@ -277,18 +277,153 @@ __device__ __forceinline__ double unit_mass(float2 mz, float m) {
 // Unit masses each lane keeps in registers (units lane + 64 k): rows of up to 128 units never reload them.
 constexpr int kUnitRegs = 4;
 
+// One row's result, valid in lane 0 of the wave that computed it.
+struct MatchRow {
+  int32_t d;     // d_{j+1} (-1 for the last row)
+  int32_t t;     // the row's sample (when drawn)
+  uint32_t f;    // the row's status bits
+  bool near;     // the sample lies within 1e-5 of a step of the normalised CDF (when drawn)
+  float m, z, g;   // row max (log2 units), normaliser, the logit gathered at d_{j+1} (0 if none)
+};
+
+// Row j of request b, one wave: one round of loads (its chunk partials, the raw (m, z) of its units, its draft
+// token and uniforms; every lane loads at clamped indices and discards what is out of range), the partials
+// merged (status, row max, normaliser, the gathered logit), the unit masses totalled in float64 and, if
+// `draw`, the sample: the unit holding u * Z from the masses in registers, then the token inside that unit.
+template <typename DT>
+__device__ MatchRow match_row(const VerifyParams& p, int b, int j, int64_t off0, int m, bool draw) {
+  constexpr int PW = kSumUnrollStream * kWave * Elem<DT>::kPerVec;   // tokens per stream piece
+  const int lane = threadIdx.x & (kWave - 1);
+  const int S = p.S;
+  const int64_t dr0 = off0 - b;
+  RowUnits ru;
+  ru.chunks = p.part + (size_t(b) * p.L + j) * S;   // P = 1: target rows only
+  ru.pieces = p.piece ? p.piece + (size_t(b) * p.L + j) * p.n_piece : nullptr;
+  ru.n = p.piece ? int((p.V + PW - 1) / PW) : S;
+  ru.width = p.piece ? int64_t(PW) : p.chunk;
+  const Part* rowp = ru.chunks;
+  const bool regs = ru.pieces ? ru.n <= kWave * kUnitRegs : S <= kWave;
+  // ---- one round of loads
+  const Part pt0 = load_part(rowp + min(lane, S - 1), true);
+  float2 ur[kUnitRegs];
+#pragma unroll
+  for (int k = 0; k < kUnitRegs; ++k)
+    ur[k] = ru.pieces ? ru.pieces[min(lane + kWave * k, ru.n - 1)] : make_float2(pt0.a, pt0.b);
+  const int jd = m > 0 ? min(j, m - 1) : 0;
+  const int32_t d_ld = m > 0 ? p.draft_tokens[dr0 + jd] : -1;
+  const float ua_ld = m > 0 ? p.u_accept[dr0 + jd] : 0.f;
+  const float uf_ld = p.u_final[b];
+  // ---- the chunk partials, merged lane-parallel
+  float mj = -INFINITY, zj = 0.f, gj = 0.f;
+  bool gathered = false;
+  for (int c0 = 0; c0 < S; c0 += kWave) {
+    const int c = c0 + lane;
+    const Part pt = c0 == 0 ? pt0 : load_part(rowp + min(c, S - 1), true);
+    float cm = c < S ? pt.a : -INFINITY, cz = c < S ? pt.b : 0.f;
+    // butterfly inside each 16-lane row (DPP), then the four row results
+    merge_mz(cm, cz, dpp_f<0xB1>(cm), dpp_f<0xB1>(cz));
+    merge_mz(cm, cz, dpp_f<0x4E>(cm), dpp_f<0x4E>(cz));
+    merge_mz(cm, cz, dpp_f<0x141>(cm), dpp_f<0x141>(cz));
+    merge_mz(cm, cz, dpp_f<0x140>(cm), dpp_f<0x140>(cz));
+    float rm = row_lanes(cm, 0), rz = row_lanes(cz, 0);
+    merge_mz(rm, rz, row_lanes(cm, 16), row_lanes(cz, 16));
+    merge_mz(rm, rz, row_lanes(cm, 32), row_lanes(cz, 32));
+    merge_mz(rm, rz, row_lanes(cm, 48), row_lanes(cz, 48));
+    merge_mz(mj, zj, rm, rz);
+    const uint64_t gm = __ballot(c < S && (pt.flags & kPartGathered));
+    if (gm) {
+      gj = row_lanes(pt.g, __ffsll((unsigned long long)gm) - 1);
+      gathered = true;
+    }
+  }
+  // ---- unit masses (float64) and their total Z
+  double ms[kUnitRegs];
+  double Z = 0.0;
+  if (regs) {
+#pragma unroll
+    for (int k = 0; k < kUnitRegs; ++k) {
+      ms[k] = lane + kWave * k < ru.n ? unit_mass(ur[k], mj) : 0.0;
+      if (kWave * k < ru.n) Z += wave_sum_dpp(ms[k]);
+    }
+  } else {
+    for (int i0 = 0; i0 < ru.n; i0 += kWave) Z += wave_sum_dpp(i0 + lane < ru.n ? ru.mass(i0 + lane, mj) : 0.0);
+  }
+  MatchRow out;
+  out.d = j < m ? d_ld : -1;
+  bool ubad = false;
+  const float u = sanitize_u(j < m ? ua_ld : uf_ld, ubad);
+  out.f = 0;
+  if (j < m && !(out.d >= 0 && int64_t(out.d) < p.V)) out.f |= SPEC_ST_BAD_TOKEN;
+  if (ubad) out.f |= SPEC_ST_BAD_UNIFORM;
+  if (z_bad(zj)) out.f |= SPEC_ST_NONFINITE;
+  out.m = mj;
+  out.z = zj;
+  out.g = gathered ? gj : 0.f;
+  out.t = -1;
+  out.near = false;
+  if (draw) {
+    const double T = double(u) * Z;
+    // the unit holding T (the first with positive mass whose cumulative mass passes T; rounding past the
+    // end: the last with positive mass)
+    int usel = -1, ulast = -1;
+    double cum0 = 0.0, cum_last = 0.0, carry = 0.0;
+    auto scan_block = [&](int i0, double mass) {
+      const double incl = carry + wave_inclusive_sum_dpp(mass);
+      const uint64_t hit = __ballot(mass > 0.0 && T < incl);
+      if (hit) {
+        const int f = __ffsll((unsigned long long)hit) - 1;
+        usel = i0 + f;
+        cum0 = row_lanes_d(incl - mass, f);
+      }
+      const uint64_t pos = __ballot(mass > 0.0);
+      if (pos) {
+        const int f = 63 - __clzll((long long)pos);
+        ulast = i0 + f;
+        cum_last = row_lanes_d(incl - mass, f);
+      }
+      carry = row_lanes_d(incl, kWave - 1);
+    };
+    if (regs) {
+#pragma unroll
+      for (int k = 0; k < kUnitRegs; ++k)
+        if (usel < 0 && kWave * k < ru.n) scan_block(kWave * k, ms[k]);
+    } else {
+      for (int i0 = 0; i0 < ru.n && usel < 0; i0 += kWave)
+        scan_block(i0, i0 + lane < ru.n ? ru.mass(i0 + lane, mj) : 0.0);
+    }
+    if (usel < 0) {   // rounding left u * Z past every unit (or nothing has mass)
+      usel = ulast < 0 ? 0 : ulast;
+      cum0 = ulast < 0 ? 0.0 : cum_last;
+    }
+    const int a = int(int64_t(usel) * ru.width);
+    const int n = int(min(p.V, int64_t(usel + 1) * ru.width)) - a;
+    const DT* row = static_cast<const DT*>(p.target) + (off0 + j) * p.V;
+    const uint32_t* mrow = p.mask ? p.mask + (off0 + j) * p.mask_words : nullptr;
+    double cum1, w_tok;
+    out.t = n <= kWave * 32 ? wave_draw_small<DT>(row, a, n, T - cum0, p.coef, mj, mrow, p.mask_words, cum1, w_tok)
+                            : wave_draw<DT>(row, a, n, T - cum0, p.coef, mj, mrow, p.mask_words, cum1, w_tok);
+    // Too close to call: u within 1e-5 of a step of the normalised CDF.
+    const double lo = (cum0 + cum1) / Z;
+    const double gap = fmin(double(u) - lo, lo + w_tok / Z - double(u));
+    out.near = !(gap >= double(kNear));
+  }
+  return out;
+}
+
+// p_k(d_{k+1}) where compared, the accept_prob output: the same fp32 arithmetic as the rejection scans.
+__device__ __forceinline__ float match_prob(const VerifyParams& p, const MatchRow& r) {
+  return r.d >= 0 && int64_t(r.d) < p.V ? exp2_fast(fmaf(r.g, p.coef, -r.m)) / r.z : 0.f;
+}
+
 template <typename DT>
 __global__ __launch_bounds__(kMatchThreads) void k_match(VerifyParams p) {
   __shared__ int32_t s_d[kMaxLen];     // d_{j+1} per row j < m
   __shared__ int32_t s_t[kMaxLen];     // the sample t_j of row j
-  __shared__ float s_m[kMaxLen];       // row max (log2 units)
-  __shared__ float s_z[kMaxLen];       // row normaliser, float (accept_prob, status)
-  __shared__ float s_g[kMaxLen];       // row j's logit at d_{j+1} (gathered while streaming)
+  __shared__ float s_pk[kMaxLen];      // p_j(d_{j+1})
   __shared__ uint8_t s_near[kMaxLen];
   __shared__ uint32_t s_flags;
   __shared__ int s_r, s_stop;
 
-  constexpr int PW = kSumUnrollStream * kWave * Elem<DT>::kPerVec;   // tokens per stream piece
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -302,142 +437,27 @@ __global__ __launch_bounds__(kMatchThreads) void k_match(VerifyParams p) {
   const int len = int(len64);
   const int m = len - 1;
   const int64_t dr0 = off0 - b;
-  const int S = p.S;
-  const Part* gp = p.part + size_t(b) * p.L * S;   // P = 1: target rows only
   if (tid == 0) {
     s_flags = 0;
     s_r = m;
     s_stop = 0;
   }
-  auto units = [&](int j) -> RowUnits {
-    RowUnits u;
-    u.chunks = gp + size_t(j) * S;
-    u.pieces = p.piece ? p.piece + (size_t(b) * p.L + j) * p.n_piece : nullptr;
-    u.n = p.piece ? int((p.V + PW - 1) / PW) : S;
-    u.width = p.piece ? int64_t(PW) : p.chunk;
-    return u;
-  };
 
-  // Rows in groups of 16 in row order, one wave per row. Each wave loads what its row needs in one round
-  // (its chunk partials, the raw (m, z) of its units, its draft token and uniforms), merges the partials
-  // (status, row max, normaliser, the gathered logit), totals its unit masses in float64 and, until a group
-  // has held a mismatch, draws its sample: the unit holding u * Z from the masses in registers, then the
-  // token inside that unit. Later groups still merge their partials (their status bits count).
+  // Rows in groups of 16 in row order, one wave per row (match_row). Until a group has held a mismatch
+  // each row draws its sample; later groups still merge their partials (their status bits count).
   uint32_t fl = 0;
   bool stopped = false;
   for (int j0 = 0; j0 < len; j0 += kMatchWaves) {
     const int j = j0 + wv;
     if (j < len) {
-      const RowUnits ru = units(j);
-      const Part* rowp = gp + size_t(j) * S;
-      const bool regs = ru.pieces ? ru.n <= kWave * kUnitRegs : S <= kWave;
-      // ---- one round of loads; every lane loads (clamped indices), what is out of range is discarded
-      const Part pt0 = load_part(rowp + min(lane, S - 1), true);
-      float2 ur[kUnitRegs];
-#pragma unroll
-      for (int k = 0; k < kUnitRegs; ++k)
-        ur[k] = ru.pieces ? ru.pieces[min(lane + kWave * k, ru.n - 1)] : make_float2(pt0.a, pt0.b);
-      const int jd = m > 0 ? min(j, m - 1) : 0;
-      const int32_t d_ld = m > 0 ? p.draft_tokens[dr0 + jd] : -1;
-      const float ua_ld = m > 0 ? p.u_accept[dr0 + jd] : 0.f;
-      const float uf_ld = p.u_final[b];
-      // ---- the chunk partials, merged lane-parallel
-      float mj = -INFINITY, zj = 0.f, gj = 0.f;
-      bool gathered = false;
-      for (int c0 = 0; c0 < S; c0 += kWave) {
-        const int c = c0 + lane;
-        const Part pt = c0 == 0 ? pt0 : load_part(rowp + min(c, S - 1), true);
-        float cm = c < S ? pt.a : -INFINITY, cz = c < S ? pt.b : 0.f;
-        // butterfly inside each 16-lane row (DPP), then the four row results
-        merge_mz(cm, cz, dpp_f<0xB1>(cm), dpp_f<0xB1>(cz));
-        merge_mz(cm, cz, dpp_f<0x4E>(cm), dpp_f<0x4E>(cz));
-        merge_mz(cm, cz, dpp_f<0x141>(cm), dpp_f<0x141>(cz));
-        merge_mz(cm, cz, dpp_f<0x140>(cm), dpp_f<0x140>(cz));
-        float rm = row_lanes(cm, 0), rz = row_lanes(cz, 0);
-        merge_mz(rm, rz, row_lanes(cm, 16), row_lanes(cz, 16));
-        merge_mz(rm, rz, row_lanes(cm, 32), row_lanes(cz, 32));
-        merge_mz(rm, rz, row_lanes(cm, 48), row_lanes(cz, 48));
-        merge_mz(mj, zj, rm, rz);
-        const uint64_t gm = __ballot(c < S && (pt.flags & kPartGathered));
-        if (gm) {
-          gj = row_lanes(pt.g, __ffsll((unsigned long long)gm) - 1);
-          gathered = true;
-        }
-      }
-      // ---- unit masses (float64) and their total Z
-      double ms[kUnitRegs];
-      double Z = 0.0;
-      if (regs) {
-#pragma unroll
-        for (int k = 0; k < kUnitRegs; ++k) {
-          ms[k] = lane + kWave * k < ru.n ? unit_mass(ur[k], mj) : 0.0;
-          if (kWave * k < ru.n) Z += wave_sum_dpp(ms[k]);
-        }
-      } else {
-        for (int i0 = 0; i0 < ru.n; i0 += kWave) Z += wave_sum_dpp(i0 + lane < ru.n ? ru.mass(i0 + lane, mj) : 0.0);
-      }
-      const int32_t d = j < m ? d_ld : -1;
-      bool ubad = false;
-      const float u = sanitize_u(j < m ? ua_ld : uf_ld, ubad);
+      const MatchRow mr = match_row<DT>(p, b, j, off0, m, !stopped);
       if (lane == 0) {
-        uint32_t f = 0;
-        if (j < m && !(d >= 0 && int64_t(d) < p.V)) f |= SPEC_ST_BAD_TOKEN;
-        if (ubad) f |= SPEC_ST_BAD_UNIFORM;
-        if (z_bad(zj)) f |= SPEC_ST_NONFINITE;
-        s_d[j] = d;
-        s_m[j] = mj;
-        s_z[j] = zj;
-        s_g[j] = gathered ? gj : 0.f;
-        fl |= f;
-      }
-      if (!stopped) {
-        const double T = double(u) * Z;
-        // the unit holding T (the first with positive mass whose cumulative mass passes T; rounding past the
-        // end: the last with positive mass)
-        int usel = -1, ulast = -1;
-        double cum0 = 0.0, cum_last = 0.0, carry = 0.0;
-        auto scan_block = [&](int i0, double mass) {
-          const double incl = carry + wave_inclusive_sum_dpp(mass);
-          const uint64_t hit = __ballot(mass > 0.0 && T < incl);
-          if (hit) {
-            const int f = __ffsll((unsigned long long)hit) - 1;
-            usel = i0 + f;
-            cum0 = row_lanes_d(incl - mass, f);
-          }
-          const uint64_t pos = __ballot(mass > 0.0);
-          if (pos) {
-            const int f = 63 - __clzll((long long)pos);
-            ulast = i0 + f;
-            cum_last = row_lanes_d(incl - mass, f);
-          }
-          carry = row_lanes_d(incl, kWave - 1);
-        };
-        if (regs) {
-#pragma unroll
-          for (int k = 0; k < kUnitRegs; ++k)
-            if (usel < 0 && kWave * k < ru.n) scan_block(kWave * k, ms[k]);
-        } else {
-          for (int i0 = 0; i0 < ru.n && usel < 0; i0 += kWave)
-            scan_block(i0, i0 + lane < ru.n ? ru.mass(i0 + lane, mj) : 0.0);
-        }
-        if (usel < 0) {   // rounding left u * Z past every unit (or nothing has mass)
-          usel = ulast < 0 ? 0 : ulast;
-          cum0 = ulast < 0 ? 0.0 : cum_last;
-        }
-        const int a = int(int64_t(usel) * ru.width);
-        const int n = int(min(p.V, int64_t(usel + 1) * ru.width)) - a;
-        const DT* row = static_cast<const DT*>(p.target) + (off0 + j) * p.V;
-        const uint32_t* mrow = p.mask ? p.mask + (off0 + j) * p.mask_words : nullptr;
-        double cum1, w_tok;
-        const int tok = n <= kWave * 32
-                            ? wave_draw_small<DT>(row, a, n, T - cum0, p.coef, mj, mrow, p.mask_words, cum1, w_tok)
-                            : wave_draw<DT>(row, a, n, T - cum0, p.coef, mj, mrow, p.mask_words, cum1, w_tok);
-        if (lane == 0) {
-          // Too close to call: u within 1e-5 of a step of the normalised CDF.
-          const double lo = (cum0 + cum1) / Z;
-          const double gap = fmin(double(u) - lo, lo + w_tok / Z - double(u));
-          s_t[j] = tok;
-          s_near[j] = !(gap >= double(kNear));
+        s_d[j] = mr.d;
+        s_pk[j] = match_prob(p, mr);
+        fl |= mr.f;
+        if (!stopped) {
+          s_t[j] = mr.t;
+          s_near[j] = mr.near;
         }
       }
     }
@@ -463,13 +483,7 @@ __global__ __launch_bounds__(kMatchThreads) void k_match(VerifyParams p) {
     p.out_tokens[off0 + k] = k < r ? s_d[k] : (k == r ? bonus : -1);
     p.accept_index[off0 + k] = k <= r ? int32_t(off0 + k) : -1;
     if (k <= r && s_near[k]) near = SPEC_ST_NEAR_CDF;
-    if (k < m && p.accept_prob) {
-      // p_k(d_{k+1}) where compared: the same fp32 arithmetic as the rejection scans
-      const int32_t d = s_d[k];
-      float pk = -1.f;
-      if (k <= r) pk = d >= 0 && int64_t(d) < p.V ? exp2_fast(fmaf(s_g[k], p.coef, -s_m[k])) / s_z[k] : 0.f;
-      p.accept_prob[dr0 + k] = pk;
-    }
+    if (k < m && p.accept_prob) p.accept_prob[dr0 + k] = k <= r ? s_pk[k] : -1.f;
   }
   if (near) atomicOr(&s_flags, near);
   __syncthreads();
@@ -482,10 +496,104 @@ __global__ __launch_bounds__(kMatchThreads) void k_match(VerifyParams p) {
   if (p.cm_on && commit_arrive<kMatchThreads>(p, b, r, nullptr)) fused_commit<kMatchThreads, false>(p);
 }
 
+// Sample-then-match on short requests (at most kMatchSplitMaxLen rows): workgroup g of request b draws rows
+// 4g .. 4g + 3 (a wave each), so that a request's rows run on several compute units instead of sharing one;
+// each row's result is published (agent-scope stores), and the request's last workgroup to count itself on
+// the request's counter (reset by the logits stream of the same call) reads them, finds the first mismatch
+// and writes the request's outputs, as k_match does.
+template <typename DT>
+__global__ __launch_bounds__(kThreads) void k_match_split(VerifyParams p) {
+  constexpr int kRows = kThreads / kWave;
+  __shared__ int s_last;
+  __shared__ uint32_t s_flags;
+  const int G = (p.L + kRows - 1) / kRows;
+  const int b = int(blockIdx.x) / G;
+  const int g = int(blockIdx.x) % G;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wv = tid / kWave;
+  int64_t off0, len64;
+  if (!chain_request(p, b, off0, len64)) {   // every workgroup of b agrees; one reports it
+    if (g == 0) {
+      if (tid == 0) write_bad_offsets(p, b);
+      if (p.cm_on && commit_arrive<kThreads>(p, b, -1, nullptr)) fused_commit<kThreads, false>(p);
+    }
+    return;
+  }
+  const int len = int(len64);
+  const int m = len - 1;
+  const int64_t dr0 = off0 - b;
+  uint4* pub = p.mrow + size_t(b) * p.L;
+  const int j = g * kRows + wv;
+  if (j < len) {
+    const MatchRow mr = match_row<DT>(p, b, j, off0, m, true);
+    if (lane == 0) {
+      const float pk = match_prob(p, mr);
+      store_agent(reinterpret_cast<unsigned long long*>(pub + j),
+                  (unsigned long long)uint32_t(mr.t) | ((unsigned long long)uint32_t(mr.d) << 32));
+      store_agent(reinterpret_cast<unsigned long long*>(pub + j) + 1,
+                  (unsigned long long)(mr.f | (mr.near ? SPEC_ST_NEAR_CDF : 0u)) |
+                      ((unsigned long long)__float_as_uint(pk) << 32));
+    }
+  }
+  complete_memory_ops();   // the published rows are stored before the workgroup is counted
+  __syncthreads();
+  if (tid == 0) s_last = uint32_t(atomicAdd(p.cnt2 + size_t(b) * kCounterWords, 1ull)) + 1u == uint32_t(G);
+  __syncthreads();
+  if (!s_last) return;
+
+  // The request's last workgroup: wave 0 reads every row (a lane each; len <= 64).
+  int r = m;
+  if (tid < kWave) {
+    const int k = lane;
+    int32_t t = -1, d = -1;
+    uint32_t f = 0;
+    float pk = 0.f;
+    if (k < len) {
+      const unsigned long long w0 = load_agent(reinterpret_cast<unsigned long long*>(pub + k));
+      const unsigned long long w1 = load_agent(reinterpret_cast<unsigned long long*>(pub + k) + 1);
+      t = int32_t(uint32_t(w0));
+      d = int32_t(uint32_t(w0 >> 32));
+      f = uint32_t(w1);
+      pk = __uint_as_float(uint32_t(w1 >> 32));
+    }
+    const uint64_t stop = __ballot(k < len && (k == m || !(d >= 0 && int64_t(d) < p.V && d == t)));
+    r = stop ? __ffsll((unsigned long long)stop) - 1 : m;
+    uint32_t fl = 0;
+#pragma unroll
+    for (uint32_t bit = 1; bit <= SPEC_ST_NEAR_CDF; bit <<= 1) {
+      const bool any = bit == SPEC_ST_NEAR_CDF ? __ballot(k <= r && (f & bit)) : __ballot(k < len && (f & bit));
+      if (any) fl |= bit;
+    }
+    const int32_t bonus = __shfl(t, r);
+    if (k < len) {
+      p.out_tokens[off0 + k] = k < r ? d : (k == r ? bonus : -1);
+      p.accept_index[off0 + k] = k <= r ? int32_t(off0 + k) : -1;
+      if (k < m && p.accept_prob) p.accept_prob[dr0 + k] = k <= r ? pk : -1.f;
+    }
+    if (k == 0) {
+      p.accept_len[b] = r;
+      p.bonus[b] = bonus;
+      p.status[b] = fl;
+      if (p.residual_mass) p.residual_mass[b] = -1.f;
+      s_flags = uint32_t(r);
+    }
+  }
+  __syncthreads();
+  r = int(s_flags);
+  if (p.cm_on && commit_arrive<kThreads>(p, b, r, nullptr)) fused_commit<kThreads, false>(p);
+}
+
 }  // namespace
 
 hipError_t launch_match(int dtype, const VerifyParams& p, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
   if (p.B <= 0) return hipSuccess;
+  if (p.L <= kMatchSplitMaxLen) {
+    constexpr int kRows = kThreads / kWave;
+    const dim3 grid{unsigned(p.B * ((p.L + kRows - 1) / kRows))}, block{unsigned(kThreads)};
+    if (dtype == SPEC_DTYPE_BF16) return launch_kernel(k_match_split<uint16_t>, grid, block, 0, stream, ev0, ev1, p);
+    return launch_kernel(k_match_split<float>, grid, block, 0, stream, ev0, ev1, p);
+  }
   const dim3 grid{unsigned(p.B)}, block{unsigned(kMatchThreads)};
   if (dtype == SPEC_DTYPE_BF16) return launch_kernel(k_match<uint16_t>, grid, block, 0, stream, ev0, ev1, p);
   return launch_kernel(k_match<float>, grid, block, 0, stream, ev0, ev1, p);
