@@ -240,7 +240,7 @@ __global__ __launch_bounds__(kThreads) void k_draw(VerifyParams p) {
   const bool sparse = SPARSE && d.row_q >= 0;
   const int32_t* adj_ids = sparse ? p.cand_ids + int64_t(d.row_q) * p.K : d.seen;
   const float* adj_a = sparse ? p.cand_q + int64_t(d.row_q) * p.K : nullptr;
-  const int n_adj = sparse ? p.K : d.n_seen;
+  const int n_adj = sparse ? p.K : (TREE ? d.n_seen : 0);   // dense rejection: none (known at compile time)
 
   // Lane l of a wave owns tokens [s*512 + 8l, s*512 + 8l + 8) of segment s; wave w takes segments
   // s_begin + w, s_begin + w + kW, ... A trip covers kTrip segments per wave with all of their loads issued

@@ -293,6 +293,7 @@ __device__ DrawPlan scan_chain_rejection(const VerifyParams& p, int b, int64_t o
       }
       const uint64_t fails = __ballot(j < m && !acc);
       const int r = fails ? min(__ffsll((unsigned long long)fails) - 1, m) : m;
+      const float mt = __shfl(t.m, r), zt = __shfl(t.z, r), mq = __shfl(qr.m, r), zqr = __shfl(qr.z, r);
       const bool examined = j < m && j <= r;
       uint32_t fl = 0;
 #pragma unroll
@@ -313,7 +314,6 @@ __device__ DrawPlan scan_chain_rejection(const VerifyParams& p, int b, int64_t o
         }
         if (j == 0) p.accept_len[b] = r;
       }
-      const float mt = __shfl(t.m, r), zt = __shfl(t.z, r), mq = __shfl(qr.m, r), zqr = __shfl(qr.z, r);
       if (j == 0) {
         DrawPlan pl;
         pl.row_t = int32_t(off0 + r);
