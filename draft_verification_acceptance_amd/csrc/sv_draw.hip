@@ -262,15 +262,13 @@ __global__ __launch_bounds__(kThreads) void k_draw(VerifyParams p) {
     sp = wave_sum_dpp(sp);
     if (lane == 0) store_seg(p.seg + seg_base + s, sw, sp);
   };
-  // Batches of p.bseg segments (whole trips) from the request's counter, which the logits stream of this call
-  // reset to 0; the next batch is asked for while this one streams. A workgroup stops at the first number past
-  // the last batch: every batch is taken by exactly one workgroup, which stores its segment sums before it
-  // counts itself below.
+  // Batches of p.bseg segments (whole trips): draw workgroup c starts with batch c, then takes batches S2, S2 + 1,
+  // ... from the request's counter, which the logits stream of this call reset to 0; the next batch is asked for
+  // while this one streams. A workgroup stops at the first number past the last batch: every batch is taken by
+  // exactly one workgroup, which stores its segment sums before it counts itself below.
   unsigned long long* next_batch = p.cnt2 + size_t(b) * kCounterWords + kBatchWord;
   const int n_batch = (p.n_seg + p.bseg - 1) / p.bseg;
-  if (tid == 0) s_batch = int(atomicAdd(next_batch, 1ull));
-  __syncthreads();
-  int batch = s_batch;
+  int batch = c;
   while (batch < n_batch) {
     const int s_begin = batch * p.bseg;
     const int s_end = min(p.n_seg, s_begin + p.bseg);
@@ -288,7 +286,7 @@ __global__ __launch_bounds__(kThreads) void k_draw(VerifyParams p) {
           if (r.xq) load_raw8<DT>(r.xq, int64_t(s) * kSeg + 8 * lane, p.V, r.vec, rq[u]);
         }
       }
-      if (t0 == s_begin && tid == 0) ask = int(atomicAdd(next_batch, 1ull));   // behind this trip's loads
+      if (t0 == s_begin && tid == 0) ask = p.S2 + int(atomicAdd(next_batch, 1ull));   // behind this trip's loads
 #pragma unroll
       for (int u = 0; u < kTrip; ++u) {
         const int s = t0 + u * kW;
