@@ -12,7 +12,7 @@ import torch
 import draft_verification_acceptance_amd as dva
 import oracle
 from draft_verification_acceptance_amd import workloads as W
-from gpu_util import dev, dev_logits, np_out
+from gpu_util import compare_chain, compare_tree, dev, dev_logits, np_out, oracle_chain, oracle_tree
 
 pytestmark = pytest.mark.gpu
 
@@ -164,3 +164,32 @@ def test_fused_commit_graph_replay(kind):
         torch.cuda.synchronize()
         for k, t in ref.items():
             assert torch.equal(call.outputs[k], t), (kind, rep, k)
+
+
+@pytest.mark.parametrize("batch,m_max", [(1024, 1), (30, 63)])
+def test_one_workgroup_greedy_chain_limits(batch, m_max):
+    """Greedy chain batches at the one-workgroup path's limits (1024 requests; requests of 64 rows): verify
+    outputs equal the oracle's, the fused commit equals the standalone commit."""
+    w = W.ragged(seed=5041, batch=batch, m_max=m_max, vocab=97, parallel=False)
+    assert w.total_rows <= 2048 and w.max_verify_len <= 64
+    print("one-workgroup greedy chain", batch, w.max_verify_len, w.total_rows, flush=True)
+    slots = np.random.default_rng(7).integers(0, 1 << 40, w.total_rows).astype(np.int64)
+    seq = np.random.default_rng(8).integers(0, 4096, w.batch).astype(np.int32)
+    g = np_out(dva.verify_chain(dev_logits(w.target), dev(w.offsets, torch.int32), dev(w.draft_tokens, torch.int32),
+                                "greedy", verify_slots=dev(slots), seq_lens=dev(seq), **_chain_kw(w, "greedy")))
+    assert compare_chain(w, "greedy", oracle_chain(w, "greedy"), g) == 0
+    _check(g, w.offsets, w.max_verify_len, slots, seq)
+
+
+@pytest.mark.parametrize("batch,n_nodes", [(1024, 2), (32, 64), (33, 62)])
+def test_one_workgroup_greedy_tree_limits(batch, n_nodes):
+    """Greedy tree batches at the one-workgroup path's limits (2048 nodes; trees of 64 nodes)."""
+    w = W.tree(seed=4041, batch=batch, n_nodes=n_nodes, vocab=301, parallel=False)
+    print("one-workgroup greedy tree", batch, n_nodes, flush=True)
+    slots = np.random.default_rng(9).integers(0, 1 << 40, w.total_rows).astype(np.int64)
+    seq = np.random.default_rng(10).integers(0, 4096, w.batch).astype(np.int32)
+    g = np_out(dva.verify_tree(dev_logits(w.target), dev(w.parents), dev(w.tokens), w.n_nodes, "greedy",
+                               verify_slots=dev(slots), seq_lens=dev(seq)))
+    assert compare_tree(w, "greedy", oracle_tree(w, "greedy"), g) == 0
+    offs = (np.arange(w.batch + 1) * w.n_nodes).astype(np.int32)
+    _check(g, offs, w.n_nodes, slots, seq)
