@@ -172,11 +172,15 @@ struct SegView {
   }
 };
 
+// Entries the adjustment list of a draw can hold.
+template <bool TREE, bool SPARSE>
+__host__ __device__ __forceinline__ int adjust_cap(const VerifyParams& p) {
+  return TREE ? p.L : (SPARSE ? p.K : 0);
+}
+
 template <typename DT, bool TREE, bool SPARSE>
 __global__ __launch_bounds__(kThreads) void k_draw(VerifyParams p) {
   extern __shared__ __align__(16) char smem[];
-  __shared__ int32_t s_seen[kMaxLen];   // adjustment list entries inside the current token range
-  __shared__ float s_seen_a[kMaxLen];
   __shared__ int s_wcnt[kThreads / kWave];
   __shared__ double red_d[kThreads / kWave];
   __shared__ int red_i[kThreads / kWave];
@@ -207,6 +211,10 @@ __global__ __launch_bounds__(kThreads) void k_draw(VerifyParams p) {
   const int nst = staged_parts(p.L, p.P, p.S);
   Part* stage = nst ? reinterpret_cast<Part*>(smem) : nullptr;
   char* rows = smem + size_t(nst) * sizeof(Part);
+  // The adjustment list entries inside the current token range (LDS after the scan's arrays; room for every
+  // entry: a tree's tried tokens are fewer than its nodes, a sparse row has K candidates).
+  int32_t* s_seen = reinterpret_cast<int32_t*>(smem + scan_smem_bytes(TREE, true, p.L, p.P, p.S));
+  float* s_seen_a = reinterpret_cast<float*>(s_seen + adjust_cap<TREE, SPARSE>(p));
   DrawPlan d;
   if (TREE) {
     d = scan_tree<DT, true>(p, b, rows, stage, writes);
@@ -456,10 +464,14 @@ hipError_t launch_draw_t(int mode, const VerifyParams& p, hipStream_t stream, hi
   const int64_t blocks = int64_t(p.B) * (p.S2 + (p.cm_on ? 1 : 0));
   if (blocks <= 0) return hipSuccess;
   const size_t smem = scan_smem_bytes(p.tree != 0, true, p.L, p.P, p.S);
+  const size_t adj = sizeof(int32_t) + sizeof(float);   // per adjustment list entry
   const dim3 grid{unsigned(blocks)}, block{unsigned(kThreads)};
-  if (p.tree) return launch_kernel(k_draw<DT, true, false>, grid, block, smem, stream, ev0, ev1, p);
+  if (p.tree)
+    return launch_kernel(k_draw<DT, true, false>, grid, block, smem + adj * adjust_cap<true, false>(p), stream, ev0,
+                         ev1, p);
   if (mode == SPEC_MODE_REJECTION_SPARSE)
-    return launch_kernel(k_draw<DT, false, true>, grid, block, smem, stream, ev0, ev1, p);
+    return launch_kernel(k_draw<DT, false, true>, grid, block, smem + adj * adjust_cap<false, true>(p), stream, ev0,
+                         ev1, p);
   return launch_kernel(k_draw<DT, false, false>, grid, block, smem, stream, ev0, ev1, p);
 }
 
