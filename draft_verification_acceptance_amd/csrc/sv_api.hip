@@ -61,7 +61,6 @@ void carve(VerifyParams& p, const Layout& lo, void* ws) {
   p.P = lo.P;
   p.S = lo.S;
   p.S2 = lo.S2;
-  p.spc = lo.spc;
   p.bseg = lo.bseg;
   p.n_seg = lo.n_seg;
 }

@@ -223,7 +223,7 @@ struct VerifyParams {
   int64_t chunk;
   int32_t B, L, P, S;
   int32_t K;                  // sparse q: candidates per draft row (0 otherwise)
-  int32_t S2, spc, n_seg;     // draw pass: workgroups per request, segments per workgroup, segments per row
+  int32_t S2, n_seg;          // draw pass: workgroups per request, segments per row
   int32_t bseg;               // draw pass: segments per batch
   float coef;                 // log2(e) / temperature (sampling modes)
   int32_t tree;               // 1: tree verify (rows node-major, B * L of them)
