@@ -4,8 +4,10 @@
 // longest matching prefix, the first mismatch replaced by the posterior's sample; [EAGLE→DFlash2] §1.2:
 // independent target sampling then prefix matching is a different implementation from p/q rejection).
 //
-// One workgroup of 1024 threads per request, one wave per row, 16 rows at a time in row order; the request
-// stops after the first group of rows that holds a mismatch. A draw does not read the whole row: the stream
+// Requests of up to 16 rows: k_match_split, four rows (a wave each) per workgroup, the request's rows spread
+// over several workgroups that hand their results to the last of them. Longer requests: k_match, one workgroup
+// of 1024 threads per request, one wave per row, 16 rows at a time in row order; the request stops after the
+// first group of rows that holds a mismatch. A draw does not read the whole row: the stream
 // stored the (m, z) of every piece of the row (2048 tokens in bf16) or, for rows that are not 16-byte
 // aligned, of its chunks, so the unit holding u * Z is known from those masses z_i 2^(m_i - m); the wave
 // then narrows that unit down (each lane sums a contiguous range of it in float64, a wave scan picks the

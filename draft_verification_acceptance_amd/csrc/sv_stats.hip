@@ -1,5 +1,6 @@
 // k_stats: one streaming pass over every verify row (target, and draft rows in rejection mode); each
-// workgroup publishes a partial of its row chunk and ends. k_scan: the greedy request scans.
+// workgroup publishes a partial of its row chunk and ends. k_scan: the greedy request scans (a workgroup per
+// request); k_scan_one / k_tree_one: the same for a small chain / tree batch in one workgroup.
 //
 // What is computed per row (the verify step scores all positions in one parallel pass; the rows after the
 // first rejection are read too: [EAGLE→DFlash2] §1.1, [SpecDec] "抽象：draft → verify → commit"):
