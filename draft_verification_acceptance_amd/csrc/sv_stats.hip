@@ -544,8 +544,9 @@ __global__ __launch_bounds__(kThreads) void k_scan(VerifyParams p) {
 // ---------------------------------------------------------------------------------------------------
 // Greedy chains of a small batch in one workgroup. Every input that the batch's scans and its commit read
 // (offsets, row partials, draft tokens; with a fused commit also seq_lens and verify_slots) goes into LDS in
-// one load round; a wave per request then runs the scan, and the commit lists follow from LDS, with no
-// hand-off between workgroups. The outputs are those of k_scan and its fused commit.
+// one load round; the scans run a request per segment of a wave's lanes (several short requests to a wave),
+// and the commit lists follow from LDS, with no hand-off between workgroups. The outputs are those of k_scan
+// and its fused commit.
 // ---------------------------------------------------------------------------------------------------
 constexpr int kOneThreads = 1024;
 constexpr int kOneWaves = kOneThreads / kWave;
@@ -561,72 +562,54 @@ struct GreedyPart {   // the greedy fields of a row partial
   uint32_t flags;
 };
 
-template <typename DT>
-__global__ __launch_bounds__(kOneThreads) void k_scan_one(VerifyParams p) {
-  __shared__ GreedyPart s_pt[kOneMaxParts];
-  __shared__ int32_t s_tok[kOneMaxRows];
-  __shared__ int64_t s_vs[kOneMaxRows];
-  __shared__ int32_t s_off[kOneMaxB + 1];
-  __shared__ int32_t s_seq[kOneMaxB];
-  __shared__ int32_t s_r[kOneMaxB];       // accepted drafts of request b, -1: its offsets failed
-  __shared__ uint64_t s_wsum[kOneWaves];
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wv = tid / kWave;
-  const int B = p.B;
-  const int S = p.S;
-  const int64_t T = p.total_rows;
-  const int n_parts = B * p.L * S;   // the part area of request b starts at b * L * S (P = 1)
-
-  // ---- the load round: every load of this thread issued before any is used ----
-  {
-    Part pv[kOnePer];
-    int32_t tv[kOnePer], ov[kOnePer];
-    int64_t vv[kOnePer];
-#pragma unroll
-    for (int k = 0; k < kOnePer; ++k) {
-      const int i = tid + k * kOneThreads;
-      pv[k] = i < n_parts ? load_part(p.part + i, false) : Part{};
-      tv[k] = i < T - B ? p.draft_tokens[i] : 0;
-      vv[k] = p.cm_on && i < T ? p.verify_slots[i] : 0;
-      ov[k] = i <= B ? p.offsets[i] : 0;
-    }
-    const int32_t sq = p.cm_on && tid < B ? p.seq_lens[tid] : 0;
-#pragma unroll
-    for (int k = 0; k < kOnePer; ++k) {
-      const int i = tid + k * kOneThreads;
-      if (i < n_parts) s_pt[i] = GreedyPart{pv[k].a, pv[k].idx, pv[k].flags};
-      if (i < T - B) s_tok[i] = tv[k];
-      if (p.cm_on && i < T) s_vs[i] = vv[k];
-      if (i <= B) s_off[i] = ov[k];
-    }
-    if (tid < B) s_seq[tid] = sq;
+// A wave holds kWave / Lp requests at a time, Lp (the smallest power of two >= L) lanes each, a lane per row.
+struct WaveSegs {
+  int Lp, G, seg, j;
+  uint64_t mask;   // the lanes of this lane's request
+  __device__ __forceinline__ explicit WaveSegs(int L) {
+    const int lane = threadIdx.x & (kWave - 1);
+    Lp = 1 << (32 - __clz(L - 1));
+    G = kWave / Lp;
+    seg = lane / Lp;
+    j = lane - seg * Lp;
+    mask = (Lp == kWave ? ~0ull : (1ull << Lp) - 1) << (seg * Lp);
   }
-  __syncthreads();
+};
 
-  // ---- the scans: a wave per request, a lane per row (the rules of scan_chain_greedy) ----
-  for (int b = wv; b < B; b += kOneWaves) {
-    const int64_t o0 = s_off[b], o1 = s_off[b + 1];
-    if (!chain_offsets_ok(p, b, o0, o1)) {
-      if (lane == 0) {
+// The scans of the batch by NW waves, a request per segment of lanes (WaveSegs). Every request output is
+// written; s_r[b] takes the accepted length (-1: the request's offsets failed).
+template <int NW>
+__device__ __forceinline__ void greedy_chain_scans(const VerifyParams& p, const GreedyPart* pt, const int32_t* s_tok,
+                                                   const int32_t* s_off, int32_t* s_r) {
+  const int wv = threadIdx.x / kWave;
+  const int S = p.S;
+  const WaveSegs sg(p.L);
+  const int j = sg.j;
+  for (int b0 = wv * sg.G; b0 < p.B; b0 += NW * sg.G) {
+    const int b = b0 + sg.seg;
+    int64_t o0 = 0, o1 = 0;
+    bool act = false;
+    if (b < p.B) {
+      o0 = s_off[b];
+      o1 = s_off[b + 1];
+      act = chain_offsets_ok(p, b, o0, o1);
+      if (!act && j == 0) {
         write_bad_offsets(p, b);
         s_r[b] = -1;
       }
-      continue;
     }
-    const int len = int(o1 - o0);
+    const int len = act ? int(o1 - o0) : 0;
     const int m = len - 1;
     const int64_t dr0 = o0 - b;
-    const int j = lane;
     GreedyPart row{-INFINITY, INT32_MAX, 0u};
     uint32_t f = 0;
     int32_t d = -1;
     bool fails = false;
     if (j < len) {
-      const GreedyPart* rp = s_pt + (size_t(b) * p.L + j) * S;
-      row = rp[0];
+      const int base = (b * p.L + j) * S;
+      row = pt[base];
       for (int c = 1; c < S; ++c) {
-        const GreedyPart q = rp[c];
+        const GreedyPart q = pt[base + c];
         if (better(q.a, q.idx, row.a, row.idx)) {
           row.a = q.a;
           row.idx = q.idx;
@@ -642,17 +625,17 @@ __global__ __launch_bounds__(kOneThreads) void k_scan_one(VerifyParams p) {
         fails = !ok || d != row.idx;
       }
     }
-    const uint64_t fm = __ballot(fails);
-    const int r = fm ? min(__ffsll((unsigned long long)fm) - 1, m) : m;
-    const uint32_t fl = (__ballot(f & SPEC_ST_NONFINITE) ? uint32_t(SPEC_ST_NONFINITE) : 0u) |
-                        (__ballot(f & SPEC_ST_BAD_TOKEN) ? uint32_t(SPEC_ST_BAD_TOKEN) : 0u);
-    const int32_t bonus = __shfl(row.idx, r);
+    const uint64_t fm = __ballot(fails) & sg.mask;
+    const int r = fm ? min(__ffsll((unsigned long long)fm) - 1 - sg.seg * sg.Lp, m) : m;
+    const uint32_t fl = ((__ballot(f & SPEC_ST_NONFINITE) & sg.mask) ? uint32_t(SPEC_ST_NONFINITE) : 0u) |
+                        ((__ballot(f & SPEC_ST_BAD_TOKEN) & sg.mask) ? uint32_t(SPEC_ST_BAD_TOKEN) : 0u);
+    const int32_t bonus = __shfl(row.idx, sg.seg * sg.Lp + max(r, 0));
     if (j < len) {
       p.out_tokens[o0 + j] = j < r ? d : (j == r ? bonus : -1);
       p.accept_index[o0 + j] = j <= r ? int32_t(o0 + j) : -1;
     }
     if (p.accept_prob && j < m) p.accept_prob[dr0 + j] = -1.f;
-    if (lane == 0) {
+    if (act && j == 0) {
       p.accept_len[b] = r;
       p.bonus[b] = bonus;
       p.status[b] = fl;
@@ -660,12 +643,21 @@ __global__ __launch_bounds__(kOneThreads) void k_scan_one(VerifyParams p) {
       s_r[b] = r;
     }
   }
-  if (!p.cm_on) return;
-  __syncthreads();
+}
 
-  // ---- the commit lists: per request counts and their exclusive scan, then the rows ----
-  int32_t* s_co = reinterpret_cast<int32_t*>(s_pt);   // the partials are no longer needed
-  int32_t* s_eo = s_co + kOneMaxB;
+// The commit lists from LDS, by NTH threads (B <= NTH): per request counts and their exclusive scan (a thread
+// each), then the rows (a request per segment of lanes, as in the scans). s_co / s_eo take the per-request
+// list offsets; s_wsum holds a word per wave. The caller synchronises after the scans (s_r complete, and
+// s_co / s_eo may reuse their LDS).
+template <int NTH>
+__device__ __forceinline__ void greedy_chain_commit(const VerifyParams& p, const int32_t* s_off, const int32_t* s_seq,
+                                                    const int32_t* s_r, const int64_t* s_vs, int32_t* s_co,
+                                                    int32_t* s_eo, uint64_t* s_wsum) {
+  constexpr int NW = NTH / kWave;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wv = tid / kWave;
+  const int B = p.B;
   {
     const int b = tid;
     const bool has = b < B;
@@ -696,12 +688,14 @@ __global__ __launch_bounds__(kOneThreads) void k_scan_one(VerifyParams p) {
     }
   }
   __syncthreads();
-  for (int b = wv; b < B; b += kOneWaves) {
-    const int r = s_r[b];
+  const WaveSegs sg(p.L);
+  for (int b0 = wv * sg.G; b0 < B; b0 += NW * sg.G) {
+    const int b = b0 + sg.seg;
+    const int r = b < B ? s_r[b] : -1;
     if (r < 0) continue;
     const int64_t o0 = s_off[b];
     const int len = int(s_off[b + 1] - o0);
-    const int k = lane;
+    const int k = sg.j;
     if (k < len) {
       const int64_t v = s_vs[o0 + k];
       if (k <= r) {
@@ -712,6 +706,53 @@ __global__ __launch_bounds__(kOneThreads) void k_scan_one(VerifyParams p) {
       }
     }
   }
+}
+
+template <typename DT>
+__global__ __launch_bounds__(kOneThreads) void k_scan_one(VerifyParams p) {
+  __shared__ GreedyPart s_pt[kOneMaxParts];
+  __shared__ int32_t s_tok[kOneMaxRows];
+  __shared__ int64_t s_vs[kOneMaxRows];
+  __shared__ int32_t s_off[kOneMaxB + 1];
+  __shared__ int32_t s_seq[kOneMaxB];
+  __shared__ int32_t s_r[kOneMaxB];       // accepted drafts of request b, -1: its offsets failed
+  __shared__ uint64_t s_wsum[kOneWaves];
+  const int tid = threadIdx.x;
+  const int B = p.B;
+  const int64_t T = p.total_rows;
+  const int n_parts = B * p.L * p.S;   // the part area of request b starts at b * L * S (P = 1)
+
+  // ---- the load round: every load of this thread issued before any is used ----
+  {
+    Part pv[kOnePer];
+    int32_t tv[kOnePer], ov[kOnePer];
+    int64_t vv[kOnePer];
+#pragma unroll
+    for (int k = 0; k < kOnePer; ++k) {
+      const int i = tid + k * kOneThreads;
+      pv[k] = i < n_parts ? load_part(p.part + i, false) : Part{};
+      tv[k] = i < T - B ? p.draft_tokens[i] : 0;
+      vv[k] = p.cm_on && i < T ? p.verify_slots[i] : 0;
+      ov[k] = i <= B ? p.offsets[i] : 0;
+    }
+    const int32_t sq = p.cm_on && tid < B ? p.seq_lens[tid] : 0;
+#pragma unroll
+    for (int k = 0; k < kOnePer; ++k) {
+      const int i = tid + k * kOneThreads;
+      if (i < n_parts) s_pt[i] = GreedyPart{pv[k].a, pv[k].idx, pv[k].flags};
+      if (i < T - B) s_tok[i] = tv[k];
+      if (p.cm_on && i < T) s_vs[i] = vv[k];
+      if (i <= B) s_off[i] = ov[k];
+    }
+    if (tid < B) s_seq[tid] = sq;
+  }
+  __syncthreads();
+
+  greedy_chain_scans<kOneWaves>(p, s_pt, s_tok, s_off, s_r);
+  if (!p.cm_on) return;
+  __syncthreads();
+  int32_t* s_co = reinterpret_cast<int32_t*>(s_pt);   // the partials are no longer needed
+  greedy_chain_commit<kOneThreads>(p, s_off, s_seq, s_r, s_vs, s_co, s_co + kOneMaxB, s_wsum);
 }
 
 // Greedy trees of a small batch in one workgroup, the same way: partials, parents, tokens (and with a fused
