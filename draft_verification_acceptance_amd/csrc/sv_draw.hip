@@ -15,8 +15,9 @@
 //
 // Layout of the work: S2 workgroups per request take batches of 512-token segments of request b's row from
 // the request's counter until none is left; each wave reduces whole segments (8 consecutive tokens per lane,
-// 16-byte loads) and stores (sum w, sum p) per segment. The request's last workgroup takes a float64 prefix
-// over the segments, then rescans the single segment holding u * Z in float64, token by token. With a fused
+// 16-byte loads) and stores sum w per segment. The request's last workgroup takes a float64 prefix over the
+// segments (when the weights sum to 0 it first forms sum p per segment itself), then rescans the single
+// segment holding u * Z in float64, token by token. With a fused
 // KV commit each request has one more workgroup that only scans and counts the request for the commit.
 #include "sv_fused.h"
 
@@ -82,9 +83,12 @@ __device__ __forceinline__ void weights8(const RowCtx& r, int64_t e, int64_t V, 
   if (r.xq) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      pv[j] = exp2_fast(fmaf(x[j], r.coef, -r.m_t)) * r.inv_zt;
+      const float et = exp2_fast(fmaf(x[j], r.coef, -r.m_t));
       const float qv = exp2_fast(fmaf(y[j], r.coef, -r.m_q)) * r.inv_zq;
-      w[j] = fmaxf(pv[j] - qv, 0.f);
+      pv[j] = et * r.inv_zt;
+      // max(p - q, 0) with one rounding; p - q <= p <= 1, so clamping to [0, 1] is that max (one instruction
+      // with the multiply-add; NaN becomes 0 as in fmaxf)
+      w[j] = __builtin_amdgcn_fmed3f(fmaf(et, r.inv_zt, -qv), 0.f, 1.f);
     }
   } else {
     float adj[8];
@@ -263,12 +267,11 @@ __global__ __launch_bounds__(kThreads) void k_draw(VerifyParams p) {
     unpack_raw8<DT>(at, x);
     if (r.xq) unpack_raw8<DT>(aq, y);
     weights8(r, e, p.V, x, y, s_seen, s_seen_a, n_seen, w, pv);
-    float sw = 0.f, sp = 0.f;
+    float sw = 0.f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) { sw += w[j]; sp += pv[j]; }
+    for (int j = 0; j < 8; ++j) sw += w[j];
     sw = wave_sum_dpp(sw);   // the wave is whole here: s is the same in all of its lanes
-    sp = wave_sum_dpp(sp);
-    if (lane == 0) store_seg(p.seg + seg_base + s, sw, sp);
+    if (lane == 0) store_seg(p.seg + seg_base + s, sw, 0.f);   // (p's sums only if the weights sum to 0)
   };
   // Batches of p.bseg segments (whole trips): draw workgroup c starts with batch c, then takes batches S2, S2 + 1,
   // ... from the request's counter, which the logits stream of this call reset to 0; the next batch is asked for
@@ -351,6 +354,37 @@ __global__ __launch_bounds__(kThreads) void k_draw(VerifyParams p) {
   if (!(Z > 0.0)) {   // weights summed to zero: draw from p instead
     use_p = true;
     flags |= SPEC_ST_ZERO_RESIDUAL;
+    // The pass sums only the weights: this workgroup forms p's segment sums (the target row alone), a wave per
+    // segment, kTrip segments' loads at a time, and stores them beside the weights' sums.
+    RowCtx rp = r;
+    rp.xq = nullptr;
+    for (int t0 = wv; t0 < p.n_seg; t0 += kStep) {
+      Raw8 rt[kTrip];
+#pragma unroll
+      for (int u = 0; u < kTrip; ++u) {
+        const int s = t0 + u * kW;
+        if (s < p.n_seg) load_raw8<DT>(rp.xt, int64_t(s) * kSeg + 8 * lane, p.V, rp.vec, rt[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < kTrip; ++u) {
+        const int s = t0 + u * kW;
+        if (s >= p.n_seg) break;
+        float x[8], w[8], pv[8];
+        unpack_raw8<DT>(rt[u], x);
+        weights8(rp, int64_t(s) * kSeg + 8 * lane, p.V, x, x, s_seen, s_seen_a, 0, w, pv);
+        float sp = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) sp += pv[j];
+        sp = wave_sum_dpp(sp);
+        if (lane == 0) store_seg(p.seg + seg_base + s, 0.f, sp);
+      }
+    }
+    complete_memory_ops();
+    __syncthreads();
+    if (regs) {
+#pragma unroll
+      for (int k = 0; k < kSegRegs; ++k) sv[k] = r_lo + k < r_hi ? seg[r_lo + k] : make_float2(0.f, 0.f);
+    }
     double loc = 0.0;
     for_segs([&](int, float2 v) { loc += double(v.y); return false; });
     block_scan_d(loc, red_d, excl, incl, Z);

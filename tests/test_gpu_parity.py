@@ -141,6 +141,33 @@ def test_chain_sparse_random_corrupt_candidates(seed):
     compare_chain(w, "rejection_sparse", oracle_chain(w, "rejection_sparse"), run_chain(w, "rejection_sparse"))
 
 
+@pytest.mark.parametrize("V", [20011, 151936])
+def test_zero_residual_falls_back_to_p(V):
+    """A rejected row whose residual weights are all zero: request 0's first target row puts p = 0.2 on five
+    tokens spread over the vocabulary (every other logit -inf), and its sparse q lists those five
+    with mass 0.5 each, so the drafted one is rejected (alpha = 0.4 < u = 0.9) and [p - q]_+ = 0 everywhere.
+    The draw then falls back to p (ZERO_RESIDUAL), whose segment sums the drawing workgroup forms itself:
+    the token and residual_mass (the mass of p) equal the oracle's."""
+    w = W.chain_sparse(seed=6301, batch=4, vocab=V, K=8, temperature=0.8, bf16=False, parallel=False)
+    toks5 = np.array([3, V // 7, V // 2 + 1, V - 2000, V - 1], np.int32)
+    w.target[0, :] = -np.inf
+    w.target[0, toks5] = 0.0
+    ids, q = w.cand_ids.copy(), w.cand_q.copy()
+    ids[0, :5], q[0, :5] = toks5, 0.5
+    ids[0, 5:], q[0, 5:] = toks5[0], 0.0
+    w.cand_ids, w.cand_q = ids, q
+    w.draft_tokens[0] = toks5[2]
+    w.u_accept[0] = 0.9
+    for uf in (0.1, 0.5, 0.95):
+        w.u_final[0] = uf
+        _say("zero residual", V, uf)
+        o = oracle_chain(w, "rejection_sparse")
+        g = run_chain(w, "rejection_sparse")
+        assert o["status"][0] & oracle.ST_ZERO_RESIDUAL and g["status"][0] & oracle.ST_ZERO_RESIDUAL
+        assert g["accept_len"][0] == 0 and g["bonus"][0] == toks5[int(uf / 0.2)]
+        compare_chain(w, "rejection_sparse", o, g)
+
+
 # Full sizes, the benchmark's launch configuration; every request is compared with the oracle and the
 # flagged ones are exactly the oracle's count for the seeded workload.
 def test_full_chain_sparse():
