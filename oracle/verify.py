@@ -356,7 +356,8 @@ def _chain_request(out, b, target, offsets, draft_tokens, mode, draft, u_accept,
             # Every draft passed: bonus from the last row, m+1 new tokens ([EAGLE→DFlash2] §1.1).
             w = ps[m]
         if np.sum(w) == 0.0:
-            st |= ST_ZERO_RESIDUAL  # READING: undefined residual (only from rounding) -> draw from p
+            st |= ST_ZERO_RESIDUAL  # READING: an all-zero residual (rounding, or a sparse q whose masses reach p
+            #                         wherever p > 0) leaves the draw undefined -> draw from p
             w = ps[r]
         x, gap, resid = draw(w, uf)
         if near_cdf(gap, resid):
