@@ -738,6 +738,25 @@ def test_sparse_one_hot_equals_tree_target_only_on_a_chain():
             assert np.array_equal(osp[k], ot[k]), k
 
 
+def test_sparse_q_covering_p_draws_from_p():
+    # p = 1/4 on four tokens (all other logits -inf) and a sparse q of mass 1/2 on each of them: alpha = 1/2, and
+    # after a rejection [p - q]_+ is 0 everywhere, so the draw falls back to p (reading R6, ZERO_RESIDUAL): the
+    # token is the (floor(4 u) + 1)-th of the four, residual_mass p's total (1), accept_prob 1/2.
+    V, sup = 12, [1, 4, 7, 11]
+    t0 = np.full(V, -np.inf, np.float32)
+    t0[sup] = 0.0
+    t1 = np.zeros(V, np.float32)
+    for uf in (0.05, 0.3, 0.55, 0.99):
+        for u1, rejected in ((0.7, True), (0.2, False)):
+            o = chain_call_sparse([t0, t1], [sup], [[0.5] * 4], [sup[2]], [u1], uf, 1.0)
+            assert o["accept_prob"][0] == 0.5
+            if rejected:
+                assert o["accept_len"][0] == 0 and o["status"][0] & oracle.ST_ZERO_RESIDUAL
+                assert o["bonus"][0] == sup[int(4 * uf)] and o["residual_mass"][0] == 1.0
+            else:
+                assert o["accept_len"][0] == 1 and not o["status"][0] & oracle.ST_ZERO_RESIDUAL
+
+
 def sparse_mass_decomposition_error(seed=7, V=6, K=3, T=0.9):
     """One draft position with a K-candidate q: accept mass of v is min(p, q)(v), rejection mass
     [p - q]_+(v) (equal to p(v) off the candidates), and the two add up to p(v)."""
