@@ -181,6 +181,40 @@ def test_one_workgroup_greedy_chain_limits(batch, m_max):
     _check(g, w.offsets, w.max_verify_len, slots, seq)
 
 
+@pytest.mark.parametrize("batch,block", [(64, 16), (256, 4), (65, 16)])
+def test_sample_match_short_request_batches(batch, block):
+    """Sample-then-match batches of short requests (the split kernel: four rows per workgroup, each request
+    finished by its last workgroup, the commit by the last request): 64 x 16 and 65 x 16 rows, 256 requests of
+    4 rows. Verify outputs equal the oracle's, the fused commit the standalone commit."""
+    w = W.block_sample(seed=7061 + batch, batch=batch, block=block, vocab=4099, parallel=False)
+    print("sample_match", batch, block, w.total_rows, flush=True)
+    slots = np.random.default_rng(12).integers(0, 1 << 40, w.total_rows).astype(np.int64)
+    seq = np.random.default_rng(13).integers(0, 4096, w.batch).astype(np.int32)
+    g = np_out(dva.verify_chain(dev_logits(w.target), dev(w.offsets, torch.int32), dev(w.draft_tokens, torch.int32),
+                                "sample_match", verify_slots=dev(slots), seq_lens=dev(seq),
+                                **_chain_kw(w, "sample_match")))
+    compare_chain(w, "sample_match", oracle_chain(w, "sample_match"), g)
+    _check(g, w.offsets, w.max_verify_len, slots, seq)
+
+
+@pytest.mark.parametrize("max_len", [1, 2, 3, 5, 8, 9, 17, 33])
+def test_one_workgroup_greedy_chain_segments(max_len):
+    """The one-workgroup greedy path packs 64 / Lp requests into a wave (Lp: the smallest power of two >= the
+    longest request): ragged batches whose longest request is 1 .. 33 rows, so segments of 1 .. 64 lanes,
+    with requests shorter than their segment. Verify outputs equal the oracle's, the fused commit the
+    standalone commit."""
+    batch = min(1024, 2048 // max_len)
+    w = W.ragged(seed=5070 + max_len, batch=batch, m_max=max_len - 1, vocab=61, parallel=False)
+    assert w.max_verify_len == max_len and w.total_rows <= 2048
+    print("one-workgroup greedy chain segments", batch, max_len, w.total_rows, flush=True)
+    slots = np.random.default_rng(14).integers(0, 1 << 40, w.total_rows).astype(np.int64)
+    seq = np.random.default_rng(15).integers(0, 4096, w.batch).astype(np.int32)
+    g = np_out(dva.verify_chain(dev_logits(w.target), dev(w.offsets, torch.int32), dev(w.draft_tokens, torch.int32),
+                                "greedy", verify_slots=dev(slots), seq_lens=dev(seq), **_chain_kw(w, "greedy")))
+    assert compare_chain(w, "greedy", oracle_chain(w, "greedy"), g) == 0
+    _check(g, w.offsets, w.max_verify_len, slots, seq)
+
+
 @pytest.mark.parametrize("batch,n_nodes", [(1024, 2), (32, 64), (33, 62)])
 def test_one_workgroup_greedy_tree_limits(batch, n_nodes):
     """Greedy tree batches at the one-workgroup path's limits (2048 nodes; trees of 64 nodes)."""
