@@ -837,11 +837,14 @@ __global__ __launch_bounds__(kOneThreads) void k_tree_one(VerifyParams p) {
         tok = tok_ok ? t : -1;
       }
     }
+    // Node i may follow its parent on the path iff its token is the parent's argmax: one shuffle for every
+    // node at once, so each step of the walk is a compare and a ballot (no shuffle on the chain of steps).
+    const int32_t want = __shfl(arg, par < 0 ? 0 : par);
+    const uint64_t ok = __ballot(i < N && par >= 0 && tok == want);
     uint64_t path = 1;   // node 0, the root
     int cur = 0, r = 0;
     while (true) {
-      const int32_t want = __shfl(arg, cur);
-      const uint64_t hit = __ballot(i < N && i > cur && par == cur && tok == want);
+      const uint64_t hit = __ballot(par == cur) & ok;   // children of cur (par < i: all past cur) that match
       if (!hit) break;
       cur = __ffsll((unsigned long long)hit) - 1;
       path |= 1ull << cur;
