@@ -548,13 +548,17 @@ __global__ __launch_bounds__(kThreads) void k_scan(VerifyParams p) {
 // and the commit lists follow from LDS, with no hand-off between workgroups. The outputs are those of k_scan
 // and its fused commit.
 // ---------------------------------------------------------------------------------------------------
-constexpr int kOneThreads = 1024;
+#ifndef SV_ONE_THREADS
+#define SV_ONE_THREADS 1024               // threads of k_scan_one / k_tree_one
+#endif
+constexpr int kOneThreads = SV_ONE_THREADS;
 constexpr int kOneWaves = kOneThreads / kWave;
 constexpr int kOneMaxB = kOneThreads;   // requests (a thread each in the commit's scan)
 constexpr int kOneMaxParts = 2048;      // B * L * S row partials
 constexpr int kOneMaxRows = 2048;       // verify rows of the batch
 constexpr int kOneMaxLen = kWave;       // rows per request (a lane each)
-constexpr int kOnePer = 2;              // loads per thread and array in the load round
+constexpr int kOnePer = kOneMaxParts / kOneThreads;   // loads per thread and array in the load round
+static_assert(kOneMaxRows == kOneMaxParts, "one load loop covers partials and rows");
 
 struct GreedyPart {   // the greedy fields of a row partial
   float a;
