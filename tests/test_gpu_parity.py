@@ -340,6 +340,39 @@ def test_ragged_lengths_including_zero_drafts():
         assert np.all(g["accept_len"][lens == 1] == 0)
 
 
+@pytest.mark.parametrize("seed", range(8))
+def test_random_shapes_match_the_oracle(seed):
+    """Seeded random batch shapes across the launch paths (one-workgroup and per-request scans, split and
+    whole-request matches, draw workgroup counts): 1..300 requests of 1..40 rows (ragged), vocab 1..5000
+    (fewer for large batches), fp32 or bf16 logits, temperature 0.3..1.5, every chain mode (the sparse q: the
+    draft row's top 1..8 tokens with their softmax mass). Every request is compared with the oracle."""
+    rng = np.random.default_rng(900 + seed)
+    B = int(rng.integers(1, 301))
+    L = int(rng.integers(1, 41))
+    lens = rng.integers(1, L + 1, B)
+    offs = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T, D = int(offs[-1]), int(offs[-1]) - B
+    V = int(max(1, min(int(rng.integers(1, 5001)), 12_000_000 // (2 * T))))
+    temp = float(rng.uniform(0.3, 1.5))
+    tl = (rng.normal(0, 2, (T, V)) * rng.uniform(0.5, 2.0)).astype(np.float32)
+    rows = np.concatenate([np.arange(offs[b], offs[b + 1] - 1) for b in range(B)]).astype(np.int64)
+    dl = (tl[rows] + rng.normal(0, 0.8, (D, V))).astype(np.float32)
+    toks = np.where(rng.random(D) < 0.6, np.argmax(tl[rows], axis=1) if D else 0,
+                    rng.integers(0, V, D)).astype(np.int32)
+    w = _chain_from(tl, dl, offs, toks, rng.random(D), rng.random(B), temp, L)
+    K = int(rng.integers(1, 9))
+    ids = np.stack([W.top_candidates(x, min(K, V)) for x in dl]) if D else np.zeros((0, min(K, V)), np.int32)
+    q = np.exp((dl[np.arange(D)[:, None], ids] - dl.max(axis=1, keepdims=True)) / temp) if D else np.zeros(ids.shape)
+    w.cand_ids, w.cand_q = ids.astype(np.int32), (q / np.maximum(q.sum(axis=1, keepdims=True), 1e-30)).astype(np.float32)
+    bf16 = bool(rng.integers(0, 2))
+    if bf16:
+        w = _chain_from(W.bf16_bits(tl), W.bf16_bits(dl), offs, toks, w.u_accept, w.u_final, temp, L)
+        w.cand_ids, w.cand_q = ids.astype(np.int32), (q / np.maximum(q.sum(axis=1, keepdims=True), 1e-30)).astype(np.float32)
+    for mode in ("greedy", "rejection", "rejection_sparse", "sample_match"):
+        _say("random shape", seed, B, L, T, V, round(temp, 2), "bf16" if bf16 else "fp32", mode)
+        compare_chain(w, mode, oracle_chain(w, mode), run_chain(w, mode))
+
+
 def test_masked_logits_ties_and_special_rows():
     rng = np.random.default_rng(11)
     V, B, m = 700, 12, 4
