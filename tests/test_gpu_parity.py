@@ -564,6 +564,33 @@ def test_random_tree_faults_match_the_oracle(seed):
         compare_tree(tw, mode, oracle_tree(tw, mode), run_tree(tw, mode))
 
 
+@pytest.mark.parametrize("seed", range(6))
+def test_random_tree_shapes_match_the_oracle(seed):
+    """Seeded random tree batches across the launch paths (one-workgroup walks, per-request scans, draw
+    workgroup counts): 1..200 trees of 1..100 nodes (parents uniform over the earlier nodes, each token the
+    parent's argmax with probability 0.6, else uniform), vocab 1..5000 (fewer for large batches), fp32 or
+    bf16 logits, temperature 0.3..1.5; greedy and target-only, every tree compared with the oracle."""
+    rng = np.random.default_rng(950 + seed)
+    B = int(rng.integers(1, 201))
+    N = int(rng.integers(1, 101))
+    V = int(max(1, min(int(rng.integers(1, 5001)), 8_000_000 // (B * N))))
+    target = (rng.normal(0, 2, (B * N, V)) * rng.uniform(0.5, 2.0)).astype(np.float32)
+    parents = np.full(B * N, -1, np.int32)
+    tokens = np.zeros(B * N, np.int32)
+    for b in range(B):
+        for i in range(1, N):
+            par = int(rng.integers(0, i))
+            parents[b * N + i] = par
+            tokens[b * N + i] = int(np.argmax(target[b * N + par])) if rng.random() < 0.6 else int(rng.integers(V))
+    if rng.integers(0, 2):
+        target = W.bf16_bits(target)
+    tw = W.TreeWorkload("random tree", V, B, N, target, parents, tokens, rng.random(B * N).astype(np.float32),
+                        rng.random(B).astype(np.float32), float(rng.uniform(0.3, 1.5)))
+    for mode in ("greedy", "target_only"):
+        _say("random tree shape", seed, B, N, V, target.dtype, mode)
+        compare_tree(tw, mode, oracle_tree(tw, mode), run_tree(tw, mode))
+
+
 def test_chain_shaped_tree_matches_chain_on_gpu():
     w = W.block_greedy(seed=3003, batch=16, vocab=5003, parallel=False)
     N = 16
