@@ -198,14 +198,16 @@ __global__ __launch_bounds__(kThreads) void k_draw(VerifyParams p) {
   // while the memory system is busy with the draws (each of its loads then waits long): in a workgroup without
   // draw work that delays no draw. The scan-only workgroups come first in the grid (b = blockIdx): they start
   // at once, and they leave early, so draw workgroups that did not fit beside them start soon after.
-  // Draw workgroup c of request b has index c * B + b: a request's workgroups are spread over the dispatch
-  // order. Waves are served oldest first, so the earlier workgroups stream faster; taking the segments in
-  // batches from a counter lets them take more, and every request ends at about the same time.
+  // Draw workgroup c of request b has index c * B + b for even c and c * B + (B - 1 - b) for odd c: a
+  // request's workgroups are spread over the dispatch order, early and late places paired. Waves are served
+  // oldest first, so the earlier workgroups stream faster; taking the segments in batches from a counter lets
+  // them take more, and every request ends at about the same time (with two workgroups per request the pairing
+  // evens out what the counter cannot move between requests).
   const int lead = p.cm_on ? 1 : 0;
   const bool scan_only = lead && int(blockIdx.x) < p.B;
   const int dw = int(blockIdx.x) - lead * p.B;   // draw workgroup index
-  const int b = scan_only ? int(blockIdx.x) : dw % p.B;
   const int c = scan_only ? -1 : dw / p.B;
+  const int b = scan_only ? int(blockIdx.x) : ((c & 1) ? p.B - 1 - dw % p.B : dw % p.B);
   const bool writes = lead ? scan_only : c == 0;   // the workgroup that writes the scan's outputs
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
