@@ -221,6 +221,9 @@ __global__ __launch_bounds__(kThreads) void k_draw(VerifyParams p) {
   // entry: a tree's tried tokens are fewer than its nodes, a sparse row has K candidates).
   int32_t* s_seen = reinterpret_cast<int32_t*>(smem + scan_smem_bytes(TREE, true, p.L, p.P, p.S));
   float* s_seen_a = reinterpret_cast<float*>(s_seen + adjust_cap<TREE, SPARSE>(p));
+  // Sparse q: the drawn row's whole candidate list, copied from global memory once (after the filtered list).
+  int32_t* s_cand = reinterpret_cast<int32_t*>(s_seen_a + adjust_cap<TREE, SPARSE>(p));
+  float* s_cand_a = reinterpret_cast<float*>(s_cand + adjust_cap<TREE, SPARSE>(p));
   DrawPlan d;
   if (TREE) {
     d = scan_tree<DT, true>(p, b, rows, stage, writes);
@@ -252,9 +255,20 @@ __global__ __launch_bounds__(kThreads) void k_draw(VerifyParams p) {
 
   // The adjustment list: the sparse candidates of the draft row, or the tokens the tree walk tried (LDS).
   const bool sparse = SPARSE && d.row_q >= 0;
-  const int32_t* adj_ids = sparse ? p.cand_ids + int64_t(d.row_q) * p.K : d.seen;
-  const float* adj_a = sparse ? p.cand_q + int64_t(d.row_q) * p.K : nullptr;
+  const int32_t* adj_ids = d.seen;
+  const float* adj_a = nullptr;
   const int n_adj = sparse ? p.K : (TREE ? d.n_seen : 0);   // dense rejection: none (known at compile time)
+  if (sparse) {   // uniform in the workgroup: every batch and the final search filter the list from LDS
+    const int32_t* g_ids = p.cand_ids + int64_t(d.row_q) * p.K;
+    const float* g_a = p.cand_q + int64_t(d.row_q) * p.K;
+    for (int i = tid; i < p.K; i += kThreads) {
+      s_cand[i] = g_ids[i];
+      s_cand_a[i] = g_a[i];
+    }
+    __syncthreads();
+    adj_ids = s_cand;
+    adj_a = s_cand_a;
+  }
 
   // Lane l of a wave owns tokens [s*512 + 8l, s*512 + 8l + 8) of segment s; wave w takes segments
   // s_begin + w, s_begin + w + kW, ... A trip covers kTrip segments per wave with all of their loads issued
@@ -505,9 +519,9 @@ hipError_t launch_draw_t(int mode, const VerifyParams& p, hipStream_t stream, hi
   if (p.tree)
     return launch_kernel(k_draw<DT, true, false>, grid, block, smem + adj * adjust_cap<true, false>(p), stream, ev0,
                          ev1, p);
-  if (mode == SPEC_MODE_REJECTION_SPARSE)
-    return launch_kernel(k_draw<DT, false, true>, grid, block, smem + adj * adjust_cap<false, true>(p), stream, ev0,
-                         ev1, p);
+  if (mode == SPEC_MODE_REJECTION_SPARSE)   // the filtered list and the whole candidate list
+    return launch_kernel(k_draw<DT, false, true>, grid, block, smem + 2 * adj * adjust_cap<false, true>(p), stream,
+                         ev0, ev1, p);
   return launch_kernel(k_draw<DT, false, false>, grid, block, smem, stream, ev0, ev1, p);
 }
 
