@@ -70,14 +70,21 @@ __device__ __forceinline__ void unpack_raw8(const Raw8& w, float* x) {
   if (sizeof(DT) == 4) Elem<DT>::unpack(w.b, x + 4);
 }
 
-// Weights of tokens [e, e+8) from their logits: w (residual [p - q]_+ from a draft row, or [p - a]_+ with
-// the adjustment list (seen, seen_a)) and p. The same arithmetic serves the segment sums and the
-// token-by-token search, so both see identical values.
-__device__ __forceinline__ void weights8(const RowCtx& r, int64_t e, int64_t V, const float* x_in, const float* y,
-                                         const int32_t* seen, const float* seen_a, int n_seen, float* w,
-                                         float* pv) {
+// Vocab mask bits of tokens [e, e + 8) of the target row (e % 8 == 0, so they lie in one word; bit j = token
+// e + j), all ones without a mask. One load, its word index clamped into the row (bits past V are not used),
+// so it can be issued together with the logits' loads.
+__device__ __forceinline__ uint32_t row_mask8(const RowCtx& r, int64_t e) {
+  if (!r.mt) return ~0u;
+  return r.mt[min(e >> 5, r.mw - 1)] >> uint32_t(e & 31);
+}
+
+// Weights of tokens [e, e+8) from their logits and mask bits mb (row_mask8): w (residual [p - q]_+ from a
+// draft row, or [p - a]_+ with the adjustment list (seen, seen_a)) and p. The same arithmetic serves the
+// segment sums and the token-by-token search, so both see identical values.
+__device__ __forceinline__ void weights8(const RowCtx& r, int64_t e, int64_t V, uint32_t mb, const float* x_in,
+                                         const float* y, const int32_t* seen, const float* seen_a, int n_seen,
+                                         float* w, float* pv) {
   float x[8];   // the target logits, disallowed ones (vocab mask) at -inf
-  const uint32_t mb = r.mt && e < V ? mask_bits8(r.mt, e, r.mw) : ~0u;
 #pragma unroll
   for (int j = 0; j < 8; ++j) x[j] = (mb >> j) & 1u ? x_in[j] : -INFINITY;
   if (r.xq) {
@@ -119,10 +126,11 @@ __device__ __forceinline__ void load_weights8(const RowCtx& r, int64_t e, int64_
   Raw8 rt, rq;
   load_raw8<DT>(r.xt, e, V, r.vec, rt);
   if (r.xq) load_raw8<DT>(r.xq, e, V, r.vec, rq);
+  const uint32_t mb = row_mask8(r, e);
   float x[8], y[8];
   unpack_raw8<DT>(rt, x);
   if (r.xq) unpack_raw8<DT>(rq, y);
-  weights8(r, e, V, x, y, seen, seen_a, n_seen, w, pv);
+  weights8(r, e, V, mb, x, y, seen, seen_a, n_seen, w, pv);
 }
 
 // The adjustment list entries whose token lies in [lo, hi), copied to LDS in list order (ids outside the
@@ -277,12 +285,12 @@ __global__ __launch_bounds__(kThreads) void k_draw(VerifyParams p) {
   constexpr int kTrip = SV_DRAW_TRIP;
   constexpr int kStep = kTrip * kW;
   const int64_t seg_base = int64_t(b) * p.n_seg;
-  auto reduce_seg = [&](const Raw8& at, const Raw8& aq, int s, int n_seen) {
+  auto reduce_seg = [&](const Raw8& at, const Raw8& aq, uint32_t mb, int s, int n_seen) {
     const int64_t e = int64_t(s) * kSeg + 8 * lane;
     float x[8], y[8], w[8], pv[8];
     unpack_raw8<DT>(at, x);
     if (r.xq) unpack_raw8<DT>(aq, y);
-    weights8(r, e, p.V, x, y, s_seen, s_seen_a, n_seen, w, pv);
+    weights8(r, e, p.V, mb, x, y, s_seen, s_seen_a, n_seen, w, pv);
     float sw = 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) sw += w[j];
@@ -305,12 +313,15 @@ __global__ __launch_bounds__(kThreads) void k_draw(VerifyParams p) {
     int ask = 0;
     for (int t0 = s_begin + wv; t0 < s_end; t0 += kStep) {
       Raw8 rt[kTrip], rq[kTrip];
+      uint32_t mk[kTrip];
 #pragma unroll
       for (int u = 0; u < kTrip; ++u) {
         const int s = t0 + u * kW;
+        mk[u] = ~0u;
         if (s < s_end) {
           load_raw8<DT>(r.xt, int64_t(s) * kSeg + 8 * lane, p.V, r.vec, rt[u]);
           if (r.xq) load_raw8<DT>(r.xq, int64_t(s) * kSeg + 8 * lane, p.V, r.vec, rq[u]);
+          mk[u] = row_mask8(r, int64_t(s) * kSeg + 8 * lane);
         }
       }
       if (t0 == s_begin && tid == 0) ask = p.S2 + int(atomicAdd(next_batch, 1ull));   // behind this trip's loads
@@ -318,7 +329,7 @@ __global__ __launch_bounds__(kThreads) void k_draw(VerifyParams p) {
       for (int u = 0; u < kTrip; ++u) {
         const int s = t0 + u * kW;
         if (s >= s_end) break;
-        reduce_seg(rt[u], rq[u], s, n_seen);
+        reduce_seg(rt[u], rq[u], mk[u], s, n_seen);
       }
     }
     __syncthreads();   // every wave is past this batch's adjustment list and s_batch
@@ -376,10 +387,15 @@ __global__ __launch_bounds__(kThreads) void k_draw(VerifyParams p) {
     rp.xq = nullptr;
     for (int t0 = wv; t0 < p.n_seg; t0 += kStep) {
       Raw8 rt[kTrip];
+      uint32_t mk[kTrip];
 #pragma unroll
       for (int u = 0; u < kTrip; ++u) {
         const int s = t0 + u * kW;
-        if (s < p.n_seg) load_raw8<DT>(rp.xt, int64_t(s) * kSeg + 8 * lane, p.V, rp.vec, rt[u]);
+        mk[u] = ~0u;
+        if (s < p.n_seg) {
+          load_raw8<DT>(rp.xt, int64_t(s) * kSeg + 8 * lane, p.V, rp.vec, rt[u]);
+          mk[u] = row_mask8(rp, int64_t(s) * kSeg + 8 * lane);
+        }
       }
 #pragma unroll
       for (int u = 0; u < kTrip; ++u) {
@@ -387,7 +403,7 @@ __global__ __launch_bounds__(kThreads) void k_draw(VerifyParams p) {
         if (s >= p.n_seg) break;
         float x[8], w[8], pv[8];
         unpack_raw8<DT>(rt[u], x);
-        weights8(rp, int64_t(s) * kSeg + 8 * lane, p.V, x, x, s_seen, s_seen_a, 0, w, pv);
+        weights8(rp, int64_t(s) * kSeg + 8 * lane, p.V, mk[u], x, x, s_seen, s_seen_a, 0, w, pv);
         float sp = 0.f;
 #pragma unroll
         for (int j = 0; j < 8; ++j) sp += pv[j];
