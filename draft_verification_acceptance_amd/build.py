@@ -20,6 +20,12 @@ HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
              "-I", INCLUDE, "-I", CSRC]
 
 
+# Per-file additions. sv_draw.hip: no atomic optimizer. It turns a one-lane atomic into a wave-wide one whose
+# result is read into a scalar at once, which makes the wave wait for every load it has in flight; the draw
+# claims its next batch of segments that way behind a trip's loads and uses the answer only at the batch's end.
+FILE_FLAGS = {"sv_draw.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]}
+
+
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
@@ -64,7 +70,7 @@ def build(verbose: bool = False, extra_flags: list[str] | None = None, sanitize:
     for src in SOURCES:
         obj = os.path.join(build_dir, src.replace(".hip", ".o"))
         objs.append(obj)
-        cmd = [cc, *flags, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [cc, *flags, *FILE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))

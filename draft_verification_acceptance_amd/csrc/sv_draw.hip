@@ -70,21 +70,24 @@ __device__ __forceinline__ void unpack_raw8(const Raw8& w, float* x) {
   if (sizeof(DT) == 4) Elem<DT>::unpack(w.b, x + 4);
 }
 
-// Vocab mask bits of tokens [e, e + 8) of the target row (e % 8 == 0, so they lie in one word; bit j = token
-// e + j), all ones without a mask. One load, its word index clamped into the row (bits past V are not used),
-// so it can be issued together with the logits' loads.
-__device__ __forceinline__ uint32_t row_mask8(const RowCtx& r, int64_t e) {
-  if (!r.mt) return ~0u;
-  return r.mt[min(e >> 5, r.mw - 1)] >> uint32_t(e & 31);
+// The vocab mask word holding tokens [e, e + 8) of the target row (e % 8 == 0, so they lie in one word), all
+// ones without a mask (always so when MASK is false). One load, its word index clamped into the row (bits past
+// V are not used), issued with the logits' loads; the shift to token e happens where the bits are used
+// (weights8), so that nothing waits for the load before then.
+template <bool MASK>
+__device__ __forceinline__ uint32_t row_mask_word(const RowCtx& r, int64_t e) {
+  if (!MASK) return ~0u;
+  return r.mt ? r.mt[min(e >> 5, r.mw - 1)] : ~0u;
 }
 
-// Weights of tokens [e, e+8) from their logits and mask bits mb (row_mask8): w (residual [p - q]_+ from a
-// draft row, or [p - a]_+ with the adjustment list (seen, seen_a)) and p. The same arithmetic serves the
+// Weights of tokens [e, e+8) from their logits and mask word mw8 (row_mask_word): w (residual [p - q]_+ from
+// a draft row, or [p - a]_+ with the adjustment list (seen, seen_a)) and p. The same arithmetic serves the
 // segment sums and the token-by-token search, so both see identical values.
-__device__ __forceinline__ void weights8(const RowCtx& r, int64_t e, int64_t V, uint32_t mb, const float* x_in,
+__device__ __forceinline__ void weights8(const RowCtx& r, int64_t e, int64_t V, uint32_t mw8, const float* x_in,
                                          const float* y, const int32_t* seen, const float* seen_a, int n_seen,
                                          float* w, float* pv) {
   float x[8];   // the target logits, disallowed ones (vocab mask) at -inf
+  const uint32_t mb = mw8 >> uint32_t(e & 31);   // bit j = token e + j
 #pragma unroll
   for (int j = 0; j < 8; ++j) x[j] = (mb >> j) & 1u ? x_in[j] : -INFINITY;
   if (r.xq) {
@@ -120,13 +123,13 @@ __device__ __forceinline__ void weights8(const RowCtx& r, int64_t e, int64_t V, 
     if (e + j >= V) { w[j] = 0.f; pv[j] = 0.f; }
 }
 
-template <typename DT>
+template <typename DT, bool MASK>
 __device__ __forceinline__ void load_weights8(const RowCtx& r, int64_t e, int64_t V, const int32_t* seen,
                                               const float* seen_a, int n_seen, float* w, float* pv) {
   Raw8 rt, rq;
   load_raw8<DT>(r.xt, e, V, r.vec, rt);
   if (r.xq) load_raw8<DT>(r.xq, e, V, r.vec, rq);
-  const uint32_t mb = row_mask8(r, e);
+  const uint32_t mb = row_mask_word<MASK>(r, e);
   float x[8], y[8];
   unpack_raw8<DT>(rt, x);
   if (r.xq) unpack_raw8<DT>(rq, y);
@@ -190,7 +193,7 @@ __host__ __device__ __forceinline__ int adjust_cap(const VerifyParams& p) {
   return TREE ? p.L : (SPARSE ? p.K : 0);
 }
 
-template <typename DT, bool TREE, bool SPARSE>
+template <typename DT, bool TREE, bool SPARSE, bool MASK>
 __global__ __launch_bounds__(kThreads) void k_draw(VerifyParams p) {
   extern __shared__ __align__(16) char smem[];
   __shared__ int s_wcnt[kThreads / kWave];
@@ -252,7 +255,7 @@ __global__ __launch_bounds__(kThreads) void k_draw(VerifyParams p) {
   RowCtx r;
   r.xt = static_cast<const DT*>(p.target) + int64_t(d.row_t) * p.V;
   r.xq = d.row_q >= 0 && p.draft ? static_cast<const DT*>(p.draft) + int64_t(d.row_q) * p.V : nullptr;
-  r.mt = p.mask ? p.mask + int64_t(d.row_t) * p.mask_words : nullptr;
+  r.mt = MASK && p.mask ? p.mask + int64_t(d.row_t) * p.mask_words : nullptr;
   r.mw = p.mask_words;
   r.coef = p.coef;
   r.m_t = d.m_t;
@@ -310,7 +313,9 @@ __global__ __launch_bounds__(kThreads) void k_draw(VerifyParams p) {
     const int n_seen = n_adj ? collect_adjust(adj_ids, adj_a, n_adj, int64_t(s_begin) * kSeg,
                                               int64_t(s_end) * kSeg, s_seen, s_seen_a, s_wcnt)
                              : 0;
-    int ask = 0;
+    // The claim of the next batch: its atomic goes out behind the first trip's loads, and nothing uses its
+    // result before the end of the batch (an add or a lane read of it here would wait for every load in flight).
+    unsigned long long claim = 0ull;
     for (int t0 = s_begin + wv; t0 < s_end; t0 += kStep) {
       Raw8 rt[kTrip], rq[kTrip];
       uint32_t mk[kTrip];
@@ -321,10 +326,10 @@ __global__ __launch_bounds__(kThreads) void k_draw(VerifyParams p) {
         if (s < s_end) {
           load_raw8<DT>(r.xt, int64_t(s) * kSeg + 8 * lane, p.V, r.vec, rt[u]);
           if (r.xq) load_raw8<DT>(r.xq, int64_t(s) * kSeg + 8 * lane, p.V, r.vec, rq[u]);
-          mk[u] = row_mask8(r, int64_t(s) * kSeg + 8 * lane);
+          mk[u] = row_mask_word<MASK>(r, int64_t(s) * kSeg + 8 * lane);
         }
       }
-      if (t0 == s_begin && tid == 0) ask = p.S2 + int(atomicAdd(next_batch, 1ull));   // behind this trip's loads
+      if (t0 == s_begin && tid == 0) claim = atomicAdd(next_batch, 1ull);
 #pragma unroll
       for (int u = 0; u < kTrip; ++u) {
         const int s = t0 + u * kW;
@@ -333,7 +338,7 @@ __global__ __launch_bounds__(kThreads) void k_draw(VerifyParams p) {
       }
     }
     __syncthreads();   // every wave is past this batch's adjustment list and s_batch
-    if (tid == 0) s_batch = ask;
+    if (tid == 0) s_batch = p.S2 + int(claim);
     __syncthreads();
     batch = s_batch;
   }
@@ -394,7 +399,7 @@ __global__ __launch_bounds__(kThreads) void k_draw(VerifyParams p) {
         mk[u] = ~0u;
         if (s < p.n_seg) {
           load_raw8<DT>(rp.xt, int64_t(s) * kSeg + 8 * lane, p.V, rp.vec, rt[u]);
-          mk[u] = row_mask8(rp, int64_t(s) * kSeg + 8 * lane);
+          mk[u] = row_mask_word<MASK>(rp, int64_t(s) * kSeg + 8 * lane);
         }
       }
 #pragma unroll
@@ -467,7 +472,7 @@ __global__ __launch_bounds__(kThreads) void k_draw(VerifyParams p) {
   if (tid < kWave) {
     // Token by token in float64, ascending: lane l holds tokens g_lo + 8l .. g_lo + 8l + 7.
     float w[8], pv[8];
-    load_weights8<DT>(r, g_lo + 8 * lane, p.V, s_seen, s_seen_a, use_p ? 0 : n_sel, w, pv);
+    load_weights8<DT, MASK>(r, g_lo + 8 * lane, p.V, s_seen, s_seen_a, use_p ? 0 : n_sel, w, pv);
     double inc[8];
     double run = 0.0;
 #pragma unroll
@@ -525,20 +530,32 @@ __global__ __launch_bounds__(kThreads) void k_draw(VerifyParams p) {
   }
 }
 
+// Chains: the maskless calls run an instantiation with no mask code at all (MASK false); masked calls and every
+// tree call run the one that reads the mask row when there is one (MASK true, checked at run time). The tree
+// kernel is kept on the latter: the maskless build of it measured 0.6 µs slower on the 64-node tree workload.
+template <typename DT, bool MASK>
+hipError_t launch_chain_draw(int mode, const VerifyParams& p, size_t smem, dim3 grid, dim3 block, hipStream_t stream,
+                             hipEvent_t ev0, hipEvent_t ev1) {
+  const size_t adj = sizeof(int32_t) + sizeof(float);   // per adjustment list entry
+  if (mode == SPEC_MODE_REJECTION_SPARSE)   // the filtered list and the whole candidate list
+    return launch_kernel(k_draw<DT, false, true, MASK>, grid, block, smem + 2 * adj * adjust_cap<false, true>(p),
+                         stream, ev0, ev1, p);
+  return launch_kernel(k_draw<DT, false, false, MASK>, grid, block, smem, stream, ev0, ev1, p);
+}
+
 template <typename DT>
 hipError_t launch_draw_t(int mode, const VerifyParams& p, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
   const int64_t blocks = int64_t(p.B) * (p.S2 + (p.cm_on ? 1 : 0));
   if (blocks <= 0) return hipSuccess;
   const size_t smem = scan_smem_bytes(p.tree != 0, true, p.L, p.P, p.S);
-  const size_t adj = sizeof(int32_t) + sizeof(float);   // per adjustment list entry
   const dim3 grid{unsigned(blocks)}, block{unsigned(kThreads)};
-  if (p.tree)
-    return launch_kernel(k_draw<DT, true, false>, grid, block, smem + adj * adjust_cap<true, false>(p), stream, ev0,
-                         ev1, p);
-  if (mode == SPEC_MODE_REJECTION_SPARSE)   // the filtered list and the whole candidate list
-    return launch_kernel(k_draw<DT, false, true>, grid, block, smem + 2 * adj * adjust_cap<false, true>(p), stream,
+  if (p.tree) {
+    const size_t adj = sizeof(int32_t) + sizeof(float);
+    return launch_kernel(k_draw<DT, true, false, true>, grid, block, smem + adj * adjust_cap<true, false>(p), stream,
                          ev0, ev1, p);
-  return launch_kernel(k_draw<DT, false, false>, grid, block, smem, stream, ev0, ev1, p);
+  }
+  if (p.mask) return launch_chain_draw<DT, true>(mode, p, smem, grid, block, stream, ev0, ev1);
+  return launch_chain_draw<DT, false>(mode, p, smem, grid, block, stream, ev0, ev1);
 }
 
 }  // namespace
