@@ -3,7 +3,12 @@
 Sizes: every workload at a reduced vocabulary that still spans several chunks per row and an unaligned
 ragged tail, then at full size in the launch configuration the benchmark times; every request is compared
 at both sizes. Edge cases and statistics follow.
+
+SPECVERIFY_FUZZ_SEEDS=n widens the seeded random tests (random shapes, random trees, fault injection, corrupt
+candidate lists) by n more seeds each, for a longer sweep than the default run.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -21,6 +26,9 @@ pytestmark = pytest.mark.gpu
 
 def _say(*a):
     print(*a, flush=True)
+
+
+_FUZZ = range(100, 100 + int(os.environ.get("SPECVERIFY_FUZZ_SEEDS", "0")))   # extra seeds of the random tests
 
 
 # ----------------------------------------------------------------------------------------------------
@@ -109,7 +117,7 @@ def test_chain_sparse_fp32_and_ragged():
     compare_chain(w, "rejection_sparse", o, g)
 
 
-@pytest.mark.parametrize("seed", [61, 62])
+@pytest.mark.parametrize("seed", [61, 62, *(1000 + s for s in _FUZZ)])
 def test_chain_sparse_random_corrupt_candidates(seed):
     """Seeded corruption of sparse candidate lists (ragged fp32 chains): ids outside [0, V), duplicated ids
     (the drafted token's among them), masses that are negative, NaN, infinite or sum past 1, a row whose
@@ -340,7 +348,7 @@ def test_ragged_lengths_including_zero_drafts():
         assert np.all(g["accept_len"][lens == 1] == 0)
 
 
-@pytest.mark.parametrize("seed", range(8))
+@pytest.mark.parametrize("seed", [*range(8), *_FUZZ])
 def test_random_shapes_match_the_oracle(seed):
     """Seeded random batch shapes across the launch paths (one-workgroup and per-request scans, split and
     whole-request matches, draw workgroup counts): 1..300 requests of 1..40 rows (ragged), vocab 1..5000
@@ -433,7 +441,8 @@ def test_status_bits_nan_bad_token_bad_uniform_bad_offsets():
     assert g["status"][2] & oracle.ST_BAD_OFFSETS
 
 
-@pytest.mark.parametrize("seed,max_len", [(41, 6), (42, 6), (43, 6), (41, 100)])
+@pytest.mark.parametrize("seed,max_len", [(41, 6), (42, 6), (43, 6), (41, 100),
+                                          *((1000 + s, 6 if s % 2 == 0 else 100) for s in _FUZZ)])
 def test_random_faults_match_the_oracle(seed, max_len):
     """Seeded fault injection over ragged requests: NaN, +inf and -inf logits (a few, or a whole row), draft
     tokens outside [0, V), uniforms that are NaN, negative or >= 1; greedy, rejection and sample-then-match.
@@ -519,7 +528,7 @@ def test_tree_edge_cases():
                 assert g["status"][3] & oracle.ST_BAD_PARENT
 
 
-@pytest.mark.parametrize("seed", [51, 52])
+@pytest.mark.parametrize("seed", [51, 52, *(1000 + s for s in _FUZZ)])
 def test_random_tree_faults_match_the_oracle(seed):
     """Seeded fault injection on trees of 12 nodes: NaN, +inf and -inf logits (a few, or a whole row), node
     tokens outside [0, V), parents that do not precede their node, uniforms that are NaN or outside [0, 1);
@@ -564,7 +573,7 @@ def test_random_tree_faults_match_the_oracle(seed):
         compare_tree(tw, mode, oracle_tree(tw, mode), run_tree(tw, mode))
 
 
-@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("seed", [*range(6), *_FUZZ])
 def test_random_tree_shapes_match_the_oracle(seed):
     """Seeded random tree batches across the launch paths (one-workgroup walks, per-request scans, draw
     workgroup counts): 1..200 trees of 1..100 nodes (parents uniform over the earlier nodes, each token the
