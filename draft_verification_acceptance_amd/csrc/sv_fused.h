@@ -73,6 +73,7 @@ __device__ void fused_commit(const VerifyParams& p) {
   __shared__ int64_t f_vs[WIN];    // verify_slots of the window rows
   __shared__ int32_t f_node[TREE ? WIN : 1];        // trees: published path entries of the window rows
   __shared__ uint32_t f_bits[TREE ? WIN / 32 : 1];  // trees: the tile's accepted nodes, by row
+  __shared__ uint8_t f_acc[TREE ? NT : 1];          // trees of at most 64 nodes: per wave, the accepted flags
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wv = tid / kWave;
@@ -163,7 +164,8 @@ __device__ void fused_commit(const VerifyParams& p) {
     for (int w = 0; w < TW; ++w) tile += f_wsum[w];
     const int n_rows = int((tile >> 32) + uint32_t(tile));
     const bool packed = f_unpacked == 0;
-    if (TREE) {
+    const bool tree_lanes = TREE && p.L <= kWave;   // trees of at most 64 nodes: a lane per node, below
+    if (TREE && !tree_lanes) {
       // the accepted path entries of the tile's requests as bits, by the tile row of the node they name
       for (int i = tid; i < n_rows; i += NT) {
         const int q = i / p.L;
@@ -183,7 +185,44 @@ __device__ void fused_commit(const VerifyParams& p) {
       }
       __syncthreads();
     }
-    for (int i = tid; i < n_rows; i += NT) {
+    if (tree_lanes) {
+      // A request per segment of Lp lanes (Lp the smallest power of two >= L), a lane per node: the lanes
+      // holding path entries flag the nodes they name in the wave's slice of f_acc (distinct nodes, so no
+      // atomics; one wave's LDS operations complete in order), each lane reads its own node's flag, and a
+      // ballot of those flags gives each accepted node its place on the path (the accepted nodes below it)
+      // and each other node its place among the evicted ones. No bitmap over the tile, no division.
+      constexpr int NW = NT / kWave;
+      const int Lp = 1 << (32 - __clz(p.L - 1));
+      const int G = kWave / Lp;
+      const int seg = lane / Lp;
+      const int k = lane - seg * Lp;
+      const uint64_t seg_below = lanes_below(lane) & ~lanes_below(seg * Lp);   // this segment's lanes below
+      uint8_t* acc = f_acc + wv * kWave;
+      for (int q0 = wv * G; q0 < nb; q0 += NW * G) {   // uniform in the wave
+        const int q = q0 + seg;
+        const bool on = q < nb && k < p.L;
+        acc[lane] = 0;
+        if (on && k <= f_r[q]) {
+          const int32_t nd = f_node[q * p.L + k];
+          if (nd >= 0 && nd < p.L) acc[seg * Lp + nd] = 1;
+        }
+        __builtin_amdgcn_wave_barrier();
+        const bool hit = on && acc[lane] != 0;
+        const uint64_t hits = __ballot(hit);
+        __builtin_amdgcn_wave_barrier();   // every lane has read its flag before the next request clears them
+        if (on) {
+          const int below = __popcll(hits & seg_below);
+          const int64_t v = f_vs[q * p.L + k];
+          if (hit) {
+            p.src_slots[int64_t(f_co[q]) + below] = v;
+            p.dst_pos[int64_t(f_co[q]) + below] = f_seq[q] + below;
+          } else if (p.evict_slots) {
+            p.evict_slots[int64_t(f_eo[q]) + (k - below)] = v;
+          }
+        }
+      }
+    }
+    for (int i = tid; i < (tree_lanes ? 0 : n_rows); i += NT) {
       const int q = TREE ? i / p.L : fc_owner(f_rows, nb, i);
       const int r0 = TREE ? q * p.L : (q ? f_rows[q - 1] : 0);   // the request's first row in the tile
       const int k = i - r0;
