@@ -222,7 +222,31 @@ __device__ void fused_commit(const VerifyParams& p) {
         }
       }
     }
-    for (int i = tid; i < (tree_lanes ? 0 : n_rows); i += NT) {
+    const bool chain_lanes = !TREE && packed && p.L <= kWave;   // packed chains of at most 64 rows
+    if (chain_lanes) {
+      // A request per segment of Lp lanes, a lane per row: row k of request q sits at the window row after
+      // the requests before it, and it is committed at place k (k <= r) or evicted at place k - r - 1.
+      constexpr int NW = NT / kWave;
+      const int Lp = 1 << (32 - __clz(p.L - 1));
+      const int G = kWave / Lp;
+      const int seg = lane / Lp;
+      const int k = lane - seg * Lp;
+      for (int q0 = wv * G; q0 < nb; q0 += NW * G) {
+        const int q = q0 + seg;
+        if (q >= nb) continue;
+        const int r0 = q ? f_rows[q - 1] : 0;
+        if (k >= f_rows[q] - r0) continue;
+        const int64_t v = f_vs[r0 + k];
+        const int rq = f_r[q];
+        if (k <= rq) {
+          p.src_slots[int64_t(f_co[q]) + k] = v;
+          p.dst_pos[int64_t(f_co[q]) + k] = f_seq[q] + k;
+        } else if (p.evict_slots) {
+          p.evict_slots[int64_t(f_eo[q]) + (k - rq - 1)] = v;
+        }
+      }
+    }
+    for (int i = tid; i < (tree_lanes || chain_lanes ? 0 : n_rows); i += NT) {
       const int q = TREE ? i / p.L : fc_owner(f_rows, nb, i);
       const int r0 = TREE ? q * p.L : (q ? f_rows[q - 1] : 0);   // the request's first row in the tile
       const int k = i - r0;
